@@ -1,0 +1,178 @@
+/*
+ * o1.h -- C ABI of the MI355X (gfx950) streaming Nystrom attention library.
+ *
+ * The operator is the streaming per-GQA-group Nystrom attention of the docs.rs
+ * source page of cortiq_engine/nystrom.rs (cortiq-engine 0.5.71): an exact
+ * window of the last w keys plus `sink` permanent keys, and a landmark far field
+ * sharing one joint denominator (module doc of that page).  This library holds
+ * the state of many independent groups -- n_seq sequences x n_layer layers x
+ * n_kv KV heads, each KV group serving hpk query heads -- in device memory and
+ * advances all of them with one kernel launch per decode step.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are f32, row-major, contiguous, in DEVICE memory owned by the
+ *     caller, unless stated otherwise.  The library never frees them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued on it asynchronously; nothing synchronises with the host.
+ *   - Group index g = (s * n_layer + l) * n_kv + kv; the hpk query heads of a
+ *     group are contiguous (head h of a model belongs to KV group h / hpk, as in
+ *     LayerKvCache::o1_step on the docs.rs LayerKvCache page).
+ *   - Return value 0 (O1_OK) on success, otherwise an O1_E* code; the
+ *     thread-local o1_last_error() then describes the failure.  A failed call
+ *     leaves the state as it was, except O1_EHIP after a launch (state undefined).
+ *   - Calls on one handle must be serialised by the caller (one stream, or
+ *     external ordering).  Distinct handles are independent.
+ */
+#ifndef O1_H
+#define O1_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define O1_ABI_VERSION 1
+
+enum o1_status {
+    O1_OK = 0,
+    O1_EINVAL = 1,       /* bad argument: null pointer, size or setting out of range */
+    O1_ESTATE = 2,       /* call not valid in this state (e.g. step before prefill)  */
+    O1_EEXACT = 3,       /* prompt too short: the exact-only mode is not carried     */
+    O1_ENOMEM = 4,       /* device allocation failed                                 */
+    O1_EHIP = 5,         /* a HIP runtime call or kernel launch failed                */
+    O1_EUNSUPPORTED = 6  /* valid for the method but not compiled into this library  */
+};
+
+/* O1Rect of the nystrom.rs source page: how the indefinite skeleton is
+ * rectified.  AGGREGATE (the page's default) drops a row's far field when its
+ * far denominator is negative; FM clamps the mixing row u = F M at zero. */
+enum o1_rect { O1_RECT_AGGREGATE = 0, O1_RECT_FM = 1 };
+
+/* Geometry of a batch of groups (NystromState::new_group on the nystrom.rs
+ * source page: m >= 4, w >= 1, q_heads >= 1).  Defaults on that page:
+ * m = 32, w = 128, sink = 4, rect = AGGREGATE.
+ * Compiled shapes: d == dv in {64, 128}, hpk in {1, 2, 4, 8}, m <= 64,
+ * sink + w <= 1024; other valid shapes return O1_EUNSUPPORTED. */
+typedef struct o1_config {
+    int32_t n_seq;    /* sequences                         (>= 1) */
+    int32_t n_layer;  /* layers per sequence               (>= 1) */
+    int32_t n_kv;     /* KV heads (groups) per layer       (>= 1) */
+    int32_t hpk;      /* query heads per KV group          (>= 1) */
+    int32_t d;        /* query / key width                 (>= 1) */
+    int32_t dv;       /* value width                       (>= 1) */
+    int32_t m;        /* landmark budget                   (>= 4) */
+    int32_t w;        /* exact window width                (>= 1) */
+    int32_t sink;     /* permanent exact sink keys         (>= 0) */
+    int32_t rect;     /* enum o1_rect                             */
+} o1_config;
+
+typedef struct o1_groups o1_groups; /* opaque; owns every state buffer */
+
+/* Optional replacements for the frozen landmarks and mixing matrix of a
+ * prefill (device pointers, f32; NULL = compute as the page does):
+ *   k_tilde [G][m_eff][d], q_tilde [G][hpk][m_eff][d],
+ *   mu      [G][hpk][m_eff][m_eff]  (row a = key landmark, column b = query
+ *                                    landmark, as NystromHead::step reads it).
+ * A replaced k_tilde / q_tilde also feeds the exp-Gram of a computed mu. */
+typedef struct o1_frozen {
+    const float *k_tilde;
+    const float *q_tilde;
+    const float *mu;
+} o1_frozen;
+
+typedef struct o1_info {
+    int32_t n_groups;     /* G = n_seq * n_layer * n_kv                         */
+    int32_t sealed;       /* 1 after a successful o1_prefill                     */
+    int32_t prompt_len;   /* T of the last prefill                               */
+    int32_t m_eff;        /* clamp(T / 8, 4, m), 0 before prefill                */
+    int64_t steps;        /* decode steps since the last prefill                 */
+    uint64_t state_bytes; /* device bytes of the persistent per-group state      */
+    uint64_t work_bytes;  /* device bytes of prefill work buffers currently held */
+} o1_info;
+
+/* Fields of the device state, for o1_field_bytes / o1_read_field /
+ * o1_write_field.  Shapes use G groups, R = sink + w near rows, m = m_eff.
+ * near_k/near_v rows 0..sink-1 are the sinks, row sink + s is ring slot s. */
+enum o1_field {
+    O1_FIELD_NEAR_K = 0,   /* f32 [G][R][d]                                    */
+    O1_FIELD_NEAR_V = 1,   /* f32 [G][R][dv]                                   */
+    O1_FIELD_K_TILDE = 2,  /* f32 [G][m][d]       key landmarks                */
+    O1_FIELD_Q_TILDE = 3,  /* f32 [G][hpk][m][d]  query landmarks              */
+    O1_FIELD_MU = 4,       /* f32 [G][hpk][m][m]  mixing matrix M              */
+    O1_FIELD_T_HAT = 5,    /* f32 [G][hpk][m][dv] far numerator at e^{-m_max}  */
+    O1_FIELD_Z_HAT = 6,    /* f64 [G][hpk][m]     far denominator at e^{-m_max} */
+    O1_FIELD_M_MAX = 7,    /* f32 [G][hpk][m]     per-landmark running max     */
+    O1_FIELD_WIN_HEAD = 8, /* i32 [G]             ring slot of the oldest key  */
+    O1_FIELD_FAR_LEN = 9,  /* i64 [G][hpk]        keys absorbed per head       */
+    O1_FIELD_LAMBDA = 10,  /* f64 [G][hpk]        ridge used by the pinv       */
+    O1_FIELD_TRIES = 11,   /* i32 [G][hpk]        Cholesky attempt that worked (13 = fallback) */
+    O1_FIELD_COUNT = 12
+};
+
+/* Validate `cfg` and allocate the state of all its groups on the current HIP
+ * device (once; decode never allocates).  *out receives the handle.
+ * Errors: O1_EINVAL (null pointer, m < 4, w < 1, hpk < 1, sink < 0, d or dv
+ * < 1, counts < 1, unknown rect), O1_EUNSUPPORTED, O1_ENOMEM, O1_EHIP. */
+int o1_create_groups(const o1_config *cfg, o1_groups **out);
+
+/* Release every buffer of the handle.  NULL is a no-op.  The caller must make
+ * sure no work using the handle is still pending. */
+void o1_destroy_groups(o1_groups *g);
+
+/* Prefill freeze (NystromState::prefill_group, NystromGroup::prefill_shared and
+ * NystromHead::seal on the nystrom.rs source page) for every group at once:
+ *   q [G][hpk][T][d]   each head's prompt queries
+ *   k [G][T][d]        the group's prompt keys
+ *   v [G][T][dv]       the group's prompt values
+ * Sets the sinks (rows 0..sink-1), the ring (the last w keys, key j in slot
+ * (j - sink) mod w), m_eff = clamp(T/8, 4, m), K~ and each head's Q~ as segment
+ * means (f64 accumulation, stored f32), M = ridge pinv of exp(Q~ K~^T / sqrt d)
+ * in f64 (lambda = 1e-6 mean diag(A^T A), grown tenfold on a failed Cholesky,
+ * up to 12 times), and the far field of keys sink .. T-w-1 (T^, Z^, running
+ * max, far_len = T - sink - w).  `frozen` may be NULL.  Resets any earlier
+ * state of the handle.
+ * Errors: O1_EINVAL (null tensor, T < 1), O1_EEXACT when T <= w + sink + 8
+ * (the page's exact-only mode, which its device path does not carry either),
+ * O1_ENOMEM (work buffers), O1_EHIP. */
+int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int32_t T,
+               const o1_frozen *frozen, void *stream);
+
+/* One decode step (NystromState::step_group on the nystrom.rs source page) for
+ * every group: insert the group's new key/value once, absorb the key leaving
+ * the window into every head's far field, and write every head's output.
+ *   q   [G][hpk][d]    queries of the new position
+ *   k   [G][d], v [G][dv]  the new key / value
+ *   out [G][hpk][dv]   outputs (may not alias the inputs)
+ * No allocation, no host synchronisation; one kernel launch.
+ * Errors: O1_EINVAL (null tensor), O1_ESTATE (no successful prefill), O1_EHIP. */
+int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float *out,
+            void *stream);
+
+/* Host-side facts about the handle; no device work. Errors: O1_EINVAL. */
+int o1_get_info(const o1_groups *g, o1_info *info);
+
+/* Bytes of one state field at the current m_eff (see enum o1_field).
+ * Errors: O1_EINVAL (unknown field, null pointer), O1_ESTATE (landmark-shaped
+ * fields before a prefill). */
+int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes);
+
+/* Copy a whole state field to `dst` / from `src` (host or device memory;
+ * `bytes` must equal o1_field_bytes), enqueued on `stream`.  For tests and
+ * state transfer; the decode path never needs them.  Writing requires a
+ * sealed handle.  Errors: O1_EINVAL, O1_ESTATE, O1_EHIP. */
+int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, void *stream);
+int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, void *stream);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char *o1_last_error(void);
+
+/* O1_ABI_VERSION of the library. */
+int o1_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* O1_H */

@@ -1,0 +1,279 @@
+"""Streaming Nystrom attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``lib/libo1.so`` (declared in
+``include/o1.h``).  Every step of the prefill and the decode runs in the HIP
+kernels of that library; this module only checks and marshals arguments
+(PyTorch supplies device memory and streams).  There is no CPU fallback: when
+the library is missing or cannot be loaded, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libo1.so")
+
+O1_OK, O1_EINVAL, O1_ESTATE, O1_EEXACT, O1_ENOMEM, O1_EHIP, O1_EUNSUPPORTED = range(7)
+RECT_AGGREGATE, RECT_FM = 0, 1
+(FIELD_NEAR_K, FIELD_NEAR_V, FIELD_K_TILDE, FIELD_Q_TILDE, FIELD_MU, FIELD_T_HAT, FIELD_Z_HAT,
+ FIELD_M_MAX, FIELD_WIN_HEAD, FIELD_FAR_LEN, FIELD_LAMBDA, FIELD_TRIES) = range(12)
+
+_STATUS_NAMES = {0: "O1_OK", 1: "O1_EINVAL", 2: "O1_ESTATE", 3: "O1_EEXACT", 4: "O1_ENOMEM",
+                 5: "O1_EHIP", 6: "O1_EUNSUPPORTED"}
+
+
+class O1Error(RuntimeError):
+    """A nonzero status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class o1_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_seq", "n_layer", "n_kv", "hpk", "d", "dv", "m", "w", "sink", "rect")]
+
+
+class o1_frozen(ctypes.Structure):
+    _fields_ = [("k_tilde", ctypes.c_void_p), ("q_tilde", ctypes.c_void_p), ("mu", ctypes.c_void_p)]
+
+
+class o1_info(ctypes.Structure):
+    _fields_ = [("n_groups", ctypes.c_int32), ("sealed", ctypes.c_int32),
+                ("prompt_len", ctypes.c_int32), ("m_eff", ctypes.c_int32),
+                ("steps", ctypes.c_int64), ("state_bytes", ctypes.c_uint64),
+                ("work_bytes", ctypes.c_uint64)]
+
+
+EXPORTS = ("o1_create_groups", "o1_destroy_groups", "o1_prefill", "o1_step", "o1_get_info",
+           "o1_field_bytes", "o1_read_field", "o1_write_field", "o1_last_error",
+           "o1_abi_version")
+
+_lib = None
+
+
+def lib():
+    """Load ``libo1.so``; raises ImportError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m streaming_nystr_attention_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    L.o1_create_groups.restype = ctypes.c_int
+    L.o1_create_groups.argtypes = [ctypes.POINTER(o1_config), ctypes.POINTER(vp)]
+    L.o1_destroy_groups.restype = None
+    L.o1_destroy_groups.argtypes = [vp]
+    L.o1_prefill.restype = ctypes.c_int
+    L.o1_prefill.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(o1_frozen), vp]
+    L.o1_step.restype = ctypes.c_int
+    L.o1_step.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.o1_get_info.restype = ctypes.c_int
+    L.o1_get_info.argtypes = [vp, ctypes.POINTER(o1_info)]
+    L.o1_field_bytes.restype = ctypes.c_int
+    L.o1_field_bytes.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.o1_read_field.restype = ctypes.c_int
+    L.o1_read_field.argtypes = [vp, i32, vp, ctypes.c_size_t, vp]
+    L.o1_write_field.restype = ctypes.c_int
+    L.o1_write_field.argtypes = [vp, i32, vp, ctypes.c_size_t, vp]
+    L.o1_last_error.restype = ctypes.c_char_p
+    L.o1_last_error.argtypes = []
+    L.o1_abi_version.restype = ctypes.c_int
+    L.o1_abi_version.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != O1_OK:
+        raise O1Error(rc, lib().o1_last_error().decode(errors="replace"))
+
+
+def _stream_handle(stream):
+    """hipStream_t of a torch stream (None = torch's current stream)."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name, numel, dtype_name="float32"):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if str(t.dtype) != f"torch.{dtype_name}":
+        raise TypeError(f"{name}: expected {dtype_name}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---- the C ABI, one Python function per entry point ----------------------
+
+def o1_create_groups(cfg: "Config"):
+    c = o1_config(cfg.n_seq, cfg.n_layer, cfg.n_kv, cfg.hpk, cfg.d, cfg.dv, cfg.m, cfg.w,
+                  cfg.sink, cfg.rect)
+    h = ctypes.c_void_p()
+    _check(lib().o1_create_groups(ctypes.byref(c), ctypes.byref(h)))
+    return h
+
+
+def o1_destroy_groups(handle):
+    lib().o1_destroy_groups(handle)
+
+
+def o1_prefill(handle, cfg, q, k, v, T: int, frozen=None, stream=None):
+    G = cfg.groups
+    qp = _dev_ptr(q, "q", G * cfg.hpk * T * cfg.d)
+    kp = _dev_ptr(k, "k", G * T * cfg.d)
+    vp = _dev_ptr(v, "v", G * T * cfg.dv)
+    fz = None
+    if frozen is not None:
+        kt, qt, mu = frozen
+        m = cfg.m_eff(T)
+        fz = o1_frozen(
+            None if kt is None else _dev_ptr(kt, "frozen k_tilde", G * m * cfg.d),
+            None if qt is None else _dev_ptr(qt, "frozen q_tilde", G * cfg.hpk * m * cfg.d),
+            None if mu is None else _dev_ptr(mu, "frozen mu", G * cfg.hpk * m * m))
+    _check(lib().o1_prefill(handle, qp, kp, vp, T, None if fz is None else ctypes.byref(fz),
+                            _stream_handle(stream)))
+
+
+def o1_step(handle, cfg, q, k, v, out, stream=None):
+    G = cfg.groups
+    _check(lib().o1_step(handle, _dev_ptr(q, "q", G * cfg.hpk * cfg.d),
+                         _dev_ptr(k, "k", G * cfg.d), _dev_ptr(v, "v", G * cfg.dv),
+                         _dev_ptr(out, "out", G * cfg.hpk * cfg.dv), _stream_handle(stream)))
+
+
+def o1_get_info(handle) -> o1_info:
+    info = o1_info()
+    _check(lib().o1_get_info(handle, ctypes.byref(info)))
+    return info
+
+
+def o1_field_bytes(handle, field: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().o1_field_bytes(handle, field, ctypes.byref(n)))
+    return n.value
+
+
+def o1_read_field(handle, field: int, dst, stream=None):
+    """Copy a state field into the tensor `dst` (device or host memory)."""
+    nbytes = dst.numel() * dst.element_size()
+    if not dst.is_contiguous():
+        raise ValueError("dst must be contiguous")
+    _check(lib().o1_read_field(handle, field, ctypes.c_void_p(dst.data_ptr()), nbytes,
+                               _stream_handle(stream)))
+
+
+def o1_write_field(handle, field: int, src, stream=None):
+    nbytes = src.numel() * src.element_size()
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    _check(lib().o1_write_field(handle, field, ctypes.c_void_p(src.data_ptr()), nbytes,
+                                _stream_handle(stream)))
+
+
+def o1_last_error() -> str:
+    return lib().o1_last_error().decode(errors="replace")
+
+
+def o1_abi_version() -> int:
+    return lib().o1_abi_version()
+
+
+# ---- convenience wrapper -------------------------------------------------
+
+@dataclass(frozen=True)
+class Config:
+    n_seq: int = 1
+    n_layer: int = 1
+    n_kv: int = 1
+    hpk: int = 1
+    d: int = 128
+    dv: int = 128
+    m: int = 32
+    w: int = 128
+    sink: int = 4
+    rect: int = RECT_AGGREGATE
+
+    @property
+    def groups(self) -> int:
+        return self.n_seq * self.n_layer * self.n_kv
+
+    @property
+    def rows(self) -> int:
+        return self.sink + self.w
+
+    def m_eff(self, T: int) -> int:
+        return max(4, min(T // 8, self.m))
+
+
+_FIELD_DTYPES = {FIELD_Z_HAT: "float64", FIELD_LAMBDA: "float64", FIELD_WIN_HEAD: "int32",
+                 FIELD_FAR_LEN: "int64", FIELD_TRIES: "int32"}
+
+
+class O1Groups:
+    """Owns one library handle: the state of cfg.groups independent groups."""
+
+    def __init__(self, cfg: Config):
+        self.cfg = cfg
+        self._h = o1_create_groups(cfg)
+        self.T = None
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            o1_destroy_groups(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def prefill(self, q, k, v, frozen=None, stream=None):
+        """q [G][hpk][T][d], k [G][T][d], v [G][T][dv]; frozen = (k_tilde, q_tilde, mu) or None."""
+        T = k.shape[-2]
+        o1_prefill(self._h, self.cfg, q, k, v, T, frozen, stream)
+        self.T = T
+
+    def step(self, q, k, v, out, stream=None):
+        """q [G][hpk][d], k [G][d], v [G][dv] -> out [G][hpk][dv]."""
+        o1_step(self._h, self.cfg, q, k, v, out, stream)
+
+    def info(self) -> o1_info:
+        return o1_get_info(self._h)
+
+    def read(self, field: int, device="cpu", stream=None):
+        """Whole state field as a tensor (synchronises the stream)."""
+        import torch
+
+        dtype = getattr(torch, _FIELD_DTYPES.get(field, "float32"))
+        n = o1_field_bytes(self._h, field) // torch.tensor([], dtype=dtype).element_size()
+        dst = torch.empty(n, dtype=dtype, device=device,
+                          pin_memory=(device == "cpu" and torch.cuda.is_available()))
+        o1_read_field(self._h, field, dst, stream)
+        (stream or torch.cuda.current_stream()).synchronize()
+        return dst
+
+    def write(self, field: int, src, stream=None):
+        o1_write_field(self._h, field, src, stream)

@@ -1,0 +1,319 @@
+// Host side of the C ABI declared in include/o1.h: argument validation, state
+// allocation (once, at o1_create_groups), stream-ordered launches, and field
+// copies for tests.  No entry point synchronises with the host.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/o1.h"
+#include "o1_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return O1_OK;
+}
+
+}  // namespace
+
+struct o1_groups {
+    o1_config cfg;
+    int device;
+    int G, R;
+    int sealed;
+    int T;
+    int64_t steps;
+    o1::DevState st;   // m_eff and pointers
+    double *lm64;      // prefill work buffer
+    size_t lm64_bytes;
+    size_t state_bytes;
+};
+
+namespace {
+
+struct FieldInfo {
+    void *ptr;
+    size_t bytes;
+};
+
+FieldInfo field_info(const o1_groups *g, int32_t field)
+{
+    const o1::DevState &s = g->st;
+    const size_t G = (size_t)g->G, H = (size_t)s.hpk, m = (size_t)s.m;
+    switch (field) {
+    case O1_FIELD_NEAR_K: return {s.near_k, G * g->R * s.d * sizeof(float)};
+    case O1_FIELD_NEAR_V: return {s.near_v, G * g->R * s.dv * sizeof(float)};
+    case O1_FIELD_K_TILDE: return {s.k_tilde, G * m * s.d * sizeof(float)};
+    case O1_FIELD_Q_TILDE: return {s.q_tilde, G * H * m * s.d * sizeof(float)};
+    case O1_FIELD_MU: return {s.mu, G * H * m * m * sizeof(float)};
+    case O1_FIELD_T_HAT: return {s.t_hat, G * H * m * s.dv * sizeof(float)};
+    case O1_FIELD_Z_HAT: return {s.z_hat, G * H * m * sizeof(double)};
+    case O1_FIELD_M_MAX: return {s.m_max, G * H * m * sizeof(float)};
+    case O1_FIELD_WIN_HEAD: return {s.win_head, G * sizeof(int32_t)};
+    case O1_FIELD_FAR_LEN: return {s.far_len, G * H * sizeof(int64_t)};
+    case O1_FIELD_LAMBDA: return {s.lambda, G * H * sizeof(double)};
+    case O1_FIELD_TRIES: return {s.tries, G * H * sizeof(int32_t)};
+    default: return {nullptr, 0};
+    }
+}
+
+bool landmark_shaped(int32_t field)
+{
+    return field == O1_FIELD_K_TILDE || field == O1_FIELD_Q_TILDE || field == O1_FIELD_MU ||
+           field == O1_FIELD_T_HAT || field == O1_FIELD_Z_HAT || field == O1_FIELD_M_MAX;
+}
+
+void free_state(o1_groups *g)
+{
+    o1::DevState &s = g->st;
+    void *ptrs[] = {s.near_k, s.near_v, s.k_tilde, s.q_tilde, s.mu, s.t_hat, s.z_hat,
+                    s.m_max, s.win_head, s.far_len, s.lambda, s.tries, g->lm64};
+    for (void *p : ptrs)
+        if (p) (void)hipFree(p);
+}
+
+int use_device(const o1_groups *g)
+{
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(O1_EHIP, "hipGetDevice failed");
+    if (cur != g->device && hipSetDevice(g->device) != hipSuccess)
+        return fail(O1_EHIP, "hipSetDevice(%d) failed", g->device);
+    return O1_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int o1_abi_version(void) { return O1_ABI_VERSION; }
+
+const char *o1_last_error(void) { return g_last_error.c_str(); }
+
+int o1_create_groups(const o1_config *cfg, o1_groups **out)
+{
+    if (!cfg || !out) return fail(O1_EINVAL, "o1_create_groups: null argument");
+    *out = nullptr;
+    const o1_config c = *cfg;
+    if (c.n_seq < 1 || c.n_layer < 1 || c.n_kv < 1)
+        return fail(O1_EINVAL, "group counts must be >= 1 (n_seq=%d n_layer=%d n_kv=%d)", c.n_seq,
+                    c.n_layer, c.n_kv);
+    if (c.m < 4) return fail(O1_EINVAL, "landmark budget must be at least 4 (m=%d)", c.m);
+    if (c.w < 1) return fail(O1_EINVAL, "window must hold at least one key (w=%d)", c.w);
+    if (c.hpk < 1) return fail(O1_EINVAL, "a GQA group needs at least one query head (hpk=%d)", c.hpk);
+    if (c.sink < 0) return fail(O1_EINVAL, "sink must be >= 0 (sink=%d)", c.sink);
+    if (c.d < 1 || c.dv < 1) return fail(O1_EINVAL, "d and dv must be >= 1 (d=%d dv=%d)", c.d, c.dv);
+    if (c.rect != O1_RECT_AGGREGATE && c.rect != O1_RECT_FM)
+        return fail(O1_EINVAL, "unknown rectifier %d", c.rect);
+    const long long G = (long long)c.n_seq * c.n_layer * c.n_kv;
+    if (G > (1LL << 30)) return fail(O1_EINVAL, "too many groups (%lld)", G);
+    const int R = c.sink + c.w;
+    const int m_cap = c.m < o1::kMaxLandmarks ? c.m : o1::kMaxLandmarks;
+    if (!o1::decode_supported(c.d, c.dv, c.hpk, 4, R) || c.m > o1::kMaxLandmarks)
+        return fail(O1_EUNSUPPORTED,
+                    "shape not compiled: needs d == dv in {64,128}, hpk in {1,2,4,8}, m <= %d, "
+                    "sink + w <= 1024 with hpk*(sink+w) <= 4096 (got d=%d dv=%d hpk=%d m=%d sink+w=%d)",
+                    o1::kMaxLandmarks, c.d, c.dv, c.hpk, c.m, R);
+
+    o1_groups *g = new o1_groups();
+    memset(&g->st, 0, sizeof g->st);
+    g->cfg = c;
+    g->G = (int)G;
+    g->R = R;
+    g->lm64 = nullptr;
+    g->lm64_bytes = 0;
+    if (hipGetDevice(&g->device) != hipSuccess) {
+        delete g;
+        return fail(O1_EHIP, "hipGetDevice failed");
+    }
+    o1::DevState &s = g->st;
+    s.G = (int)G;
+    s.hpk = c.hpk;
+    s.d = c.d;
+    s.dv = c.dv;
+    s.w = c.w;
+    s.sink = c.sink;
+    s.R = R;
+    s.rect = c.rect;
+    s.m = 0;
+    s.scale = 1.0f / sqrtf((float)c.d);
+
+    const size_t Gs = (size_t)G, H = (size_t)c.hpk, M = (size_t)m_cap;
+    struct Alloc {
+        void **p;
+        size_t bytes;
+    } allocs[] = {
+        {(void **)&s.near_k, Gs * R * c.d * sizeof(float)},
+        {(void **)&s.near_v, Gs * R * c.dv * sizeof(float)},
+        {(void **)&s.k_tilde, Gs * M * c.d * sizeof(float)},
+        {(void **)&s.q_tilde, Gs * H * M * c.d * sizeof(float)},
+        {(void **)&s.mu, Gs * H * M * M * sizeof(float)},
+        {(void **)&s.t_hat, Gs * H * M * c.dv * sizeof(float)},
+        {(void **)&s.z_hat, Gs * H * M * sizeof(double)},
+        {(void **)&s.m_max, Gs * H * M * sizeof(float)},
+        {(void **)&s.win_head, Gs * sizeof(int32_t)},
+        {(void **)&s.far_len, Gs * H * sizeof(int64_t)},
+        {(void **)&s.lambda, Gs * H * sizeof(double)},
+        {(void **)&s.tries, Gs * H * sizeof(int32_t)},
+    };
+    size_t total = 0;
+    for (auto &a : allocs) {
+        if (hipMalloc(a.p, a.bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            free_state(g);
+            delete g;
+            return fail(O1_ENOMEM, "hipMalloc of %zu bytes failed", a.bytes);
+        }
+        total += a.bytes;
+    }
+    g->state_bytes = total;
+    *out = g;
+    return ok();
+}
+
+void o1_destroy_groups(o1_groups *g)
+{
+    if (!g) return;
+    (void)use_device(g);
+    free_state(g);
+    delete g;
+}
+
+int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int32_t T,
+               const o1_frozen *frozen, void *stream)
+{
+    if (!g || !q || !k || !v) return fail(O1_EINVAL, "o1_prefill: null argument");
+    const o1_config &c = g->cfg;
+    if (T < 1) return fail(O1_EINVAL, "prompt length must be >= 1 (T=%d)", T);
+    if ((long long)T <= (long long)c.w + c.sink + o1::kExactSlack)
+        return fail(O1_EEXACT,
+                    "prompt of %d tokens is in the exact-only mode (T <= w + sink + %d = %d), "
+                    "which the device path does not carry",
+                    T, o1::kExactSlack, c.w + c.sink + o1::kExactSlack);
+    if ((long long)T * g->G * c.hpk * c.d > (1LL << 40))
+        return fail(O1_EINVAL, "prompt too large (T=%d)", T);
+    int rc = use_device(g);
+    if (rc) return rc;
+    int m_eff = T / 8;
+    if (m_eff < 4) m_eff = 4;
+    if (m_eff > c.m) m_eff = c.m;
+
+    const size_t need = sizeof(double) * (size_t)g->G * (1 + c.hpk) * m_eff * c.d;
+    if (need > g->lm64_bytes) {
+        if (g->lm64) {
+            if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+                return fail(O1_EHIP, "hipStreamSynchronize failed");
+            (void)hipFree(g->lm64);
+            g->lm64 = nullptr;
+            g->lm64_bytes = 0;
+        }
+        if (hipMalloc((void **)&g->lm64, need) != hipSuccess) {
+            (void)hipGetLastError();
+            g->lm64 = nullptr;
+            return fail(O1_ENOMEM, "hipMalloc of %zu bytes of prefill work space failed", need);
+        }
+        g->lm64_bytes = need;
+    }
+
+    g->sealed = 0;
+    g->st.m = m_eff;
+    o1::PrefillIO io;
+    io.q = q;
+    io.k = k;
+    io.v = v;
+    io.T = T;
+    io.fz_kt = frozen ? frozen->k_tilde : nullptr;
+    io.fz_qt = frozen ? frozen->q_tilde : nullptr;
+    io.fz_mu = frozen ? frozen->mu : nullptr;
+    io.lm64 = g->lm64;
+    hipError_t err = o1::launch_prefill(g->st, io, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(O1_EHIP, "prefill launch failed: %s", hipGetErrorString(err));
+    g->T = T;
+    g->steps = 0;
+    g->sealed = 1;
+    return ok();
+}
+
+int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float *out, void *stream)
+{
+    if (!g || !q || !k || !v || !out) return fail(O1_EINVAL, "o1_step: null argument");
+    if (!g->sealed) return fail(O1_ESTATE, "o1_step before a successful o1_prefill");
+    int rc = use_device(g);
+    if (rc) return rc;
+    o1::DecodeIO io{q, k, v, out};
+    hipError_t err = o1::launch_decode(g->st, io, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(O1_EHIP, "decode launch failed: %s", hipGetErrorString(err));
+    g->steps += 1;
+    return ok();
+}
+
+int o1_get_info(const o1_groups *g, o1_info *info)
+{
+    if (!g || !info) return fail(O1_EINVAL, "o1_get_info: null argument");
+    info->n_groups = g->G;
+    info->sealed = g->sealed;
+    info->prompt_len = g->sealed ? g->T : 0;
+    info->m_eff = g->sealed ? g->st.m : 0;
+    info->steps = g->steps;
+    info->state_bytes = g->state_bytes;
+    info->work_bytes = g->lm64_bytes;
+    return ok();
+}
+
+int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes)
+{
+    if (!g || !bytes) return fail(O1_EINVAL, "o1_field_bytes: null argument");
+    if (field < 0 || field >= O1_FIELD_COUNT) return fail(O1_EINVAL, "unknown field %d", field);
+    if (landmark_shaped(field) && !g->sealed)
+        return fail(O1_ESTATE, "field %d has no shape before a prefill", field);
+    *bytes = field_info(g, field).bytes;
+    return ok();
+}
+
+int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, void *stream)
+{
+    size_t want = 0;
+    int rc = o1_field_bytes(g, field, &want);
+    if (rc) return rc;
+    if (!dst) return fail(O1_EINVAL, "o1_read_field: null destination");
+    if (bytes != want) return fail(O1_EINVAL, "field %d holds %zu bytes, not %zu", field, want, bytes);
+    if ((rc = use_device(g))) return rc;
+    hipError_t err = hipMemcpyAsync(dst, field_info(g, field).ptr, bytes, hipMemcpyDefault,
+                                    (hipStream_t)stream);
+    if (err != hipSuccess) return fail(O1_EHIP, "hipMemcpyAsync failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, void *stream)
+{
+    if (g && !g->sealed) return fail(O1_ESTATE, "o1_write_field before a successful o1_prefill");
+    size_t want = 0;
+    int rc = o1_field_bytes(g, field, &want);
+    if (rc) return rc;
+    if (!src) return fail(O1_EINVAL, "o1_write_field: null source");
+    if (bytes != want) return fail(O1_EINVAL, "field %d holds %zu bytes, not %zu", field, want, bytes);
+    if ((rc = use_device(g))) return rc;
+    hipError_t err = hipMemcpyAsync(field_info(g, field).ptr, src, bytes, hipMemcpyDefault,
+                                    (hipStream_t)stream);
+    if (err != hipSuccess) return fail(O1_EHIP, "hipMemcpyAsync failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,340 @@
+// Prefill freeze of streaming Nystrom attention for every group at once:
+// NystromGroup::prefill_shared, NystromHead::seal, ridge_pinv / cholesky and
+// the replay of NystromState::prefill_group on the nystrom.rs source page.
+//
+//   landmarks_kernel   grid (G, 1 + hpk): segment means of the keys (K~) and of
+//                      each head's queries (Q~), f64 accumulation in row order,
+//                      stored f32 (state) and f64 (work, for the exp-Gram).
+//   scatter_kernel     grid G: sinks (prompt rows 0..sink-1) and the ring (the
+//                      last w prompt keys, key j in slot (j - sink) mod w), the
+//                      ring head and far_len after the replay.
+//   gram_pinv_kernel   grid G * hpk: A = exp(Q~ K~^T * scale) in f64, G = A^T A,
+//                      lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
+//                      G + lambda I in LDS (lambda x10 on a failed pivot, up to 12
+//                      attempts, then diag(1/mean diag)), M = (G + lambda I)^-1 A^T.
+//   far_replay_kernel  grid G * hpk: the far field of keys sink .. T-w-1, i.e. the
+//                      state the page's sequential replay through far_insert
+//                      reaches, computed in tiles with an online per-landmark
+//                      max: m_max_i = max_j l_ij, Z^_i = sum_j e^{l_ij - m_max_i},
+//                      T^_i = sum_j e^{l_ij - m_max_i} v_j (f64 accumulation).
+#include <float.h>
+
+#include "o1_internal.h"
+
+namespace o1 {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, PrefillIO io)
+{
+    const int g = blockIdx.x, src = blockIdx.y;  // src 0 = keys, 1 + h = head h
+    const int d = s.d, m = s.m, T = io.T, H = s.hpk;
+    const float *x;
+    float *dst32;
+    const float *fz;
+    if (src == 0) {
+        x = io.k + (size_t)g * T * d;
+        dst32 = s.k_tilde + (size_t)g * m * d;
+        fz = io.fz_kt ? io.fz_kt + (size_t)g * m * d : nullptr;
+    } else {
+        const size_t gh = (size_t)g * H + (src - 1);
+        x = io.q + gh * T * d;
+        dst32 = s.q_tilde + gh * m * d;
+        fz = io.fz_qt ? io.fz_qt + gh * m * d : nullptr;
+    }
+    double *dst64 = io.lm64 + ((size_t)g * (1 + H) + src) * m * d;
+    for (int t = threadIdx.x; t < m * d; t += kThreads) {
+        if (fz) {
+            const float v = fz[t];
+            dst32[t] = v;
+            dst64[t] = (double)v;
+            continue;
+        }
+        const int a = t / d, c = t - a * d;
+        const long lo = (long)a * T / m, hi = (long)(a + 1) * T / m;
+        double acc = 0.0;
+        for (long j = lo; j < hi; ++j) acc += (double)x[(size_t)j * d + c];
+        const double mean = acc * (1.0 / (double)(hi - lo));
+        dst64[t] = mean;
+        dst32[t] = (float)mean;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO io)
+{
+    const int g = blockIdx.x;
+    const int S = s.sink, w = s.w, R = s.R, T = io.T;
+    const int ck = s.d / 4, cv = s.dv / 4;
+    const float4 *kin = reinterpret_cast<const float4 *>(io.k) + (size_t)g * T * ck;
+    const float4 *vin = reinterpret_cast<const float4 *>(io.v) + (size_t)g * T * cv;
+    float4 *nk = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * R * ck;
+    float4 *nv = reinterpret_cast<float4 *>(s.near_v) + (size_t)g * R * cv;
+    const int base = T - w;          // first prompt key still in the window
+    const int shift = base - S;      // >= 9 in skeleton mode
+    for (int t = threadIdx.x; t < R * (ck + cv); t += kThreads) {
+        const int r = t / (ck + cv), c = t - r * (ck + cv);
+        int j;
+        if (r < S) {
+            j = r;
+        } else {
+            const int slot = r - S;
+            j = base + ((slot - shift) % w + w) % w;  // (j - S) mod w == slot
+        }
+        if (c < ck) nk[(size_t)r * ck + c] = kin[(size_t)j * ck + c];
+        else nv[(size_t)r * cv + (c - ck)] = vin[(size_t)j * cv + (c - ck)];
+    }
+    const int evictions = T - S - w;
+    if (threadIdx.x == 0) s.win_head[g] = evictions % w;
+    for (int h = threadIdx.x; h < s.hpk; h += kThreads) s.far_len[(size_t)g * s.hpk + h] = evictions;
+}
+
+// One block per (group, head).  Dynamic LDS: A and L, each [m][m + 1] f64.
+__global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, PrefillIO io, double ridge_rel)
+{
+    const int gh = blockIdx.x, H = s.hpk, g = gh / H, h = gh - g * H;
+    const int m = s.m, d = s.d, ld = m + 1, tid = threadIdx.x;
+    extern __shared__ double lds[];
+    double *A = lds;
+    double *L = lds + (size_t)m * ld;
+    __shared__ double mean_diag_s;
+    __shared__ int fail_s;
+
+    const double *kt = io.lm64 + ((size_t)g * (1 + H)) * m * d;
+    const double *qt = io.lm64 + ((size_t)g * (1 + H) + 1 + h) * m * d;
+    const double sc = (double)s.scale;
+
+    // exp-Gram: A[i][j] = exp(q~_i . k~_j * scale), contraction in index order
+    for (int t = tid; t < m * m; t += kThreads) {
+        const int i = t / m, j = t - i * m;
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc = fma(qt[(size_t)i * d + c], kt[(size_t)j * d + c], acc);
+        A[i * ld + j] = exp(acc * sc);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double md = 0.0;
+        for (int i = 0; i < m; ++i) {
+            double acc = 0.0;
+            for (int k = 0; k < m; ++k) acc = fma(A[k * ld + i], A[k * ld + i], acc);
+            md += acc;
+        }
+        mean_diag_s = md / (double)m;
+    }
+    __syncthreads();
+    const double floor_diag = mean_diag_s > DBL_MIN ? mean_diag_s : DBL_MIN;
+    double lambda = ridge_rel * floor_diag;
+    int result = kRidgeTries + 1;
+
+    for (int attempt = 1; attempt <= kRidgeTries; ++attempt) {
+        // L <- A^T A + lambda I
+        for (int t = tid; t < m * m; t += kThreads) {
+            const int i = t / m, j = t - i * m;
+            double acc = 0.0;
+            for (int k = 0; k < m; ++k) acc = fma(A[k * ld + i], A[k * ld + j], acc);
+            L[i * ld + j] = acc + (i == j ? lambda : 0.0);
+        }
+        __syncthreads();
+        // Cholesky, one column at a time: pivot, then the column below it.
+        for (int j = 0; j < m; ++j) {
+            if (tid == 0) {
+                double p = L[j * ld + j];
+                for (int k = 0; k < j; ++k) p -= L[j * ld + k] * L[j * ld + k];
+                const int bad = !(p > 0.0) || !isfinite(p);
+                if (!bad) L[j * ld + j] = sqrt(p);
+                fail_s = bad;
+            }
+            __syncthreads();
+            if (fail_s) break;
+            for (int i = j + 1 + tid; i < m; i += kThreads) {
+                double v = L[i * ld + j];
+                for (int k = 0; k < j; ++k) v -= L[i * ld + k] * L[j * ld + k];
+                L[i * ld + j] = v / L[j * ld + j];
+            }
+            __syncthreads();
+        }
+        const int failed = fail_s;
+        __syncthreads();
+        if (!failed) {
+            result = attempt;
+            break;
+        }
+        lambda *= 10.0;
+    }
+
+    float *mu = s.mu + (size_t)gh * m * m;
+    if (result <= kRidgeTries) {
+        // Column b of M solves (L L^T) x = (row b of A); done in place in row b.
+        for (int b = tid; b < m; b += kThreads) {
+            double *x = A + (size_t)b * ld;
+            for (int i = 0; i < m; ++i) {
+                double v = x[i];
+                for (int k = 0; k < i; ++k) v -= L[i * ld + k] * x[k];
+                x[i] = v / L[i * ld + i];
+            }
+            for (int i = m - 1; i >= 0; --i) {
+                double v = x[i];
+                for (int k = i + 1; k < m; ++k) v -= L[k * ld + i] * x[k];
+                x[i] = v / L[i * ld + i];
+            }
+        }
+        __syncthreads();
+        for (int t = tid; t < m * m; t += kThreads) {
+            const int a = t / m, b = t - a * m;
+            mu[t] = (float)A[(size_t)b * ld + a];
+        }
+    } else {
+        for (int t = tid; t < m * m; t += kThreads) {
+            const int a = t / m, b = t - a * m;
+            mu[t] = (a == b) ? (float)(1.0 / floor_diag) : 0.0f;
+        }
+    }
+    if (tid == 0) {
+        s.lambda[gh] = lambda;
+        s.tries[gh] = result;
+    }
+}
+
+constexpr int kTile = 16;  // far keys per tile
+
+// One block per (group, head).  Static LDS: Q~ (f32), a key tile, a value tile,
+// the tile's logits / weights, per-landmark running max and rescale.
+__global__ __launch_bounds__(kThreads) void far_replay_kernel(DevState s, PrefillIO io)
+{
+    const int gh = blockIdx.x, H = s.hpk, g = gh / H;
+    const int m = s.m, d = s.d, dv = s.dv, tid = threadIdx.x;
+    const int S = s.sink, T = io.T, nf = T - S - s.w;
+    const double sc = (double)s.scale;
+    const double NEG_INF = -__builtin_inf();
+
+    __shared__ float q_lds[kMaxLandmarks * 128];
+    __shared__ float k_lds[kTile][128 + 1];
+    __shared__ float v_lds[kTile][128];
+    __shared__ double p_lds[kMaxLandmarks][kTile];
+    __shared__ double mx_lds[kMaxLandmarks], fac_lds[kMaxLandmarks], z_lds[kMaxLandmarks];
+
+    const float *qt = s.q_tilde + (size_t)gh * m * d;
+    for (int t = tid; t < m * d; t += kThreads) q_lds[t] = qt[t];
+    if (tid < m) {
+        mx_lds[tid] = NEG_INF;
+        z_lds[tid] = 0.0;
+    }
+    // accumulator entries owned by this thread: t = tid + 256 k over [m][dv]
+    constexpr int kAcc = kMaxLandmarks * 128 / kThreads;
+    double acc[kAcc];
+#pragma unroll
+    for (int k = 0; k < kAcc; ++k) acc[k] = 0.0;
+    __syncthreads();
+
+    const float *K = io.k + ((size_t)g * T + S) * d;
+    const float *V = io.v + ((size_t)g * T + S) * dv;
+    for (int j0 = 0; j0 < nf; j0 += kTile) {
+        const int nt = min(kTile, nf - j0);
+        for (int t = tid; t < kTile * d; t += kThreads) {
+            const int jj = t / d, c = t - jj * d;
+            k_lds[jj][c] = jj < nt ? K[(size_t)(j0 + jj) * d + c] : 0.0f;
+        }
+        for (int t = tid; t < kTile * dv; t += kThreads) {
+            const int jj = t / dv, c = t - jj * dv;
+            v_lds[jj][c] = jj < nt ? V[(size_t)(j0 + jj) * dv + c] : 0.0f;
+        }
+        __syncthreads();
+        // logits of the tile
+        for (int t = tid; t < m * kTile; t += kThreads) {
+            const int i = t / kTile, jj = t - i * kTile;
+            double l = NEG_INF;
+            if (jj < nt) {
+                double a = 0.0;
+                for (int c = 0; c < d; ++c) a = fma((double)q_lds[i * d + c], (double)k_lds[jj][c], a);
+                l = a * sc;
+            }
+            p_lds[i][jj] = l;
+        }
+        __syncthreads();
+        // per-landmark max over the tile and the rescale of earlier mass
+        if (tid < m) {
+            double tmax = NEG_INF;
+            for (int jj = 0; jj < nt; ++jj) tmax = fmax(tmax, p_lds[tid][jj]);
+            const double old = mx_lds[tid];
+            const double nw = fmax(old, tmax);
+            const double f = exp(old - nw);  // 0 on the first tile
+            fac_lds[tid] = f;
+            mx_lds[tid] = nw;
+            double z = z_lds[tid] * f;
+            for (int jj = 0; jj < nt; ++jj) {
+                const double p = exp(p_lds[tid][jj] - nw);
+                p_lds[tid][jj] = p;
+                z += p;
+            }
+            for (int jj = nt; jj < kTile; ++jj) p_lds[tid][jj] = 0.0;
+            z_lds[tid] = z;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kAcc; ++k) {
+            const int t = tid + kThreads * k;
+            if (t < m * dv) {
+                const int i = t / dv, c = t - i * dv;
+                double a = acc[k] * fac_lds[i];
+#pragma unroll
+                for (int jj = 0; jj < kTile; ++jj) a = fma(p_lds[i][jj], (double)v_lds[jj][c], a);
+                acc[k] = a;
+            }
+        }
+        __syncthreads();
+    }
+
+    // Store at the scale of the f32 running max actually kept in the state.
+    if (tid < m) {
+        const float mf = (float)mx_lds[tid];
+        const double corr = exp(mx_lds[tid] - (double)mf);
+        fac_lds[tid] = corr;
+        s.m_max[(size_t)gh * m + tid] = mf;
+        s.z_hat[(size_t)gh * m + tid] = z_lds[tid] * corr;
+    }
+    __syncthreads();
+    float *th = s.t_hat + (size_t)gh * m * dv;
+#pragma unroll
+    for (int k = 0; k < kAcc; ++k) {
+        const int t = tid + kThreads * k;
+        if (t < m * dv) th[t] = (float)(acc[k] * fac_lds[t / dv]);
+    }
+}
+
+__global__ void copy_mu_kernel(DevState s, const float *src)
+{
+    const size_t n = (size_t)s.G * s.hpk * s.m * s.m;
+    for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (size_t)gridDim.x * blockDim.x)
+        s.mu[t] = src[t];
+    const size_t nh = (size_t)s.G * s.hpk;
+    for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < nh; t += (size_t)gridDim.x * blockDim.x) {
+        s.lambda[t] = 0.0;
+        s.tries[t] = 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t stream)
+{
+    if (s.d > 128 || s.dv > 128 || s.m > kMaxLandmarks) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(landmarks_kernel, dim3(s.G, 1 + s.hpk), dim3(kThreads), 0, stream, s, io);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(scatter_kernel, dim3(s.G), dim3(kThreads), 0, stream, s, io);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (io.fz_mu) {
+        hipLaunchKernelGGL(copy_mu_kernel, dim3(1024), dim3(kThreads), 0, stream, s, io.fz_mu);
+    } else {
+        const size_t lds = sizeof(double) * 2 * (size_t)s.m * (s.m + 1);
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gram_pinv_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(gram_pinv_kernel, dim3(s.G * s.hpk), dim3(kThreads), lds, stream, s, io, kRidgeRel);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(far_replay_kernel, dim3(s.G * s.hpk), dim3(kThreads), 0, stream, s, io);
+    return hipGetLastError();
+}
+
+}  // namespace o1

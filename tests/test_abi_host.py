@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/o1.h declares, and rejects invalid arguments before
+touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "o1.h")
+
+
+def _lib():
+    import streaming_nystr_attention_amd as P
+
+    if not os.path.exists(P.LIB_PATH):
+        from streaming_nystr_attention_amd import build
+
+        build.build()
+    return P, P.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(o1_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("o1_create_groups", "o1_prefill", "o1_step", "o1_destroy_groups"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    P, L = _lib()
+    names = declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(P.EXPORTS) == set(names)
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_abi_version():
+    P, L = _lib()
+    assert P.o1_abi_version() == 1
+
+
+def _create(P, L, **kw):
+    base = dict(n_seq=1, n_layer=1, n_kv=1, hpk=1, d=64, dv=64, m=8, w=16, sink=2, rect=0)
+    base.update(kw)
+    cfg = P.o1_config(*[base[f] for f, _ in P.o1_config._fields_])
+    h = ctypes.c_void_p()
+    rc = L.o1_create_groups(ctypes.byref(cfg), ctypes.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=3), 1), (dict(w=0), 1), (dict(hpk=0), 1), (dict(sink=-1), 1), (dict(d=0), 1),
+    (dict(dv=0), 1), (dict(n_seq=0), 1), (dict(n_layer=0), 1), (dict(n_kv=0), 1), (dict(rect=7), 1),
+    (dict(d=96, dv=96), 6), (dict(hpk=3), 6), (dict(m=65), 6), (dict(d=64, dv=128), 6),
+    (dict(w=2000), 6),
+])
+def test_create_rejects_before_touching_the_device(kw, code):
+    P, L = _lib()
+    rc, h = _create(P, L, **kw)
+    assert rc == code, (kw, rc, P.o1_last_error())
+    assert not h.value
+    assert P.o1_last_error()
+
+
+def test_null_arguments_are_rejected():
+    P, L = _lib()
+    assert L.o1_create_groups(None, None) == P.O1_EINVAL
+    assert L.o1_prefill(None, None, None, None, 300, None, None) == P.O1_EINVAL
+    assert L.o1_step(None, None, None, None, None, None) == P.O1_EINVAL
+    info = P.o1_info()
+    assert L.o1_get_info(None, ctypes.byref(info)) == P.O1_EINVAL
+    n = ctypes.c_size_t()
+    assert L.o1_field_bytes(None, 0, ctypes.byref(n)) == P.O1_EINVAL
+    assert L.o1_read_field(None, 0, None, 0, None) == P.O1_EINVAL
+    assert L.o1_write_field(None, 0, None, 0, None) == P.O1_EINVAL
+    L.o1_destroy_groups(None)  # no-op
+    assert "null" in P.o1_last_error()
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    P, L = _lib()
+    with pytest.raises((ValueError, TypeError)):
+        P._dev_ptr(torch.zeros(4), "x", 4)

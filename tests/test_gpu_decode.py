@@ -1,0 +1,193 @@
+"""GPU parity of the decode step (o1_step) against the CPU oracle.
+
+The GPU prefill runs with the oracle's frozen K~, Q~ and M (the `frozen` hook of
+o1_prefill), so the decode outputs are compared at the benchmark spec tolerance
+(1e-4 of the row norm) without the ill-conditioned pinv's elementwise spread.
+Counters (far_len, win_head) are compared bit-exactly for every group, ring and
+sink rows bit-exactly for the sampled groups.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import streaming_nystr_attention_amd as P
+from streaming_nystr_attention_amd import workloads as W
+
+from parity_util import (DECODE_TOL, DecodeRun, cpu, frozen_tensors_with_oracle, oracle_decode,
+                         oracle_prefill, row_errors, say)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    P.lib()  # raises when the HIP library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def stack_frozen(orc_groups):
+    sts = [g.state() for g in orc_groups]
+    kt = torch.from_numpy(np.stack([s["k_tilde"] for s in sts])).to(DEV)
+    qt = torch.from_numpy(np.stack([s["q_tilde"] for s in sts])).to(DEV)
+    mu = torch.from_numpy(np.stack([s["mu"] for s in sts])).to(DEV)
+    return kt, qt, mu
+
+
+def decode_parity(wl, sample=None, steps=None, rect=O.RECT_AGGREGATE, frozen_override=None):
+    steps = wl.steps if steps is None else steps
+    G = wl.groups
+    sample = list(range(G)) if sample is None else sample
+    say(f"[decode] {wl.name}: G={G} hpk={wl.hpk} d={wl.d} m={wl.m} w={wl.w} sink={wl.sink} "
+        f"T={wl.T} steps={steps} rect={rect} sampled={len(sample)}")
+    q, k, v = W.prompt(wl, DEV)
+    si = torch.tensor(sample, device=DEV)
+    qh, kh, vh = cpu(q[si]), cpu(k[si]), cpu(v[si])
+    fz_orc = None
+    if frozen_override is not None:
+        fz_orc = [O.Frozen(mu=frozen_override) for _ in sample]
+    orc = oracle_prefill(wl, qh, kh, vh, frozen=fz_orc, rect=rect)
+    cfg = wl.config
+    cfg = P.Config(**{**cfg.__dict__, "rect": rect})
+    grp = P.O1Groups(cfg)
+    if len(sample) == G:
+        frozen = stack_frozen(orc)
+    else:
+        grp.prefill(q, k, v)
+        frozen = frozen_tensors_with_oracle(grp, wl, sample, orc)
+    grp.prefill(q, k, v, frozen=frozen)
+    del q, k, v, frozen
+    run = DecodeRun(wl, sample, steps)
+    qs, ks, vs, gout = run.run(grp)
+    out, alt, amb = oracle_decode(orc, qs, ks, vs)
+    err = row_errors(gout, out, alt, amb)
+    say(f"  rows={err.size} max_err={err.max():.3e} median={np.median(err):.3e} "
+        f"ambiguous={int(amb.sum())}")
+
+    # counters of every group, bit-exact
+    E = wl.T - wl.sink - wl.w + steps
+    far_len = grp.read(P.FIELD_FAR_LEN).numpy()
+    win_head = grp.read(P.FIELD_WIN_HEAD).numpy()
+    assert (far_len == E).all(), "far_len must equal the eviction count for every head"
+    assert (win_head == E % wl.w).all()
+    for i in range(len(sample)):
+        assert orc[i].far_len(0) == E and orc[i].win_head == E % wl.w
+
+    # ring and sink rows of the sampled groups, bit-exact
+    R = wl.sink + wl.w
+    nk = grp.read(P.FIELD_NEAR_K).view(G, R, wl.d)[sample].numpy()
+    nv = grp.read(P.FIELD_NEAR_V).view(G, R, wl.dv)[sample].numpy()
+    for i in range(len(sample)):
+        st = orc[i].state()
+        np.testing.assert_array_equal(nk[i, : wl.sink], st["sink_k"])
+        np.testing.assert_array_equal(nv[i, : wl.sink], st["sink_v"])
+        np.testing.assert_array_equal(nk[i, wl.sink:], st["win_k"])
+        np.testing.assert_array_equal(nv[i, wl.sink:], st["win_v"])
+    grp.close()
+    assert err.max() <= DECODE_TOL, f"max row error {err.max():.3e}"
+    return err
+
+
+def test_decode_single_head():
+    decode_parity(W.WORKLOADS["single_head"])
+
+
+def test_decode_qwen3_layer():
+    decode_parity(W.WORKLOADS["qwen3_layer"])
+
+
+@pytest.mark.parametrize("name", [f"stress_m{m}_s{s}" for m in (8, 16, 32) for s in (0, 4)])
+def test_decode_stress(name):
+    wl = W.WORKLOADS[name]
+    decode_parity(wl, sample=W.sample_groups(wl, extra=2))
+
+
+def test_decode_wide_gqa():
+    wl = W.WORKLOADS["wide_gqa"]
+    decode_parity(wl, sample=[0, 1, 7, 8, 128, 200, 255])
+
+
+def test_decode_qwen3_stack_full_size():
+    # the bench workload: 64 x 28 x 8 groups, 1024 steps, sampled outputs
+    wl = W.WORKLOADS["qwen3_stack_b64"]
+    decode_parity(wl, sample=W.sample_groups(wl, extra=4))
+
+
+# ---- edge cases ----------------------------------------------------------
+
+def test_decode_ragged_prompt_and_small_window():
+    # T = 100: m_eff = 12 with 8- and 9-row segments; prompt just long enough
+    wl = W.Workload("ragged", 3, 1, 2, 2, 128, 128, 32, 16, 2, T=100, steps=70, seed=11)
+    decode_parity(wl)
+
+
+def test_decode_shortest_skeleton_prompt():
+    # T = w + sink + 9: the first prompt length with a skeleton (9 evictions)
+    wl = W.Workload("shortest", 2, 1, 2, 4, 64, 64, 8, 24, 3, T=36, steps=40, seed=12)
+    decode_parity(wl)
+
+
+def test_decode_d64_hpk8_fm_rectifier():
+    wl = W.Workload("d64_hpk8_fm", 2, 1, 3, 8, 64, 64, 16, 32, 4, T=200, steps=50, q_std=2.0,
+                    k_std=2.0, seed=13)
+    decode_parity(wl, rect=O.RECT_FM)
+
+
+def test_decode_negative_mixing_drops_far_field():
+    wl = W.Workload("neg_mu", 2, 1, 2, 2, 128, 128, 8, 16, 2, T=64, steps=20, seed=14)
+    mu = -np.eye(wl.m_eff, dtype=np.float32)[None].repeat(wl.hpk, 0)
+    decode_parity(wl, frozen_override=mu)
+
+
+def test_decode_hpk1_window1():
+    wl = W.Workload("w1", 2, 1, 1, 1, 128, 128, 4, 1, 0, T=40, steps=30, seed=15)
+    decode_parity(wl)
+
+
+def test_gqa_group_equals_single_head_groups_bitwise():
+    wl = W.WORKLOADS["qwen3_layer"].with_(n_kv=4, steps=30)
+    q, k, v = W.prompt(wl, DEV)
+    grp = P.O1Groups(wl.config)
+    grp.prefill(q, k, v)
+    singles = []
+    for h in range(wl.hpk):
+        s = P.O1Groups(wl.config.__class__(**{**wl.config.__dict__, "hpk": 1}))
+        s.prefill(q[:, h:h + 1].contiguous(), k, v)
+        singles.append(s)
+    G = wl.groups
+    out = torch.empty(G, wl.hpk, wl.dv, device=DEV)
+    o1 = torch.empty(G, 1, wl.dv, device=DEV)
+    for t in range(wl.steps):
+        qq, kk, vv = W.decode_inputs(wl, t, DEV)
+        grp.step(qq, kk, vv, out)
+        for h, s in enumerate(singles):
+            s.step(qq[:, h:h + 1].contiguous(), kk, vv, o1)
+            assert torch.equal(o1[:, 0], out[:, h]), (t, h)
+
+
+def test_entry_point_errors_on_device():
+    wl = W.WORKLOADS["single_head"]
+    grp = P.O1Groups(wl.config)
+    G = wl.groups
+    q = torch.zeros(G, 1, 64, device=DEV)
+    k = torch.zeros(G, 64, device=DEV)
+    v = torch.zeros(G, 64, device=DEV)
+    out = torch.zeros(G, 1, 64, device=DEV)
+    with pytest.raises(P.O1Error) as e:
+        grp.step(q, k, v, out)
+    assert e.value.status == P.O1_ESTATE
+    T = wl.w + wl.sink + 8
+    qp = torch.zeros(G, 1, T, 64, device=DEV)
+    kp = torch.zeros(G, T, 64, device=DEV)
+    with pytest.raises(P.O1Error) as e:
+        grp.prefill(qp, kp, kp.clone())
+    assert e.value.status == P.O1_EEXACT
+    with pytest.raises(P.O1Error) as e:
+        grp.write(P.FIELD_T_HAT, torch.zeros(4, device=DEV))
+    assert e.value.status == P.O1_ESTATE
+    info = grp.info()
+    assert info.sealed == 0 and info.n_groups == G
