@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of batched streaming Nystrom attention on one MI355X.
+
+One bench step is one whole job over the workload: the prefill freeze of every
+group (o1_prefill) followed by the workload's decode steps (one o1_step launch
+each, every group of every sequence and layer per launch).  All inputs are
+generated into HBM before the timed region; each job re-prefills, so every
+timed job does identical work.
+
+value       decode group-steps per second over the whole timed job (prefill
+            time included); tokens_per_s = sequences x decode steps / time.
+roofline    the decode kernel: algorithmic bytes per launch / its average
+            launch time from HIP events on the launch stream, against the
+            MI355X HBM peak of 8 TB/s.
+cpu_baseline  the CPU oracle (tests' reference implementation, untuned) on a
+            bounded sample of the same workload, on this host's cores.
+
+Default workload: qwen3_stack_b64 (64 sequences x 28 layers x 8 KV heads, 2 query
+heads per KV head, d = dv = 128, m = 32, w = 128, sink = 4, 256-token prefill,
+1024 decode steps).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Nyström decode group-steps/sec & tokens/s at 1 GPU; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def decode_bytes_per_group_step(wl) -> tuple[int, int]:
+    """Algorithmic HBM bytes of one group-step: each stored value read once,
+    each modified value written once (f32 state, Z^ f64, far_len i64)."""
+    S, w, d, dv, m, H = wl.sink, wl.w, wl.d, wl.dv, wl.m_eff, wl.hpk
+    read = ((S + w) * (d + dv) * 4           # sinks + ring rows
+            + m * d * 4                      # key landmarks
+            + H * (m * d * 4 + m * m * 4     # per head: query landmarks, M
+                   + m * dv * 4 + m * 8 + m * 4)  # T^, Z^ (f64), running max
+            + (H * d + d + dv) * 4           # inputs q, k, v
+            + 4 + H * 8)                     # win_head, far_len
+    write = ((d + dv) * 4                    # the new ring row
+             + H * (m * dv * 4 + m * 8 + m * 4)  # T^, Z^, running max
+             + H * dv * 4                    # outputs
+             + 4 + H * 8)
+    return read, write
+
+
+def cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads, per_thread):
+    """Time the oracle on a bounded sample of groups (whole jobs)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    n = threads * per_thread
+    g = torch.Generator().manual_seed(1234)
+    idx = torch.randperm(wl.groups, generator=g)[:n].sort().values
+    di = idx.to(q.device)
+    qh, kh, vh = (t.index_select(0, di).cpu().numpy() for t in (q, k, v))
+    Qh = Q.index_select(1, di).cpu().numpy()
+    Kh = K.index_select(1, di).cpu().numpy()
+    Vh = V.index_select(1, di).cpu().numpy()
+
+    def one(i):
+        grp = O.Group(wl.m, wl.w, wl.sink, wl.hpk)
+        grp.prefill(qh[i], kh[i], vh[i])
+        grp.step_many(np.ascontiguousarray(Qh[:, i]), np.ascontiguousarray(Kh[:, i]),
+                      np.ascontiguousarray(Vh[:, i]))
+        return 0
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(n)))
+    dt = time.perf_counter() - t0
+    return {
+        "value": n * n_dec / dt,
+        "unit": "group-steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} of the {wl.groups} groups of {wl.name} (seeded pick), each a whole job: "
+                   f"prefill of {wl.T} tokens + {n_dec} decode steps; f64 C oracle, "
+                   f"{threads} threads, {dt:.1f} s wall"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3, help="timed jobs")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed jobs first")
+    ap.add_argument("--workload", default="qwen3_stack_b64")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="decode steps per job (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-per-thread", type=int, default=32, help="oracle groups per thread")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device copy of this size (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; every group is independent, so more "
+              "GPUs would each run the same kernel on their own share of the groups. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import streaming_nystr_attention_amd as P
+    from streaming_nystr_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    P.lib()  # fails loudly when the HIP library is missing
+    dev = "cuda"
+    wl = W.WORKLOADS[args.workload]
+    n_dec = args.decode_steps or wl.steps
+    G, H = wl.groups, wl.hpk
+
+    # ---- inputs resident in HBM before any timing -------------------------
+    q, k, v = W.prompt(wl, dev)
+    Q = torch.empty(n_dec, G, H, wl.d, device=dev)
+    K = torch.empty(n_dec, G, wl.d, device=dev)
+    V = torch.empty(n_dec, G, wl.dv, device=dev)
+    for t in range(n_dec):
+        W.decode_inputs(wl, t, dev, out=(Q[t], K[t], V[t]))
+    out = torch.empty(G, H, wl.dv, device=dev)
+    grp = P.O1Groups(wl.config)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        a = torch.empty(n, device=dev)
+        b = torch.empty(n, device=dev)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def job():
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        grp.prefill(q, k, v)
+        e[1].record()
+        for t in range(n_dec):
+            grp.step(Q[t], K[t], V[t], out)
+        e[2].record()
+        return e
+
+    for _ in range(args.warmup):
+        job()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    events = [job() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    prefill_ms = sum(e[0].elapsed_time(e[1]) for e in events) / len(events)
+    decode_ms = sum(e[1].elapsed_time(e[2]) for e in events) / len(events)
+    launch_us = decode_ms * 1e3 / n_dec
+    rd, wr = decode_bytes_per_group_step(wl)
+    bytes_per_launch = (rd + wr) * G
+    achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
+    group_steps = args.steps * n_dec * G
+
+    res = {
+        "metric": METRIC,
+        "value": group_steps / elapsed,
+        "unit": "group-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "n_seq": wl.n_seq, "n_layer": wl.n_layer, "n_kv": wl.n_kv,
+            "hpk": H, "d": wl.d, "dv": wl.dv, "m": wl.m, "m_eff": wl.m_eff, "w": wl.w,
+            "sink": wl.sink, "prompt_len": wl.T, "decode_steps": n_dec, "groups_per_launch": G,
+            "step": "prefill of every group + decode_steps o1_step launches",
+            "state": "f32 rows/landmarks/M/T^/running max, f64 Z^; f64 arithmetic",
+        },
+        "tokens_per_s": args.steps * n_dec * wl.n_seq / elapsed,
+        "decode_group_steps_per_s": n_dec * G / (decode_ms * 1e-3),
+        "decode_us_per_launch": launch_us,
+        "prefill_ms": prefill_ms,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel<128,128,2>" if (wl.d == 128 and H == 2) else "decode_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_group_step": rd + wr,
+        },
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads,
+                                           args.cpu_per_thread)
+    else:
+        res["cpu_baseline"] = None
+    grp.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

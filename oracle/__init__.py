@@ -85,6 +85,8 @@ def lib():
                                     ctypes.c_int, vp, vp, vp, vp]
     L.orc_step_group.restype = ctypes.c_int
     L.orc_step_group.argtypes = [vp, _f32p, _f32p, _f32p, _f64p, vp, vp]
+    L.orc_step_many.restype = ctypes.c_int
+    L.orc_step_many.argtypes = [vp, ctypes.c_int, _f32p, _f32p, _f32p, _f64p, vp, vp]
     for name in ("orc_m_eff", "orc_exact_only", "orc_win_len", "orc_win_head", "orc_sink_len",
                  "orc_num_q_heads"):
         getattr(L, name).restype = ctypes.c_int
@@ -236,6 +238,26 @@ class Group:
         if rc != 0:
             raise RuntimeError("step before prefill")
         return out, alt, list(diags)
+
+    def step_many(self, qs, ks, vs, with_alt: bool = False):
+        """`steps` consecutive step() calls in one foreign call:
+        qs [steps][hpk][d], ks [steps][d], vs [steps][dv] -> out [steps][hpk][dv];
+        with ``with_alt`` also (alt [steps][hpk][dv], diags [steps][hpk] OrcDiag)."""
+        qs, ks, vs = _f32(qs), _f32(ks), _f32(vs)
+        n = qs.shape[0]
+        assert qs.shape[1:] == (self.hpk, self.d) and ks.shape == (n, self.d)
+        assert vs.shape == (n, self.dv)
+        out = np.zeros((n, self.hpk, self.dv), np.float64)
+        if not with_alt:
+            if self._L.orc_step_many(self._h, n, qs, ks, vs, out, None, None) != 0:
+                raise RuntimeError("step before prefill")
+            return out
+        alt = np.full((n, self.hpk, self.dv), np.nan, np.float64)
+        diags = (OrcDiag * (n * self.hpk))()
+        if self._L.orc_step_many(self._h, n, qs, ks, vs, out, _ptr(alt),
+                                 ctypes.cast(diags, ctypes.c_void_p)) != 0:
+            raise RuntimeError("step before prefill")
+        return out, alt, diags
 
     # getters
     @property

@@ -623,3 +623,19 @@ void orc_export_landmarks64(const orc_group *g, double *k_tilde64, double *q_til
     if (k_tilde64) memcpy(k_tilde64, g->k_tilde64, sizeof(double) * m * g->d);
     if (q_tilde64) memcpy(q_tilde64, g->q_tilde64, sizeof(double) * g->hpk * m * g->d);
 }
+
+/* `steps` consecutive step_group calls (a plain loop, no other change):
+ * q_all [steps][q_heads][d], k [steps][d], v [steps][dv] -> out_all
+ * [steps][q_heads][dv]; out_alt and diag as in orc_step_group, per step (may
+ * be NULL).  Returns 0, or -1 before prefill.                                */
+int orc_step_many(orc_group *g, int steps, const float *q_all, const float *k, const float *v,
+                  double *out_all, double *out_alt, orc_diag *diag)
+{
+    if (!g || !g->sealed) return -1;
+    const size_t H = (size_t)g->hpk;
+    for (int t = 0; t < steps; ++t)
+        orc_step_group(g, q_all + (size_t)t * H * g->d, k + (size_t)t * g->d, v + (size_t)t * g->dv,
+                       out_all + (size_t)t * H * g->dv, out_alt ? out_alt + (size_t)t * H * g->dv : NULL,
+                       diag ? diag + (size_t)t * H : NULL);
+    return 0;
+}

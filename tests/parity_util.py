@@ -59,12 +59,12 @@ def oracle_decode(groups, qs, ks, vs):
 
     def one(i):
         g = groups[i]
-        for t in range(steps):
-            o, a, dg = g.step(qs[t, i], ks[t, i], vs[t, i], with_alt=True)
-            out[t, i] = o
-            alt[t, i] = a
-            for h in range(hpk):
-                amb[t, i, h] = dg[h].have_far and abs(dg[h].far_den) < AMBIG_REL * dg[h].far_abs
+        o, a, dg = g.step_many(np.ascontiguousarray(qs[:, i]), np.ascontiguousarray(ks[:, i]),
+                               np.ascontiguousarray(vs[:, i]), with_alt=True)
+        out[:, i] = o
+        alt[:, i] = a
+        fd = np.ctypeslib.as_array(dg).reshape(steps, hpk)
+        amb[:, i] = (fd["have_far"] != 0) & (np.abs(fd["far_den"]) < AMBIG_REL * fd["far_abs"])
 
     with ThreadPoolExecutor(THREADS) as ex:
         list(ex.map(one, range(n)))
