@@ -2,24 +2,33 @@
 // NystromState::step_group of the nystrom.rs source page (advance, then
 // NystromHead::step per query head), batched as one work-group per group.
 //
-// Per work-group (256 threads = 4 wave64), in dependency order:
-//   0. read the evicted ring slot e = win_head (row sink+e) and the new k/v into
-//      LDS, then overwrite row sink+e with the new k/v (advance).  Nothing reads
+// The step reads each group's whole state once, so it is bound by HBM, and a
+// work-group's time is mostly memory latency.  The kernel is organised to keep
+// few dependent round trips per group and many bytes in flight:
+//
+//   0. prologue, one round of loads into LDS: the ring head e = win_head, the
+//      queries, the new k/v, the evicted ring row (row sink+e), each head's
+//      running max and Z^, and (small shapes) each head's mixing matrix M.
+//      Then row sink+e is overwritten by the new k/v (advance); nothing reads
 //      that row from global memory afterwards.
-//   1. row-dot pass, f64 accumulation, lanes split each row across LPR lanes:
+//   1. row-dot pass, f64 accumulation, each row split over LPR lanes and four
+//      rows per lane in flight:
 //        near logits  lg[h][r] = q_h . k_r * scale       (sink + w rows, all heads)
 //        landmark     s[h][a]  = q_h . k~_a * scale      (m rows, all heads)
 //        far insert   l[h][i]  = q~_{h,i} . k_e * scale  (hpk * m rows)
+//      The T^ rows this thread updates later are loaded at the end of the pass,
+//      so their latency overlaps step 2.
 //   2. per head (one wave): c = max lg, f = max s, fh = e^{s - f}; running-max
-//      update of the evicted key (NystromHead::far_insert): r_i, e_i, Z^ and
+//      update for the evicted key (NystromHead::far_insert): r_i, e_i, Z^ and
 //      m_max written back; u = fh . M; c_all = max(c, f + m_max); gain =
-//      u e^{f + m_max - c_all}; far_den = gain . Z^; aggregate rectifier.
-//   3. near weights p = e^{lg - shift} and the joint denominator.
-//   4. column pass, one float4 column chunk per lane: T^ <- T^ r + e v_e written
-//      back and contracted with gain in the same pass; V rows contracted with p.
-//   5. reduce the row-lanes, one division per output, counters.
-// The HBM stream is each group's state read once and its modified part (one
-// ring row, T^, Z^, m_max, counters) written once.
+//      u e^{f + m_max - c_all}; far_den = gain . Z^; aggregate rectifier; near
+//      weights p = e^{lg - shift} and the joint denominator.
+//   3. column pass, one float4 column chunk per lane: T^ <- T^ r + e v_e written
+//      back and contracted with gain in the same pass; V rows contracted with p,
+//      eight rows per lane in flight.
+//   4. reduce the row lanes, one division per output, counters.
+// HBM traffic: each group's state read once and its modified part (one ring
+// row, T^, Z^, m_max, counters) written once.
 #include "o1_internal.h"
 
 namespace o1 {
@@ -28,7 +37,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-template <int D, int DV, int HPK>
+template <int D, int DV, int HPK, int MM>
 struct DecodeShape {
     static constexpr int CH = D / 4;                                   // float4 per key row
     static constexpr int LPR_WANT = HPK <= 2 ? 8 : (HPK <= 4 ? 16 : 32);
@@ -36,11 +45,17 @@ struct DecodeShape {
     static constexpr int CPL = CH / LPR;                               // float4 per lane per row
     static constexpr int RPW = 64 / LPR;                               // rows per wave per pass
     static constexpr int RPB = RPW * kWaves;                           // rows per block per pass
+    static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 2 ? 4 : 8);      // rows per lane in flight
     static constexpr int VCH = DV / 4;                                 // float4 per value row
     static constexpr int RL = kThreads / VCH;                          // row lanes, column pass
+    static constexpr int TPT = (MM + RL - 1) / RL;                     // T^ rows per lane per head
+    static constexpr bool STAGE_M = HPK * MM * MM <= 2048;             // M staged in LDS
+    static constexpr bool PRE_T = HPK * TPT <= 8;                      // T^ prefetched in registers
+    static constexpr int RED_H = HPK == 2 ? 2 : 1;                     // heads per reduction round
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
     static_assert(kThreads % VCH == 0, "value width must divide the block");
     static_assert(CH <= 64 && VCH <= 64, "rows wider than 256 floats are not compiled");
+    static_assert(HPK % RED_H == 0, "heads must split into reduction rounds");
 };
 
 __device__ __forceinline__ double dot4(const float4 a, const float4 b)
@@ -52,10 +67,10 @@ __device__ __forceinline__ double dot4(const float4 a, const float4 b)
     return s;
 }
 
-template <int D, int DV, int HPK>
+template <int D, int DV, int HPK, int MM>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO io)
 {
-    using C = DecodeShape<D, DV, HPK>;
+    using C = DecodeShape<D, DV, HPK, MM>;
     const int g = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = s.sink, R = s.R, m = s.m;
@@ -65,13 +80,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     __shared__ float4 q_s[HPK][C::CH];
     __shared__ float4 kn_s[C::CH], ke_s[C::CH];
     __shared__ float4 vn_s[C::VCH], ve_s[C::VCH];
-    __shared__ double land_s[HPK][kMaxLandmarks];  // landmark logits
-    __shared__ double lf_s[HPK][kMaxLandmarks];    // far-insert logits
-    __shared__ double r_s[HPK][kMaxLandmarks];     // T^ rescale factor per landmark
-    __shared__ double e_s[HPK][kMaxLandmarks];     // weight of the evicted key per landmark
-    __shared__ double gain_s[HPK][kMaxLandmarks];  // far mixing gains (0 when dropped)
-    __shared__ double shift_s[HPK], den_s[HPK];
-    __shared__ double red_s[C::RL][DV];
+    __shared__ float mo_s[HPK][MM];                // running max before this step
+    __shared__ double zo_s[HPK][MM];               // Z^ before this step
+    __shared__ float mu_s[C::STAGE_M ? HPK * MM * MM : 1];
+    __shared__ double land_s[HPK][MM];             // landmark logits
+    __shared__ double lf_s[HPK][MM];               // far-insert logits
+    __shared__ double r_s[HPK][MM];                // T^ rescale factor per landmark
+    __shared__ double e_s[HPK][MM];                // weight of the evicted key per landmark
+    __shared__ double gain_s[HPK][MM];             // far mixing gains (0 when dropped)
+    __shared__ double den_s[HPK];
+    __shared__ double red_s[C::RL][C::RED_H * DV];
     extern __shared__ double lg_s[];               // [HPK][R] near logits, then weights
 
     const size_t gh0 = (size_t)g * HPK;  // first head of this group
@@ -81,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     float4 *nk = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * R * C::CH;
     float4 *nv = reinterpret_cast<float4 *>(s.near_v) + (size_t)g * R * C::VCH;
 
-    // ---- 0. inputs and the evicted row into LDS; ring write -------------
+    // ---- 0. prologue: one round of small loads into LDS --------------------
     {
         const float4 *qg = reinterpret_cast<const float4 *>(io.q) + gh0 * C::CH;
         for (int i = tid; i < HPK * C::CH; i += kThreads) (&q_s[0][0])[i] = qg[i];
@@ -94,29 +112,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
             vn_s[c] = reinterpret_cast<const float4 *>(io.v)[(size_t)g * C::VCH + c];
             ve_s[c] = nv[(size_t)slot_row * C::VCH + c];
         }
+        for (int i = tid; i < HPK * m; i += kThreads) {
+            const int h = i / m, a = i - h * m;
+            mo_s[h][a] = s.m_max[gh0 * m + i];
+            zo_s[h][a] = s.z_hat[gh0 * m + i];
+        }
+        if constexpr (C::STAGE_M) {
+            const float *mu = s.mu + gh0 * (size_t)m * m;
+            for (int i = tid; i < HPK * m * m; i += kThreads) mu_s[i] = mu[i];
+        }
     }
     __syncthreads();
     if (tid < C::CH) nk[(size_t)slot_row * C::CH + tid] = kn_s[tid];
     if (tid >= 128 && tid < 128 + C::VCH) nv[(size_t)slot_row * C::VCH + tid - 128] = vn_s[tid - 128];
 
-    // ---- 1. row-dot pass --------------------------------------------------
+    // ---- 1. row-dot pass ----------------------------------------------------
+    const int cc = tid % C::VCH, rl = tid / C::VCH;  // column-pass mapping
+    float4 tpre[C::PRE_T ? HPK : 1][C::PRE_T ? C::TPT : 1];
     {
         const int sub = lane % C::LPR, rsub = lane / C::LPR;
-        float4 qr[HPK][C::CPL];
-#pragma unroll
-        for (int h = 0; h < HPK; ++h)
-#pragma unroll
-            for (int k = 0; k < C::CPL; ++k) qr[h][k] = q_s[h][sub + C::LPR * k];
-
         const float4 *kt = reinterpret_cast<const float4 *>(s.k_tilde) + (size_t)g * m * C::CH;
         const int NA = R + m;  // near rows, then landmark rows
-        for (int base = wave * C::RPW; base < NA; base += 2 * C::RPB) {
-            float4 x[2][C::CPL];
-            int rr[2];
+        for (int base = wave * C::RPW; base < NA; base += C::UNR * C::RPB) {
+            float4 x[C::UNR][C::CPL];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < C::UNR; ++u) {
                 const int r = base + u * C::RPB + rsub;
-                rr[u] = r;
 #pragma unroll
                 for (int k = 0; k < C::CPL; ++k) {
                     const int c = sub + C::LPR * k;
@@ -127,13 +148,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int r = rr[u];
+            for (int u = 0; u < C::UNR; ++u) {
+                const int r = base + u * C::RPB + rsub;
 #pragma unroll
                 for (int h = 0; h < HPK; ++h) {
+                    // keep q in LDS: re-read per row instead of pinning it in registers
+                    asm volatile("" ::: "memory");
                     double acc = 0.0;
 #pragma unroll
-                    for (int k = 0; k < C::CPL; ++k) acc += dot4(qr[h][k], x[u][k]);
+                    for (int k = 0; k < C::CPL; ++k) acc += dot4(q_s[h][sub + C::LPR * k], x[u][k]);
                     acc = group_sum<C::LPR>(acc);
                     if (sub == 0) {
                         if (r < R) lg_s[h * R + r] = acc * scale;
@@ -149,10 +172,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
         for (int k = 0; k < C::CPL; ++k) kr[k] = ke_s[sub + C::LPR * k];
         const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
         const int NQ = HPK * m;
-        for (int base = wave * C::RPW; base < NQ; base += 2 * C::RPB) {
-            float4 x[2][C::CPL];
+        for (int base = wave * C::RPW; base < NQ; base += C::UNR * C::RPB) {
+            float4 x[C::UNR][C::CPL];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < C::UNR; ++u) {
                 const int r = base + u * C::RPB + rsub;
 #pragma unroll
                 for (int k = 0; k < C::CPL; ++k)
@@ -160,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
                                        : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < C::UNR; ++u) {
                 const int r = base + u * C::RPB + rsub;
                 double acc = 0.0;
 #pragma unroll
@@ -169,10 +192,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
                 if (sub == 0 && r < NQ) lf_s[r / m][r % m] = acc * scale;
             }
         }
+
+        if constexpr (C::PRE_T) {
+            const float4 *th = reinterpret_cast<const float4 *>(s.t_hat) + gh0 * m * C::VCH;
+#pragma unroll
+            for (int h = 0; h < HPK; ++h)
+#pragma unroll
+                for (int j = 0; j < C::TPT; ++j) {
+                    const int b = rl + j * C::RL;
+                    tpre[h][j] = (b < m) ? th[((size_t)h * m + b) * C::VCH + cc]
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+        }
     }
     __syncthreads();
 
-    // ---- 2. per-head landmark work (one wave per head) --------------------
+    // ---- 2. per-head landmark work and near weights (one wave per head) ----
     for (int h = wave; h < HPK; h += kWaves) {
         double c = NEG_INF;
         for (int r = lane; r < R; r += 64) c = fmax(c, lg_s[h * R + r]);
@@ -190,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
         double mn = NEG_INF, zn = 0.0;
         if (act) {
             const double l = lf_s[h][lane];
-            const float mo = s.m_max[hi];
+            const float mo = mo_s[h][lane];
             float mnf = mo;
             double r = 1.0;
             if (l > (double)mo) {
@@ -199,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
             }
             mn = (double)mnf;
             const double ee = exp(l - mn);
-            zn = s.z_hat[hi] * r + ee;
+            zn = zo_s[h][lane] * r + ee;
             s.m_max[hi] = mnf;
             s.z_hat[hi] = zn;
             r_s[h][lane] = r;
@@ -207,11 +242,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
         }
 
         // u_b = sum_a fh_a M[a][b]  (lane = b)
-        const float *mu = s.mu + (gh0 + h) * (size_t)m * m;
         double u = 0.0;
-        for (int a = 0; a < m; ++a) {
-            const double fa = __shfl(fh, a, 64);
-            if (act) u = fma(fa, (double)mu[(size_t)a * m + lane], u);
+        if constexpr (C::STAGE_M) {
+            const float *mu = mu_s + (size_t)h * m * m;
+            for (int a = 0; a < m; ++a) {
+                const double fa = __shfl(fh, a, 64);
+                if (act) u = fma(fa, (double)mu[a * m + lane], u);
+            }
+        } else {
+            const float *mu = s.mu + (gh0 + h) * (size_t)m * m;
+            for (int a0 = 0; a0 < m; a0 += 8) {
+                float mv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) mv[j] = (act && a0 + j < m) ? mu[(size_t)(a0 + j) * m + lane] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const double fa = __shfl(fh, (a0 + j) & 63, 64);
+                    u = fma(fa, (double)mv[j], u);
+                }
+            }
         }
         if (s.rect == 1) u = fmax(u, 0.0);  // O1Rect::Fm
 
@@ -220,29 +269,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
         const double far_den = wave_sum(gain * zn);
         const bool keep = far_den >= 0.0;  // aggregate rectifier (0 keeps)
         if (act) gain_s[h][lane] = keep ? gain : 0.0;
-        if (lane == 0) {
-            shift_s[h] = keep ? call : c;  // dropped far field: near-only shift
-            den_s[h] = keep ? far_den : 0.0;
-        }
-    }
-    __syncthreads();
+        const double shift = keep ? call : c;  // dropped far field: near-only shift
 
-    // ---- 3. near weights and the joint denominator ------------------------
-    for (int h = wave; h < HPK; h += kWaves) {
-        const double sh = shift_s[h];
         double acc = 0.0;
         for (int r = lane; r < R; r += 64) {
-            const double p = exp(lg_s[h * R + r] - sh);
+            const double p = exp(lg_s[h * R + r] - shift);
             lg_s[h * R + r] = p;
             acc += p;
         }
         acc = wave_sum(acc);
-        if (lane == 0) den_s[h] += acc;
+        if (lane == 0) den_s[h] = (keep ? far_den : 0.0) + acc;
     }
     __syncthreads();
 
-    // ---- 4. column pass: T^ update + far contraction, V contraction -------
-    const int cc = tid % C::VCH, rl = tid / C::VCH;
+    // ---- 3. column pass: T^ update + far contraction, V contraction --------
     double acc[HPK][4];
 #pragma unroll
     for (int h = 0; h < HPK; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.0;
@@ -251,9 +291,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
         const float4 vev = ve_s[cc];
 #pragma unroll
         for (int h = 0; h < HPK; ++h) {
-            for (int b = rl; b < m; b += C::RL) {
+#pragma unroll
+            for (int j = 0; j < C::TPT; ++j) {
+                const int b = rl + j * C::RL;
+                if (b >= m) break;
                 const size_t idx = ((size_t)h * m + b) * C::VCH + cc;
-                const float4 t = th[idx];
+                float4 t;
+                if constexpr (C::PRE_T) t = tpre[h][j];
+                else t = th[idx];
                 const double rb = r_s[h][b], eb = e_s[h][b], gb = gain_s[h][b];
                 const double t0 = fma((double)t.x, rb, eb * (double)vev.x);
                 const double t1 = fma((double)t.y, rb, eb * (double)vev.y);
@@ -268,64 +313,88 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
         }
     }
     {
-#pragma unroll 4
-        for (int r = rl; r < R; r += C::RL) {
-            const float4 x = (r == slot_row) ? vn_s[cc] : nv[(size_t)r * C::VCH + cc];
+        constexpr int VU = 8;
+        for (int r0 = rl; r0 < R; r0 += VU * C::RL) {
+            float4 x[VU];
 #pragma unroll
-            for (int h = 0; h < HPK; ++h) {
-                const double p = lg_s[h * R + r];
-                acc[h][0] = fma(p, (double)x.x, acc[h][0]);
-                acc[h][1] = fma(p, (double)x.y, acc[h][1]);
-                acc[h][2] = fma(p, (double)x.z, acc[h][2]);
-                acc[h][3] = fma(p, (double)x.w, acc[h][3]);
+            for (int j = 0; j < VU; ++j) {
+                const int r = r0 + j * C::RL;
+                x[j] = (r < R) ? ((r == slot_row) ? vn_s[cc] : nv[(size_t)r * C::VCH + cc])
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int j = 0; j < VU; ++j) {
+                const int r = r0 + j * C::RL;
+                if (r >= R) break;
+#pragma unroll
+                for (int h = 0; h < HPK; ++h) {
+                    const double p = lg_s[h * R + r];
+                    acc[h][0] = fma(p, (double)x[j].x, acc[h][0]);
+                    acc[h][1] = fma(p, (double)x[j].y, acc[h][1]);
+                    acc[h][2] = fma(p, (double)x[j].z, acc[h][2]);
+                    acc[h][3] = fma(p, (double)x[j].w, acc[h][3]);
+                }
             }
         }
     }
 
-    // ---- 5. reduce row lanes, joint division, counters --------------------
+    // ---- 4. reduce row lanes, joint division, counters ---------------------
     float4 *outp = reinterpret_cast<float4 *>(io.out) + gh0 * C::VCH;
 #pragma unroll
-    for (int h = 0; h < HPK; ++h) {
-        red_s[rl][cc * 4 + 0] = acc[h][0];
-        red_s[rl][cc * 4 + 1] = acc[h][1];
-        red_s[rl][cc * 4 + 2] = acc[h][2];
-        red_s[rl][cc * 4 + 3] = acc[h][3];
+    for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
+#pragma unroll
+        for (int hh = 0; hh < C::RED_H; ++hh) {
+            double *dst = &red_s[rl][hh * DV + cc * 4];
+            dst[0] = acc[h0 + hh][0];
+            dst[1] = acc[h0 + hh][1];
+            dst[2] = acc[h0 + hh][2];
+            dst[3] = acc[h0 + hh][3];
+        }
         __syncthreads();
-        if (tid < C::VCH) {
+        if (tid < C::RED_H * C::VCH) {
+            const int hh = tid / C::VCH, c4 = tid - hh * C::VCH;
             double o0 = 0.0, o1 = 0.0, o2 = 0.0, o3 = 0.0;
 #pragma unroll
             for (int j = 0; j < C::RL; ++j) {
-                o0 += red_s[j][tid * 4 + 0];
-                o1 += red_s[j][tid * 4 + 1];
-                o2 += red_s[j][tid * 4 + 2];
-                o3 += red_s[j][tid * 4 + 3];
+                const double *src = &red_s[j][hh * DV + c4 * 4];
+                o0 += src[0];
+                o1 += src[1];
+                o2 += src[2];
+                o3 += src[3];
             }
-            const double den = fmax(den_s[h], kDenEps);
-            outp[(size_t)h * C::VCH + tid] =
+            const double den = fmax(den_s[h0 + hh], kDenEps);
+            outp[(size_t)(h0 + hh) * C::VCH + c4] =
                 make_float4((float)(o0 / den), (float)(o1 / den), (float)(o2 / den), (float)(o3 / den));
         }
-        __syncthreads();
+        if (h0 + C::RED_H < HPK) __syncthreads();
     }
     if (tid == 0) s.win_head[g] = (e + 1 == s.w) ? 0 : e + 1;
     if (tid < HPK) s.far_len[gh0 + tid] += 1;
 }
 
-template <int D, int DV, int HPK>
+template <int D, int DV, int HPK, int MM>
 hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     const size_t dyn = sizeof(double) * (size_t)HPK * s.R;
-    hipLaunchKernelGGL((decode_kernel<D, DV, HPK>), dim3(s.G), dim3(kThreads), dyn, stream, s, io);
+    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM>), dim3(s.G), dim3(kThreads), dyn, stream, s, io);
     return hipGetLastError();
+}
+
+template <int D, int DV, int HPK>
+hipError_t launch_m(const DevState &s, const DecodeIO &io, hipStream_t stream)
+{
+    if (s.m <= 32) return launch_shape<D, DV, HPK, 32>(s, io, stream);
+    return launch_shape<D, DV, HPK, kMaxLandmarks>(s, io, stream);
 }
 
 template <int D, int DV>
 hipError_t launch_hpk(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     switch (s.hpk) {
-    case 1: return launch_shape<D, DV, 1>(s, io, stream);
-    case 2: return launch_shape<D, DV, 2>(s, io, stream);
-    case 4: return launch_shape<D, DV, 4>(s, io, stream);
-    case 8: return launch_shape<D, DV, 8>(s, io, stream);
+    case 1: return launch_m<D, DV, 1>(s, io, stream);
+    case 2: return launch_m<D, DV, 2>(s, io, stream);
+    case 4: return launch_m<D, DV, 4>(s, io, stream);
+    case 8: return launch_m<D, DV, 8>(s, io, stream);
     default: return hipErrorInvalidValue;
     }
 }
