@@ -52,6 +52,8 @@ struct DecodeShape {
     static constexpr bool STAGE_M = HPK * MM * MM <= 2048;             // M staged in LDS
     static constexpr bool PRE_T = HPK * TPT <= 8;                      // T^ prefetched in registers
     static constexpr int RED_H = HPK == 2 ? 2 : 1;                     // heads per reduction round
+    static constexpr int VPRE = HPK <= 2 ? 8 : 4;                      // V rows prefetched per lane
+    static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
     static_assert(kThreads % VCH == 0, "value width must divide the block");
     static_assert(CH <= 64 && VCH <= 64, "rows wider than 256 floats are not compiled");
@@ -127,8 +129,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     if (tid >= 128 && tid < 128 + C::VCH) nv[(size_t)slot_row * C::VCH + tid - 128] = vn_s[tid - 128];
 
     // ---- 1. row-dot pass ----------------------------------------------------
+    // Loads are unconditional (row indices clamped into range, results of
+    // out-of-range rows discarded) so each batch issues back to back.
     const int cc = tid % C::VCH, rl = tid / C::VCH;  // column-pass mapping
     float4 tpre[C::PRE_T ? HPK : 1][C::PRE_T ? C::TPT : 1];
+    float4 vpre[C::VPRE];
     {
         const int sub = lane % C::LPR, rsub = lane / C::LPR;
         const float4 *kt = reinterpret_cast<const float4 *>(s.k_tilde) + (size_t)g * m * C::CH;
@@ -137,19 +142,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
             float4 x[C::UNR][C::CPL];
 #pragma unroll
             for (int u = 0; u < C::UNR; ++u) {
-                const int r = base + u * C::RPB + rsub;
+                const int r = min(base + u * C::RPB + rsub, NA - 1);
+                const float4 *row = (r < R) ? nk + (size_t)r * C::CH : kt + (size_t)(r - R) * C::CH;
 #pragma unroll
-                for (int k = 0; k < C::CPL; ++k) {
-                    const int c = sub + C::LPR * k;
-                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (r < R) v = (r == slot_row) ? kn_s[c] : nk[(size_t)r * C::CH + c];
-                    else if (r < NA) v = kt[(size_t)(r - R) * C::CH + c];
-                    x[u][k] = v;
-                }
+                for (int k = 0; k < C::CPL; ++k) x[u][k] = row[sub + C::LPR * k];
             }
 #pragma unroll
             for (int u = 0; u < C::UNR; ++u) {
                 const int r = base + u * C::RPB + rsub;
+                if (r == slot_row) {  // the ring slot already holds the new key
+#pragma unroll
+                    for (int k = 0; k < C::CPL; ++k) x[u][k] = kn_s[sub + C::LPR * k];
+                }
 #pragma unroll
                 for (int h = 0; h < HPK; ++h) {
                     // keep q in LDS: re-read per row instead of pinning it in registers
@@ -176,11 +180,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
             float4 x[C::UNR][C::CPL];
 #pragma unroll
             for (int u = 0; u < C::UNR; ++u) {
-                const int r = base + u * C::RPB + rsub;
+                const int r = min(base + u * C::RPB + rsub, NQ - 1);
 #pragma unroll
-                for (int k = 0; k < C::CPL; ++k)
-                    x[u][k] = (r < NQ) ? qt[(size_t)r * C::CH + sub + C::LPR * k]
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int k = 0; k < C::CPL; ++k) x[u][k] = qt[(size_t)r * C::CH + sub + C::LPR * k];
             }
 #pragma unroll
             for (int u = 0; u < C::UNR; ++u) {
@@ -193,16 +195,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
             }
         }
 
+        // prefetch: this thread's T^ rows and its first V rows
         if constexpr (C::PRE_T) {
             const float4 *th = reinterpret_cast<const float4 *>(s.t_hat) + gh0 * m * C::VCH;
 #pragma unroll
             for (int h = 0; h < HPK; ++h)
 #pragma unroll
                 for (int j = 0; j < C::TPT; ++j) {
-                    const int b = rl + j * C::RL;
-                    tpre[h][j] = (b < m) ? th[((size_t)h * m + b) * C::VCH + cc]
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const int b = min(rl + j * C::RL, m - 1);
+                    tpre[h][j] = th[((size_t)h * m + b) * C::VCH + cc];
                 }
+        }
+#pragma unroll
+        for (int j = 0; j < C::VPRE; ++j) {
+            const int r = min(rl + j * C::RL, R - 1);
+            vpre[j] = nv[(size_t)r * C::VCH + cc];
         }
     }
     __syncthreads();
@@ -313,19 +320,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
         }
     }
     {
-        constexpr int VU = 8;
-        for (int r0 = rl; r0 < R; r0 += VU * C::RL) {
-            float4 x[VU];
+        // V rows r = rl + j * RL: the first VPRE were prefetched before step 2
 #pragma unroll
-            for (int j = 0; j < VU; ++j) {
-                const int r = r0 + j * C::RL;
-                x[j] = (r < R) ? ((r == slot_row) ? vn_s[cc] : nv[(size_t)r * C::VCH + cc])
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < C::VPRE; ++j) {
+            const int r = rl + j * C::RL;
+            if (r >= R) break;
+            const float4 x = (r == slot_row) ? vn_s[cc] : vpre[j];
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) {
+                const double p = lg_s[h * R + r];
+                acc[h][0] = fma(p, (double)x.x, acc[h][0]);
+                acc[h][1] = fma(p, (double)x.y, acc[h][1]);
+                acc[h][2] = fma(p, (double)x.z, acc[h][2]);
+                acc[h][3] = fma(p, (double)x.w, acc[h][3]);
             }
+        }
+        for (int r0 = rl + C::VPRE * C::RL; r0 < R; r0 += C::VU * C::RL) {
+            float4 x[C::VU];
 #pragma unroll
-            for (int j = 0; j < VU; ++j) {
+            for (int j = 0; j < C::VU; ++j) x[j] = nv[(size_t)min(r0 + j * C::RL, R - 1) * C::VCH + cc];
+#pragma unroll
+            for (int j = 0; j < C::VU; ++j) {
                 const int r = r0 + j * C::RL;
                 if (r >= R) break;
+                if (r == slot_row) x[j] = vn_s[cc];
 #pragma unroll
                 for (int h = 0; h < HPK; ++h) {
                     const double p = lg_s[h * R + r];
