@@ -33,6 +33,20 @@ if ROOT not in sys.path:
 
 METRIC = "Nyström decode group-steps/sec & tokens/s at 1 GPU; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", "o1_decode.hip")
+# HBM bytes per decode launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by
+# a 1 GiB copy in the same process), keyed by (workload, decode source sha256 prefix).
+# A changed kernel source has no entry, and the roofline's traffic is then reported as null.
+MEASURED_TRAFFIC = {
+    ("qwen3_stack_b64", "5b11cee8cf2d6752"): 3793410551,
+}
+
+
+def decode_source_sha() -> str:
+    import hashlib
+
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def decode_bytes_per_group_step(wl) -> tuple[int, int]:
@@ -205,7 +219,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": MEASURED_TRAFFIC.get((wl.name, decode_source_sha())),
+            "traffic_unit": "bytes per launch",
+            "bytes_per_launch": bytes_per_launch,
             "bytes_per_group_step": rd + wr,
         },
     }
