@@ -8,7 +8,7 @@
 
 #include <string>
 
-#include "../../include/o1.h"
+#include "o1.h"
 #include "o1_internal.h"
 
 namespace {

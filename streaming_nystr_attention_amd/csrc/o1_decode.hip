@@ -11,53 +11,62 @@
 //      running max and Z^, and (small shapes) each head's mixing matrix M.
 //      Then row sink+e is overwritten by the new k/v (advance); nothing reads
 //      that row from global memory afterwards.
-//   1. row-dot pass, f64 accumulation, each row split over LPR lanes and four
+//   1. row-dot pass, f64 accumulation, each row split over LPR lanes and UNR
 //      rows per lane in flight:
 //        near logits  lg[h][r] = q_h . k_r * scale       (sink + w rows, all heads)
 //        landmark     s[h][a]  = q_h . k~_a * scale      (m rows, all heads)
 //        far insert   l[h][i]  = q~_{h,i} . k_e * scale  (hpk * m rows)
-//      The T^ rows this thread updates later are loaded at the end of the pass,
-//      so their latency overlaps step 2.
+//      The hpk partial dots of a row are reduced over the row's lanes by
+//      halving exchanges (each step keeps half the heads), so the lanes of a
+//      row end with one head's total each.  T^ rows and the first V rows this
+//      thread contracts later are loaded at the end of the pass, so their
+//      latency overlaps step 2.
 //   2. per head (one wave): c = max lg, f = max s, fh = e^{s - f}; running-max
 //      update for the evicted key (NystromHead::far_insert): r_i, e_i, Z^ and
 //      m_max written back; u = fh . M; c_all = max(c, f + m_max); gain =
 //      u e^{f + m_max - c_all}; far_den = gain . Z^; aggregate rectifier; near
 //      weights p = e^{lg - shift} and the joint denominator.
 //   3. column pass, one float4 column chunk per lane: T^ <- T^ r + e v_e written
-//      back and contracted with gain in the same pass; V rows contracted with p,
-//      eight rows per lane in flight.
-//   4. reduce the row lanes, one division per output, counters.
+//      back and contracted with gain in the same pass; V rows contracted with p.
+//   4. reduce the row lanes (shuffles within a wave, LDS across waves), one
+//      division per output, counters.
 // HBM traffic: each group's state read once and its modified part (one ring
 // row, T^, Z^, m_max, counters) written once.
+//
+// Work-group size: 256 threads when the launch has many groups (several
+// work-groups per CU hide each other's latency), 512 when it has few.
 #include "o1_internal.h"
 
 namespace o1 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kMaxDynLds = 32 * 1024;  // near logits: hpk * (sink + w) doubles
 
-template <int D, int DV, int HPK, int MM>
+template <int D, int DV, int HPK, int MM, int NT>
 struct DecodeShape {
+    static constexpr int NW = NT / 64;                                 // waves
     static constexpr int CH = D / 4;                                   // float4 per key row
     static constexpr int LPR_WANT = HPK <= 2 ? 8 : (HPK <= 4 ? 16 : 32);
     static constexpr int LPR = LPR_WANT < CH ? LPR_WANT : CH;          // lanes per row
     static constexpr int CPL = CH / LPR;                               // float4 per lane per row
     static constexpr int RPW = 64 / LPR;                               // rows per wave per pass
-    static constexpr int RPB = RPW * kWaves;                           // rows per block per pass
+    static constexpr int RPB = RPW * NW;                               // rows per block per pass
     static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 2 ? 4 : 8);      // rows per lane in flight
     static constexpr int VCH = DV / 4;                                 // float4 per value row
-    static constexpr int RL = kThreads / VCH;                          // row lanes, column pass
+    static constexpr int RL = NT / VCH;                                // row lanes, column pass
+    static constexpr int RLW = 64 / VCH;                               // row lanes per wave
     static constexpr int TPT = (MM + RL - 1) / RL;                     // T^ rows per lane per head
     static constexpr bool STAGE_M = HPK * MM * MM <= 2048;             // M staged in LDS
-    static constexpr bool PRE_T = HPK * TPT <= 8;                      // T^ prefetched in registers
-    static constexpr int RED_H = HPK == 2 ? 2 : 1;                     // heads per reduction round
-    static constexpr int VPRE = HPK <= 2 ? 8 : 4;                      // V rows prefetched per lane
+    static constexpr bool PRE_T = HPK * TPT <= (NT == 256 ? 8 : 32);   // T^ prefetched in registers
+    static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : 8;    // V rows prefetched per lane
     static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
+    static constexpr int RED_CAP = 16384 / (NW * DV * 8);              // heads per LDS round
+    static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
-    static_assert(kThreads % VCH == 0, "value width must divide the block");
+    static_assert(HPK <= LPR, "the head reduction needs at least hpk lanes per row");
+    static_assert(64 % VCH == 0, "value rows must tile a wave");
     static_assert(CH <= 64 && VCH <= 64, "rows wider than 256 floats are not compiled");
-    static_assert(HPK % RED_H == 0, "heads must split into reduction rounds");
+    static_assert(RED_H >= 1 && HPK % RED_H == 0, "heads must split into reduction rounds");
 };
 
 __device__ __forceinline__ double dot4(const float4 a, const float4 b)
@@ -69,10 +78,36 @@ __device__ __forceinline__ double dot4(const float4 a, const float4 b)
     return s;
 }
 
-template <int D, int DV, int HPK, int MM>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO io)
+// Reduce N per-lane partial sums over aligned groups of W lanes.  Each halving
+// step exchanges half of the remaining values with the partner lane; lanes keep
+// the lower or upper half by their lane bit.  Returns, in every lane, the group
+// total of value index (lane % W) / (W / N).
+template <int W, int N>
+__device__ __forceinline__ double head_reduce(const double *v, int lane)
 {
-    using C = DecodeShape<D, DV, HPK, MM>;
+    if constexpr (N == 1) {
+        double x = v[0];
+#pragma unroll
+        for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+        return x;
+    } else {
+        constexpr int off = W / 2;
+        const bool hi = (lane & off) != 0;
+        double nv[N / 2];
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const double mine = hi ? v[N / 2 + i] : v[i];
+            const double send = hi ? v[i] : v[N / 2 + i];
+            nv[i] = mine + __shfl_xor(send, off, 64);
+        }
+        return head_reduce<W / 2, N / 2>(nv, lane);
+    }
+}
+
+template <int D, int DV, int HPK, int MM, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
+{
+    using C = DecodeShape<D, DV, HPK, MM, NT>;
     const int g = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = s.sink, R = s.R, m = s.m;
@@ -91,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     __shared__ double e_s[HPK][MM];                // weight of the evicted key per landmark
     __shared__ double gain_s[HPK][MM];             // far mixing gains (0 when dropped)
     __shared__ double den_s[HPK];
-    __shared__ double red_s[C::RL][C::RED_H * DV];
+    __shared__ double red_s[C::NW][C::RED_H * DV];
     extern __shared__ double lg_s[];               // [HPK][R] near logits, then weights
 
     const size_t gh0 = (size_t)g * HPK;  // first head of this group
@@ -104,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     // ---- 0. prologue: one round of small loads into LDS --------------------
     {
         const float4 *qg = reinterpret_cast<const float4 *>(io.q) + gh0 * C::CH;
-        for (int i = tid; i < HPK * C::CH; i += kThreads) (&q_s[0][0])[i] = qg[i];
+        for (int i = tid; i < HPK * C::CH; i += NT) (&q_s[0][0])[i] = qg[i];
         if (tid < C::CH) {
             kn_s[tid] = reinterpret_cast<const float4 *>(io.k)[(size_t)g * C::CH + tid];
             ke_s[tid] = nk[(size_t)slot_row * C::CH + tid];
@@ -114,14 +149,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
             vn_s[c] = reinterpret_cast<const float4 *>(io.v)[(size_t)g * C::VCH + c];
             ve_s[c] = nv[(size_t)slot_row * C::VCH + c];
         }
-        for (int i = tid; i < HPK * m; i += kThreads) {
+        for (int i = tid; i < HPK * m; i += NT) {
             const int h = i / m, a = i - h * m;
             mo_s[h][a] = s.m_max[gh0 * m + i];
             zo_s[h][a] = s.z_hat[gh0 * m + i];
         }
         if constexpr (C::STAGE_M) {
             const float *mu = s.mu + gh0 * (size_t)m * m;
-            for (int i = tid; i < HPK * m * m; i += kThreads) mu_s[i] = mu[i];
+            for (int i = tid; i < HPK * m * m; i += NT) mu_s[i] = mu[i];
         }
     }
     __syncthreads();
@@ -136,6 +171,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     float4 vpre[C::VPRE];
     {
         const int sub = lane % C::LPR, rsub = lane / C::LPR;
+        constexpr int HSTRIDE = C::LPR / HPK;  // lanes per head after the head reduction
+        const int my_head = sub / HSTRIDE;
+        const bool writer = (sub % HSTRIDE) == 0;
         const float4 *kt = reinterpret_cast<const float4 *>(s.k_tilde) + (size_t)g * m * C::CH;
         const int NA = R + m;  // near rows, then landmark rows
         for (int base = wave * C::RPW; base < NA; base += C::UNR * C::RPB) {
@@ -154,6 +192,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
 #pragma unroll
                     for (int k = 0; k < C::CPL; ++k) x[u][k] = kn_s[sub + C::LPR * k];
                 }
+                double part[HPK];
 #pragma unroll
                 for (int h = 0; h < HPK; ++h) {
                     // keep q in LDS: re-read per row instead of pinning it in registers
@@ -161,11 +200,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
                     double acc = 0.0;
 #pragma unroll
                     for (int k = 0; k < C::CPL; ++k) acc += dot4(q_s[h][sub + C::LPR * k], x[u][k]);
-                    acc = group_sum<C::LPR>(acc);
-                    if (sub == 0) {
-                        if (r < R) lg_s[h * R + r] = acc * scale;
-                        else if (r < NA) land_s[h][r - R] = acc * scale;
-                    }
+                    part[h] = acc;
+                }
+                const double tot = head_reduce<C::LPR, HPK>(part, lane) * scale;
+                if (writer) {
+                    if (r < R) lg_s[my_head * R + r] = tot;
+                    else if (r < NA) land_s[my_head][r - R] = tot;
                 }
             }
         }
@@ -215,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     __syncthreads();
 
     // ---- 2. per-head landmark work and near weights (one wave per head) ----
-    for (int h = wave; h < HPK; h += kWaves) {
+    for (int h = wave; h < HPK; h += C::NW) {
         double c = NEG_INF;
         for (int r = lane; r < R; r += 64) c = fmax(c, lg_s[h * R + r]);
         c = wave_max(c);
@@ -357,23 +397,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     }
 
     // ---- 4. reduce row lanes, joint division, counters ---------------------
+    // within a wave: the RLW row lanes sit VCH lanes apart
+#pragma unroll
+    for (int h = 0; h < HPK; ++h)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int off = C::VCH; off < 64; off <<= 1) acc[h][c] += __shfl_xor(acc[h][c], off, 64);
     float4 *outp = reinterpret_cast<float4 *>(io.out) + gh0 * C::VCH;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
+        if (lane < C::VCH) {
 #pragma unroll
-        for (int hh = 0; hh < C::RED_H; ++hh) {
-            double *dst = &red_s[rl][hh * DV + cc * 4];
-            dst[0] = acc[h0 + hh][0];
-            dst[1] = acc[h0 + hh][1];
-            dst[2] = acc[h0 + hh][2];
-            dst[3] = acc[h0 + hh][3];
+            for (int hh = 0; hh < C::RED_H; ++hh) {
+                double *dst = &red_s[wave][hh * DV + cc * 4];
+                dst[0] = acc[h0 + hh][0];
+                dst[1] = acc[h0 + hh][1];
+                dst[2] = acc[h0 + hh][2];
+                dst[3] = acc[h0 + hh][3];
+            }
         }
         __syncthreads();
         if (tid < C::RED_H * C::VCH) {
             const int hh = tid / C::VCH, c4 = tid - hh * C::VCH;
             double o0 = 0.0, o1 = 0.0, o2 = 0.0, o3 = 0.0;
 #pragma unroll
-            for (int j = 0; j < C::RL; ++j) {
+            for (int j = 0; j < C::NW; ++j) {
                 const double *src = &red_s[j][hh * DV + c4 * 4];
                 o0 += src[0];
                 o1 += src[1];
@@ -390,19 +439,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DevState s, DecodeIO i
     if (tid < HPK) s.far_len[gh0 + tid] += 1;
 }
 
-template <int D, int DV, int HPK, int MM>
+template <int D, int DV, int HPK, int MM, int NT>
 hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
+    // Static LDS of the wide shapes plus the near logits can pass 64 KB; raise
+    // the kernel's dynamic limit once (an unsupported size fails the launch).
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, HPK, MM, NT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
+    if (attr != hipSuccess) return attr;
     const size_t dyn = sizeof(double) * (size_t)HPK * s.R;
-    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM>), dim3(s.G), dim3(kThreads), dyn, stream, s, io);
+    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM, NT>), dim3(s.G), dim3(NT), dyn, stream, s, io);
     return hipGetLastError();
+}
+
+// Few groups per launch leave CUs with a single work-group, whose latency is
+// then exposed: use 512 threads per group there.
+constexpr int kSmallGrid = 1024;
+
+template <int D, int DV, int HPK, int MM>
+hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
+{
+    if (s.G < kSmallGrid) return launch_shape<D, DV, HPK, MM, 512>(s, io, stream);
+    return launch_shape<D, DV, HPK, MM, 256>(s, io, stream);
 }
 
 template <int D, int DV, int HPK>
 hipError_t launch_m(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    if (s.m <= 32) return launch_shape<D, DV, HPK, 32>(s, io, stream);
-    return launch_shape<D, DV, HPK, kMaxLandmarks>(s, io, stream);
+    if (s.m <= 32) return launch_nt<D, DV, HPK, 32>(s, io, stream);
+    return launch_nt<D, DV, HPK, kMaxLandmarks>(s, io, stream);
 }
 
 template <int D, int DV>
@@ -426,7 +492,7 @@ bool decode_supported(int d, int dv, int hpk, int m, int R)
     if (m < 4 || m > kMaxLandmarks) return false;
     if (R < 1 || R > 1024) return false;
     // dynamic LDS for the near logits stays within 32 KB
-    return (size_t)hpk * R * sizeof(double) <= 32 * 1024;
+    return (size_t)hpk * R * sizeof(double) <= (size_t)kMaxDynLds;
 }
 
 hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stream)

@@ -12,11 +12,11 @@
 //                      lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
 //                      G + lambda I in LDS (lambda x10 on a failed pivot, up to 12
 //                      attempts, then diag(1/mean diag)), M = (G + lambda I)^-1 A^T.
-//   far_replay_kernel  grid G * hpk: the far field of keys sink .. T-w-1, i.e. the
+//   far_mfma_kernel    grid G * hpk: the far field of keys sink .. T-w-1, i.e. the
 //                      state the page's sequential replay through far_insert
-//                      reaches, computed in tiles with an online per-landmark
-//                      max: m_max_i = max_j l_ij, Z^_i = sum_j e^{l_ij - m_max_i},
-//                      T^_i = sum_j e^{l_ij - m_max_i} v_j (f64 accumulation).
+//                      reaches, computed in 16-key tiles on f64 MFMA with an
+//                      online per-landmark max: m_max_i = max_j l_ij,
+//                      Z^_i = sum_j e^{l_ij - m_max_i}, T^_i = sum_j e^{l_ij - m_max_i} v_j.
 #include <float.h>
 
 #include "o1_internal.h"
@@ -195,109 +195,132 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
     }
 }
 
-constexpr int kTile = 16;  // far keys per tile
+// ---- far field of the prompt on the matrix cores (f64 MFMA) ---------------
+//
+// One work-group per (group, head), one wave per block of 16 query landmarks.
+// For each tile of 16 far keys (staged in LDS):
+//   L   = Q~_blk K_tile^T * scale        16 x 16, d/4 MFMA 16x16x4 f64
+//   online per-landmark max, P = e^{L - max}, Z^ += row sums of P
+//   T^ <- T^ * e^{max_old - max_new} + P V_tile   16 x dv, 4 * dv/16 MFMAs
+// v_mfma_f64_16x16x4f64 operand layout (wave64): A[i][k] in lane i + 16 k,
+// B[k][j] in lane j + 16 k, and D[i][j] in lane j + 16 (i % 4), element i / 4.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// One block per (group, head).  Static LDS: Q~ (f32), a key tile, a value tile,
-// the tile's logits / weights, per-landmark running max and rescale.
-__global__ __launch_bounds__(kThreads) void far_replay_kernel(DevState s, PrefillIO io)
+template <int D, int DV>
+__global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
 {
+    constexpr int KS = D / 4;    // k-steps of the logit product
+    constexpr int CB = DV / 16;  // 16-wide column blocks of T^
+    constexpr int TK = 16;       // keys per tile
     const int gh = blockIdx.x, H = s.hpk, g = gh / H;
-    const int m = s.m, d = s.d, dv = s.dv, tid = threadIdx.x;
+    const int m = s.m, tid = threadIdx.x, lane = tid & 63, rb = tid >> 6, nthr = blockDim.x;
     const int S = s.sink, T = io.T, nf = T - S - s.w;
     const double sc = (double)s.scale;
     const double NEG_INF = -__builtin_inf();
 
-    __shared__ float q_lds[kMaxLandmarks * 128];
-    __shared__ float k_lds[kTile][128 + 1];
-    __shared__ float v_lds[kTile][128];
-    __shared__ double p_lds[kMaxLandmarks][kTile];
-    __shared__ double mx_lds[kMaxLandmarks], fac_lds[kMaxLandmarks], z_lds[kMaxLandmarks];
+    __shared__ float k_lds[TK][D + 1];
+    __shared__ float v_lds[TK][DV + 4];
+    __shared__ double p_lds[4][16][17];
 
-    const float *qt = s.q_tilde + (size_t)gh * m * d;
-    for (int t = tid; t < m * d; t += kThreads) q_lds[t] = qt[t];
-    if (tid < m) {
-        mx_lds[tid] = NEG_INF;
-        z_lds[tid] = 0.0;
+    const int li = lane & 15, lk = lane >> 4;  // A/B fragment coordinates
+    // Q~ block of this wave in LDS (rows past m are zero)
+    __shared__ float q_lds[4][16][D + 1];
+    for (int t = lane; t < 16 * D; t += 64) {
+        const int ii = t / D, c = t - ii * D, i = rb * 16 + ii;
+        q_lds[rb][ii][c] = (i < m) ? s.q_tilde[((size_t)gh * m + i) * D + c] : 0.0f;
     }
-    // accumulator entries owned by this thread: t = tid + 256 k over [m][dv]
-    constexpr int kAcc = kMaxLandmarks * 128 / kThreads;
-    double acc[kAcc];
+    f64x4 tacc[CB];
 #pragma unroll
-    for (int k = 0; k < kAcc; ++k) acc[k] = 0.0;
-    __syncthreads();
-
-    const float *K = io.k + ((size_t)g * T + S) * d;
-    const float *V = io.v + ((size_t)g * T + S) * dv;
-    for (int j0 = 0; j0 < nf; j0 += kTile) {
-        const int nt = min(kTile, nf - j0);
-        for (int t = tid; t < kTile * d; t += kThreads) {
-            const int jj = t / d, c = t - jj * d;
-            k_lds[jj][c] = jj < nt ? K[(size_t)(j0 + jj) * d + c] : 0.0f;
-        }
-        for (int t = tid; t < kTile * dv; t += kThreads) {
-            const int jj = t / dv, c = t - jj * dv;
-            v_lds[jj][c] = jj < nt ? V[(size_t)(j0 + jj) * dv + c] : 0.0f;
-        }
-        __syncthreads();
-        // logits of the tile
-        for (int t = tid; t < m * kTile; t += kThreads) {
-            const int i = t / kTile, jj = t - i * kTile;
-            double l = NEG_INF;
-            if (jj < nt) {
-                double a = 0.0;
-                for (int c = 0; c < d; ++c) a = fma((double)q_lds[i * d + c], (double)k_lds[jj][c], a);
-                l = a * sc;
-            }
-            p_lds[i][jj] = l;
-        }
-        __syncthreads();
-        // per-landmark max over the tile and the rescale of earlier mass
-        if (tid < m) {
-            double tmax = NEG_INF;
-            for (int jj = 0; jj < nt; ++jj) tmax = fmax(tmax, p_lds[tid][jj]);
-            const double old = mx_lds[tid];
-            const double nw = fmax(old, tmax);
-            const double f = exp(old - nw);  // 0 on the first tile
-            fac_lds[tid] = f;
-            mx_lds[tid] = nw;
-            double z = z_lds[tid] * f;
-            for (int jj = 0; jj < nt; ++jj) {
-                const double p = exp(p_lds[tid][jj] - nw);
-                p_lds[tid][jj] = p;
-                z += p;
-            }
-            for (int jj = nt; jj < kTile; ++jj) p_lds[tid][jj] = 0.0;
-            z_lds[tid] = z;
-        }
-        __syncthreads();
+    for (int cb = 0; cb < CB; ++cb) tacc[cb] = f64x4{0.0, 0.0, 0.0, 0.0};
+    double mx[4], zs[4];
 #pragma unroll
-        for (int k = 0; k < kAcc; ++k) {
-            const int t = tid + kThreads * k;
-            if (t < m * dv) {
-                const int i = t / dv, c = t - i * dv;
-                double a = acc[k] * fac_lds[i];
-#pragma unroll
-                for (int jj = 0; jj < kTile; ++jj) a = fma(p_lds[i][jj], (double)v_lds[jj][c], a);
-                acc[k] = a;
-            }
-        }
-        __syncthreads();
+    for (int r = 0; r < 4; ++r) {
+        mx[r] = NEG_INF;
+        zs[r] = 0.0;
     }
 
-    // Store at the scale of the f32 running max actually kept in the state.
-    if (tid < m) {
-        const float mf = (float)mx_lds[tid];
-        const double corr = exp(mx_lds[tid] - (double)mf);
-        fac_lds[tid] = corr;
-        s.m_max[(size_t)gh * m + tid] = mf;
-        s.z_hat[(size_t)gh * m + tid] = z_lds[tid] * corr;
-    }
-    __syncthreads();
-    float *th = s.t_hat + (size_t)gh * m * dv;
+    const float *K = io.k + ((size_t)g * T + S) * D;
+    const float *V = io.v + ((size_t)g * T + S) * DV;
+    for (int j0 = 0; j0 < nf; j0 += TK) {
+        const int nt = min(TK, nf - j0);
+        for (int t = tid; t < TK * (D / 4); t += nthr) {
+            const int jj = t / (D / 4), c4 = t - jj * (D / 4);
+            float4 x = jj < nt ? reinterpret_cast<const float4 *>(K + (size_t)(j0 + jj) * D)[c4]
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            k_lds[jj][c4 * 4 + 0] = x.x;
+            k_lds[jj][c4 * 4 + 1] = x.y;
+            k_lds[jj][c4 * 4 + 2] = x.z;
+            k_lds[jj][c4 * 4 + 3] = x.w;
+        }
+        for (int t = tid; t < TK * (DV / 4); t += nthr) {
+            const int jj = t / (DV / 4), c4 = t - jj * (DV / 4);
+            float4 x = jj < nt ? reinterpret_cast<const float4 *>(V + (size_t)(j0 + jj) * DV)[c4]
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<float4 *>(&v_lds[jj][c4 * 4]) = x;
+        }
+        __syncthreads();
+
+        // logits of this landmark block against the tile
+        f64x4 L = {0.0, 0.0, 0.0, 0.0}, L2 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int k = 0; k < kAcc; ++k) {
-        const int t = tid + kThreads * k;
-        if (t < m * dv) th[t] = (float)(acc[k] * fac_lds[t / dv]);
+        for (int ks = 0; ks < KS; ks += 2) {
+            L = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q_lds[rb][li][ks * 4 + lk],
+                                                    (double)k_lds[li][ks * 4 + lk], L, 0, 0, 0);
+            L2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q_lds[rb][li][ks * 4 + 4 + lk],
+                                                     (double)k_lds[li][ks * 4 + 4 + lk], L2, 0, 0, 0);
+        }
+        L += L2;
+        // lane holds L[row lk + 4 r][key li]
+        const bool live = li < nt;
+        double p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const double l = live ? L[r] * sc : NEG_INF;
+            double t = l;
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) t = fmax(t, __shfl_xor(t, off, 64));
+            const double nw = fmax(mx[r], t);
+            const double f = exp(mx[r] - nw);  // 0 on the first tile
+            mx[r] = nw;
+            p[r] = live ? exp(l - nw) : 0.0;
+            double ps = p[r];
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 64);
+            zs[r] = zs[r] * f + ps;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) tacc[cb][r] *= f;
+        }
+        // P from the result layout to the A-operand layout through LDS
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p_lds[rb][lk + 4 * r][li] = p[r];
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        double pa[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) pa[kk] = p_lds[rb][li][kk * 4 + lk];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                tacc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                    pa[kk], (double)v_lds[kk * 4 + lk][cb * 16 + li], tacc[cb], 0, 0, 0);
+        __syncthreads();
+    }
+
+    // store at the scale of the f32 running max kept in the state
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = rb * 16 + lk + 4 * r;
+        if (i >= m) continue;
+        const float mf = (float)mx[r];
+        const double corr = exp(mx[r] - (double)mf);
+        if (li == 0) {
+            s.m_max[(size_t)gh * m + i] = mf;
+            s.z_hat[(size_t)gh * m + i] = zs[r] * corr;
+        }
+        float *th = s.t_hat + ((size_t)gh * m + i) * DV;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) th[cb * 16 + li] = (float)(tacc[cb][r] * corr);
     }
 }
 
@@ -333,7 +356,13 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
         hipLaunchKernelGGL(gram_pinv_kernel, dim3(s.G * s.hpk), dim3(kThreads), lds, stream, s, io, kRidgeRel);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(far_replay_kernel, dim3(s.G * s.hpk), dim3(kThreads), 0, stream, s, io);
+    const int nrb = (s.m + 15) / 16;
+    if (s.d == 128 && s.dv == 128)
+        hipLaunchKernelGGL((far_mfma_kernel<128, 128>), dim3(s.G * s.hpk), dim3(64 * nrb), 0, stream, s, io);
+    else if (s.d == 64 && s.dv == 64)
+        hipLaunchKernelGGL((far_mfma_kernel<64, 64>), dim3(s.G * s.hpk), dim3(64 * nrb), 0, stream, s, io);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
