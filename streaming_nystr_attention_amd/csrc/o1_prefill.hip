@@ -8,8 +8,8 @@
 //   scatter_kernel     grid G: sinks (prompt rows 0..sink-1) and the ring (the
 //                      last w prompt keys, key j in slot (j - sink) mod w), the
 //                      ring head and far_len after the replay.
-//   gram_pinv_kernel   grid G * hpk: A = exp(Q~ K~^T * scale) in f64, G = A^T A,
-//                      lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
+//   gram_pinv_kernel   grid G * hpk: A = exp(Q~ K~^T * scale) and G = A^T A on f64
+//                      MFMA, lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
 //                      G + lambda I in LDS (lambda x10 on a failed pivot, up to 12
 //                      attempts, then diag(1/mean diag)), M = (G + lambda I)^-1 A^T.
 //   far_mfma_kernel    grid G * hpk: the far field of keys sink .. T-w-1, i.e. the
@@ -89,36 +89,66 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO
     for (int h = threadIdx.x; h < s.hpk; h += kThreads) s.far_len[(size_t)g * s.hpk + h] = evictions;
 }
 
-// One block per (group, head).  Dynamic LDS: A and L, each [m][m + 1] f64.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// One block per (group, head), 256 threads.  Dynamic LDS: A, G and L, each
+// [mp][mp + 1] f64 with mp = m rounded up to 16 (padding rows/columns of A are 0).
+// The exp-Gram and A^T A run on v_mfma_f64_16x16x4f64 (operand layout: A[i][k] in
+// lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i % 4),
+// element i / 4); the Cholesky with its retries and the triangular solves run on
+// the vector units from LDS.
 __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, PrefillIO io, double ridge_rel)
 {
     const int gh = blockIdx.x, H = s.hpk, g = gh / H, h = gh - g * H;
-    const int m = s.m, d = s.d, ld = m + 1, tid = threadIdx.x;
+    const int m = s.m, d = s.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = (m + 15) / 16, mp = nb * 16, ld = mp + 1;
     extern __shared__ double lds[];
     double *A = lds;
-    double *L = lds + (size_t)m * ld;
+    double *Gm = lds + (size_t)mp * ld;
+    double *L = lds + 2 * (size_t)mp * ld;
     __shared__ double mean_diag_s;
     __shared__ int fail_s;
 
     const double *kt = io.lm64 + ((size_t)g * (1 + H)) * m * d;
     const double *qt = io.lm64 + ((size_t)g * (1 + H) + 1 + h) * m * d;
     const double sc = (double)s.scale;
+    const int li = lane & 15, lk = lane >> 4;
 
-    // exp-Gram: A[i][j] = exp(q~_i . k~_j * scale), contraction in index order
-    for (int t = tid; t < m * m; t += kThreads) {
-        const int i = t / m, j = t - i * m;
-        double acc = 0.0;
-        for (int c = 0; c < d; ++c) acc = fma(qt[(size_t)i * d + c], kt[(size_t)j * d + c], acc);
-        A[i * ld + j] = exp(acc * sc);
+    // exp-Gram: A[i][j] = exp(q~_i . k~_j * scale), one 16x16 block per wave pass
+    for (int blk = wave; blk < nb * nb; blk += kThreads / 64) {
+        const int bi = blk / nb, bj = blk - bi * nb;
+        const int qi = bi * 16 + li, kj = bj * 16 + li;
+        const double *qrow = qt + (size_t)(qi < m ? qi : 0) * d;
+        const double *krow = kt + (size_t)(kj < m ? kj : 0) * d;
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
+        for (int ks = 0; ks < d / 4; ks += 2) {
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + lk] : 0.0,
+                                                      kj < m ? krow[ks * 4 + lk] : 0.0, acc, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + 4 + lk] : 0.0,
+                                                       kj < m ? krow[ks * 4 + 4 + lk] : 0.0, acc2, 0, 0, 0);
+        }
+        acc += acc2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = bi * 16 + lk + 4 * r, j = bj * 16 + li;
+            A[i * ld + j] = (i < m && j < m) ? exp(acc[r] * sc) : 0.0;
+        }
+    }
+    __syncthreads();
+    // G = A^T A (padding rows of A are zero)
+    for (int blk = wave; blk < nb * nb; blk += kThreads / 64) {
+        const int bi = blk / nb, bj = blk - bi * nb;
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+        for (int ks = 0; ks < mp / 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A[(ks * 4 + lk) * ld + bi * 16 + li],
+                                                      A[(ks * 4 + lk) * ld + bj * 16 + li], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Gm[(bi * 16 + lk + 4 * r) * ld + bj * 16 + li] = acc[r];
     }
     __syncthreads();
     if (tid == 0) {
         double md = 0.0;
-        for (int i = 0; i < m; ++i) {
-            double acc = 0.0;
-            for (int k = 0; k < m; ++k) acc = fma(A[k * ld + i], A[k * ld + i], acc);
-            md += acc;
-        }
+        for (int i = 0; i < m; ++i) md += Gm[i * ld + i];
         mean_diag_s = md / (double)m;
     }
     __syncthreads();
@@ -127,12 +157,9 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
     int result = kRidgeTries + 1;
 
     for (int attempt = 1; attempt <= kRidgeTries; ++attempt) {
-        // L <- A^T A + lambda I
         for (int t = tid; t < m * m; t += kThreads) {
             const int i = t / m, j = t - i * m;
-            double acc = 0.0;
-            for (int k = 0; k < m; ++k) acc = fma(A[k * ld + i], A[k * ld + j], acc);
-            L[i * ld + j] = acc + (i == j ? lambda : 0.0);
+            L[i * ld + j] = Gm[i * ld + j] + (i == j ? lambda : 0.0);
         }
         __syncthreads();
         // Cholesky, one column at a time: pivot, then the column below it.
@@ -204,7 +231,6 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
 //   T^ <- T^ * e^{max_old - max_new} + P V_tile   16 x dv, 4 * dv/16 MFMAs
 // v_mfma_f64_16x16x4f64 operand layout (wave64): A[i][k] in lane i + 16 k,
 // B[k][j] in lane j + 16 k, and D[i][j] in lane j + 16 (i % 4), element i / 4.
-typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int D, int DV>
 __global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
@@ -349,7 +375,8 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
     if (io.fz_mu) {
         hipLaunchKernelGGL(copy_mu_kernel, dim3(1024), dim3(kThreads), 0, stream, s, io.fz_mu);
     } else {
-        const size_t lds = sizeof(double) * 2 * (size_t)s.m * (s.m + 1);
+        const size_t mp = (size_t)((s.m + 15) / 16) * 16;
+        const size_t lds = sizeof(double) * 3 * mp * (mp + 1);
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gram_pinv_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
