@@ -60,6 +60,7 @@ struct DecodeShape {
     static constexpr bool PRE_T = HPK * TPT <= (NT == 256 ? 8 : 32);   // T^ prefetched in registers
     static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : 8;    // V rows prefetched per lane
     static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
+    static constexpr int MB = NT == 256 ? 16 : 32;                     // M rows in flight (unstaged M)
     static constexpr int RED_CAP = 16384 / (NW * DV * 8);              // heads per LDS round
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
@@ -297,15 +298,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
                 if (act) u = fma(fa, (double)mu[a * m + lane], u);
             }
         } else {
+            // M from global memory, MB rows per lane in flight
             const float *mu = s.mu + (gh0 + h) * (size_t)m * m;
-            for (int a0 = 0; a0 < m; a0 += 8) {
-                float mv[8];
+            const int col = act ? lane : 0;
+            for (int a0 = 0; a0 < m; a0 += C::MB) {
+                float mv[C::MB];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) mv[j] = (act && a0 + j < m) ? mu[(size_t)(a0 + j) * m + lane] : 0.f;
+                for (int j = 0; j < C::MB; ++j) mv[j] = mu[(size_t)min(a0 + j, m - 1) * m + col];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < C::MB; ++j) {
                     const double fa = __shfl(fh, (a0 + j) & 63, 64);
-                    u = fma(fa, (double)mv[j], u);
+                    if (a0 + j < m && act) u = fma(fa, (double)mv[j], u);
                 }
             }
         }
