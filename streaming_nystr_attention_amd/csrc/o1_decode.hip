@@ -61,6 +61,7 @@ struct DecodeShape {
     static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : 8;    // V rows prefetched per lane
     static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
     static constexpr int MB = NT == 256 ? 16 : 32;                     // M rows in flight (unstaged M)
+    static constexpr bool NTL = NT == 256;                             // streaming accesses (large grids)
     static constexpr int RED_CAP = 16384 / (NW * DV * 8);              // heads per LDS round
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
@@ -69,6 +70,32 @@ struct DecodeShape {
     static_assert(CH <= 64 && VCH <= 64, "rows wider than 256 floats are not compiled");
     static_assert(RED_H >= 1 && HPK % RED_H == 0, "heads must split into reduction rounds");
 };
+
+// Streaming (nontemporal) accesses for state that is touched once per step and
+// is far larger than the caches; plain accesses otherwise.
+typedef float nt_f4 __attribute__((ext_vector_type(4)));
+
+template <bool NTL>
+__device__ __forceinline__ float4 ld4(const float4 *p)
+{
+    if constexpr (NTL) {
+        const nt_f4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_f4 *>(p));
+        return make_float4(t.x, t.y, t.z, t.w);
+    } else {
+        return *p;
+    }
+}
+
+template <bool NTL>
+__device__ __forceinline__ void st4(float4 *p, const float4 v)
+{
+    if constexpr (NTL) {
+        const nt_f4 t = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<nt_f4 *>(p));
+    } else {
+        *p = v;
+    }
+}
 
 __device__ __forceinline__ double dot4(const float4 a, const float4 b)
 {
@@ -184,7 +211,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
                 const int r = min(base + u * C::RPB + rsub, NA - 1);
                 const float4 *row = (r < R) ? nk + (size_t)r * C::CH : kt + (size_t)(r - R) * C::CH;
 #pragma unroll
-                for (int k = 0; k < C::CPL; ++k) x[u][k] = row[sub + C::LPR * k];
+                for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
             }
 #pragma unroll
             for (int u = 0; u < C::UNR; ++u) {
@@ -223,7 +250,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
             for (int u = 0; u < C::UNR; ++u) {
                 const int r = min(base + u * C::RPB + rsub, NQ - 1);
 #pragma unroll
-                for (int k = 0; k < C::CPL; ++k) x[u][k] = qt[(size_t)r * C::CH + sub + C::LPR * k];
+                for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(qt + (size_t)r * C::CH + sub + C::LPR * k);
             }
 #pragma unroll
             for (int u = 0; u < C::UNR; ++u) {
@@ -244,13 +271,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
 #pragma unroll
                 for (int j = 0; j < C::TPT; ++j) {
                     const int b = min(rl + j * C::RL, m - 1);
-                    tpre[h][j] = th[((size_t)h * m + b) * C::VCH + cc];
+                    tpre[h][j] = ld4<C::NTL>(th + ((size_t)h * m + b) * C::VCH + cc);
                 }
         }
 #pragma unroll
         for (int j = 0; j < C::VPRE; ++j) {
             const int r = min(rl + j * C::RL, R - 1);
-            vpre[j] = nv[(size_t)r * C::VCH + cc];
+            vpre[j] = ld4<C::NTL>(nv + (size_t)r * C::VCH + cc);
         }
     }
     __syncthreads();
@@ -348,13 +375,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
                 const size_t idx = ((size_t)h * m + b) * C::VCH + cc;
                 float4 t;
                 if constexpr (C::PRE_T) t = tpre[h][j];
-                else t = th[idx];
+                else t = ld4<C::NTL>(th + idx);
                 const double rb = r_s[h][b], eb = e_s[h][b], gb = gain_s[h][b];
                 const double t0 = fma((double)t.x, rb, eb * (double)vev.x);
                 const double t1 = fma((double)t.y, rb, eb * (double)vev.y);
                 const double t2 = fma((double)t.z, rb, eb * (double)vev.z);
                 const double t3 = fma((double)t.w, rb, eb * (double)vev.w);
-                th[idx] = make_float4((float)t0, (float)t1, (float)t2, (float)t3);
+                st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
                 acc[h][0] = fma(gb, t0, acc[h][0]);
                 acc[h][1] = fma(gb, t1, acc[h][1]);
                 acc[h][2] = fma(gb, t2, acc[h][2]);
@@ -381,7 +408,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
         for (int r0 = rl + C::VPRE * C::RL; r0 < R; r0 += C::VU * C::RL) {
             float4 x[C::VU];
 #pragma unroll
-            for (int j = 0; j < C::VU; ++j) x[j] = nv[(size_t)min(r0 + j * C::RL, R - 1) * C::VCH + cc];
+            for (int j = 0; j < C::VU; ++j) x[j] = ld4<C::NTL>(nv + (size_t)min(r0 + j * C::RL, R - 1) * C::VCH + cc);
 #pragma unroll
             for (int j = 0; j < C::VU; ++j) {
                 const int r = r0 + j * C::RL;
