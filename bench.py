@@ -38,7 +38,7 @@ DECODE_SRC = os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", "o1_dec
 # a 1 GiB copy in the same process), keyed by (workload, decode source sha256 prefix).
 # A changed kernel source has no entry, and the roofline's traffic is then reported as null.
 MEASURED_TRAFFIC = {
-    ("qwen3_stack_b64", "5b11cee8cf2d6752"): 3793410551,
+    ("qwen3_stack_b64", "2c62cf6bdce9dd08"): 3788978077,
 }
 
 
