@@ -1,0 +1,123 @@
+"""GPU tests of the state interface: field copies, partial frozen prefills,
+re-prefill on a handle, and the info record."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import streaming_nystr_attention_amd as P
+from streaming_nystr_attention_amd import workloads as W
+
+from parity_util import DECODE_TOL, DecodeRun, cpu, oracle_decode, oracle_prefill, row_errors, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    P.lib()
+    yield
+
+
+WL = W.Workload("state", 2, 1, 3, 2, 128, 128, 16, 32, 4, T=180, steps=40, q_std=2.0, k_std=2.0,
+                seed=31)
+
+
+def test_field_roundtrip_bit_exact():
+    wl = WL
+    q, k, v = W.prompt(wl, DEV)
+    grp = P.O1Groups(wl.config)
+    grp.prefill(q, k, v)
+    for field in range(12):
+        a = grp.read(field, device=DEV)
+        grp.write(field, torch.zeros_like(a))
+        assert torch.count_nonzero(grp.read(field, device=DEV)) == 0
+        grp.write(field, a)
+        assert torch.equal(grp.read(field, device=DEV), a), field
+        # host-side copies go through the same entry points
+        h = grp.read(field, device="cpu")
+        assert torch.equal(h.to(DEV), a)
+    with pytest.raises(P.O1Error) as e:
+        grp.write(P.FIELD_T_HAT, torch.zeros(3, device=DEV))
+    assert e.value.status == P.O1_EINVAL
+
+
+def test_decode_from_uploaded_oracle_far_field():
+    """Decode parity with the whole far field (T^, Z^, running max) taken from
+    the oracle's sequential replay, so the decode kernel is checked apart from
+    the prefill's far-field kernel."""
+    wl = WL
+    G, H, m = wl.groups, wl.hpk, wl.m_eff
+    q, k, v = W.prompt(wl, DEV)
+    orc = oracle_prefill(wl, cpu(q), cpu(k), cpu(v))
+    sts = [g.state() for g in orc]
+    frozen = tuple(torch.from_numpy(np.stack([s[n] for s in sts])).to(DEV)
+                   for n in ("k_tilde", "q_tilde", "mu"))
+    grp = P.O1Groups(wl.config)
+    grp.prefill(q, k, v, frozen=frozen)
+    th = torch.from_numpy(np.stack([s["t_hat"] for s in sts]).astype(np.float32)).to(DEV)
+    zh = torch.from_numpy(np.stack([s["z_hat"] for s in sts])).to(DEV)
+    mx = torch.from_numpy(np.stack([s["m_max"] for s in sts]).astype(np.float32)).to(DEV)
+    # the f32 running max must stay consistent with T^ and Z^: rescale them to it
+    corr = torch.exp(torch.from_numpy(np.stack([s["m_max"] for s in sts])).to(DEV) - mx.double())
+    grp.write(P.FIELD_T_HAT, (th.double() * corr[..., None]).float().contiguous().view(-1))
+    grp.write(P.FIELD_Z_HAT, (zh * corr).contiguous().view(-1))
+    grp.write(P.FIELD_M_MAX, mx.contiguous().view(-1))
+    run = DecodeRun(wl, list(range(G)), wl.steps)
+    qs, ks, vs, gout = run.run(grp)
+    out, alt, amb = oracle_decode(orc, qs, ks, vs)
+    err = row_errors(gout, out, alt, amb)
+    say(f"  uploaded far field: max_err={err.max():.3e}")
+    assert err.max() <= DECODE_TOL
+
+
+def test_frozen_mixing_matrix_only():
+    """frozen = (None, None, M): landmarks computed on the device, M given."""
+    wl = WL
+    G, H, m = wl.groups, wl.hpk, wl.m_eff
+    q, k, v = W.prompt(wl, DEV)
+    rng = np.random.default_rng(5)
+    mu = (rng.standard_normal((G, H, m, m)) * 0.1).astype(np.float32)
+    orc = oracle_prefill(wl, cpu(q), cpu(k), cpu(v), frozen=[O.Frozen(mu=mu[i]) for i in range(G)])
+    grp = P.O1Groups(wl.config)
+    grp.prefill(q, k, v, frozen=(None, None, torch.from_numpy(mu).to(DEV)))
+    assert torch.equal(grp.read(P.FIELD_MU).view(G, H, m, m), torch.from_numpy(mu))
+    kt = grp.read(P.FIELD_K_TILDE).view(G, m, wl.d).numpy()
+    for i, g in enumerate(orc):
+        np.testing.assert_array_equal(kt[i], g.state()["k_tilde"])
+    tries = grp.read(P.FIELD_TRIES).numpy()
+    assert (tries == 0).all()
+    run = DecodeRun(wl, list(range(G)), 20)
+    qs, ks, vs, gout = run.run(grp)
+    out, alt, amb = oracle_decode(orc, qs, ks, vs)
+    err = row_errors(gout, out, alt, amb)
+    say(f"  frozen M only: max_err={err.max():.3e}")
+    assert err.max() <= DECODE_TOL
+
+
+def test_reprefill_resets_state_and_info():
+    wl = WL
+    G = wl.groups
+    grp = P.O1Groups(wl.config)
+    info = grp.info()
+    assert info.sealed == 0 and info.m_eff == 0 and info.state_bytes > 0
+    q, k, v = W.prompt(wl, DEV)
+    grp.prefill(q, k, v)
+    out = torch.empty(G, wl.hpk, wl.dv, device=DEV)
+    for t in range(5):
+        grp.step(*W.decode_inputs(wl, t, DEV), out)
+    info = grp.info()
+    assert info.sealed == 1 and info.steps == 5 and info.prompt_len == wl.T and info.m_eff == wl.m_eff
+    # a second, shorter prompt on the same handle: state as if freshly created
+    wl2 = wl.with_(T=120, seed=32)
+    q2, k2, v2 = W.prompt(wl2, DEV)
+    grp.prefill(q2, k2, v2)
+    info = grp.info()
+    assert info.steps == 0 and info.prompt_len == 120 and info.m_eff == wl2.m_eff
+    fresh = P.O1Groups(wl.config)
+    fresh.prefill(q2, k2, v2)
+    for field in range(12):
+        assert torch.equal(grp.read(field), fresh.read(field)), field
