@@ -106,6 +106,44 @@ def cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads, per_thread):
     }
 
 
+def exact_comparator(wl, ctx, nystrom_us, dev):
+    """Exact grouped-GQA attention over `ctx` stored keys per group at the same
+    shape (o1_exact_attend): the O(context) decode the O(1) operator replaces."""
+    import torch
+
+    import streaming_nystr_attention_amd as P
+
+    G, H = wl.groups, wl.hpk
+    try:
+        g = torch.Generator(device=dev).manual_seed(77)
+        kc = torch.randn(G, ctx, wl.d, device=dev, generator=g)
+        vc = torch.randn(G, ctx, wl.dv, device=dev, generator=g)
+        q = torch.randn(G, H, wl.d, device=dev, generator=g)
+        out = torch.empty(G, H, wl.dv, device=dev)
+        desc = P._exact_desc(q, kc, ctx, 0, None)
+        need = P.o1_exact_workspace_bytes(desc)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            P.o1_exact_attend(q, kc, vc, out, ctx, 0, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            P.o1_exact_attend(q, kc, vc, out, ctx, 0, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = G * ctx * (wl.d + wl.dv) * 4 + G * H * (wl.d + wl.dv) * 4
+        del kc, vc
+        torch.cuda.empty_cache()
+        return {"context": ctx, "us_per_launch": us, "bytes_per_launch": nbytes,
+                "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+                "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                "nystrom_decode_us": nystrom_us, "exact_over_nystrom": us / nystrom_us}
+    except Exception as exc:  # the comparator is context, never the headline
+        return {"context": ctx, "error": str(exc)[:200]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +154,9 @@ def main():
                     help="decode steps per job (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-per-thread", type=int, default=32, help="oracle groups per thread")
+    ap.add_argument("--exact-context", type=int, default=-1,
+                    help="also time the exact grouped-GQA comparator over this many keys per "
+                         "group (-1: the job's final context, 0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -225,7 +266,19 @@ def main():
             "bytes_per_group_step": rd + wr,
         },
     }
+    ctx = wl.T + n_dec if args.exact_context < 0 else args.exact_context
+    if ctx > 0:
+        del Q, K, V  # make room for the comparator's KV cache
+        torch.cuda.empty_cache()
+        res["exact_comparator"] = exact_comparator(wl, ctx, launch_us, dev)
+        Q = K = V = None
     if not args.no_cpu_baseline:
+        if Q is None:
+            Q = torch.empty(n_dec, G, H, wl.d, device=dev)
+            K = torch.empty(n_dec, G, wl.d, device=dev)
+            V = torch.empty(n_dec, G, wl.dv, device=dev)
+            for t in range(n_dec):
+                W.decode_inputs(wl, t, dev, out=(Q[t], K[t], V[t]))
         threads = max(1, min(16, os.cpu_count() or 1))
         res["cpu_baseline"] = cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads,
                                            args.cpu_per_thread)

@@ -165,6 +165,39 @@ int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes);
 int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, void *stream);
 int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, void *stream);
 
+/* ---- exact grouped-GQA attention: the O(p) comparator -------------------
+ * Exact softmax attention of every query head of a KV group over that group's
+ * stored keys (LayerKvCache::attend_group on the docs.rs LayerKvCache page:
+ * one pass over the K rows and one over the V rows for all heads of a group;
+ * keys before `first` get zero probability):
+ *   out[g][h] = sum_{j = first .. n_keys-1} softmax_j(q[g][h] . k[g][j] * scale) v[g][j]
+ * The caller owns the cache; nothing is stored between calls.  q8 storage,
+ * logit soft-capping and the importance accumulator of that method are not
+ * part of this entry point. */
+typedef struct o1_exact_desc {
+    int32_t n_groups; /* G                                        (>= 1)      */
+    int32_t hpk;      /* query heads per group                   {1,2,4,8}   */
+    int32_t d, dv;    /* widths, d == dv                         {64, 128}   */
+    int32_t cap;      /* rows allocated per group (row stride of k and v)   */
+    int32_t first;    /* earliest visible key, 0 <= first < n_keys          */
+    int32_t n_keys;   /* keys 0 .. n_keys-1 are stored, n_keys <= cap       */
+    float scale;      /* score scale; <= 0 selects f32 1/sqrt(d)            */
+} o1_exact_desc;
+
+/* Bytes of device work space o1_exact_attend needs for `desc` (0 when it
+ * needs none).  Errors: O1_EINVAL, O1_EUNSUPPORTED. */
+int o1_exact_workspace_bytes(const o1_exact_desc *desc, size_t *bytes);
+
+/* Exact attention for all G groups in one launch (two when the key range is
+ * split across work-groups):
+ *   q [G][hpk][d], k [G][cap][d], v [G][cap][dv] -> out [G][hpk][dv]
+ * `workspace` (device, caller-owned) must hold o1_exact_workspace_bytes; it
+ * may be NULL when that is 0.  No allocation, no host synchronisation.
+ * Errors: O1_EINVAL (null pointer, bad sizes, short work space),
+ * O1_EUNSUPPORTED, O1_EHIP. */
+int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, const float *v,
+                    float *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char *o1_last_error(void);
 

@@ -48,9 +48,15 @@ class o1_info(ctypes.Structure):
                 ("work_bytes", ctypes.c_uint64)]
 
 
+class o1_exact_desc(ctypes.Structure):
+    _fields_ = [("n_groups", ctypes.c_int32), ("hpk", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("cap", ctypes.c_int32), ("first", ctypes.c_int32),
+                ("n_keys", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
 EXPORTS = ("o1_create_groups", "o1_destroy_groups", "o1_prefill", "o1_step", "o1_get_info",
-           "o1_field_bytes", "o1_read_field", "o1_write_field", "o1_last_error",
-           "o1_abi_version")
+           "o1_field_bytes", "o1_read_field", "o1_write_field", "o1_exact_workspace_bytes",
+           "o1_exact_attend", "o1_last_error", "o1_abi_version")
 
 _lib = None
 
@@ -81,6 +87,12 @@ def lib():
     L.o1_read_field.argtypes = [vp, i32, vp, ctypes.c_size_t, vp]
     L.o1_write_field.restype = ctypes.c_int
     L.o1_write_field.argtypes = [vp, i32, vp, ctypes.c_size_t, vp]
+    L.o1_exact_workspace_bytes.restype = ctypes.c_int
+    L.o1_exact_workspace_bytes.argtypes = [ctypes.POINTER(o1_exact_desc),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    L.o1_exact_attend.restype = ctypes.c_int
+    L.o1_exact_attend.argtypes = [ctypes.POINTER(o1_exact_desc), vp, vp, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
     L.o1_last_error.restype = ctypes.c_char_p
     L.o1_last_error.argtypes = []
     L.o1_abi_version.restype = ctypes.c_int
@@ -184,6 +196,38 @@ def o1_write_field(handle, field: int, src, stream=None):
         raise ValueError("src must be contiguous")
     _check(lib().o1_write_field(handle, field, ctypes.c_void_p(src.data_ptr()), nbytes,
                                 _stream_handle(stream)))
+
+
+def _exact_desc(q, k, n_keys, first, scale):
+    G, H, d = q.shape
+    cap = k.shape[1]
+    return o1_exact_desc(G, H, d, d, cap, first, n_keys, 0.0 if scale is None else scale)
+
+
+def o1_exact_workspace_bytes(desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().o1_exact_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def o1_exact_attend(q, k, v, out, n_keys: int, first: int = 0, scale=None, workspace=None,
+                    stream=None):
+    """Exact grouped attention: q [G][hpk][d], k [G][cap][d], v [G][cap][dv] ->
+    out [G][hpk][dv] over keys first .. n_keys-1.  `workspace` is a device
+    tensor of at least o1_exact_workspace_bytes bytes (allocated here if None)."""
+    import torch
+
+    desc = _exact_desc(q, k, n_keys, first, scale)
+    G, H, d = q.shape
+    cap, dv = k.shape[1], v.shape[2]
+    need = o1_exact_workspace_bytes(desc)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp, wb = (None, 0) if workspace is None else (ctypes.c_void_p(workspace.data_ptr()),
+                                                   workspace.numel() * workspace.element_size())
+    _check(lib().o1_exact_attend(ctypes.byref(desc), _dev_ptr(q, "q", G * H * d),
+                                 _dev_ptr(k, "k", G * cap * d), _dev_ptr(v, "v", G * cap * dv),
+                                 _dev_ptr(out, "out", G * H * dv), wp, wb, _stream_handle(stream)))
 
 
 def o1_last_error() -> str:

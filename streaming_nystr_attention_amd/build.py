@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libo1.so")
-SOURCES = ["o1_api.hip", "o1_decode.hip", "o1_prefill.hip"]
+SOURCES = ["o1_api.hip", "o1_decode.hip", "o1_prefill.hip", "o1_exact.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -316,4 +316,66 @@ int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, v
     return ok();
 }
 
+static int exact_check(const o1_exact_desc *x, int *splits, size_t *bytes)
+{
+    if (!x) return fail(O1_EINVAL, "o1_exact: null descriptor");
+    if (x->n_groups < 1 || x->hpk < 1 || x->d < 1 || x->dv < 1 || x->cap < 1)
+        return fail(O1_EINVAL, "o1_exact: sizes must be >= 1");
+    if (x->n_keys < 1 || x->n_keys > x->cap || x->first < 0 || x->first >= x->n_keys)
+        return fail(O1_EINVAL, "o1_exact: need 0 <= first < n_keys <= cap (first=%d n_keys=%d cap=%d)",
+                    x->first, x->n_keys, x->cap);
+    if (!(x->d == x->dv && (x->d == 64 || x->d == 128)) ||
+        !(x->hpk == 1 || x->hpk == 2 || x->hpk == 4 || x->hpk == 8))
+        return fail(O1_EUNSUPPORTED, "o1_exact: compiled for d == dv in {64,128}, hpk in {1,2,4,8}");
+    *splits = o1::exact_splits(x->n_groups, x->n_keys - x->first);
+    *bytes = *splits == 1 ? 0
+                          : sizeof(double) * (size_t)x->n_groups * *splits * x->hpk * (x->dv + 2);
+    return O1_OK;
+}
+
+int o1_exact_workspace_bytes(const o1_exact_desc *desc, size_t *bytes)
+{
+    if (!bytes) return fail(O1_EINVAL, "o1_exact_workspace_bytes: null argument");
+    int splits = 0;
+    int rc = exact_check(desc, &splits, bytes);
+    return rc ? rc : ok();
+}
+
+int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, const float *v,
+                    float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int splits = 0;
+    size_t need = 0;
+    int rc = exact_check(desc, &splits, &need);
+    if (rc) return rc;
+    if (!q || !k || !v || !out) return fail(O1_EINVAL, "o1_exact_attend: null tensor");
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(O1_EINVAL, "o1_exact_attend: work space of %zu bytes needed", need);
+    const o1_exact_desc &x = *desc;
+    o1::ExactIO io;
+    io.q = q;
+    io.k = k;
+    io.v = v;
+    io.out = out;
+    io.G = x.n_groups;
+    io.hpk = x.hpk;
+    io.d = x.d;
+    io.dv = x.dv;
+    io.cap = x.cap;
+    io.first = x.first;
+    io.n_keys = x.n_keys;
+    const int visible = x.n_keys - x.first;
+    io.per_split = (visible + splits - 1) / splits;
+    splits = (visible + io.per_split - 1) / io.per_split;  // no empty ranges
+    io.scale = x.scale > 0.0f ? x.scale : 1.0f / sqrtf((float)x.d);
+    double *ws = static_cast<double *>(workspace);
+    const size_t parts = (size_t)x.n_groups * splits * x.hpk;
+    io.ws_max = ws;
+    io.ws_sum = ws ? ws + parts : nullptr;
+    io.ws_num = ws ? ws + 2 * parts : nullptr;
+    hipError_t err = o1::launch_exact(io, splits, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(O1_EHIP, "exact attention launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
 }  // extern "C"

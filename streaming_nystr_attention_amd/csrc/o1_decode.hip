@@ -71,67 +71,6 @@ struct DecodeShape {
     static_assert(RED_H >= 1 && HPK % RED_H == 0, "heads must split into reduction rounds");
 };
 
-// Streaming (nontemporal) accesses for state that is touched once per step and
-// is far larger than the caches; plain accesses otherwise.
-typedef float nt_f4 __attribute__((ext_vector_type(4)));
-
-template <bool NTL>
-__device__ __forceinline__ float4 ld4(const float4 *p)
-{
-    if constexpr (NTL) {
-        const nt_f4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_f4 *>(p));
-        return make_float4(t.x, t.y, t.z, t.w);
-    } else {
-        return *p;
-    }
-}
-
-template <bool NTL>
-__device__ __forceinline__ void st4(float4 *p, const float4 v)
-{
-    if constexpr (NTL) {
-        const nt_f4 t = {v.x, v.y, v.z, v.w};
-        __builtin_nontemporal_store(t, reinterpret_cast<nt_f4 *>(p));
-    } else {
-        *p = v;
-    }
-}
-
-__device__ __forceinline__ double dot4(const float4 a, const float4 b)
-{
-    double s = (double)a.x * (double)b.x;
-    s = fma((double)a.y, (double)b.y, s);
-    s = fma((double)a.z, (double)b.z, s);
-    s = fma((double)a.w, (double)b.w, s);
-    return s;
-}
-
-// Reduce N per-lane partial sums over aligned groups of W lanes.  Each halving
-// step exchanges half of the remaining values with the partner lane; lanes keep
-// the lower or upper half by their lane bit.  Returns, in every lane, the group
-// total of value index (lane % W) / (W / N).
-template <int W, int N>
-__device__ __forceinline__ double head_reduce(const double *v, int lane)
-{
-    if constexpr (N == 1) {
-        double x = v[0];
-#pragma unroll
-        for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-        return x;
-    } else {
-        constexpr int off = W / 2;
-        const bool hi = (lane & off) != 0;
-        double nv[N / 2];
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i) {
-            const double mine = hi ? v[N / 2 + i] : v[i];
-            const double send = hi ? v[i] : v[N / 2 + i];
-            nv[i] = mine + __shfl_xor(send, off, 64);
-        }
-        return head_reduce<W / 2, N / 2>(nv, lane);
-    }
-}
-
 template <int D, int DV, int HPK, int MM, int NT>
 __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
 {

@@ -1,0 +1,277 @@
+// Exact grouped-GQA decode attention over a stored KV cache: the comparator the
+// O(1) operator replaces (LayerKvCache::attend_group on the docs.rs LayerKvCache
+// page: all query heads of one KV group in one pass over the stored K rows and
+// one pass over the V rows; keys before `first` get zero probability).
+//
+//   out_h = sum_{j in [first, n_keys)} softmax_j(q_h . k_j * scale) v_j
+//
+// exact_attend_kernel: grid (G, splits), 256 threads.  A work-group owns one
+// key range of one group and walks it in chunks of kChunk keys with an online
+// per-head max: row-dot pass (f64, the decode kernel's lane split and head
+// reduction) -> per-head chunk max, weights and running sum -> V pass with the
+// running rescale.  With one split it writes the normalised output; otherwise
+// it writes (max, sum, numerator) partials that exact_combine_kernel merges.
+// Bound: HBM (n_keys * (d + dv) * 4 B per group, read once, nontemporal).
+#include "o1_internal.h"
+
+namespace o1 {
+namespace {
+
+constexpr int kNT = 256, kNW = kNT / 64, kChunk = 128;
+
+template <int D, int DV, int HPK>
+struct ExactShape {
+    static constexpr int CH = D / 4;
+    static constexpr int LPR_WANT = HPK <= 2 ? 8 : (HPK <= 4 ? 16 : 32);
+    static constexpr int LPR = LPR_WANT < CH ? LPR_WANT : CH;
+    static constexpr int CPL = CH / LPR;
+    static constexpr int RPW = 64 / LPR;
+    static constexpr int RPB = RPW * kNW;
+    static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 2 ? 4 : 8);
+    static constexpr int VCH = DV / 4;
+    static constexpr int RL = kNT / VCH;
+    static constexpr int RED_CAP = 16384 / (kNW * DV * 8);
+    static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
+    static_assert(HPK <= LPR && HPK % RED_H == 0, "unsupported head count");
+};
+
+template <int D, int DV, int HPK>
+__global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
+{
+    using C = ExactShape<D, DV, HPK>;
+    const int g = blockIdx.x, sp = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int k0 = a.first + sp * a.per_split;
+    const int k1 = min(k0 + a.per_split, a.n_keys);
+    const double scale = (double)a.scale;
+    const double NEG_INF = -__builtin_inf();
+
+    __shared__ float4 q_s[HPK][C::CH];
+    __shared__ double lg_s[HPK][kChunk];
+    __shared__ double fac_s[HPK];
+    __shared__ double red_s[kNW][C::RED_H * DV];
+
+    const size_t gh0 = (size_t)g * HPK;
+    const float4 *qg = reinterpret_cast<const float4 *>(a.q) + gh0 * C::CH;
+    for (int i = tid; i < HPK * C::CH; i += kNT) (&q_s[0][0])[i] = qg[i];
+    const float4 *kc = reinterpret_cast<const float4 *>(a.k) + (size_t)g * a.cap * C::CH;
+    const float4 *vc = reinterpret_cast<const float4 *>(a.v) + (size_t)g * a.cap * C::VCH;
+
+    const int sub = lane % C::LPR, rsub = lane / C::LPR;
+    constexpr int HSTRIDE = C::LPR / HPK;
+    const int my_head = sub / HSTRIDE;
+    const bool writer = (sub % HSTRIDE) == 0;
+    const int cc = tid % C::VCH, rl = tid / C::VCH;
+
+    constexpr int HPW = (HPK + kNW - 1) / kNW;  // heads per wave: h = wave + j * kNW
+    double run_max[HPW], run_sum[HPW];          // running max / sum of the wave's heads
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+        run_max[j] = NEG_INF;
+        run_sum[j] = 0.0;
+    }
+    double acc[HPK][4];
+#pragma unroll
+    for (int h = 0; h < HPK; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.0;
+    __syncthreads();
+
+    for (int c0 = k0; c0 < k1; c0 += kChunk) {
+        const int nr = min(kChunk, k1 - c0);
+        // row dots of this chunk's keys
+        for (int base = wave * C::RPW; base < nr; base += C::UNR * C::RPB) {
+            float4 x[C::UNR][C::CPL];
+#pragma unroll
+            for (int u = 0; u < C::UNR; ++u) {
+                const int r = min(base + u * C::RPB + rsub, nr - 1);
+#pragma unroll
+                for (int k = 0; k < C::CPL; ++k)
+                    x[u][k] = ld4<true>(kc + (size_t)(c0 + r) * C::CH + sub + C::LPR * k);
+            }
+#pragma unroll
+            for (int u = 0; u < C::UNR; ++u) {
+                const int r = base + u * C::RPB + rsub;
+                double part[HPK];
+#pragma unroll
+                for (int h = 0; h < HPK; ++h) {
+                    asm volatile("" ::: "memory");
+                    double s = 0.0;
+#pragma unroll
+                    for (int k = 0; k < C::CPL; ++k) s += dot4(q_s[h][sub + C::LPR * k], x[u][k]);
+                    part[h] = s;
+                }
+                const double tot = head_reduce<C::LPR, HPK>(part, lane) * scale;
+                if (writer && r < nr) lg_s[my_head][r] = tot;
+            }
+        }
+        __syncthreads();
+        // per head: chunk max, running rescale, weights
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+            const int h = wave + j * kNW;
+            if (h >= HPK) break;
+            double cm = NEG_INF;
+            for (int r = lane; r < nr; r += 64) cm = fmax(cm, lg_s[h][r]);
+            cm = wave_max(cm);
+            const double nm = fmax(run_max[j], cm);
+            const double f = exp(run_max[j] - nm);  // 0 on the first chunk
+            double ps = 0.0;
+            for (int r = lane; r < nr; r += 64) {
+                const double p = exp(lg_s[h][r] - nm);
+                lg_s[h][r] = p;
+                ps += p;
+            }
+            ps = wave_sum(ps);
+            run_sum[j] = run_sum[j] * f + ps;
+            run_max[j] = nm;
+            if (lane == 0) fac_s[h] = f;
+        }
+        __syncthreads();
+        // V pass with the running rescale
+#pragma unroll
+        for (int h = 0; h < HPK; ++h) {
+            const double f = fac_s[h];
+            acc[h][0] *= f;
+            acc[h][1] *= f;
+            acc[h][2] *= f;
+            acc[h][3] *= f;
+        }
+        constexpr int VU = 8;
+        for (int r0 = rl; r0 < nr; r0 += VU * C::RL) {
+            float4 x[VU];
+#pragma unroll
+            for (int j = 0; j < VU; ++j)
+                x[j] = ld4<true>(vc + (size_t)(c0 + min(r0 + j * C::RL, nr - 1)) * C::VCH + cc);
+#pragma unroll
+            for (int j = 0; j < VU; ++j) {
+                const int r = r0 + j * C::RL;
+                if (r >= nr) break;
+#pragma unroll
+                for (int h = 0; h < HPK; ++h) {
+                    const double p = lg_s[h][r];
+                    acc[h][0] = fma(p, (double)x[j].x, acc[h][0]);
+                    acc[h][1] = fma(p, (double)x[j].y, acc[h][1]);
+                    acc[h][2] = fma(p, (double)x[j].z, acc[h][2]);
+                    acc[h][3] = fma(p, (double)x[j].w, acc[h][3]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // running max / sum of each head into LDS for every thread
+    __shared__ double hmax_s[HPK], hsum_s[HPK];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+        const int h = wave + j * kNW;
+        if (h < HPK && lane == 0) {
+            hmax_s[h] = run_max[j];
+            hsum_s[h] = run_sum[j];
+        }
+    }
+    // reduce the row lanes: shuffles inside a wave, then LDS across waves
+#pragma unroll
+    for (int h = 0; h < HPK; ++h)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int off = C::VCH; off < 64; off <<= 1) acc[h][c] += __shfl_xor(acc[h][c], off, 64);
+    const bool final_out = gridDim.y == 1;
+#pragma unroll
+    for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
+        if (lane < C::VCH) {
+#pragma unroll
+            for (int hh = 0; hh < C::RED_H; ++hh) {
+                double *dst = &red_s[wave][hh * DV + cc * 4];
+                dst[0] = acc[h0 + hh][0];
+                dst[1] = acc[h0 + hh][1];
+                dst[2] = acc[h0 + hh][2];
+                dst[3] = acc[h0 + hh][3];
+            }
+        }
+        __syncthreads();
+        if (tid < C::RED_H * C::VCH) {
+            const int hh = tid / C::VCH, c4 = tid - hh * C::VCH, h = h0 + hh;
+            double o[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int j = 0; j < kNW; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o[c] += red_s[j][hh * DV + c4 * 4 + c];
+            if (final_out) {
+                const double den = hsum_s[h];
+                reinterpret_cast<float4 *>(a.out)[(gh0 + h) * C::VCH + c4] =
+                    make_float4((float)(o[0] / den), (float)(o[1] / den), (float)(o[2] / den),
+                                (float)(o[3] / den));
+            } else {
+                const size_t part = ((size_t)g * gridDim.y + sp) * HPK + h;
+                double *num = a.ws_num + part * DV + c4 * 4;
+                num[0] = o[0];
+                num[1] = o[1];
+                num[2] = o[2];
+                num[3] = o[3];
+                if (c4 == 0) {
+                    a.ws_max[part] = hmax_s[h];
+                    a.ws_sum[part] = hsum_s[h];
+                }
+            }
+        }
+        if (h0 + C::RED_H < HPK) __syncthreads();
+    }
+}
+
+// One block of dv threads per (group, head): merge the key-range partials.
+__global__ void exact_combine_kernel(ExactIO a, int splits)
+{
+    const int gh = blockIdx.x, H = a.hpk, g = gh / H, h = gh - g * H, c = threadIdx.x;
+    double mx = -__builtin_inf();
+    for (int s = 0; s < splits; ++s) mx = fmax(mx, a.ws_max[((size_t)g * splits + s) * H + h]);
+    double den = 0.0, num = 0.0;
+    for (int s = 0; s < splits; ++s) {
+        const size_t part = ((size_t)g * splits + s) * H + h;
+        const double w = exp(a.ws_max[part] - mx);  // empty ranges carry -inf -> 0
+        den += a.ws_sum[part] * w;
+        num += a.ws_num[part * a.dv + c] * w;
+    }
+    a.out[(size_t)gh * a.dv + c] = (float)(num / den);
+}
+
+template <int D, int DV, int HPK>
+hipError_t launch_exact_shape(const ExactIO &a, int splits, hipStream_t stream)
+{
+    hipLaunchKernelGGL((exact_attend_kernel<D, DV, HPK>), dim3(a.G, splits), dim3(kNT), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || splits == 1) return err;
+    hipLaunchKernelGGL(exact_combine_kernel, dim3(a.G * a.hpk), dim3(a.dv), 0, stream, a, splits);
+    return hipGetLastError();
+}
+
+template <int D, int DV>
+hipError_t launch_exact_hpk(const ExactIO &a, int splits, hipStream_t stream)
+{
+    switch (a.hpk) {
+    case 1: return launch_exact_shape<D, DV, 1>(a, splits, stream);
+    case 2: return launch_exact_shape<D, DV, 2>(a, splits, stream);
+    case 4: return launch_exact_shape<D, DV, 4>(a, splits, stream);
+    case 8: return launch_exact_shape<D, DV, 8>(a, splits, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int exact_splits(int G, int n_visible)
+{
+    // enough work-groups to cover the CUs several times, at least one chunk each
+    const int want = (4 * 256 + G - 1) / G;
+    const int most = (n_visible + kChunk - 1) / kChunk;
+    int s = want < most ? want : most;
+    return s < 1 ? 1 : s;
+}
+
+hipError_t launch_exact(const ExactIO &a, int splits, hipStream_t stream)
+{
+    if (a.d == 64 && a.dv == 64) return launch_exact_hpk<64, 64>(a, splits, stream);
+    if (a.d == 128 && a.dv == 128) return launch_exact_hpk<128, 128>(a, splits, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace o1

@@ -96,3 +96,26 @@ def test_binding_refuses_host_tensors():
     P, L = _lib()
     with pytest.raises((ValueError, TypeError)):
         P._dev_ptr(torch.zeros(4), "x", 4)
+
+
+def test_exact_comparator_validation_without_device():
+    P, L = _lib()
+    n = ctypes.c_size_t()
+    good = dict(n_groups=4, hpk=2, d=128, dv=128, cap=100, first=0, n_keys=100, scale=0.0)
+    for kw, code in [(dict(first=100), 1), (dict(n_keys=101), 1), (dict(first=-1), 1),
+                     (dict(n_groups=0), 1), (dict(hpk=3), 6), (dict(d=96, dv=96), 6),
+                     (dict(dv=64), 6)]:
+        args = {**good, **kw}
+        desc = P.o1_exact_desc(*[args[f] for f, _ in P.o1_exact_desc._fields_])
+        assert L.o1_exact_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == code, kw
+    desc = P.o1_exact_desc(*[good[f] for f, _ in P.o1_exact_desc._fields_])
+    assert L.o1_exact_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == 0
+    assert n.value == 0  # 100 keys fit one chunk of one work-group: no partials
+    # few groups and 1000 keys: the range splits over ceil(1000/128) = 8 work-groups,
+    # each writing (max, sum, numerator[dv]) per head
+    args = {**good, "cap": 1000, "n_keys": 1000}
+    desc = P.o1_exact_desc(*[args[f] for f, _ in P.o1_exact_desc._fields_])
+    assert L.o1_exact_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == 0
+    assert n.value == 8 * (4 * 8 * 2 * (128 + 2))
+    assert L.o1_exact_attend(ctypes.byref(desc), None, None, None, None, None, 0, None) == 1
+    assert L.o1_exact_workspace_bytes(None, ctypes.byref(n)) == 1
