@@ -14,6 +14,10 @@ roofline    the decode kernel: algorithmic bytes per launch / its average
             MI355X HBM peak of 8 TB/s.
 cpu_baseline  the CPU oracle (tests' reference implementation, untuned) on a
             bounded sample of the same workload, on this host's cores.
+exact_comparator  exact grouped-GQA attention (o1_exact_attend) over the job's
+            final context at the same shape: the O(context) decode replaced.
+exact_only_mode  o1_step in the exact-only mode (prompt of w + sink + 8 tokens,
+            every key kept exactly) at the same group count and shape.
 
 Default workload: qwen3_stack_b64 (64 sequences x 28 layers x 8 KV heads, 2 query
 heads per KV head, d = dv = 128, m = 32, w = 128, sink = 4, 256-token prefill,
@@ -33,20 +37,25 @@ if ROOT not in sys.path:
 
 METRIC = "Nyström decode group-steps/sec & tokens/s at 1 GPU; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
-DECODE_SRC = os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", "o1_decode.hip")
+DECODE_SRC = [os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", f)
+              for f in ("o1_decode.hip", "o1_internal.h")]
 # HBM bytes per decode launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by
-# a 1 GiB copy in the same process), keyed by (workload, decode source sha256 prefix).
+# a 1 GiB copy in the same process), keyed by (workload, sha256 prefix of the decode
+# kernel's sources).
 # A changed kernel source has no entry, and the roofline's traffic is then reported as null.
 MEASURED_TRAFFIC = {
-    ("qwen3_stack_b64", "2c62cf6bdce9dd08"): 3788978077,
+    ("qwen3_stack_b64", "9d15eaeac98eca95"): 3788993209,
 }
 
 
 def decode_source_sha() -> str:
     import hashlib
 
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def decode_bytes_per_group_step(wl) -> tuple[int, int]:
@@ -144,6 +153,56 @@ def exact_comparator(wl, ctx, nystrom_us, dev):
         return {"context": ctx, "error": str(exc)[:200]}
 
 
+def exact_only_mode(wl, n_steps, dev):
+    """Decode steps in the exact-only mode at the workload's group count and
+    shape: an exact-only prefill of the longest such prompt (w + sink + 8
+    tokens, q not read), then n_steps o1_step launches, each appending one key
+    and attending exactly over all of them."""
+    import dataclasses
+
+    import torch
+
+    import streaming_nystr_attention_amd as P
+    from streaming_nystr_attention_amd import workloads as W
+
+    T = wl.w + wl.sink + 8
+    G, H = wl.groups, wl.hpk
+    try:
+        cfg = dataclasses.replace(wl.config, exact_cap=T + n_steps)
+        _, k, v = W.prompt(wl.with_(T=T), dev)
+        Q = torch.empty(n_steps, G, H, wl.d, device=dev)
+        K = torch.empty(n_steps, G, wl.d, device=dev)
+        V = torch.empty(n_steps, G, wl.dv, device=dev)
+        for t in range(n_steps):
+            W.decode_inputs(wl, t, dev, out=(Q[t], K[t], V[t]))
+        out = torch.empty(G, H, wl.dv, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with P.O1Groups(cfg) as grp:
+            for timed in (False, True):  # the first pass warms up, the second is timed
+                grp.prefill(None, k, v)
+                if timed:
+                    e0.record()
+                for t in range(n_steps):
+                    grp.step(Q[t], K[t], V[t], out)
+                if timed:
+                    e1.record()
+            torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n_steps
+        # step t reads T + t stored rows and the new one, stores the new row,
+        # reads the queries and writes the outputs
+        row = (wl.d + wl.dv) * 4
+        rows_read = n_steps * (T + 1) + n_steps * (n_steps - 1) // 2
+        nbytes = G * (rows_read * row + n_steps * row + n_steps * H * row) / n_steps
+        del Q, K, V, k, v
+        torch.cuda.empty_cache()
+        return {"prompt_len": T, "decode_steps": n_steps, "exact_cap": T + n_steps,
+                "us_per_launch": us, "bytes_per_launch": nbytes,
+                "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+                "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    except Exception as exc:  # context, never the headline
+        return {"prompt_len": T, "error": str(exc)[:200]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +216,8 @@ def main():
     ap.add_argument("--exact-context", type=int, default=-1,
                     help="also time the exact grouped-GQA comparator over this many keys per "
                          "group (-1: the job's final context, 0: skip)")
+    ap.add_argument("--exact-only-steps", type=int, default=64,
+                    help="also time this many decode steps in the exact-only mode (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -272,6 +333,8 @@ def main():
         torch.cuda.empty_cache()
         res["exact_comparator"] = exact_comparator(wl, ctx, launch_us, dev)
         Q = K = V = None
+    if args.exact_only_steps > 0:
+        res["exact_only_mode"] = exact_only_mode(wl, args.exact_only_steps, dev)
     if not args.no_cpu_baseline:
         if Q is None:
             Q = torch.empty(n_dec, G, H, wl.d, device=dev)

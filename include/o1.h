@@ -33,16 +33,17 @@
 extern "C" {
 #endif
 
-#define O1_ABI_VERSION 1
+#define O1_ABI_VERSION 2
 
 enum o1_status {
     O1_OK = 0,
     O1_EINVAL = 1,       /* bad argument: null pointer, size or setting out of range */
     O1_ESTATE = 2,       /* call not valid in this state (e.g. step before prefill)  */
-    O1_EEXACT = 3,       /* prompt too short: the exact-only mode is not carried     */
+    O1_EEXACT = 3,       /* exact-only prompt on a handle created with exact_cap 0   */
     O1_ENOMEM = 4,       /* device allocation failed                                 */
     O1_EHIP = 5,         /* a HIP runtime call or kernel launch failed                */
-    O1_EUNSUPPORTED = 6  /* valid for the method but not compiled into this library  */
+    O1_EUNSUPPORTED = 6, /* valid for the method but not compiled into this library  */
+    O1_EFULL = 7         /* an exact-only group would exceed exact_cap keys           */
 };
 
 /* O1Rect of the nystrom.rs source page: how the indefinite skeleton is
@@ -54,7 +55,14 @@ enum o1_rect { O1_RECT_AGGREGATE = 0, O1_RECT_FM = 1 };
  * source page: m >= 4, w >= 1, q_heads >= 1).  Defaults on that page:
  * m = 32, w = 128, sink = 4, rect = AGGREGATE.
  * Compiled shapes: d == dv in {64, 128}, hpk in {1, 2, 4, 8}, m <= 64,
- * sink + w <= 1024; other valid shapes return O1_EUNSUPPORTED. */
+ * sink + w <= 1024; other valid shapes return O1_EUNSUPPORTED.
+ *
+ * exact_cap sizes the exact-only mode (NystromGroup::prefill_shared on the
+ * nystrom.rs source page): a prompt of T <= w + sink + 8 tokens builds no
+ * skeleton; the group keeps every key exactly and each decode step appends one,
+ * so the window grows without bound on that page.  Here it grows into buffers
+ * of exact_cap keys per group, allocated once by o1_create_groups; 0 allocates
+ * nothing and such prompts return O1_EEXACT. */
 typedef struct o1_config {
     int32_t n_seq;    /* sequences                         (>= 1) */
     int32_t n_layer;  /* layers per sequence               (>= 1) */
@@ -66,6 +74,7 @@ typedef struct o1_config {
     int32_t w;        /* exact window width                (>= 1) */
     int32_t sink;     /* permanent exact sink keys         (>= 0) */
     int32_t rect;     /* enum o1_rect                             */
+    int32_t exact_cap;/* keys an exact-only group may hold   (>= 0) */
 } o1_config;
 
 typedef struct o1_groups o1_groups; /* opaque; owns every state buffer */
@@ -90,6 +99,8 @@ typedef struct o1_info {
     int64_t steps;        /* decode steps since the last prefill                 */
     uint64_t state_bytes; /* device bytes of the persistent per-group state      */
     uint64_t work_bytes;  /* device bytes of prefill work buffers currently held */
+    int32_t exact_only;   /* 1 when the last prefill took the exact-only mode    */
+    int32_t exact_keys;   /* keys held exactly: sink + w, or T + steps when exact-only */
 } o1_info;
 
 /* Fields of the device state, for o1_field_bytes / o1_read_field /
@@ -108,13 +119,16 @@ enum o1_field {
     O1_FIELD_FAR_LEN = 9,  /* i64 [G][hpk]        keys absorbed per head       */
     O1_FIELD_LAMBDA = 10,  /* f64 [G][hpk]        ridge used by the pinv       */
     O1_FIELD_TRIES = 11,   /* i32 [G][hpk]        Cholesky attempt that worked (13 = fallback) */
-    O1_FIELD_COUNT = 12
+    O1_FIELD_EXACT_K = 12, /* f32 [G][exact_cap][d]  exact-only keys, row j = position j   */
+    O1_FIELD_EXACT_V = 13, /* f32 [G][exact_cap][dv] exact-only values                     */
+    O1_FIELD_COUNT = 14
 };
 
 /* Validate `cfg` and allocate the state of all its groups on the current HIP
  * device (once; decode never allocates).  *out receives the handle.
  * Errors: O1_EINVAL (null pointer, m < 4, w < 1, hpk < 1, sink < 0, d or dv
- * < 1, counts < 1, unknown rect), O1_EUNSUPPORTED, O1_ENOMEM, O1_EHIP. */
+ * < 1, counts < 1, unknown rect, exact_cap < 0 or too large), O1_EUNSUPPORTED,
+ * O1_ENOMEM, O1_EHIP. */
 int o1_create_groups(const o1_config *cfg, o1_groups **out);
 
 /* Release every buffer of the handle.  NULL is a no-op.  The caller must make
@@ -133,8 +147,13 @@ void o1_destroy_groups(o1_groups *g);
  * up to 12 times), and the far field of keys sink .. T-w-1 (T^, Z^, running
  * max, far_len = T - sink - w).  `frozen` may be NULL.  Resets any earlier
  * state of the handle.
- * Errors: O1_EINVAL (null tensor, T < 1), O1_EEXACT when T <= w + sink + 8
- * (the page's exact-only mode, which its device path does not carry either),
+ * A prompt of T <= w + sink + 8 tokens takes the exact-only mode instead: the
+ * T keys and values become rows 0 .. T-1 of the group's exact buffers, there
+ * are no sinks, landmarks or far field (m_eff = 0, far_len = 0), and `q`
+ * (which may then be NULL) and `frozen` are not read.
+ * Errors: O1_EINVAL (null tensor, T < 1, T * G * hpk * d > 2^40),
+ * O1_EEXACT (exact-only prompt and
+ * exact_cap = 0), O1_EFULL (exact-only prompt longer than exact_cap),
  * O1_ENOMEM (work buffers), O1_EHIP. */
 int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int32_t T,
                const o1_frozen *frozen, void *stream);
@@ -145,8 +164,14 @@ int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int
  *   q   [G][hpk][d]    queries of the new position
  *   k   [G][d], v [G][dv]  the new key / value
  *   out [G][hpk][dv]   outputs (may not alias the inputs)
+ * In the exact-only mode the step appends (k, v) as key n = T + steps and
+ * writes, per head, softmax attention over keys 0 .. n (NystromHead::step with
+ * no sinks and no far field); one launch, two when a group's keys are split
+ * across work-groups.
  * No allocation, no host synchronisation; one kernel launch.
- * Errors: O1_EINVAL (null tensor), O1_ESTATE (no successful prefill), O1_EHIP. */
+ * Errors: O1_EINVAL (null tensor), O1_ESTATE (no successful prefill), O1_EFULL
+ * (exact-only group already holding exact_cap keys; nothing is changed),
+ * O1_EHIP. */
 int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float *out,
             void *stream);
 
@@ -154,8 +179,9 @@ int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float 
 int o1_get_info(const o1_groups *g, o1_info *info);
 
 /* Bytes of one state field at the current m_eff (see enum o1_field).
- * Errors: O1_EINVAL (unknown field, null pointer), O1_ESTATE (landmark-shaped
- * fields before a prefill). */
+ * Errors: O1_EINVAL (unknown field, null pointer, exact buffers of a handle
+ * created with exact_cap = 0), O1_ESTATE (landmark-shaped fields before a
+ * skeleton prefill, or in the exact-only mode). */
 int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes);
 
 /* Copy a whole state field to `dst` / from `src` (host or device memory;

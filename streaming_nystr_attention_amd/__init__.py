@@ -15,13 +15,15 @@ from dataclasses import dataclass
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libo1.so")
 
-O1_OK, O1_EINVAL, O1_ESTATE, O1_EEXACT, O1_ENOMEM, O1_EHIP, O1_EUNSUPPORTED = range(7)
+O1_OK, O1_EINVAL, O1_ESTATE, O1_EEXACT, O1_ENOMEM, O1_EHIP, O1_EUNSUPPORTED, O1_EFULL = range(8)
 RECT_AGGREGATE, RECT_FM = 0, 1
 (FIELD_NEAR_K, FIELD_NEAR_V, FIELD_K_TILDE, FIELD_Q_TILDE, FIELD_MU, FIELD_T_HAT, FIELD_Z_HAT,
- FIELD_M_MAX, FIELD_WIN_HEAD, FIELD_FAR_LEN, FIELD_LAMBDA, FIELD_TRIES) = range(12)
+ FIELD_M_MAX, FIELD_WIN_HEAD, FIELD_FAR_LEN, FIELD_LAMBDA, FIELD_TRIES, FIELD_EXACT_K,
+ FIELD_EXACT_V) = range(14)
+FIELD_COUNT = 14
 
 _STATUS_NAMES = {0: "O1_OK", 1: "O1_EINVAL", 2: "O1_ESTATE", 3: "O1_EEXACT", 4: "O1_ENOMEM",
-                 5: "O1_EHIP", 6: "O1_EUNSUPPORTED"}
+                 5: "O1_EHIP", 6: "O1_EUNSUPPORTED", 7: "O1_EFULL"}
 
 
 class O1Error(RuntimeError):
@@ -34,7 +36,8 @@ class O1Error(RuntimeError):
 
 class o1_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("n_seq", "n_layer", "n_kv", "hpk", "d", "dv", "m", "w", "sink", "rect")]
+                ("n_seq", "n_layer", "n_kv", "hpk", "d", "dv", "m", "w", "sink", "rect",
+                 "exact_cap")]
 
 
 class o1_frozen(ctypes.Structure):
@@ -45,7 +48,8 @@ class o1_info(ctypes.Structure):
     _fields_ = [("n_groups", ctypes.c_int32), ("sealed", ctypes.c_int32),
                 ("prompt_len", ctypes.c_int32), ("m_eff", ctypes.c_int32),
                 ("steps", ctypes.c_int64), ("state_bytes", ctypes.c_uint64),
-                ("work_bytes", ctypes.c_uint64)]
+                ("work_bytes", ctypes.c_uint64), ("exact_only", ctypes.c_int32),
+                ("exact_keys", ctypes.c_int32)]
 
 
 class o1_exact_desc(ctypes.Structure):
@@ -135,7 +139,7 @@ def _dev_ptr(t, name, numel, dtype_name="float32"):
 
 def o1_create_groups(cfg: "Config"):
     c = o1_config(cfg.n_seq, cfg.n_layer, cfg.n_kv, cfg.hpk, cfg.d, cfg.dv, cfg.m, cfg.w,
-                  cfg.sink, cfg.rect)
+                  cfg.sink, cfg.rect, cfg.exact_cap)
     h = ctypes.c_void_p()
     _check(lib().o1_create_groups(ctypes.byref(c), ctypes.byref(h)))
     return h
@@ -147,7 +151,9 @@ def o1_destroy_groups(handle):
 
 def o1_prefill(handle, cfg, q, k, v, T: int, frozen=None, stream=None):
     G = cfg.groups
-    qp = _dev_ptr(q, "q", G * cfg.hpk * T * cfg.d)
+    # an exact-only prefill does not read q; None is accepted for it
+    qp = (ctypes.c_void_p(0) if q is None and cfg.exact_only(T)
+          else _dev_ptr(q, "q", G * cfg.hpk * T * cfg.d))
     kp = _dev_ptr(k, "k", G * T * cfg.d)
     vp = _dev_ptr(v, "v", G * T * cfg.dv)
     fz = None
@@ -252,6 +258,7 @@ class Config:
     w: int = 128
     sink: int = 4
     rect: int = RECT_AGGREGATE
+    exact_cap: int = 0  # keys an exact-only group may hold (0: that mode is refused)
 
     @property
     def groups(self) -> int:
@@ -260,6 +267,10 @@ class Config:
     @property
     def rows(self) -> int:
         return self.sink + self.w
+
+    def exact_only(self, T: int) -> bool:
+        """A prompt of T tokens takes the exact-only mode (no skeleton)."""
+        return T <= self.w + self.sink + 8
 
     def m_eff(self, T: int) -> int:
         return max(4, min(T // 8, self.m))

@@ -45,6 +45,12 @@ struct o1_groups {
     double *lm64;      // prefill work buffer
     size_t lm64_bytes;
     size_t state_bytes;
+    // exact-only mode: keys [G][exact_cap][d], values [G][exact_cap][dv], and the
+    // split partials of its decode step (all allocated at create when exact_cap > 0)
+    int exact;         // the last prefill took the exact-only mode
+    float *exact_k, *exact_v;
+    double *exact_ws;
+    size_t exact_ws_bytes;
 };
 
 namespace {
@@ -71,6 +77,8 @@ FieldInfo field_info(const o1_groups *g, int32_t field)
     case O1_FIELD_FAR_LEN: return {s.far_len, G * H * sizeof(int64_t)};
     case O1_FIELD_LAMBDA: return {s.lambda, G * H * sizeof(double)};
     case O1_FIELD_TRIES: return {s.tries, G * H * sizeof(int32_t)};
+    case O1_FIELD_EXACT_K: return {g->exact_k, G * g->cfg.exact_cap * s.d * sizeof(float)};
+    case O1_FIELD_EXACT_V: return {g->exact_v, G * g->cfg.exact_cap * s.dv * sizeof(float)};
     default: return {nullptr, 0};
     }
 }
@@ -84,8 +92,9 @@ bool landmark_shaped(int32_t field)
 void free_state(o1_groups *g)
 {
     o1::DevState &s = g->st;
-    void *ptrs[] = {s.near_k, s.near_v, s.k_tilde, s.q_tilde, s.mu, s.t_hat, s.z_hat,
-                    s.m_max, s.win_head, s.far_len, s.lambda, s.tries, g->lm64};
+    void *ptrs[] = {s.near_k, s.near_v, s.k_tilde, s.q_tilde, s.mu,     s.t_hat,
+                    s.z_hat,  s.m_max,  s.win_head, s.far_len, s.lambda, s.tries,
+                    g->lm64,  g->exact_k, g->exact_v, g->exact_ws};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
 }
@@ -124,6 +133,9 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         return fail(O1_EINVAL, "unknown rectifier %d", c.rect);
     const long long G = (long long)c.n_seq * c.n_layer * c.n_kv;
     if (G > (1LL << 30)) return fail(O1_EINVAL, "too many groups (%lld)", G);
+    if (c.exact_cap < 0 || (double)G * c.exact_cap * ((double)c.d + c.dv) * 4.0 > 0x1p50)
+        return fail(O1_EINVAL, "exact_cap must be >= 0 and its buffers below 2^50 bytes (exact_cap=%d)",
+                    c.exact_cap);
     const int R = c.sink + c.w;
     const int m_cap = c.m < o1::kMaxLandmarks ? c.m : o1::kMaxLandmarks;
     if (!o1::decode_supported(c.d, c.dv, c.hpk, 4, R) || c.m > o1::kMaxLandmarks)
@@ -139,6 +151,10 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     g->R = R;
     g->lm64 = nullptr;
     g->lm64_bytes = 0;
+    g->exact = 0;
+    g->exact_k = g->exact_v = nullptr;
+    g->exact_ws = nullptr;
+    g->exact_ws_bytes = 0;
     if (hipGetDevice(&g->device) != hipSuccess) {
         delete g;
         return fail(O1_EHIP, "hipGetDevice failed");
@@ -155,7 +171,11 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     s.m = 0;
     s.scale = 1.0f / sqrtf((float)c.d);
 
-    const size_t Gs = (size_t)G, H = (size_t)c.hpk, M = (size_t)m_cap;
+    const size_t Gs = (size_t)G, H = (size_t)c.hpk, M = (size_t)m_cap, E = (size_t)c.exact_cap;
+    // the largest split of an exact-only step covers every count of keys up to exact_cap
+    const size_t ws_parts = E ? Gs * o1::exact_splits((int)G, c.exact_cap) * H : 0;
+    const size_t ws_bytes = ws_parts > Gs * H ? sizeof(double) * ws_parts * (c.dv + 2) : 0;
+    g->exact_ws_bytes = ws_bytes;
     struct Alloc {
         void **p;
         size_t bytes;
@@ -172,9 +192,13 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         {(void **)&s.far_len, Gs * H * sizeof(int64_t)},
         {(void **)&s.lambda, Gs * H * sizeof(double)},
         {(void **)&s.tries, Gs * H * sizeof(int32_t)},
+        {(void **)&g->exact_k, Gs * E * c.d * sizeof(float)},
+        {(void **)&g->exact_v, Gs * E * c.dv * sizeof(float)},
+        {(void **)&g->exact_ws, ws_bytes},
     };
     size_t total = 0;
     for (auto &a : allocs) {
+        if (a.bytes == 0) continue;  // exact-only buffers of a handle without that mode
         if (hipMalloc(a.p, a.bytes) != hipSuccess) {
             (void)hipGetLastError();
             free_state(g);
@@ -199,14 +223,33 @@ void o1_destroy_groups(o1_groups *g)
 int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int32_t T,
                const o1_frozen *frozen, void *stream)
 {
-    if (!g || !q || !k || !v) return fail(O1_EINVAL, "o1_prefill: null argument");
+    if (!g || !k || !v) return fail(O1_EINVAL, "o1_prefill: null argument");
     const o1_config &c = g->cfg;
     if (T < 1) return fail(O1_EINVAL, "prompt length must be >= 1 (T=%d)", T);
-    if ((long long)T <= (long long)c.w + c.sink + o1::kExactSlack)
-        return fail(O1_EEXACT,
-                    "prompt of %d tokens is in the exact-only mode (T <= w + sink + %d = %d), "
-                    "which the device path does not carry",
-                    T, o1::kExactSlack, c.w + c.sink + o1::kExactSlack);
+    if ((long long)T <= (long long)c.w + c.sink + o1::kExactSlack) {
+        // exact-only mode (NystromGroup::prefill_shared): every key stays exact
+        if (c.exact_cap == 0)
+            return fail(O1_EEXACT,
+                        "prompt of %d tokens is in the exact-only mode (T <= w + sink + %d = %d) "
+                        "and the handle was created with exact_cap = 0",
+                        T, o1::kExactSlack, c.w + c.sink + o1::kExactSlack);
+        if (T > c.exact_cap)
+            return fail(O1_EFULL, "exact-only prompt of %d tokens exceeds exact_cap = %d", T, c.exact_cap);
+        int rc = use_device(g);
+        if (rc) return rc;
+        g->sealed = 0;
+        hipError_t err = o1::launch_exact_seal(g->st, k, v, T, g->exact_k, g->exact_v, c.exact_cap,
+                                               (hipStream_t)stream);
+        if (err != hipSuccess)
+            return fail(O1_EHIP, "exact-only prefill launch failed: %s", hipGetErrorString(err));
+        g->st.m = 0;
+        g->exact = 1;
+        g->T = T;
+        g->steps = 0;
+        g->sealed = 1;
+        return ok();
+    }
+    if (!q) return fail(O1_EINVAL, "o1_prefill: null queries");
     if ((long long)T * g->G * c.hpk * c.d > (1LL << 40))
         return fail(O1_EINVAL, "prompt too large (T=%d)", T);
     int rc = use_device(g);
@@ -233,6 +276,7 @@ int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int
     }
 
     g->sealed = 0;
+    g->exact = 0;
     g->st.m = m_eff;
     o1::PrefillIO io;
     io.q = q;
@@ -255,6 +299,45 @@ int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float 
 {
     if (!g || !q || !k || !v || !out) return fail(O1_EINVAL, "o1_step: null argument");
     if (!g->sealed) return fail(O1_ESTATE, "o1_step before a successful o1_prefill");
+    if (g->exact) {
+        const long long held = (long long)g->T + g->steps;
+        if (held >= g->cfg.exact_cap)
+            return fail(O1_EFULL, "exact-only groups already hold exact_cap = %d keys", g->cfg.exact_cap);
+        int rc = use_device(g);
+        if (rc) return rc;
+        const int n = (int)held + 1;  // keys 0 .. n-1 after appending this step's key
+        o1::ExactIO io{};
+        io.q = q;
+        io.k = g->exact_k;
+        io.v = g->exact_v;
+        io.out = out;
+        io.G = g->G;
+        io.hpk = g->cfg.hpk;
+        io.d = g->cfg.d;
+        io.dv = g->cfg.dv;
+        io.cap = g->cfg.exact_cap;
+        io.first = 0;
+        io.n_keys = n;
+        int splits = o1::exact_splits(g->G, n);
+        io.per_split = (n + splits - 1) / splits;
+        splits = (n + io.per_split - 1) / io.per_split;
+        io.scale = g->st.scale;
+        const size_t parts = (size_t)g->G * splits * g->cfg.hpk;
+        if (splits > 1) {
+            io.ws_max = g->exact_ws;
+            io.ws_sum = g->exact_ws + parts;
+            io.ws_num = g->exact_ws + 2 * parts;
+        }
+        io.k_new = k;
+        io.v_new = v;
+        io.k_dst = g->exact_k;
+        io.v_dst = g->exact_v;
+        hipError_t err = o1::launch_exact(io, splits, (hipStream_t)stream);
+        if (err != hipSuccess)
+            return fail(O1_EHIP, "exact-only decode launch failed: %s", hipGetErrorString(err));
+        g->steps += 1;
+        return ok();
+    }
     int rc = use_device(g);
     if (rc) return rc;
     o1::DecodeIO io{q, k, v, out};
@@ -274,6 +357,8 @@ int o1_get_info(const o1_groups *g, o1_info *info)
     info->steps = g->steps;
     info->state_bytes = g->state_bytes;
     info->work_bytes = g->lm64_bytes;
+    info->exact_only = g->sealed ? g->exact : 0;
+    info->exact_keys = !g->sealed ? 0 : g->exact ? (int32_t)(g->T + g->steps) : g->R;
     return ok();
 }
 
@@ -281,8 +366,10 @@ int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes)
 {
     if (!g || !bytes) return fail(O1_EINVAL, "o1_field_bytes: null argument");
     if (field < 0 || field >= O1_FIELD_COUNT) return fail(O1_EINVAL, "unknown field %d", field);
-    if (landmark_shaped(field) && !g->sealed)
-        return fail(O1_ESTATE, "field %d has no shape before a prefill", field);
+    if ((field == O1_FIELD_EXACT_K || field == O1_FIELD_EXACT_V) && g->cfg.exact_cap == 0)
+        return fail(O1_EINVAL, "field %d: the handle was created with exact_cap = 0", field);
+    if (landmark_shaped(field) && (!g->sealed || g->exact))
+        return fail(O1_ESTATE, "field %d has no shape before a skeleton-mode prefill", field);
     *bytes = field_info(g, field).bytes;
     return ok();
 }
@@ -352,7 +439,7 @@ int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, c
     if (need && (!workspace || workspace_bytes < need))
         return fail(O1_EINVAL, "o1_exact_attend: work space of %zu bytes needed", need);
     const o1_exact_desc &x = *desc;
-    o1::ExactIO io;
+    o1::ExactIO io{};
     io.q = q;
     io.k = k;
     io.v = v;

@@ -12,6 +12,11 @@
 // running rescale.  With one split it writes the normalised output; otherwise
 // it writes (max, sum, numerator) partials that exact_combine_kernel merges.
 // Bound: HBM (n_keys * (d + dv) * 4 B per group, read once, nontemporal).
+//
+// In append mode (the exact-only decode step of NystromState::step_group: the
+// new key joins the window before any output) the last key comes from k_new /
+// v_new; the work-group whose range holds it also stores it into the cache, and
+// no other work-group reads that row.
 #include "o1_internal.h"
 
 namespace o1 {
@@ -56,6 +61,14 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
     for (int i = tid; i < HPK * C::CH; i += kNT) (&q_s[0][0])[i] = qg[i];
     const float4 *kc = reinterpret_cast<const float4 *>(a.k) + (size_t)g * a.cap * C::CH;
     const float4 *vc = reinterpret_cast<const float4 *>(a.v) + (size_t)g * a.cap * C::VCH;
+    const int new_row = a.k_new ? a.n_keys - 1 : -1;  // absolute index of the appended key
+    const float4 *kn = reinterpret_cast<const float4 *>(a.k_new) + (size_t)g * C::CH;
+    const float4 *vn = reinterpret_cast<const float4 *>(a.v_new) + (size_t)g * C::VCH;
+    if (new_row >= k0 && new_row < k1) {
+        if (tid < C::CH) reinterpret_cast<float4 *>(a.k_dst)[((size_t)g * a.cap + new_row) * C::CH + tid] = kn[tid];
+        if (tid >= 128 && tid < 128 + C::VCH)
+            reinterpret_cast<float4 *>(a.v_dst)[((size_t)g * a.cap + new_row) * C::VCH + tid - 128] = vn[tid - 128];
+    }
 
     const int sub = lane % C::LPR, rsub = lane / C::LPR;
     constexpr int HSTRIDE = C::LPR / HPK;
@@ -82,10 +95,10 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
             float4 x[C::UNR][C::CPL];
 #pragma unroll
             for (int u = 0; u < C::UNR; ++u) {
-                const int r = min(base + u * C::RPB + rsub, nr - 1);
+                const int r = c0 + min(base + u * C::RPB + rsub, nr - 1);
+                const float4 *row = (r == new_row) ? kn : kc + (size_t)r * C::CH;
 #pragma unroll
-                for (int k = 0; k < C::CPL; ++k)
-                    x[u][k] = ld4<true>(kc + (size_t)(c0 + r) * C::CH + sub + C::LPR * k);
+                for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<true>(row + sub + C::LPR * k);
             }
 #pragma unroll
             for (int u = 0; u < C::UNR; ++u) {
@@ -139,8 +152,10 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
         for (int r0 = rl; r0 < nr; r0 += VU * C::RL) {
             float4 x[VU];
 #pragma unroll
-            for (int j = 0; j < VU; ++j)
-                x[j] = ld4<true>(vc + (size_t)(c0 + min(r0 + j * C::RL, nr - 1)) * C::VCH + cc);
+            for (int j = 0; j < VU; ++j) {
+                const int r = c0 + min(r0 + j * C::RL, nr - 1);
+                x[j] = ld4<true>(((r == new_row) ? vn : vc + (size_t)r * C::VCH) + cc);
+            }
 #pragma unroll
             for (int j = 0; j < VU; ++j) {
                 const int r = r0 + j * C::RL;
@@ -256,7 +271,35 @@ hipError_t launch_exact_hpk(const ExactIO &a, int splits, hipStream_t stream)
     }
 }
 
+// One work-group per group: copy the prompt rows into the exact buffers and
+// clear the counters the skeleton mode would have set.
+__global__ __launch_bounds__(256) void exact_seal_kernel(DevState s, const float4 *k, const float4 *v,
+                                                         int T, float4 *ek, float4 *ev, int cap)
+{
+    const int g = blockIdx.x, tid = threadIdx.x;
+    const int ck = s.d / 4, cv = s.dv / 4;
+    const size_t nk = (size_t)T * ck, nv = (size_t)T * cv;
+    for (size_t i = tid; i < nk; i += 256) ek[(size_t)g * cap * ck + i] = k[(size_t)g * nk + i];
+    for (size_t i = tid; i < nv; i += 256) ev[(size_t)g * cap * cv + i] = v[(size_t)g * nv + i];
+    if (tid == 0) s.win_head[g] = 0;
+    if (tid < s.hpk) {
+        const size_t gh = (size_t)g * s.hpk + tid;
+        s.far_len[gh] = 0;
+        s.lambda[gh] = 0.0;
+        s.tries[gh] = 0;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_exact_seal(const DevState &s, const float *k, const float *v, int T, float *ek,
+                             float *ev, int cap, hipStream_t stream)
+{
+    hipLaunchKernelGGL(exact_seal_kernel, dim3(s.G), dim3(256), 0, stream, s,
+                       reinterpret_cast<const float4 *>(k), reinterpret_cast<const float4 *>(v), T,
+                       reinterpret_cast<float4 *>(ek), reinterpret_cast<float4 *>(ev), cap);
+    return hipGetLastError();
+}
 
 int exact_splits(int G, int n_visible)
 {

@@ -43,16 +43,26 @@ struct PrefillIO {
     double *lm64;                        // work: [G][1 + hpk][m][d] f64 landmarks
 };
 
-// Exact grouped-GQA attention over a stored KV cache (the O(p) comparator).
+// Exact grouped-GQA attention over a stored KV cache: the O(p) comparator, and
+// the decode step of the exact-only mode.
 struct ExactIO {
     const float *q, *k, *v;  // q [G][hpk][d], k [G][cap][d], v [G][cap][dv]
     float *out;              // [G][hpk][dv]
     int G, hpk, d, dv, cap, first, n_keys, per_split;
     float scale;
     double *ws_max, *ws_sum, *ws_num;  // split partials [G][splits][hpk](x dv)
+    // Append mode (exact-only decode), else all null: key n_keys-1 is the new
+    // one, read from k_new [G][d] / v_new [G][dv] and stored into row n_keys-1
+    // of k_dst / v_dst (the same buffers as k / v).
+    const float *k_new, *v_new;
+    float *k_dst, *v_dst;
 };
 int exact_splits(int G, int n_visible);
 hipError_t launch_exact(const ExactIO &io, int splits, hipStream_t stream);
+// Exact-only prefill: prompt rows k [G][T][d], v [G][T][dv] into rows 0..T-1
+// of ek [G][cap][d], ev [G][cap][dv]; win_head, far_len, lambda, tries cleared.
+hipError_t launch_exact_seal(const DevState &s, const float *k, const float *v, int T, float *ek,
+                             float *ev, int cap, hipStream_t stream);
 
 // True when the decode kernel is compiled for this shape.
 bool decode_supported(int d, int dv, int hpk, int m, int R);

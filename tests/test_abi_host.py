@@ -49,11 +49,35 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version():
     P, L = _lib()
-    assert P.o1_abi_version() == 1
+    assert P.o1_abi_version() == 2
+
+
+def _header_enum(prefix):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return {n: int(v) for n, v in re.findall(rf"\b({prefix}[A-Z_0-9]+)\s*=\s*(\d+)", text)}
+
+
+def test_binding_constants_match_the_header():
+    P, _ = _lib()
+    status = _header_enum("O1_E")
+    assert re.search(r"\bO1_OK\s*=\s*0\b", open(HEADER).read()) and P.O1_OK == 0
+    assert len(status) == 7
+    for name, val in status.items():
+        assert getattr(P, name) == val, name
+    fields = _header_enum("O1_FIELD_")
+    for name, val in fields.items():
+        assert getattr(P, name[3:]) == val, name
+    cfg_fields = re.search(r"typedef struct o1_config \{(.*?)\} o1_config;", open(HEADER).read(), re.S)
+    names = re.findall(r"int32_t\s+(\w+);", cfg_fields.group(1))
+    assert names == [f for f, _ in P.o1_config._fields_]
+    info_fields = re.search(r"typedef struct o1_info \{(.*?)\} o1_info;", open(HEADER).read(), re.S)
+    names = re.findall(r"int\d+_t\s+(\w+);", info_fields.group(1))
+    assert names == [f for f, _ in P.o1_info._fields_]
 
 
 def _create(P, L, **kw):
-    base = dict(n_seq=1, n_layer=1, n_kv=1, hpk=1, d=64, dv=64, m=8, w=16, sink=2, rect=0)
+    base = dict(n_seq=1, n_layer=1, n_kv=1, hpk=1, d=64, dv=64, m=8, w=16, sink=2, rect=0,
+                exact_cap=0)
     base.update(kw)
     cfg = P.o1_config(*[base[f] for f, _ in P.o1_config._fields_])
     h = ctypes.c_void_p()
@@ -65,7 +89,7 @@ def _create(P, L, **kw):
     (dict(m=3), 1), (dict(w=0), 1), (dict(hpk=0), 1), (dict(sink=-1), 1), (dict(d=0), 1),
     (dict(dv=0), 1), (dict(n_seq=0), 1), (dict(n_layer=0), 1), (dict(n_kv=0), 1), (dict(rect=7), 1),
     (dict(d=96, dv=96), 6), (dict(hpk=3), 6), (dict(m=65), 6), (dict(d=64, dv=128), 6),
-    (dict(w=2000), 6),
+    (dict(w=2000), 6), (dict(exact_cap=-1), 1), (dict(n_seq=1 << 20, exact_cap=1 << 22), 1),
 ])
 def test_create_rejects_before_touching_the_device(kw, code):
     P, L = _lib()
