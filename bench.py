@@ -18,6 +18,9 @@ exact_comparator  exact grouped-GQA attention (o1_exact_attend) over the job's
             final context at the same shape: the O(context) decode replaced.
 exact_only_mode  o1_step in the exact-only mode (prompt of w + sink + 8 tokens,
             every key kept exactly) at the same group count and shape.
+per_layer_mode  the same state sealed layer by layer from model-layout buffers
+            and stepped with one o1_step_layer launch per layer and token,
+            eager and from a captured HIP graph.
 
 Default workload: qwen3_stack_b64 (64 sequences x 28 layers x 8 KV heads, 2 query
 heads per KV head, d = dv = 128, m = 32, w = 128, sink = 4, 256-token prefill,
@@ -203,6 +206,96 @@ def exact_only_mode(wl, n_steps, dev):
         return {"prompt_len": T, "error": str(exc)[:200]}
 
 
+def per_layer_mode(wl, n_tokens, dev):
+    """The workload driven one layer at a time, as a model runs it: every layer
+    sealed from a position-major query trace and per-KV-head caches
+    (o1_prefill_layer), then per token one o1_step_layer launch per layer
+    (n_seq * n_kv groups each), eager and replayed from a captured HIP graph."""
+    import torch
+
+    import streaming_nystr_attention_amd as P
+    from streaming_nystr_attention_amd import workloads as W
+
+    B, L, K, H = wl.n_seq, wl.n_layer, wl.n_kv, wl.hpk
+    T = wl.T
+    try:
+        grp = P.O1Groups(wl.config)
+        q, k, v = W.prompt(wl, dev)
+        layer_idx = [torch.tensor([(s * L + l) * K + kv for s in range(B) for kv in range(K)],
+                                  device=dev) for l in range(L)]
+        # model-side buffers of each layer, built outside the timed region
+        bufs = []
+        for l in range(L):
+            ql = q.index_select(0, layer_idx[l]).view(B, K, H, T, wl.d)
+            trace = ql.permute(0, 3, 1, 2, 4).reshape(B, T, K * H, wl.d).contiguous()
+            kc = k.index_select(0, layer_idx[l]).view(B, K, T, wl.d).contiguous()
+            vc = v.index_select(0, layer_idx[l]).view(B, K, T, wl.dv).contiguous()
+            bufs.append((trace, kc, vc))
+        del q, k, v
+        Q = torch.empty(n_tokens, L, B, K * H, wl.d, device=dev)
+        Kn = torch.empty(n_tokens, L, B, K, wl.d, device=dev)
+        Vn = torch.empty(n_tokens, L, B, K, wl.dv, device=dev)
+        for t in range(n_tokens):
+            qa, ka, va = W.decode_inputs(wl, t, dev)
+            for l in range(L):
+                Q[t, l] = qa.index_select(0, layer_idx[l]).view(B, K * H, wl.d)
+                Kn[t, l] = ka.index_select(0, layer_idx[l]).view(B, K, wl.d)
+                Vn[t, l] = va.index_select(0, layer_idx[l]).view(B, K, wl.dv)
+        out = torch.empty(L, B, K * H, wl.dv, device=dev)
+
+        def seal():
+            for l in range(L):
+                trace, kc, vc = bufs[l]
+                grp.prefill_layer(l, trace.permute(0, 2, 1, 3), kc, vc)
+
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        seal()
+        torch.cuda.synchronize()
+        ev[0].record()
+        seal()
+        ev[1].record()
+        for t in range(n_tokens):
+            for l in range(L):
+                grp.step_layer(l, Q[t, l], Kn[t, l], Vn[t, l], out[l])
+        ev[2].record()
+        torch.cuda.synchronize()
+        seal_ms = ev[0].elapsed_time(ev[1])
+        eager_us = ev[1].elapsed_time(ev[2]) * 1e3 / n_tokens
+
+        # one token's L launches captured once and replayed (static inputs)
+        sq, sk, sv = Q[0].clone(), Kn[0].clone(), Vn[0].clone()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for l in range(L):  # warm launch on the capture stream
+                grp.step_layer(l, sq[l], sk[l], sv[l], out[l])
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            for l in range(L):
+                grp.step_layer(l, sq[l], sk[l], sv[l], out[l])
+        graph.replay()
+        torch.cuda.synchronize()
+        ev[2].record()
+        for _ in range(n_tokens):
+            graph.replay()
+        ev[3].record()
+        torch.cuda.synchronize()
+        graph_us = ev[2].elapsed_time(ev[3]) * 1e3 / n_tokens
+        rd, wr = decode_bytes_per_group_step(wl)
+        nbytes = (rd + wr) * wl.groups  # one token over every layer
+        grp.close()
+        del bufs, Q, Kn, Vn
+        torch.cuda.empty_cache()
+        return {"launches_per_token": L, "groups_per_launch": B * K, "tokens": n_tokens,
+                "seal_ms": seal_ms, "eager_us_per_token": eager_us,
+                "graph_us_per_token": graph_us, "graph_us_per_launch": graph_us / L,
+                "achieved_GBps_graph": nbytes / (graph_us * 1e-6) / 1e9,
+                "frac_of_peak_graph": nbytes / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    except Exception as exc:  # context, never the headline
+        return {"error": str(exc)[:200]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +311,8 @@ def main():
                          "group (-1: the job's final context, 0: skip)")
     ap.add_argument("--exact-only-steps", type=int, default=64,
                     help="also time this many decode steps in the exact-only mode (0: skip)")
+    ap.add_argument("--per-layer-tokens", type=int, default=32,
+                    help="also time this many tokens stepped one layer at a time (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -335,6 +430,8 @@ def main():
         Q = K = V = None
     if args.exact_only_steps > 0:
         res["exact_only_mode"] = exact_only_mode(wl, args.exact_only_steps, dev)
+    if args.per_layer_tokens > 0 and wl.n_layer > 1:
+        res["per_layer_mode"] = per_layer_mode(wl, args.per_layer_tokens, dev)
     if not args.no_cpu_baseline:
         if Q is None:
             Q = torch.empty(n_dec, G, H, wl.d, device=dev)

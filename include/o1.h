@@ -93,14 +93,18 @@ typedef struct o1_frozen {
 
 typedef struct o1_info {
     int32_t n_groups;     /* G = n_seq * n_layer * n_kv                         */
-    int32_t sealed;       /* 1 after a successful o1_prefill                     */
-    int32_t prompt_len;   /* T of the last prefill                               */
-    int32_t m_eff;        /* clamp(T / 8, 4, m), 0 before prefill                */
-    int64_t steps;        /* decode steps since the last prefill                 */
+    int32_t sealed;       /* 1 when every layer has a successful prefill         */
+    int32_t prompt_len;   /* T of the sealed layers (0 when none is)             */
+    int32_t m_eff;        /* clamp(T / 8, 4, m); 0 when none is sealed or exact-only */
+    int64_t steps;        /* decode steps of the least advanced sealed layer     */
     uint64_t state_bytes; /* device bytes of the persistent per-group state      */
     uint64_t work_bytes;  /* device bytes of prefill work buffers currently held */
-    int32_t exact_only;   /* 1 when the last prefill took the exact-only mode    */
-    int32_t exact_keys;   /* keys held exactly: sink + w, or T + steps when exact-only */
+    int32_t exact_only;   /* 1 when the sealed prompt took the exact-only mode   */
+    int32_t exact_keys;   /* keys held exactly per group: sink + w, or, exact-only,
+                             T + max_steps (the fullest layer)                   */
+    int32_t n_layer;      /* layers per sequence                                 */
+    int32_t layers_sealed;/* layers with a successful prefill of the prompt      */
+    int64_t max_steps;    /* decode steps of the most advanced sealed layer      */
 } o1_info;
 
 /* Fields of the device state, for o1_field_bytes / o1_read_field /
@@ -151,7 +155,8 @@ void o1_destroy_groups(o1_groups *g);
  * T keys and values become rows 0 .. T-1 of the group's exact buffers, there
  * are no sinks, landmarks or far field (m_eff = 0, far_len = 0), and `q`
  * (which may then be NULL) and `frozen` are not read.
- * Errors: O1_EINVAL (null tensor, T < 1, T * G * hpk * d > 2^40),
+ * Every tensor must be 16-byte aligned.
+ * Errors: O1_EINVAL (null or misaligned tensor, T < 1, T * G * hpk * d > 2^40),
  * O1_EEXACT (exact-only prompt and
  * exact_cap = 0), O1_EFULL (exact-only prompt longer than exact_cap),
  * O1_ENOMEM (work buffers), O1_EHIP. */
@@ -169,11 +174,65 @@ int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int
  * no sinks and no far field); one launch, two when a group's keys are split
  * across work-groups.
  * No allocation, no host synchronisation; one kernel launch.
- * Errors: O1_EINVAL (null tensor), O1_ESTATE (no successful prefill), O1_EFULL
+ * Graph capture: in the skeleton mode a step (and o1_step_layer) may be
+ * captured into a HIP graph and replayed; each replay advances the device
+ * state as a call does, but the step counts o1_get_info reports count calls
+ * only.  An exact-only step fixes its key count at capture, so it must not be
+ * replayed.
+ * Errors: O1_EINVAL (null or misaligned tensor), O1_ESTATE (a layer without a
+ * successful prefill), O1_EFULL
  * (exact-only group already holding exact_cap keys; nothing is changed),
  * O1_EHIP. */
 int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float *out,
             void *stream);
+
+/* ---- one layer at a time, from a model's own buffers ----------------------
+ * A model seals each layer at the end of its exact prompt pass and then steps
+ * it once per token (LayerKvCache::o1_begin / o1_push_q / o1_seal / o1_step on
+ * the docs.rs LayerKvCache page).  These two entry points cover the groups of
+ * one layer l of every sequence -- groups (s * n_layer + l) * n_kv + kv -- and
+ * read the prompt in place.
+ *
+ * The prompt of one layer, as element strides (in floats).  For sequence s, KV
+ * head kv, query head j of that group (model head kv * hpk + j), position t
+ * and component c:
+ *   q[s * q_seq + (kv * hpk + j) * q_head + t * q_pos + c]
+ *   k[s * k_seq + kv * k_kv + t * k_pos + c],   v likewise with v_*.
+ * Rows are contiguous; every stride is a non-negative multiple of 4 and every
+ * pointer 16-byte aligned.  Examples: the query trace o1_push_q collects,
+ * [n_seq][T][n_kv * hpk][d], has q_seq = T * n_kv * hpk * d, q_head = d,
+ * q_pos = n_kv * hpk * d; per-KV-head caches [n_seq][n_kv][cap][d] (the page's
+ * k_heads / v_heads) have k_seq = n_kv * cap * d, k_kv = cap * d, k_pos = d. */
+typedef struct o1_prompt_view {
+    const float *q;
+    int64_t q_seq, q_head, q_pos;
+    const float *k;
+    int64_t k_seq, k_kv, k_pos;
+    const float *v;
+    int64_t v_seq, v_kv, v_pos;
+} o1_prompt_view;
+
+/* Prefill freeze of layer `layer` of every sequence, as o1_prefill does for
+ * the whole handle (same steps, modes and errors), reading the first T
+ * positions of `p`.  `frozen` arrays, if given, cover the layer's groups in
+ * the order (s, kv).  Every layer of a handle shares one prompt length: a
+ * layer prefill with a T other than the sealed layers' starts a new prompt
+ * and leaves the other layers unsealed until they are sealed again.
+ * Errors: those of o1_prefill; O1_EINVAL also for a layer out of range, a
+ * misaligned pointer or a bad stride. */
+int o1_prefill_layer(o1_groups *g, int32_t layer, const o1_prompt_view *p, int32_t T,
+                     const o1_frozen *frozen, void *stream);
+
+/* One decode step of layer `layer` of every sequence (LayerKvCache::o1_step):
+ *   q   [n_seq][n_kv * hpk][d]   the layer's queries, model head order
+ *   k   [n_seq][n_kv][d], v [n_seq][n_kv][dv]
+ *   out [n_seq][n_kv * hpk][dv]
+ * One launch, as o1_step; the layer's step count advances by one.
+ * Errors: O1_EINVAL (null or misaligned tensor, layer out of range),
+ * O1_ESTATE (layer not sealed), O1_EFULL (exact-only layer holding exact_cap
+ * keys), O1_EHIP. */
+int o1_step_layer(o1_groups *g, int32_t layer, const float *q, const float *k, const float *v,
+                  float *out, void *stream);
 
 /* Host-side facts about the handle; no device work. Errors: O1_EINVAL. */
 int o1_get_info(const o1_groups *g, o1_info *info);
@@ -187,7 +246,7 @@ int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes);
 /* Copy a whole state field to `dst` / from `src` (host or device memory;
  * `bytes` must equal o1_field_bytes), enqueued on `stream`.  For tests and
  * state transfer; the decode path never needs them.  Writing requires a
- * sealed handle.  Errors: O1_EINVAL, O1_ESTATE, O1_EHIP. */
+ * sealed layer.  Errors: O1_EINVAL, O1_ESTATE, O1_EHIP. */
 int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, void *stream);
 int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, void *stream);
 

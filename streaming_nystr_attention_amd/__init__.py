@@ -49,7 +49,15 @@ class o1_info(ctypes.Structure):
                 ("prompt_len", ctypes.c_int32), ("m_eff", ctypes.c_int32),
                 ("steps", ctypes.c_int64), ("state_bytes", ctypes.c_uint64),
                 ("work_bytes", ctypes.c_uint64), ("exact_only", ctypes.c_int32),
-                ("exact_keys", ctypes.c_int32)]
+                ("exact_keys", ctypes.c_int32), ("n_layer", ctypes.c_int32),
+                ("layers_sealed", ctypes.c_int32), ("max_steps", ctypes.c_int64)]
+
+
+class o1_prompt_view(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("q_seq", ctypes.c_int64), ("q_head", ctypes.c_int64),
+                ("q_pos", ctypes.c_int64), ("k", ctypes.c_void_p), ("k_seq", ctypes.c_int64),
+                ("k_kv", ctypes.c_int64), ("k_pos", ctypes.c_int64), ("v", ctypes.c_void_p),
+                ("v_seq", ctypes.c_int64), ("v_kv", ctypes.c_int64), ("v_pos", ctypes.c_int64)]
 
 
 class o1_exact_desc(ctypes.Structure):
@@ -58,7 +66,8 @@ class o1_exact_desc(ctypes.Structure):
                 ("n_keys", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
-EXPORTS = ("o1_create_groups", "o1_destroy_groups", "o1_prefill", "o1_step", "o1_get_info",
+EXPORTS = ("o1_create_groups", "o1_destroy_groups", "o1_prefill", "o1_step", "o1_prefill_layer",
+           "o1_step_layer", "o1_get_info",
            "o1_field_bytes", "o1_read_field", "o1_write_field", "o1_exact_workspace_bytes",
            "o1_exact_attend", "o1_last_error", "o1_abi_version")
 
@@ -83,6 +92,11 @@ def lib():
     L.o1_prefill.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(o1_frozen), vp]
     L.o1_step.restype = ctypes.c_int
     L.o1_step.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.o1_prefill_layer.restype = ctypes.c_int
+    L.o1_prefill_layer.argtypes = [vp, i32, ctypes.POINTER(o1_prompt_view), i32,
+                                   ctypes.POINTER(o1_frozen), vp]
+    L.o1_step_layer.restype = ctypes.c_int
+    L.o1_step_layer.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     L.o1_get_info.restype = ctypes.c_int
     L.o1_get_info.argtypes = [vp, ctypes.POINTER(o1_info)]
     L.o1_field_bytes.restype = ctypes.c_int
@@ -173,6 +187,59 @@ def o1_step(handle, cfg, q, k, v, out, stream=None):
     _check(lib().o1_step(handle, _dev_ptr(q, "q", G * cfg.hpk * cfg.d),
                          _dev_ptr(k, "k", G * cfg.d), _dev_ptr(v, "v", G * cfg.dv),
                          _dev_ptr(out, "out", G * cfg.hpk * cfg.dv), _stream_handle(stream)))
+
+
+def _strided(t, name, shape, T):
+    """(pointer, strides) of a logical 4-D view [outer][inner][position][c] whose
+    rows are contiguous; positions 0..T-1 are read."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda or t.dtype != torch.float32:
+        raise TypeError(f"{name}: expected a float32 device tensor")
+    if t.dim() != 4 or tuple(t.shape[:2]) != shape[:2] or t.shape[3] != shape[3] or t.shape[2] < T:
+        raise ValueError(f"{name}: expected shape [{shape[0]}][{shape[1]}][>= {T}][{shape[3]}], "
+                         f"got {list(t.shape)}")
+    st = t.stride()
+    if st[3] != 1 or any(x < 0 or x % 4 for x in st[:3]) or t.data_ptr() % 16:
+        raise ValueError(f"{name}: rows must be contiguous and 16-byte aligned, strides multiples "
+                         f"of 4 (strides {st})")
+    return ctypes.c_void_p(t.data_ptr()), st[0], st[1], st[2]
+
+
+def o1_prefill_layer(handle, cfg, layer: int, q, k, v, T: int, frozen=None, stream=None):
+    """Seal one layer from a model's buffers, read in place:
+    q [n_seq][n_kv * hpk][>= T][d] (a logical view: the trace [n_seq][T][H][d]
+    permuted to (0, 2, 1, 3) qualifies), k [n_seq][n_kv][>= T][d], v likewise;
+    q may be None for an exact-only prompt."""
+    B, K, H = cfg.n_seq, cfg.n_kv, cfg.n_kv * cfg.hpk
+    if q is None:
+        qp, qs = ctypes.c_void_p(0), (0, 0, 0)
+    else:
+        qp, *qs = _strided(q, "q", (B, H, T, cfg.d), T)
+    kp, *ks = _strided(k, "k", (B, K, T, cfg.d), T)
+    vp_, *vs = _strided(v, "v", (B, K, T, cfg.dv), T)
+    view = o1_prompt_view(qp, *qs, kp, *ks, vp_, *vs)
+    fz = None
+    if frozen is not None:
+        kt, qt, mu = frozen
+        n, m = B * K, cfg.m_eff(T)
+        fz = o1_frozen(
+            None if kt is None else _dev_ptr(kt, "frozen k_tilde", n * m * cfg.d),
+            None if qt is None else _dev_ptr(qt, "frozen q_tilde", n * cfg.hpk * m * cfg.d),
+            None if mu is None else _dev_ptr(mu, "frozen mu", n * cfg.hpk * m * m))
+    _check(lib().o1_prefill_layer(handle, layer, ctypes.byref(view), T,
+                                  None if fz is None else ctypes.byref(fz), _stream_handle(stream)))
+
+
+def o1_step_layer(handle, cfg, layer: int, q, k, v, out, stream=None):
+    """q [n_seq][n_kv * hpk][d], k [n_seq][n_kv][d], v [n_seq][n_kv][dv] ->
+    out [n_seq][n_kv * hpk][dv]: one decode step of one layer."""
+    n = cfg.n_seq * cfg.n_kv
+    _check(lib().o1_step_layer(handle, layer, _dev_ptr(q, "q", n * cfg.hpk * cfg.d),
+                               _dev_ptr(k, "k", n * cfg.d), _dev_ptr(v, "v", n * cfg.dv),
+                               _dev_ptr(out, "out", n * cfg.hpk * cfg.dv), _stream_handle(stream)))
 
 
 def o1_get_info(handle) -> o1_info:
@@ -314,6 +381,17 @@ class O1Groups:
     def step(self, q, k, v, out, stream=None):
         """q [G][hpk][d], k [G][d], v [G][dv] -> out [G][hpk][dv]."""
         o1_step(self._h, self.cfg, q, k, v, out, stream)
+
+    def prefill_layer(self, layer, q, k, v, T=None, frozen=None, stream=None):
+        """Seal one layer in place from q [n_seq][H][>= T][d] (logical view),
+        k [n_seq][n_kv][>= T][d], v [n_seq][n_kv][>= T][dv]."""
+        T = k.shape[2] if T is None else T
+        o1_prefill_layer(self._h, self.cfg, layer, q, k, v, T, frozen, stream)
+        self.T = T
+
+    def step_layer(self, layer, q, k, v, out, stream=None):
+        """q [n_seq][H][d], k [n_seq][n_kv][d], v [n_seq][n_kv][dv] -> out [n_seq][H][dv]."""
+        o1_step_layer(self._h, self.cfg, layer, q, k, v, out, stream)
 
     def info(self) -> o1_info:
         return o1_get_info(self._h)

@@ -1,12 +1,16 @@
 // Host side of the C ABI declared in include/o1.h: argument validation, state
 // allocation (once, at o1_create_groups), stream-ordered launches, and field
-// copies for tests.  No entry point synchronises with the host.
+// copies for tests.  No entry point synchronises with the host, except that a
+// prefill needing a larger work buffer than it holds waits for its stream
+// before freeing the old one.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
+#include <vector>
 
 #include "o1.h"
 #include "o1_internal.h"
@@ -38,22 +42,53 @@ struct o1_groups {
     o1_config cfg;
     int device;
     int G, R;
-    int sealed;
-    int T;
-    int64_t steps;
-    o1::DevState st;   // m_eff and pointers
-    double *lm64;      // prefill work buffer
+    int T;      // prompt length shared by every sealed layer
+    int exact;  // that prompt took the exact-only mode
+    std::vector<uint8_t> layer_sealed;
+    std::vector<int64_t> layer_steps;  // decode steps since each layer's prefill
+    o1::DevState st;                   // m_eff and pointers
+    double *lm64;                      // prefill work buffer
     size_t lm64_bytes;
     size_t state_bytes;
     // exact-only mode: keys [G][exact_cap][d], values [G][exact_cap][dv], and the
     // split partials of its decode step (all allocated at create when exact_cap > 0)
-    int exact;         // the last prefill took the exact-only mode
     float *exact_k, *exact_v;
     double *exact_ws;
     size_t exact_ws_bytes;
+
+    bool any_sealed() const
+    {
+        return std::any_of(layer_sealed.begin(), layer_sealed.end(), [](uint8_t v) { return v != 0; });
+    }
+    bool all_sealed() const
+    {
+        return std::all_of(layer_sealed.begin(), layer_sealed.end(), [](uint8_t v) { return v != 0; });
+    }
+    // fewest / most decode steps over the sealed layers (0 when none is sealed)
+    int64_t steps_extreme(bool largest) const
+    {
+        int64_t r = -1;
+        for (size_t l = 0; l < layer_sealed.size(); ++l)
+            if (layer_sealed[l] && (r < 0 || (largest ? layer_steps[l] > r : layer_steps[l] < r)))
+                r = layer_steps[l];
+        return r < 0 ? 0 : r;
+    }
 };
 
 namespace {
+
+// All groups of the handle (call index = group index).
+o1::GroupMap whole_map(const o1_groups *g)
+{
+    return {g->G, g->cfg.n_kv, g->cfg.n_kv, 0};
+}
+
+// Layer l of every sequence: call index i = s * n_kv + kv.
+o1::GroupMap layer_map(const o1_groups *g, int l)
+{
+    const o1_config &c = g->cfg;
+    return {c.n_seq * c.n_kv, c.n_kv, c.n_layer * c.n_kv, l * c.n_kv};
+}
 
 struct FieldInfo {
     void *ptr;
@@ -108,6 +143,157 @@ int use_device(const o1_groups *g)
     return O1_OK;
 }
 
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+bool stride_ok(int64_t s) { return s >= 0 && s % 4 == 0; }
+
+// Split partials of an exact-only step over `count` call indices, in doubles.
+size_t exact_ws_doubles(int count, int hpk, int dv, int n_keys)
+{
+    const int splits = o1::exact_splits(count, n_keys);
+    return splits == 1 ? 0 : (size_t)count * splits * hpk * (dv + 2);
+}
+
+// The prefill shared by o1_prefill (layer < 0: every group) and o1_prefill_layer.
+int prefill_groups(o1_groups *g, int layer, const o1::PromptView &pv, int32_t T,
+                   const o1_frozen *frozen, void *stream)
+{
+    const o1_config &c = g->cfg;
+    const o1::GroupMap map = layer < 0 ? whole_map(g) : layer_map(g, layer);
+    const bool exact = (long long)T <= (long long)c.w + c.sink + o1::kExactSlack;
+    if (exact) {
+        // exact-only mode (NystromGroup::prefill_shared): every key stays exact
+        if (c.exact_cap == 0)
+            return fail(O1_EEXACT,
+                        "prompt of %d tokens is in the exact-only mode (T <= w + sink + %d = %d) "
+                        "and the handle was created with exact_cap = 0",
+                        T, o1::kExactSlack, c.w + c.sink + o1::kExactSlack);
+        if (T > c.exact_cap)
+            return fail(O1_EFULL, "exact-only prompt of %d tokens exceeds exact_cap = %d", T, c.exact_cap);
+    } else if (!pv.q) {
+        return fail(O1_EINVAL, "prefill: null queries");
+    }
+    if ((long long)T * map.count * c.hpk * c.d > (1LL << 40))
+        return fail(O1_EINVAL, "prompt too large (T=%d)", T);
+    int rc = use_device(g);
+    if (rc) return rc;
+    int m_eff = T / 8;
+    if (m_eff < 4) m_eff = 4;
+    if (m_eff > c.m) m_eff = c.m;
+
+    if (!exact) {
+        const size_t need = sizeof(double) * (size_t)map.count * (1 + c.hpk) * m_eff * c.d;
+        if (need > g->lm64_bytes) {
+            if (g->lm64) {
+                if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+                    return fail(O1_EHIP, "hipStreamSynchronize failed");
+                (void)hipFree(g->lm64);
+                g->lm64 = nullptr;
+                g->lm64_bytes = 0;
+            }
+            if (hipMalloc((void **)&g->lm64, need) != hipSuccess) {
+                (void)hipGetLastError();
+                g->lm64 = nullptr;
+                return fail(O1_ENOMEM, "hipMalloc of %zu bytes of prefill work space failed", need);
+            }
+            g->lm64_bytes = need;
+        }
+    }
+
+    // A whole-handle prefill, or a layer prefill of another prompt length,
+    // starts a new prompt: every layer is unsealed until sealed again (the
+    // landmark count, hence the state layout, follows the prompt length).
+    if (layer < 0 || !g->any_sealed() || T != g->T)
+        std::fill(g->layer_sealed.begin(), g->layer_sealed.end(), 0);
+    if (layer >= 0) g->layer_sealed[layer] = 0;
+    g->T = T;
+    g->exact = exact;
+    g->st.m = exact ? 0 : m_eff;
+
+    hipError_t err;
+    if (exact) {
+        err = o1::launch_exact_seal(g->st, pv, map, T, g->exact_k, g->exact_v, c.exact_cap,
+                                    (hipStream_t)stream);
+    } else {
+        o1::PrefillIO io;
+        io.p = pv;
+        io.map = map;
+        io.T = T;
+        io.fz_kt = frozen ? frozen->k_tilde : nullptr;
+        io.fz_qt = frozen ? frozen->q_tilde : nullptr;
+        io.fz_mu = frozen ? frozen->mu : nullptr;
+        io.lm64 = g->lm64;
+        err = o1::launch_prefill(g->st, io, (hipStream_t)stream);
+    }
+    if (err != hipSuccess) return fail(O1_EHIP, "prefill launch failed: %s", hipGetErrorString(err));
+    for (int l = 0; l < c.n_layer; ++l) {
+        if (layer >= 0 && l != layer) continue;
+        g->layer_sealed[l] = 1;
+        g->layer_steps[l] = 0;
+    }
+    return ok();
+}
+
+// The decode step shared by o1_step (layer < 0: every group) and o1_step_layer.
+int step_groups(o1_groups *g, int layer, const float *q, const float *k, const float *v, float *out,
+                void *stream)
+{
+    if (!q || !k || !v || !out) return fail(O1_EINVAL, "step: null tensor");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(O1_EINVAL, "step: tensors must be 16-byte aligned");
+    if (layer < 0 && !g->all_sealed())
+        return fail(O1_ESTATE, "o1_step before every layer has a successful prefill");
+    if (layer >= 0 && !g->layer_sealed[layer])
+        return fail(O1_ESTATE, "o1_step_layer before a successful prefill of layer %d", layer);
+    const o1::GroupMap map = layer < 0 ? whole_map(g) : layer_map(g, layer);
+    hipError_t err;
+    if (g->exact) {
+        const long long held =
+            (long long)g->T + (layer < 0 ? g->steps_extreme(true) : g->layer_steps[layer]);
+        if (held >= g->cfg.exact_cap)
+            return fail(O1_EFULL, "exact-only groups already hold exact_cap = %d keys", g->cfg.exact_cap);
+        int rc = use_device(g);
+        if (rc) return rc;
+        const int n = (int)held + 1;  // keys 0 .. n-1 after appending this step's key
+        o1::ExactIO io{};
+        io.q = q;
+        io.k = g->exact_k;
+        io.v = g->exact_v;
+        io.out = out;
+        io.map = map;
+        io.hpk = g->cfg.hpk;
+        io.d = g->cfg.d;
+        io.dv = g->cfg.dv;
+        io.cap = g->cfg.exact_cap;
+        io.first = 0;
+        io.n_keys = n;
+        int splits = o1::exact_splits(map.count, n);
+        io.per_split = (n + splits - 1) / splits;
+        splits = (n + io.per_split - 1) / io.per_split;
+        io.scale = g->st.scale;
+        const size_t parts = (size_t)map.count * splits * g->cfg.hpk;
+        if (splits > 1) {
+            io.ws_max = g->exact_ws;
+            io.ws_sum = g->exact_ws + parts;
+            io.ws_num = g->exact_ws + 2 * parts;
+        }
+        io.k_new = k;
+        io.v_new = v;
+        io.k_dst = g->exact_k;
+        io.v_dst = g->exact_v;
+        err = o1::launch_exact(io, splits, (hipStream_t)stream);
+    } else {
+        int rc = use_device(g);
+        if (rc) return rc;
+        o1::DecodeIO io{q, k, v, out, map};
+        err = o1::launch_decode(g->st, io, (hipStream_t)stream);
+    }
+    if (err != hipSuccess) return fail(O1_EHIP, "decode launch failed: %s", hipGetErrorString(err));
+    for (int l = 0; l < g->cfg.n_layer; ++l)
+        if (layer < 0 || l == layer) g->layer_steps[l] += 1;
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,9 +335,12 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     g->cfg = c;
     g->G = (int)G;
     g->R = R;
+    g->T = 0;
+    g->exact = 0;
+    g->layer_sealed.assign(c.n_layer, 0);
+    g->layer_steps.assign(c.n_layer, 0);
     g->lm64 = nullptr;
     g->lm64_bytes = 0;
-    g->exact = 0;
     g->exact_k = g->exact_v = nullptr;
     g->exact_ws = nullptr;
     g->exact_ws_bytes = 0;
@@ -172,9 +361,11 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     s.scale = 1.0f / sqrtf((float)c.d);
 
     const size_t Gs = (size_t)G, H = (size_t)c.hpk, M = (size_t)m_cap, E = (size_t)c.exact_cap;
-    // the largest split of an exact-only step covers every count of keys up to exact_cap
-    const size_t ws_parts = E ? Gs * o1::exact_splits((int)G, c.exact_cap) * H : 0;
-    const size_t ws_bytes = ws_parts > Gs * H ? sizeof(double) * ws_parts * (c.dv + 2) : 0;
+    // split partials of the largest exact-only step, whole handle or one layer
+    const size_t ws_bytes =
+        E ? sizeof(double) * std::max(exact_ws_doubles((int)G, c.hpk, c.dv, c.exact_cap),
+                                      exact_ws_doubles(c.n_seq * c.n_kv, c.hpk, c.dv, c.exact_cap))
+          : 0;
     g->exact_ws_bytes = ws_bytes;
     struct Alloc {
         void **p;
@@ -224,141 +415,88 @@ int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int
                const o1_frozen *frozen, void *stream)
 {
     if (!g || !k || !v) return fail(O1_EINVAL, "o1_prefill: null argument");
-    const o1_config &c = g->cfg;
     if (T < 1) return fail(O1_EINVAL, "prompt length must be >= 1 (T=%d)", T);
-    if ((long long)T <= (long long)c.w + c.sink + o1::kExactSlack) {
-        // exact-only mode (NystromGroup::prefill_shared): every key stays exact
-        if (c.exact_cap == 0)
-            return fail(O1_EEXACT,
-                        "prompt of %d tokens is in the exact-only mode (T <= w + sink + %d = %d) "
-                        "and the handle was created with exact_cap = 0",
-                        T, o1::kExactSlack, c.w + c.sink + o1::kExactSlack);
-        if (T > c.exact_cap)
-            return fail(O1_EFULL, "exact-only prompt of %d tokens exceeds exact_cap = %d", T, c.exact_cap);
-        int rc = use_device(g);
-        if (rc) return rc;
-        g->sealed = 0;
-        hipError_t err = o1::launch_exact_seal(g->st, k, v, T, g->exact_k, g->exact_v, c.exact_cap,
-                                               (hipStream_t)stream);
-        if (err != hipSuccess)
-            return fail(O1_EHIP, "exact-only prefill launch failed: %s", hipGetErrorString(err));
-        g->st.m = 0;
-        g->exact = 1;
-        g->T = T;
-        g->steps = 0;
-        g->sealed = 1;
-        return ok();
-    }
-    if (!q) return fail(O1_EINVAL, "o1_prefill: null queries");
-    if ((long long)T * g->G * c.hpk * c.d > (1LL << 40))
-        return fail(O1_EINVAL, "prompt too large (T=%d)", T);
-    int rc = use_device(g);
-    if (rc) return rc;
-    int m_eff = T / 8;
-    if (m_eff < 4) m_eff = 4;
-    if (m_eff > c.m) m_eff = c.m;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+        return fail(O1_EINVAL, "o1_prefill: tensors must be 16-byte aligned");
+    const o1_config &c = g->cfg;
+    // q [G][hpk][T][d], k [G][T][d], v [G][T][dv], seen as call index i = group
+    // = (s * n_layer + l) * n_kv + kv with outer index i / n_kv and KV head i % n_kv
+    o1::PromptView pv;
+    pv.q = q;
+    pv.k = k;
+    pv.v = v;
+    pv.q_outer = (int64_t)c.n_kv * c.hpk * T * c.d;
+    pv.q_head = (int64_t)T * c.d;
+    pv.q_pos = c.d;
+    pv.k_outer = (int64_t)c.n_kv * T * c.d;
+    pv.k_inner = (int64_t)T * c.d;
+    pv.k_pos = c.d;
+    pv.v_outer = (int64_t)c.n_kv * T * c.dv;
+    pv.v_inner = (int64_t)T * c.dv;
+    pv.v_pos = c.dv;
+    return prefill_groups(g, -1, pv, T, frozen, stream);
+}
 
-    const size_t need = sizeof(double) * (size_t)g->G * (1 + c.hpk) * m_eff * c.d;
-    if (need > g->lm64_bytes) {
-        if (g->lm64) {
-            if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
-                return fail(O1_EHIP, "hipStreamSynchronize failed");
-            (void)hipFree(g->lm64);
-            g->lm64 = nullptr;
-            g->lm64_bytes = 0;
-        }
-        if (hipMalloc((void **)&g->lm64, need) != hipSuccess) {
-            (void)hipGetLastError();
-            g->lm64 = nullptr;
-            return fail(O1_ENOMEM, "hipMalloc of %zu bytes of prefill work space failed", need);
-        }
-        g->lm64_bytes = need;
-    }
-
-    g->sealed = 0;
-    g->exact = 0;
-    g->st.m = m_eff;
-    o1::PrefillIO io;
-    io.q = q;
-    io.k = k;
-    io.v = v;
-    io.T = T;
-    io.fz_kt = frozen ? frozen->k_tilde : nullptr;
-    io.fz_qt = frozen ? frozen->q_tilde : nullptr;
-    io.fz_mu = frozen ? frozen->mu : nullptr;
-    io.lm64 = g->lm64;
-    hipError_t err = o1::launch_prefill(g->st, io, (hipStream_t)stream);
-    if (err != hipSuccess) return fail(O1_EHIP, "prefill launch failed: %s", hipGetErrorString(err));
-    g->T = T;
-    g->steps = 0;
-    g->sealed = 1;
-    return ok();
+int o1_prefill_layer(o1_groups *g, int32_t layer, const o1_prompt_view *p, int32_t T,
+                     const o1_frozen *frozen, void *stream)
+{
+    if (!g || !p || !p->k || !p->v) return fail(O1_EINVAL, "o1_prefill_layer: null argument");
+    if (layer < 0 || layer >= g->cfg.n_layer)
+        return fail(O1_EINVAL, "layer %d out of range (n_layer=%d)", layer, g->cfg.n_layer);
+    if (T < 1) return fail(O1_EINVAL, "prompt length must be >= 1 (T=%d)", T);
+    if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v))
+        return fail(O1_EINVAL, "o1_prefill_layer: tensors must be 16-byte aligned");
+    if (!stride_ok(p->q_seq) || !stride_ok(p->q_head) || !stride_ok(p->q_pos) || !stride_ok(p->k_seq) ||
+        !stride_ok(p->k_kv) || !stride_ok(p->k_pos) || !stride_ok(p->v_seq) || !stride_ok(p->v_kv) ||
+        !stride_ok(p->v_pos))
+        return fail(O1_EINVAL, "o1_prefill_layer: strides must be non-negative multiples of 4 floats");
+    o1::PromptView pv;
+    pv.q = p->q;
+    pv.k = p->k;
+    pv.v = p->v;
+    pv.q_outer = p->q_seq;
+    pv.q_head = p->q_head;
+    pv.q_pos = p->q_pos;
+    pv.k_outer = p->k_seq;
+    pv.k_inner = p->k_kv;
+    pv.k_pos = p->k_pos;
+    pv.v_outer = p->v_seq;
+    pv.v_inner = p->v_kv;
+    pv.v_pos = p->v_pos;
+    return prefill_groups(g, layer, pv, T, frozen, stream);
 }
 
 int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float *out, void *stream)
 {
-    if (!g || !q || !k || !v || !out) return fail(O1_EINVAL, "o1_step: null argument");
-    if (!g->sealed) return fail(O1_ESTATE, "o1_step before a successful o1_prefill");
-    if (g->exact) {
-        const long long held = (long long)g->T + g->steps;
-        if (held >= g->cfg.exact_cap)
-            return fail(O1_EFULL, "exact-only groups already hold exact_cap = %d keys", g->cfg.exact_cap);
-        int rc = use_device(g);
-        if (rc) return rc;
-        const int n = (int)held + 1;  // keys 0 .. n-1 after appending this step's key
-        o1::ExactIO io{};
-        io.q = q;
-        io.k = g->exact_k;
-        io.v = g->exact_v;
-        io.out = out;
-        io.G = g->G;
-        io.hpk = g->cfg.hpk;
-        io.d = g->cfg.d;
-        io.dv = g->cfg.dv;
-        io.cap = g->cfg.exact_cap;
-        io.first = 0;
-        io.n_keys = n;
-        int splits = o1::exact_splits(g->G, n);
-        io.per_split = (n + splits - 1) / splits;
-        splits = (n + io.per_split - 1) / io.per_split;
-        io.scale = g->st.scale;
-        const size_t parts = (size_t)g->G * splits * g->cfg.hpk;
-        if (splits > 1) {
-            io.ws_max = g->exact_ws;
-            io.ws_sum = g->exact_ws + parts;
-            io.ws_num = g->exact_ws + 2 * parts;
-        }
-        io.k_new = k;
-        io.v_new = v;
-        io.k_dst = g->exact_k;
-        io.v_dst = g->exact_v;
-        hipError_t err = o1::launch_exact(io, splits, (hipStream_t)stream);
-        if (err != hipSuccess)
-            return fail(O1_EHIP, "exact-only decode launch failed: %s", hipGetErrorString(err));
-        g->steps += 1;
-        return ok();
-    }
-    int rc = use_device(g);
-    if (rc) return rc;
-    o1::DecodeIO io{q, k, v, out};
-    hipError_t err = o1::launch_decode(g->st, io, (hipStream_t)stream);
-    if (err != hipSuccess) return fail(O1_EHIP, "decode launch failed: %s", hipGetErrorString(err));
-    g->steps += 1;
-    return ok();
+    if (!g) return fail(O1_EINVAL, "o1_step: null argument");
+    return step_groups(g, -1, q, k, v, out, stream);
+}
+
+int o1_step_layer(o1_groups *g, int32_t layer, const float *q, const float *k, const float *v,
+                  float *out, void *stream)
+{
+    if (!g) return fail(O1_EINVAL, "o1_step_layer: null argument");
+    if (layer < 0 || layer >= g->cfg.n_layer)
+        return fail(O1_EINVAL, "layer %d out of range (n_layer=%d)", layer, g->cfg.n_layer);
+    return step_groups(g, layer, q, k, v, out, stream);
 }
 
 int o1_get_info(const o1_groups *g, o1_info *info)
 {
     if (!g || !info) return fail(O1_EINVAL, "o1_get_info: null argument");
+    const bool any = g->any_sealed();
     info->n_groups = g->G;
-    info->sealed = g->sealed;
-    info->prompt_len = g->sealed ? g->T : 0;
-    info->m_eff = g->sealed ? g->st.m : 0;
-    info->steps = g->steps;
+    info->sealed = g->all_sealed();
+    info->prompt_len = any ? g->T : 0;
+    info->m_eff = any ? g->st.m : 0;
+    info->steps = g->steps_extreme(false);
     info->state_bytes = g->state_bytes;
     info->work_bytes = g->lm64_bytes;
-    info->exact_only = g->sealed ? g->exact : 0;
-    info->exact_keys = !g->sealed ? 0 : g->exact ? (int32_t)(g->T + g->steps) : g->R;
+    info->exact_only = any ? g->exact : 0;
+    info->exact_keys = !any ? 0 : g->exact ? (int32_t)(g->T + g->steps_extreme(true)) : g->R;
+    info->n_layer = g->cfg.n_layer;
+    info->layers_sealed = (int32_t)std::count(g->layer_sealed.begin(), g->layer_sealed.end(), 1);
+    info->max_steps = g->steps_extreme(true);
     return ok();
 }
 
@@ -368,7 +506,7 @@ int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes)
     if (field < 0 || field >= O1_FIELD_COUNT) return fail(O1_EINVAL, "unknown field %d", field);
     if ((field == O1_FIELD_EXACT_K || field == O1_FIELD_EXACT_V) && g->cfg.exact_cap == 0)
         return fail(O1_EINVAL, "field %d: the handle was created with exact_cap = 0", field);
-    if (landmark_shaped(field) && (!g->sealed || g->exact))
+    if (landmark_shaped(field) && (!g->any_sealed() || g->exact))
         return fail(O1_ESTATE, "field %d has no shape before a skeleton-mode prefill", field);
     *bytes = field_info(g, field).bytes;
     return ok();
@@ -390,7 +528,7 @@ int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, vo
 
 int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, void *stream)
 {
-    if (g && !g->sealed) return fail(O1_ESTATE, "o1_write_field before a successful o1_prefill");
+    if (g && !g->any_sealed()) return fail(O1_ESTATE, "o1_write_field before a successful prefill");
     size_t want = 0;
     int rc = o1_field_bytes(g, field, &want);
     if (rc) return rc;
@@ -436,6 +574,8 @@ int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, c
     int rc = exact_check(desc, &splits, &need);
     if (rc) return rc;
     if (!q || !k || !v || !out) return fail(O1_EINVAL, "o1_exact_attend: null tensor");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(O1_EINVAL, "o1_exact_attend: tensors must be 16-byte aligned");
     if (need && (!workspace || workspace_bytes < need))
         return fail(O1_EINVAL, "o1_exact_attend: work space of %zu bytes needed", need);
     const o1_exact_desc &x = *desc;
@@ -444,7 +584,7 @@ int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, c
     io.k = k;
     io.v = v;
     io.out = out;
-    io.G = x.n_groups;
+    io.map = {x.n_groups, x.n_groups, 0, 0};  // cache group = call index
     io.hpk = x.hpk;
     io.d = x.d;
     io.dv = x.dv;

@@ -35,6 +35,8 @@
 //
 // Work-group size: 256 threads when the launch has many groups (several
 // work-groups per CU hide each other's latency), 512 when it has few.
+// A launch covers the groups of a GroupMap: the whole handle, or one layer of
+// every sequence; inputs and outputs are indexed by the launch's own index.
 #include "o1_internal.h"
 
 namespace o1 {
@@ -75,7 +77,8 @@ template <int D, int DV, int HPK, int MM, int NT>
 __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
 {
     using C = DecodeShape<D, DV, HPK, MM, NT>;
-    const int g = blockIdx.x;
+    const int ci = blockIdx.x;            // call index: inputs and outputs
+    const int g = io.map.state(ci);       // state group
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = s.sink, R = s.R, m = s.m;
     const double scale = (double)s.scale;
@@ -105,15 +108,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
 
     // ---- 0. prologue: one round of small loads into LDS --------------------
     {
-        const float4 *qg = reinterpret_cast<const float4 *>(io.q) + gh0 * C::CH;
+        const float4 *qg = reinterpret_cast<const float4 *>(io.q) + (size_t)ci * HPK * C::CH;
         for (int i = tid; i < HPK * C::CH; i += NT) (&q_s[0][0])[i] = qg[i];
         if (tid < C::CH) {
-            kn_s[tid] = reinterpret_cast<const float4 *>(io.k)[(size_t)g * C::CH + tid];
+            kn_s[tid] = reinterpret_cast<const float4 *>(io.k)[(size_t)ci * C::CH + tid];
             ke_s[tid] = nk[(size_t)slot_row * C::CH + tid];
         }
         if (tid >= 128 && tid < 128 + C::VCH) {
             const int c = tid - 128;
-            vn_s[c] = reinterpret_cast<const float4 *>(io.v)[(size_t)g * C::VCH + c];
+            vn_s[c] = reinterpret_cast<const float4 *>(io.v)[(size_t)ci * C::VCH + c];
             ve_s[c] = nv[(size_t)slot_row * C::VCH + c];
         }
         for (int i = tid; i < HPK * m; i += NT) {
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int off = C::VCH; off < 64; off <<= 1) acc[h][c] += __shfl_xor(acc[h][c], off, 64);
-    float4 *outp = reinterpret_cast<float4 *>(io.out) + gh0 * C::VCH;
+    float4 *outp = reinterpret_cast<float4 *>(io.out) + (size_t)ci * HPK * C::VCH;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
         if (lane < C::VCH) {
@@ -418,7 +421,7 @@ hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t strea
                             hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
     if (attr != hipSuccess) return attr;
     const size_t dyn = sizeof(double) * (size_t)HPK * s.R;
-    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM, NT>), dim3(s.G), dim3(NT), dyn, stream, s, io);
+    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM, NT>), dim3(io.map.count), dim3(NT), dyn, stream, s, io);
     return hipGetLastError();
 }
 
@@ -429,7 +432,7 @@ constexpr int kSmallGrid = 1024;
 template <int D, int DV, int HPK, int MM>
 hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    if (s.G < kSmallGrid) return launch_shape<D, DV, HPK, MM, 512>(s, io, stream);
+    if (io.map.count < kSmallGrid) return launch_shape<D, DV, HPK, MM, 512>(s, io, stream);
     return launch_shape<D, DV, HPK, MM, 256>(s, io, stream);
 }
 

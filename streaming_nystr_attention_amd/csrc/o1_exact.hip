@@ -44,7 +44,8 @@ template <int D, int DV, int HPK>
 __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
 {
     using C = ExactShape<D, DV, HPK>;
-    const int g = blockIdx.x, sp = blockIdx.y;
+    const int ci = blockIdx.x, sp = blockIdx.y;  // call index (q, out, new key, partials)
+    const int g = a.map.state(ci);              // cache group
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int k0 = a.first + sp * a.per_split;
     const int k1 = min(k0 + a.per_split, a.n_keys);
@@ -56,14 +57,14 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
     __shared__ double fac_s[HPK];
     __shared__ double red_s[kNW][C::RED_H * DV];
 
-    const size_t gh0 = (size_t)g * HPK;
+    const size_t gh0 = (size_t)ci * HPK;
     const float4 *qg = reinterpret_cast<const float4 *>(a.q) + gh0 * C::CH;
     for (int i = tid; i < HPK * C::CH; i += kNT) (&q_s[0][0])[i] = qg[i];
     const float4 *kc = reinterpret_cast<const float4 *>(a.k) + (size_t)g * a.cap * C::CH;
     const float4 *vc = reinterpret_cast<const float4 *>(a.v) + (size_t)g * a.cap * C::VCH;
     const int new_row = a.k_new ? a.n_keys - 1 : -1;  // absolute index of the appended key
-    const float4 *kn = reinterpret_cast<const float4 *>(a.k_new) + (size_t)g * C::CH;
-    const float4 *vn = reinterpret_cast<const float4 *>(a.v_new) + (size_t)g * C::VCH;
+    const float4 *kn = reinterpret_cast<const float4 *>(a.k_new) + (size_t)ci * C::CH;
+    const float4 *vn = reinterpret_cast<const float4 *>(a.v_new) + (size_t)ci * C::VCH;
     if (new_row >= k0 && new_row < k1) {
         if (tid < C::CH) reinterpret_cast<float4 *>(a.k_dst)[((size_t)g * a.cap + new_row) * C::CH + tid] = kn[tid];
         if (tid >= 128 && tid < 128 + C::VCH)
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
                     make_float4((float)(o[0] / den), (float)(o[1] / den), (float)(o[2] / den),
                                 (float)(o[3] / den));
             } else {
-                const size_t part = ((size_t)g * gridDim.y + sp) * HPK + h;
+                const size_t part = ((size_t)ci * gridDim.y + sp) * HPK + h;
                 double *num = a.ws_num + part * DV + c4 * 4;
                 num[0] = o[0];
                 num[1] = o[1];
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
     }
 }
 
-// One block of dv threads per (group, head): merge the key-range partials.
+// One block of dv threads per (call index, head): merge the key-range partials.
 __global__ void exact_combine_kernel(ExactIO a, int splits)
 {
     const int gh = blockIdx.x, H = a.hpk, g = gh / H, h = gh - g * H, c = threadIdx.x;
@@ -252,10 +253,10 @@ __global__ void exact_combine_kernel(ExactIO a, int splits)
 template <int D, int DV, int HPK>
 hipError_t launch_exact_shape(const ExactIO &a, int splits, hipStream_t stream)
 {
-    hipLaunchKernelGGL((exact_attend_kernel<D, DV, HPK>), dim3(a.G, splits), dim3(kNT), 0, stream, a);
+    hipLaunchKernelGGL((exact_attend_kernel<D, DV, HPK>), dim3(a.map.count, splits), dim3(kNT), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || splits == 1) return err;
-    hipLaunchKernelGGL(exact_combine_kernel, dim3(a.G * a.hpk), dim3(a.dv), 0, stream, a, splits);
+    hipLaunchKernelGGL(exact_combine_kernel, dim3(a.map.count * a.hpk), dim3(a.dv), 0, stream, a, splits);
     return hipGetLastError();
 }
 
@@ -271,16 +272,24 @@ hipError_t launch_exact_hpk(const ExactIO &a, int splits, hipStream_t stream)
     }
 }
 
-// One work-group per group: copy the prompt rows into the exact buffers and
-// clear the counters the skeleton mode would have set.
-__global__ __launch_bounds__(256) void exact_seal_kernel(DevState s, const float4 *k, const float4 *v,
-                                                         int T, float4 *ek, float4 *ev, int cap)
+// One work-group per call index: copy the prompt rows into the mapped group's
+// exact buffers and clear the counters the skeleton mode would have set.
+__global__ __launch_bounds__(256) void exact_seal_kernel(DevState s, PromptView p, GroupMap map, int T,
+                                                         float4 *ek, float4 *ev, int cap)
 {
-    const int g = blockIdx.x, tid = threadIdx.x;
+    const int ci = blockIdx.x, g = map.state(ci), tid = threadIdx.x;
     const int ck = s.d / 4, cv = s.dv / 4;
-    const size_t nk = (size_t)T * ck, nv = (size_t)T * cv;
-    for (size_t i = tid; i < nk; i += 256) ek[(size_t)g * cap * ck + i] = k[(size_t)g * nk + i];
-    for (size_t i = tid; i < nv; i += 256) ev[(size_t)g * cap * cv + i] = v[(size_t)g * nv + i];
+    const float4 *k = reinterpret_cast<const float4 *>(p.k_row(map, ci, 0));
+    const float4 *v = reinterpret_cast<const float4 *>(p.v_row(map, ci, 0));
+    const int64_t kp = p.k_pos / 4, vp = p.v_pos / 4;
+    for (int i = tid; i < T * ck; i += 256) {
+        const int t = i / ck, c = i - t * ck;
+        ek[((size_t)g * cap + t) * ck + c] = k[(int64_t)t * kp + c];
+    }
+    for (int i = tid; i < T * cv; i += 256) {
+        const int t = i / cv, c = i - t * cv;
+        ev[((size_t)g * cap + t) * cv + c] = v[(int64_t)t * vp + c];
+    }
     if (tid == 0) s.win_head[g] = 0;
     if (tid < s.hpk) {
         const size_t gh = (size_t)g * s.hpk + tid;
@@ -292,11 +301,10 @@ __global__ __launch_bounds__(256) void exact_seal_kernel(DevState s, const float
 
 }  // namespace
 
-hipError_t launch_exact_seal(const DevState &s, const float *k, const float *v, int T, float *ek,
-                             float *ev, int cap, hipStream_t stream)
+hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const GroupMap &map, int T,
+                             float *ek, float *ev, int cap, hipStream_t stream)
 {
-    hipLaunchKernelGGL(exact_seal_kernel, dim3(s.G), dim3(256), 0, stream, s,
-                       reinterpret_cast<const float4 *>(k), reinterpret_cast<const float4 *>(v), T,
+    hipLaunchKernelGGL(exact_seal_kernel, dim3(map.count), dim3(256), 0, stream, s, p, map, T,
                        reinterpret_cast<float4 *>(ek), reinterpret_cast<float4 *>(ev), cap);
     return hipGetLastError();
 }

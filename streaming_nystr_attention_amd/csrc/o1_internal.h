@@ -31,38 +31,76 @@ struct DevState {
     int64_t *far_len;
 };
 
-struct DecodeIO {
+// The groups one call covers.  Its inputs and outputs are indexed by the call's
+// own index i in [0, count); state group g = (i / per) * stride + offset + i % per.
+//   whole handle:   per = stride = n_kv, offset = 0        (g = i)
+//   one layer l:    per = n_kv, stride = n_layer * n_kv, offset = l * n_kv
+//                   (i = s * n_kv + kv, the layer's groups of every sequence)
+struct GroupMap {
+    int count, per, stride, offset;
+    __host__ __device__ int state(int i) const { return (i / per) * stride + offset + i % per; }
+};
+
+// A prompt in place, element strides in floats.  For call index i (o = i / per,
+// n = i % per), query head j of the group, position t and component c:
+//   q(i, j, t, c) = q[o * q_outer + (n * hpk + j) * q_head + t * q_pos + c]
+//   k(i, t, c)    = k[o * k_outer + n * k_inner + t * k_pos + c]     (v alike)
+// Rows are contiguous; strides are multiples of 4 floats (float4 rows).
+struct PromptView {
     const float *q, *k, *v;
-    float *out;
+    int64_t q_outer, q_head, q_pos;
+    int64_t k_outer, k_inner, k_pos;
+    int64_t v_outer, v_inner, v_pos;
+    __host__ __device__ const float *q_row(const GroupMap &mp, int hpk, int i, int j, int64_t t) const
+    {
+        return q + (int64_t)(i / mp.per) * q_outer + ((int64_t)(i % mp.per) * hpk + j) * q_head + t * q_pos;
+    }
+    __host__ __device__ const float *k_row(const GroupMap &mp, int i, int64_t t) const
+    {
+        return k + (int64_t)(i / mp.per) * k_outer + (int64_t)(i % mp.per) * k_inner + t * k_pos;
+    }
+    __host__ __device__ const float *v_row(const GroupMap &mp, int i, int64_t t) const
+    {
+        return v + (int64_t)(i / mp.per) * v_outer + (int64_t)(i % mp.per) * v_inner + t * v_pos;
+    }
+};
+
+struct DecodeIO {
+    const float *q, *k, *v;  // q [count][hpk][d], k [count][d], v [count][dv]
+    float *out;              // [count][hpk][dv]
+    GroupMap map;
 };
 
 struct PrefillIO {
-    const float *q, *k, *v;  // prompt [G][hpk][T][d], [G][T][d], [G][T][dv]
+    PromptView p;
+    GroupMap map;
     int T;
-    const float *fz_kt, *fz_qt, *fz_mu;  // optional frozen replacements
-    double *lm64;                        // work: [G][1 + hpk][m][d] f64 landmarks
+    const float *fz_kt, *fz_qt, *fz_mu;  // optional frozen replacements, [count][...]
+    double *lm64;                        // work: [count][1 + hpk][m][d] f64 landmarks
 };
 
 // Exact grouped-GQA attention over a stored KV cache: the O(p) comparator, and
-// the decode step of the exact-only mode.
+// the decode step of the exact-only mode.  q, out, k_new, v_new and the split
+// partials are indexed by the call index i, the cache by the state group map.state(i).
 struct ExactIO {
-    const float *q, *k, *v;  // q [G][hpk][d], k [G][cap][d], v [G][cap][dv]
-    float *out;              // [G][hpk][dv]
-    int G, hpk, d, dv, cap, first, n_keys, per_split;
+    const float *q, *k, *v;  // q [count][hpk][d], k [G][cap][d], v [G][cap][dv]
+    float *out;              // [count][hpk][dv]
+    GroupMap map;
+    int hpk, d, dv, cap, first, n_keys, per_split;
     float scale;
-    double *ws_max, *ws_sum, *ws_num;  // split partials [G][splits][hpk](x dv)
+    double *ws_max, *ws_sum, *ws_num;  // split partials [count][splits][hpk](x dv)
     // Append mode (exact-only decode), else all null: key n_keys-1 is the new
-    // one, read from k_new [G][d] / v_new [G][dv] and stored into row n_keys-1
-    // of k_dst / v_dst (the same buffers as k / v).
+    // one, read from k_new [count][d] / v_new [count][dv] and stored into row
+    // n_keys-1 of k_dst / v_dst (the same buffers as k / v).
     const float *k_new, *v_new;
     float *k_dst, *v_dst;
 };
 int exact_splits(int G, int n_visible);
 hipError_t launch_exact(const ExactIO &io, int splits, hipStream_t stream);
-// Exact-only prefill: prompt rows k [G][T][d], v [G][T][dv] into rows 0..T-1
-// of ek [G][cap][d], ev [G][cap][dv]; win_head, far_len, lambda, tries cleared.
-hipError_t launch_exact_seal(const DevState &s, const float *k, const float *v, int T, float *ek,
-                             float *ev, int cap, hipStream_t stream);
+// Exact-only prefill of the groups in `map`: prompt rows 0..T-1 into rows
+// 0..T-1 of ek [G][cap][d], ev [G][cap][dv]; win_head, far_len, lambda, tries cleared.
+hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const GroupMap &map, int T,
+                             float *ek, float *ev, int cap, hipStream_t stream);
 
 // True when the decode kernel is compiled for this shape.
 bool decode_supported(int d, int dv, int hpk, int m, int R);

@@ -17,6 +17,11 @@
 //                      reaches, computed in 16-key tiles on f64 MFMA with an
 //                      online per-landmark max: m_max_i = max_j l_ij,
 //                      Z^_i = sum_j e^{l_ij - m_max_i}, T^_i = sum_j e^{l_ij - m_max_i} v_j.
+//
+// G above is the number of groups a launch covers, given by a GroupMap (the
+// whole handle, or one layer of every sequence): the prompt is read in place
+// through a PromptView by the launch's own index, the state is written at the
+// mapped group.
 #include <float.h>
 
 #include "o1_internal.h"
@@ -28,22 +33,25 @@ constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, PrefillIO io)
 {
-    const int g = blockIdx.x, src = blockIdx.y;  // src 0 = keys, 1 + h = head h
+    const int ci = blockIdx.x, src = blockIdx.y;  // src 0 = keys, 1 + h = head h
+    const int g = io.map.state(ci);
     const int d = s.d, m = s.m, T = io.T, H = s.hpk;
-    const float *x;
+    const float *x;  // prompt row 0 of the source; rows are `pos` floats apart
+    int64_t pos;
     float *dst32;
     const float *fz;
     if (src == 0) {
-        x = io.k + (size_t)g * T * d;
+        x = io.p.k_row(io.map, ci, 0);
+        pos = io.p.k_pos;
         dst32 = s.k_tilde + (size_t)g * m * d;
-        fz = io.fz_kt ? io.fz_kt + (size_t)g * m * d : nullptr;
+        fz = io.fz_kt ? io.fz_kt + (size_t)ci * m * d : nullptr;
     } else {
-        const size_t gh = (size_t)g * H + (src - 1);
-        x = io.q + gh * T * d;
-        dst32 = s.q_tilde + gh * m * d;
-        fz = io.fz_qt ? io.fz_qt + gh * m * d : nullptr;
+        x = io.p.q_row(io.map, H, ci, src - 1, 0);
+        pos = io.p.q_pos;
+        dst32 = s.q_tilde + ((size_t)g * H + (src - 1)) * m * d;
+        fz = io.fz_qt ? io.fz_qt + ((size_t)ci * H + (src - 1)) * m * d : nullptr;
     }
-    double *dst64 = io.lm64 + ((size_t)g * (1 + H) + src) * m * d;
+    double *dst64 = io.lm64 + ((size_t)ci * (1 + H) + src) * m * d;
     for (int t = threadIdx.x; t < m * d; t += kThreads) {
         if (fz) {
             const float v = fz[t];
@@ -54,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, Prefill
         const int a = t / d, c = t - a * d;
         const long lo = (long)a * T / m, hi = (long)(a + 1) * T / m;
         double acc = 0.0;
-        for (long j = lo; j < hi; ++j) acc += (double)x[(size_t)j * d + c];
+        for (long j = lo; j < hi; ++j) acc += (double)x[(int64_t)j * pos + c];
         const double mean = acc * (1.0 / (double)(hi - lo));
         dst64[t] = mean;
         dst32[t] = (float)mean;
@@ -63,11 +71,12 @@ __global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, Prefill
 
 __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO io)
 {
-    const int g = blockIdx.x;
+    const int ci = blockIdx.x, g = io.map.state(ci);
     const int S = s.sink, w = s.w, R = s.R, T = io.T;
     const int ck = s.d / 4, cv = s.dv / 4;
-    const float4 *kin = reinterpret_cast<const float4 *>(io.k) + (size_t)g * T * ck;
-    const float4 *vin = reinterpret_cast<const float4 *>(io.v) + (size_t)g * T * cv;
+    const float4 *kin = reinterpret_cast<const float4 *>(io.p.k_row(io.map, ci, 0));
+    const float4 *vin = reinterpret_cast<const float4 *>(io.p.v_row(io.map, ci, 0));
+    const int64_t kp = io.p.k_pos / 4, vp = io.p.v_pos / 4;  // row strides in float4
     float4 *nk = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * R * ck;
     float4 *nv = reinterpret_cast<float4 *>(s.near_v) + (size_t)g * R * cv;
     const int base = T - w;          // first prompt key still in the window
@@ -81,8 +90,8 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO
             const int slot = r - S;
             j = base + ((slot - shift) % w + w) % w;  // (j - S) mod w == slot
         }
-        if (c < ck) nk[(size_t)r * ck + c] = kin[(size_t)j * ck + c];
-        else nv[(size_t)r * cv + (c - ck)] = vin[(size_t)j * cv + (c - ck)];
+        if (c < ck) nk[(size_t)r * ck + c] = kin[(int64_t)j * kp + c];
+        else nv[(size_t)r * cv + (c - ck)] = vin[(int64_t)j * vp + (c - ck)];
     }
     const int evictions = T - S - w;
     if (threadIdx.x == 0) s.win_head[g] = evictions % w;
@@ -99,7 +108,8 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // the vector units from LDS.
 __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, PrefillIO io, double ridge_rel)
 {
-    const int gh = blockIdx.x, H = s.hpk, g = gh / H, h = gh - g * H;
+    const int H = s.hpk, ci = blockIdx.x / H, h = blockIdx.x - ci * H;
+    const size_t gh = (size_t)io.map.state(ci) * H + h;  // state head
     const int m = s.m, d = s.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = (m + 15) / 16, mp = nb * 16, ld = mp + 1;
     extern __shared__ double lds[];
@@ -109,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
     __shared__ double mean_diag_s;
     __shared__ int fail_s;
 
-    const double *kt = io.lm64 + ((size_t)g * (1 + H)) * m * d;
-    const double *qt = io.lm64 + ((size_t)g * (1 + H) + 1 + h) * m * d;
+    const double *kt = io.lm64 + ((size_t)ci * (1 + H)) * m * d;
+    const double *qt = io.lm64 + ((size_t)ci * (1 + H) + 1 + h) * m * d;
     const double sc = (double)s.scale;
     const int li = lane & 15, lk = lane >> 4;
 
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
         lambda *= 10.0;
     }
 
-    float *mu = s.mu + (size_t)gh * m * m;
+    float *mu = s.mu + gh * m * m;
     if (result <= kRidgeTries) {
         // Column b of M solves (L L^T) x = (row b of A); done in place in row b.
         for (int b = tid; b < m; b += kThreads) {
@@ -238,7 +248,8 @@ __global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
     constexpr int KS = D / 4;    // k-steps of the logit product
     constexpr int CB = DV / 16;  // 16-wide column blocks of T^
     constexpr int TK = 16;       // keys per tile
-    const int gh = blockIdx.x, H = s.hpk, g = gh / H;
+    const int H = s.hpk, ci = blockIdx.x / H;
+    const size_t gh = (size_t)io.map.state(ci) * H + (blockIdx.x - ci * H);  // state head
     const int m = s.m, tid = threadIdx.x, lane = tid & 63, rb = tid >> 6, nthr = blockDim.x;
     const int S = s.sink, T = io.T, nf = T - S - s.w;
     const double sc = (double)s.scale;
@@ -253,7 +264,7 @@ __global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
     __shared__ float q_lds[4][16][D + 1];
     for (int t = lane; t < 16 * D; t += 64) {
         const int ii = t / D, c = t - ii * D, i = rb * 16 + ii;
-        q_lds[rb][ii][c] = (i < m) ? s.q_tilde[((size_t)gh * m + i) * D + c] : 0.0f;
+        q_lds[rb][ii][c] = (i < m) ? s.q_tilde[(gh * m + i) * D + c] : 0.0f;
     }
     f64x4 tacc[CB];
 #pragma unroll
@@ -265,13 +276,14 @@ __global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
         zs[r] = 0.0;
     }
 
-    const float *K = io.k + ((size_t)g * T + S) * D;
-    const float *V = io.v + ((size_t)g * T + S) * DV;
+    const float *K = io.p.k_row(io.map, ci, S);  // far keys S .. T-w-1 in place
+    const float *V = io.p.v_row(io.map, ci, S);
+    const int64_t kpos = io.p.k_pos, vpos = io.p.v_pos;
     for (int j0 = 0; j0 < nf; j0 += TK) {
         const int nt = min(TK, nf - j0);
         for (int t = tid; t < TK * (D / 4); t += nthr) {
             const int jj = t / (D / 4), c4 = t - jj * (D / 4);
-            float4 x = jj < nt ? reinterpret_cast<const float4 *>(K + (size_t)(j0 + jj) * D)[c4]
+            float4 x = jj < nt ? reinterpret_cast<const float4 *>(K + (int64_t)(j0 + jj) * kpos)[c4]
                                : make_float4(0.f, 0.f, 0.f, 0.f);
             k_lds[jj][c4 * 4 + 0] = x.x;
             k_lds[jj][c4 * 4 + 1] = x.y;
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
         }
         for (int t = tid; t < TK * (DV / 4); t += nthr) {
             const int jj = t / (DV / 4), c4 = t - jj * (DV / 4);
-            float4 x = jj < nt ? reinterpret_cast<const float4 *>(V + (size_t)(j0 + jj) * DV)[c4]
+            float4 x = jj < nt ? reinterpret_cast<const float4 *>(V + (int64_t)(j0 + jj) * vpos)[c4]
                                : make_float4(0.f, 0.f, 0.f, 0.f);
             *reinterpret_cast<float4 *>(&v_lds[jj][c4 * 4]) = x;
         }
@@ -341,24 +353,30 @@ __global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
         const float mf = (float)mx[r];
         const double corr = exp(mx[r] - (double)mf);
         if (li == 0) {
-            s.m_max[(size_t)gh * m + i] = mf;
-            s.z_hat[(size_t)gh * m + i] = zs[r] * corr;
+            s.m_max[gh * m + i] = mf;
+            s.z_hat[gh * m + i] = zs[r] * corr;
         }
-        float *th = s.t_hat + ((size_t)gh * m + i) * DV;
+        float *th = s.t_hat + (gh * m + i) * DV;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) th[cb * 16 + li] = (float)(tacc[cb][r] * corr);
     }
 }
 
-__global__ void copy_mu_kernel(DevState s, const float *src)
+// Frozen M, [count][hpk][m][m] in call order, into the mapped groups' state.
+__global__ void copy_mu_kernel(DevState s, GroupMap map, const float *src)
 {
-    const size_t n = (size_t)s.G * s.hpk * s.m * s.m;
-    for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (size_t)gridDim.x * blockDim.x)
-        s.mu[t] = src[t];
-    const size_t nh = (size_t)s.G * s.hpk;
+    const size_t per_g = (size_t)s.hpk * s.m * s.m;
+    const size_t n = (size_t)map.count * per_g;
+    for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (size_t)gridDim.x * blockDim.x) {
+        const size_t ci = t / per_g;
+        s.mu[(size_t)map.state((int)ci) * per_g + (t - ci * per_g)] = src[t];
+    }
+    const size_t nh = (size_t)map.count * s.hpk;
     for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < nh; t += (size_t)gridDim.x * blockDim.x) {
-        s.lambda[t] = 0.0;
-        s.tries[t] = 0;
+        const size_t ci = t / s.hpk;
+        const size_t gh = (size_t)map.state((int)ci) * s.hpk + (t - ci * s.hpk);
+        s.lambda[gh] = 0.0;
+        s.tries[gh] = 0;
     }
 }
 
@@ -367,27 +385,28 @@ __global__ void copy_mu_kernel(DevState s, const float *src)
 hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t stream)
 {
     if (s.d > 128 || s.dv > 128 || s.m > kMaxLandmarks) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(landmarks_kernel, dim3(s.G, 1 + s.hpk), dim3(kThreads), 0, stream, s, io);
+    const int n = io.map.count;
+    hipLaunchKernelGGL(landmarks_kernel, dim3(n, 1 + s.hpk), dim3(kThreads), 0, stream, s, io);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(scatter_kernel, dim3(s.G), dim3(kThreads), 0, stream, s, io);
+    hipLaunchKernelGGL(scatter_kernel, dim3(n), dim3(kThreads), 0, stream, s, io);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (io.fz_mu) {
-        hipLaunchKernelGGL(copy_mu_kernel, dim3(1024), dim3(kThreads), 0, stream, s, io.fz_mu);
+        hipLaunchKernelGGL(copy_mu_kernel, dim3(1024), dim3(kThreads), 0, stream, s, io.map, io.fz_mu);
     } else {
         const size_t mp = (size_t)((s.m + 15) / 16) * 16;
         const size_t lds = sizeof(double) * 3 * mp * (mp + 1);
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gram_pinv_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(gram_pinv_kernel, dim3(s.G * s.hpk), dim3(kThreads), lds, stream, s, io, kRidgeRel);
+        hipLaunchKernelGGL(gram_pinv_kernel, dim3(n * s.hpk), dim3(kThreads), lds, stream, s, io, kRidgeRel);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int nrb = (s.m + 15) / 16;
     if (s.d == 128 && s.dv == 128)
-        hipLaunchKernelGGL((far_mfma_kernel<128, 128>), dim3(s.G * s.hpk), dim3(64 * nrb), 0, stream, s, io);
+        hipLaunchKernelGGL((far_mfma_kernel<128, 128>), dim3(n * s.hpk), dim3(64 * nrb), 0, stream, s, io);
     else if (s.d == 64 && s.dv == 64)
-        hipLaunchKernelGGL((far_mfma_kernel<64, 64>), dim3(s.G * s.hpk), dim3(64 * nrb), 0, stream, s, io);
+        hipLaunchKernelGGL((far_mfma_kernel<64, 64>), dim3(n * s.hpk), dim3(64 * nrb), 0, stream, s, io);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -104,6 +104,8 @@ def test_null_arguments_are_rejected():
     assert L.o1_create_groups(None, None) == P.O1_EINVAL
     assert L.o1_prefill(None, None, None, None, 300, None, None) == P.O1_EINVAL
     assert L.o1_step(None, None, None, None, None, None) == P.O1_EINVAL
+    assert L.o1_prefill_layer(None, 0, None, 300, None, None) == P.O1_EINVAL
+    assert L.o1_step_layer(None, 0, None, None, None, None, None) == P.O1_EINVAL
     info = P.o1_info()
     assert L.o1_get_info(None, ctypes.byref(info)) == P.O1_EINVAL
     n = ctypes.c_size_t()
