@@ -148,6 +148,22 @@ def test_decode_hpk1_window1():
     decode_parity(wl)
 
 
+MAX_SIZES = [
+    # the largest near block compiled, sink + w = 1024, with hpk 4 (the 32 KB of
+    # near logits the kernel reserves) and the largest landmark count, m = 64
+    W.Workload("max_window_hpk4", 2, 1, 2, 4, 128, 128, 64, 1000, 24, T=1100, steps=40,
+               q_std=2.0, k_std=2.0, seed=16),
+    # the most heads, hpk 8, at d = 64 with sink + w = 512 and m = 64
+    W.Workload("max_heads_d64", 2, 1, 2, 8, 64, 64, 64, 500, 12, T=700, steps=30, seed=17),
+]
+
+
+@pytest.mark.parametrize("wl", MAX_SIZES, ids=[w.name for w in MAX_SIZES])
+def test_decode_maximum_sizes(wl):
+    assert wl.hpk * (wl.sink + wl.w) * 8 == 32 * 1024 and wl.m_eff == 64
+    decode_parity(wl)
+
+
 def test_gqa_group_equals_single_head_groups_bitwise():
     wl = W.WORKLOADS["qwen3_layer"].with_(n_kv=4, steps=30)
     q, k, v = W.prompt(wl, DEV)

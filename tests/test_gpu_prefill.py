@@ -130,3 +130,14 @@ def test_prefill_ragged_segments():
 def test_prefill_prompt_longer_than_budget():
     # T / 8 above the budget: m_eff clamps to m (the warn-once case of the page)
     prefill_parity(W.Workload("clamped", 2, 1, 2, 2, 64, 64, 16, 32, 4, T=300, steps=0, seed=21))
+
+
+@pytest.mark.parametrize("wl", [
+    W.Workload("max_window_hpk4", 2, 1, 2, 4, 128, 128, 64, 1000, 24, T=1100, steps=0, q_std=2.0,
+               k_std=2.0, seed=16),
+    W.Workload("max_heads_d64", 2, 1, 2, 8, 64, 64, 64, 500, 12, T=700, steps=0, seed=17),
+], ids=["max_window_hpk4", "max_heads_d64"])
+def test_prefill_maximum_sizes(wl):
+    """The largest compiled near block (sink + w = 1024) and head count (hpk 8),
+    both with m = 64."""
+    prefill_parity(wl)
