@@ -95,6 +95,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
     __shared__ double r_s[HPK][MM];                // T^ rescale factor per landmark
     __shared__ double e_s[HPK][MM];                // weight of the evicted key per landmark
     __shared__ double gain_s[HPK][MM];             // far mixing gains (0 when dropped)
+    __shared__ double fh_s[C::STAGE_M ? HPK : 1][MM];  // landmark weights e^{s - f} (0 past m)
     __shared__ double den_s[HPK];
     __shared__ double red_s[C::NW][C::RED_H * DV];
     extern __shared__ double lg_s[];               // [HPK][R] near logits, then weights
@@ -261,11 +262,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
         // u_b = sum_a fh_a M[a][b]  (lane = b)
         double u = 0.0;
         if constexpr (C::STAGE_M) {
+            // fh goes through LDS (zero past m): the loop runs over the
+            // compile-time bound MM with broadcast reads and clamped rows of
+            // the staged M, without branches or cross-lane shuffles.
+            if (lane < MM) fh_s[h][lane] = fh;
+            __builtin_amdgcn_wave_barrier();
             const float *mu = mu_s + (size_t)h * m * m;
-            for (int a = 0; a < m; ++a) {
-                const double fa = __shfl(fh, a, 64);
-                if (act) u = fma(fa, (double)mu[a * m + lane], u);
-            }
+            const int col = act ? lane : 0;
+#pragma unroll 8
+            for (int a = 0; a < MM; ++a) u = fma(fh_s[h][a], (double)mu[min(a, m - 1) * m + col], u);
+            if (!act) u = 0.0;
         } else {
             // M from global memory, MB rows per lane in flight
             const float *mu = s.mu + (gh0 + h) * (size_t)m * m;
