@@ -37,6 +37,8 @@
 // work-groups per CU hide each other's latency), 512 when it has few.
 // A launch covers the groups of a GroupMap: the whole handle, or one layer of
 // every sequence; inputs and outputs are indexed by the launch's own index.
+#include <atomic>
+
 #include "o1_internal.h"
 
 namespace o1 {
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
                 double acc = 0.0;
 #pragma unroll
                 for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kr[k]);
-                acc = group_sum<C::LPR>(acc);
+                acc = group_sum<C::LPR>(acc, lane);
                 if (sub == 0 && r < NQ) lf_s[r / m][r % m] = acc * scale;
             }
         }
@@ -229,11 +231,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
     for (int h = wave; h < HPK; h += C::NW) {
         double c = NEG_INF;
         for (int r = lane; r < R; r += 64) c = fmax(c, lg_s[h * R + r]);
-        c = wave_max(c);
+        c = wave_max(c, lane);
 
         const bool act = lane < m;
         const double sa = act ? land_s[h][lane] : NEG_INF;
-        const double f = wave_max(sa);
+        const double f = wave_max(sa, lane);
         const double fh = act ? exp(sa - f) : 0.0;
 
         // NystromHead::far_insert for landmark i = lane: strict ">" growth of
@@ -282,16 +284,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
                 for (int j = 0; j < C::MB; ++j) mv[j] = mu[(size_t)min(a0 + j, m - 1) * m + col];
 #pragma unroll
                 for (int j = 0; j < C::MB; ++j) {
-                    const double fa = __shfl(fh, (a0 + j) & 63, 64);
+                    const double fa = lane_value(fh, (a0 + j) & 63);
                     if (a0 + j < m && act) u = fma(fa, (double)mv[j], u);
                 }
             }
         }
         if (s.rect == 1) u = fmax(u, 0.0);  // O1Rect::Fm
 
-        const double call = fmax(c, wave_max(act ? f + mn : NEG_INF));
+        const double call = fmax(c, wave_max(act ? f + mn : NEG_INF, lane));
         const double gain = act ? u * exp(f + mn - call) : 0.0;
-        const double far_den = wave_sum(gain * zn);
+        const double far_den = wave_sum(gain * zn, lane);
         const bool keep = far_den >= 0.0;  // aggregate rectifier (0 keeps)
         if (act) gain_s[h][lane] = keep ? gain : 0.0;
         const double shift = keep ? call : c;  // dropped far field: near-only shift
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
             lg_s[h * R + r] = p;
             acc += p;
         }
-        acc = wave_sum(acc);
+        acc = wave_sum(acc, lane);
         if (lane == 0) den_s[h] = (keep ? far_den : 0.0) + acc;
     }
     __syncthreads();
@@ -379,9 +381,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
 #pragma unroll
     for (int h = 0; h < HPK; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int off = C::VCH; off < 64; off <<= 1) acc[h][c] += __shfl_xor(acc[h][c], off, 64);
+        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCH>(acc[h][c], lane);
     float4 *outp = reinterpret_cast<float4 *>(io.out) + (size_t)ci * HPK * C::VCH;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
@@ -421,11 +421,19 @@ template <int D, int DV, int HPK, int MM, int NT>
 hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     // Static LDS of the wide shapes plus the near logits can pass 64 KB; raise
-    // the kernel's dynamic limit once (an unsupported size fails the launch).
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, HPK, MM, NT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
-    if (attr != hipSuccess) return attr;
+    // the kernel's dynamic limit once per device (function attributes are per
+    // device; an unsupported size fails the launch).
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    const uint64_t bit = dev < 64 ? 1ull << dev : 0;
+    if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, HPK, MM, NT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
+        if (err != hipSuccess) return err;
+        done.fetch_or(bit, std::memory_order_release);
+    }
     const size_t dyn = sizeof(double) * (size_t)HPK * s.R;
     hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM, NT>), dim3(io.map.count), dim3(NT), dyn, stream, s, io);
     return hipGetLastError();

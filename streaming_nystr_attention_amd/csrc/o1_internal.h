@@ -108,24 +108,100 @@ hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stre
 hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t stream);
 
 // ---- wavefront helpers (wave64) ------------------------------------------
+//
+// Cross-lane exchanges of f64 values on the vector ALU (no LDS crossbar): the
+// value of a partner lane whose lane bit `OFF` is flipped.  Within 16-lane rows
+// the partners come from DPP (lane ^ 1 and lane ^ 2 by quad permutes, 7 - i in
+// each 8-lane half row and 15 - i in each row by the mirrors); across rows and
+// wave halves from v_permlane16_swap / v_permlane32_swap (lane ^ 16, lane ^ 32).
+// A reduction that pairs every lane with one lane of the other half at each
+// level sums every lane exactly once, whichever partner of that half it is.
+namespace lanes {
+
+__device__ __forceinline__ unsigned lo32(double x) { return (unsigned)__double_as_longlong(x); }
+__device__ __forceinline__ unsigned hi32(double x) { return (unsigned)(__double_as_longlong(x) >> 32); }
+__device__ __forceinline__ double join(unsigned lo, unsigned hi)
+{
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x)
+{
+    return join((unsigned)__builtin_amdgcn_update_dpp(0, (int)lo32(x), CTRL, 0xf, 0xf, false),
+                 (unsigned)__builtin_amdgcn_update_dpp(0, (int)hi32(x), CTRL, 0xf, 0xf, false));
+}
+
+}  // namespace lanes
+
+template <int OFF>
+__device__ __forceinline__ double partner(double x, int lane)
+{
+    static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "lane bit");
+    if constexpr (OFF == 1) {
+        return lanes::dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    } else if constexpr (OFF == 2) {
+        return lanes::dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    } else if constexpr (OFF == 4) {
+        return lanes::dpp<0x141>(x);  // row_half_mirror: 7 - i within 8 lanes
+    } else if constexpr (OFF == 8) {
+        return lanes::dpp<0x140>(x);  // row_mirror: 15 - i within 16 lanes
+    } else if constexpr (OFF == 16) {
+        // swap odd rows of the first operand with even rows of the second
+        const auto a = __builtin_amdgcn_permlane16_swap(lanes::lo32(x), lanes::lo32(x), false, false);
+        const auto b = __builtin_amdgcn_permlane16_swap(lanes::hi32(x), lanes::hi32(x), false, false);
+        return (lane & 16) ? lanes::join(a[0], b[0]) : lanes::join(a[1], b[1]);
+    } else {
+        // swap the upper half of the first operand with the lower half of the second
+        const auto a = __builtin_amdgcn_permlane32_swap(lanes::lo32(x), lanes::lo32(x), false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(lanes::hi32(x), lanes::hi32(x), false, false);
+        return (lane & 32) ? lanes::join(a[0], b[0]) : lanes::join(a[1], b[1]);
+    }
+}
 
 // Sum over aligned groups of W lanes (W a power of two <= 64); every lane of
 // the group receives the group total.
 template <int W>
-__device__ __forceinline__ double group_sum(double x)
+__device__ __forceinline__ double group_sum(double x, int lane)
 {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    if constexpr (W >= 64) x += partner<32>(x, lane);
+    if constexpr (W >= 32) x += partner<16>(x, lane);
+    if constexpr (W >= 16) x += partner<8>(x, lane);
+    if constexpr (W >= 8) x += partner<4>(x, lane);
+    if constexpr (W >= 4) x += partner<2>(x, lane);
+    if constexpr (W >= 2) x += partner<1>(x, lane);
     return x;
 }
 
-__device__ __forceinline__ double wave_sum(double x) { return group_sum<64>(x); }
+__device__ __forceinline__ double wave_sum(double x, int lane) { return group_sum<64>(x, lane); }
 
-__device__ __forceinline__ double wave_max(double x)
+__device__ __forceinline__ double wave_max(double x, int lane)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmax(x, __shfl_xor(x, off, 64));
+    x = fmax(x, partner<32>(x, lane));
+    x = fmax(x, partner<16>(x, lane));
+    x = fmax(x, partner<8>(x, lane));
+    x = fmax(x, partner<4>(x, lane));
+    x = fmax(x, partner<2>(x, lane));
+    return fmax(x, partner<1>(x, lane));
+}
+
+// Sum over the lanes that differ from this one only in lane bits >= FROM: the
+// partners are exact (lane ^ 16, lane ^ 32), so the lower lane bits -- a column
+// index, say -- are kept.
+template <int FROM>
+__device__ __forceinline__ double sum_high_lanes(double x, int lane)
+{
+    static_assert(FROM == 16 || FROM == 32 || FROM == 64, "only whole 16-lane rows are exchanged exactly");
+    if constexpr (FROM <= 16) x += partner<16>(x, lane);
+    if constexpr (FROM <= 32) x += partner<32>(x, lane);
     return x;
+}
+
+// Value of lane `src` (uniform across the wave) in every lane.
+__device__ __forceinline__ double lane_value(double x, int src)
+{
+    return lanes::join((unsigned)__builtin_amdgcn_readlane((int)lanes::lo32(x), src),
+                       (unsigned)__builtin_amdgcn_readlane((int)lanes::hi32(x), src));
 }
 
 // ---- row arithmetic shared by the decode and exact-attention kernels ------
@@ -166,17 +242,14 @@ __device__ __forceinline__ double dot4(const float4 a, const float4 b)
 }
 
 // Reduce N per-lane partial sums over aligned groups of W lanes.  Each halving
-// step exchanges half of the remaining values with the partner lane; lanes keep
-// the lower or upper half by their lane bit.  Returns, in every lane, the group
-// total of value index (lane % W) / (W / N).
+// step exchanges half of the remaining values with a partner lane of the other
+// half; lanes keep the lower or upper half by their lane bit.  Returns, in every
+// lane, the group total of value index (lane % W) / (W / N).
 template <int W, int N>
 __device__ __forceinline__ double head_reduce(const double *v, int lane)
 {
     if constexpr (N == 1) {
-        double x = v[0];
-#pragma unroll
-        for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-        return x;
+        return group_sum<W>(v[0], lane);
     } else {
         constexpr int off = W / 2;
         const bool hi = (lane & off) != 0;
@@ -185,7 +258,7 @@ __device__ __forceinline__ double head_reduce(const double *v, int lane)
         for (int i = 0; i < N / 2; ++i) {
             const double mine = hi ? v[N / 2 + i] : v[i];
             const double send = hi ? v[i] : v[N / 2 + i];
-            nv[i] = mine + __shfl_xor(send, off, 64);
+            nv[i] = mine + partner<off>(send, lane);
         }
         return head_reduce<W / 2, N / 2>(nv, lane);
     }
