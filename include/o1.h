@@ -22,6 +22,9 @@
  *     leaves the state as it was, except O1_EHIP after a launch (state undefined).
  *   - Calls on one handle must be serialised by the caller (one stream, or
  *     external ordering).  Distinct handles are independent.
+ *   - A handle lives on the device that was current at o1_create_groups; its
+ *     entry points switch to that device for their duration and restore the
+ *     caller's current device before returning.
  */
 #ifndef O1_H
 #define O1_H

@@ -134,14 +134,31 @@ void free_state(o1_groups *g)
         if (p) (void)hipFree(p);
 }
 
-int use_device(const o1_groups *g)
-{
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess) return fail(O1_EHIP, "hipGetDevice failed");
-    if (cur != g->device && hipSetDevice(g->device) != hipSuccess)
-        return fail(O1_EHIP, "hipSetDevice(%d) failed", g->device);
-    return O1_OK;
-}
+// Makes the handle's device current for the scope of an entry point and
+// restores the caller's device on exit.
+class DeviceScope {
+  public:
+    explicit DeviceScope(const o1_groups *g)
+    {
+        if (hipGetDevice(&prev_) != hipSuccess) {
+            rc_ = fail(O1_EHIP, "hipGetDevice failed");
+        } else if (prev_ != g->device) {
+            if (hipSetDevice(g->device) != hipSuccess)
+                rc_ = fail(O1_EHIP, "hipSetDevice(%d) failed", g->device);
+            else
+                switched_ = true;
+        }
+    }
+    ~DeviceScope()
+    {
+        if (switched_) (void)hipSetDevice(prev_);
+    }
+    int status() const { return rc_; }
+
+  private:
+    int prev_ = -1, rc_ = O1_OK;
+    bool switched_ = false;
+};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
@@ -175,8 +192,8 @@ int prefill_groups(o1_groups *g, int layer, const o1::PromptView &pv, int32_t T,
     }
     if ((long long)T * map.count * c.hpk * c.d > (1LL << 40))
         return fail(O1_EINVAL, "prompt too large (T=%d)", T);
-    int rc = use_device(g);
-    if (rc) return rc;
+    DeviceScope dev(g);
+    if (int rc = dev.status()) return rc;
     int m_eff = T / 8;
     if (m_eff < 4) m_eff = 4;
     if (m_eff > c.m) m_eff = c.m;
@@ -252,8 +269,8 @@ int step_groups(o1_groups *g, int layer, const float *q, const float *k, const f
             (long long)g->T + (layer < 0 ? g->steps_extreme(true) : g->layer_steps[layer]);
         if (held >= g->cfg.exact_cap)
             return fail(O1_EFULL, "exact-only groups already hold exact_cap = %d keys", g->cfg.exact_cap);
-        int rc = use_device(g);
-        if (rc) return rc;
+        DeviceScope dev(g);
+        if (int rc = dev.status()) return rc;
         const int n = (int)held + 1;  // keys 0 .. n-1 after appending this step's key
         o1::ExactIO io{};
         io.q = q;
@@ -283,8 +300,8 @@ int step_groups(o1_groups *g, int layer, const float *q, const float *k, const f
         io.v_dst = g->exact_v;
         err = o1::launch_exact(io, splits, (hipStream_t)stream);
     } else {
-        int rc = use_device(g);
-        if (rc) return rc;
+        DeviceScope dev(g);
+        if (int rc = dev.status()) return rc;
         o1::DecodeIO io{q, k, v, out, map};
         err = o1::launch_decode(g->st, io, (hipStream_t)stream);
     }
@@ -406,7 +423,7 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
 void o1_destroy_groups(o1_groups *g)
 {
     if (!g) return;
-    (void)use_device(g);
+    DeviceScope dev(g);
     free_state(g);
     delete g;
 }
@@ -519,7 +536,8 @@ int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, vo
     if (rc) return rc;
     if (!dst) return fail(O1_EINVAL, "o1_read_field: null destination");
     if (bytes != want) return fail(O1_EINVAL, "field %d holds %zu bytes, not %zu", field, want, bytes);
-    if ((rc = use_device(g))) return rc;
+    DeviceScope dev(g);
+    if ((rc = dev.status())) return rc;
     hipError_t err = hipMemcpyAsync(dst, field_info(g, field).ptr, bytes, hipMemcpyDefault,
                                     (hipStream_t)stream);
     if (err != hipSuccess) return fail(O1_EHIP, "hipMemcpyAsync failed: %s", hipGetErrorString(err));
@@ -534,7 +552,8 @@ int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, v
     if (rc) return rc;
     if (!src) return fail(O1_EINVAL, "o1_write_field: null source");
     if (bytes != want) return fail(O1_EINVAL, "field %d holds %zu bytes, not %zu", field, want, bytes);
-    if ((rc = use_device(g))) return rc;
+    DeviceScope dev(g);
+    if ((rc = dev.status())) return rc;
     hipError_t err = hipMemcpyAsync(field_info(g, field).ptr, src, bytes, hipMemcpyDefault,
                                     (hipStream_t)stream);
     if (err != hipSuccess) return fail(O1_EHIP, "hipMemcpyAsync failed: %s", hipGetErrorString(err));
