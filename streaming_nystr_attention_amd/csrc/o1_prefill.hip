@@ -12,7 +12,7 @@
 //                      MFMA, lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
 //                      G + lambda I in LDS (lambda x10 on a failed pivot, up to 12
 //                      attempts, then diag(1/mean diag)), M = (G + lambda I)^-1 A^T.
-//   far_mfma_kernel    grid G * hpk: the far field of keys sink .. T-w-1, i.e. the
+//   far_mfma_kernel    grid G * ceil(hpk / HB): the far field of keys sink .. T-w-1, i.e. the
 //                      state the page's sequential replay through far_insert
 //                      reaches, computed in 16-key tiles on f64 MFMA with an
 //                      online per-landmark max: m_max_i = max_j l_ij,
@@ -234,38 +234,102 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
 
 // ---- far field of the prompt on the matrix cores (f64 MFMA) ---------------
 //
-// One work-group per (group, head), one wave per block of 16 query landmarks.
-// For each tile of 16 far keys (staged in LDS):
-//   L   = Q~_blk K_tile^T * scale        16 x 16, d/4 MFMA 16x16x4 f64
+// One work-group per (group, block of HB heads): the far keys' K and V tiles are
+// loaded once and used by every head of the block, and the head blocks of one
+// group run on one XCD (work-group b goes to XCD b mod 8), so they share its L2.
+// One wave per 16-landmark row block of one head, its Q~ rows held in registers.
+// For each tile of 16 far keys (staged in LDS while the next one is in flight):
+//   L   = Q~_blk K_tile^T * scale        16 x 16, D/4 MFMA 16x16x4 f64
 //   online per-landmark max, P = e^{L - max}, Z^ += row sums of P
 //   T^ <- T^ * e^{max_old - max_new} + P V_tile   16 x dv, 4 * dv/16 MFMAs
+// The logit product runs over a permuted component order: at step ks, lane
+// (i, k) holds A[i][k] = Q~[i][k * D/4 + ks] and B[k][j] = K[j][k * D/4 + ks],
+// so each lane's Q~ operands are one contiguous run of D/4 components and the
+// sum over k and ks still covers every component once.
 // v_mfma_f64_16x16x4f64 operand layout (wave64): A[i][k] in lane i + 16 k,
 // B[k][j] in lane j + 16 k, and D[i][j] in lane j + 16 (i % 4), element i / 4.
 
-template <int D, int DV>
-__global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
+// (At least two waves per SIMD: otherwise a 4-wave work-group may take the
+// whole register file, and one work-group per CU leaves the MFMAs idle on loads.)
+template <int D, int DV, int MM, int HB>
+__global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevState s, PrefillIO io)
 {
-    constexpr int KS = D / 4;    // k-steps of the logit product
+    constexpr int NRB = MM / 16, NW = HB * NRB, NT = 64 * NW;
+    constexpr int KS = D / 4;    // k-steps of the logit product = components per lane
     constexpr int CB = DV / 16;  // 16-wide column blocks of T^
     constexpr int TK = 16;       // keys per tile
-    const int H = s.hpk, ci = blockIdx.x / H;
-    const size_t gh = (size_t)io.map.state(ci) * H + (blockIdx.x - ci * H);  // state head
-    const int m = s.m, tid = threadIdx.x, lane = tid & 63, rb = tid >> 6, nthr = blockDim.x;
-    const int S = s.sink, T = io.T, nf = T - S - s.w;
+    constexpr int K4 = TK * (D / 4), KV4 = K4 + TK * (DV / 4);  // float4 of a K tile, of K and V
+    constexpr int PT = (KV4 + NT - 1) / NT;                     // float4 per thread per tile
+    const int H = s.hpk, nhb = (H + HB - 1) / HB;
+    const int jb = blockIdx.x >> 3;
+    const int ci = (jb / nhb) * 8 + (blockIdx.x & 7), hb = jb - (jb / nhb) * nhb;
+    if (ci >= io.map.count) return;
+    const int g = io.map.state(ci);
+    const int m = s.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = hb * HB + wave / NRB, rb = wave % NRB;
+    const bool live = h < H && rb * 16 < m;  // waves past hpk or m hold no rows
+    const size_t gh = (size_t)g * H + min(h, H - 1);
+    const int S = s.sink, nf = io.T - S - s.w;
     const double sc = (double)s.scale;
     const double NEG_INF = -__builtin_inf();
+    const int li = lane & 15, lk = lane >> 4;
 
-    __shared__ float k_lds[TK][D + 1];
+    __shared__ float k_lds[TK][4][KS + 1];
     __shared__ float v_lds[TK][DV + 4];
-    __shared__ double p_lds[4][16][17];
+    __shared__ double p_lds[NW][16][17];
 
-    const int li = lane & 15, lk = lane >> 4;  // A/B fragment coordinates
-    // Q~ block of this wave in LDS (rows past m are zero)
-    __shared__ float q_lds[4][16][D + 1];
-    for (int t = lane; t < 16 * D; t += 64) {
-        const int ii = t / D, c = t - ii * D, i = rb * 16 + ii;
-        q_lds[rb][ii][c] = (i < m) ? s.q_tilde[(gh * m + i) * D + c] : 0.0f;
+    // Q~ fragment of this wave: row rb * 16 + li, components lk * KS .. lk * KS + KS - 1
+    float qa[KS];
+    {
+        const int row = rb * 16 + li;
+        const float4 *src =
+            reinterpret_cast<const float4 *>(s.q_tilde + (gh * m + min(row, m - 1)) * D + lk * KS);
+        const bool use = live && row < m;
+#pragma unroll
+        for (int c = 0; c < KS / 4; ++c) {
+            const float4 x = src[c];
+            qa[4 * c + 0] = use ? x.x : 0.0f;
+            qa[4 * c + 1] = use ? x.y : 0.0f;
+            qa[4 * c + 2] = use ? x.z : 0.0f;
+            qa[4 * c + 3] = use ? x.w : 0.0f;
+        }
     }
+
+    // K and V tiles: thread slot p covers float4 tid + p * NT of [K tile | V tile];
+    // key indices are clamped (dead keys get -inf logits and zero weights below)
+    const float *K = io.p.k_row(io.map, ci, S);
+    const float *V = io.p.v_row(io.map, ci, S);
+    const int64_t kpos = io.p.k_pos, vpos = io.p.v_pos;
+    float4 pre[PT];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int p = 0; p < PT; ++p) {
+            const int idx = min(tid + p * NT, KV4 - 1);
+            const bool isk = idx < K4;
+            const int e = isk ? idx : idx - K4, per = isk ? D / 4 : DV / 4;
+            const int key = min(j0 + e / per, nf - 1), c4 = e % per;
+            const float *row = isk ? K + (int64_t)key * kpos : V + (int64_t)key * vpos;
+            pre[p] = reinterpret_cast<const float4 *>(row)[c4];
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int p = 0; p < PT; ++p) {
+            const int idx = tid + p * NT;
+            if (idx < K4) {
+                const int key = idx / (D / 4), c = (idx % (D / 4)) * 4;  // component of .x
+                float *dst = &k_lds[key][c / KS][c % KS];
+                dst[0] = pre[p].x;
+                dst[1] = pre[p].y;
+                dst[2] = pre[p].z;
+                dst[3] = pre[p].w;
+            } else if (idx < KV4) {
+                const int e = idx - K4, key = e / (DV / 4), c4 = e % (DV / 4);
+                *reinterpret_cast<float4 *>(&v_lds[key][c4 * 4]) = pre[p];
+            }
+        }
+    };
+
     f64x4 tacc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) tacc[cb] = f64x4{0.0, 0.0, 0.0, 0.0};
@@ -276,75 +340,71 @@ __global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
         zs[r] = 0.0;
     }
 
-    const float *K = io.p.k_row(io.map, ci, S);  // far keys S .. T-w-1 in place
-    const float *V = io.p.v_row(io.map, ci, S);
-    const int64_t kpos = io.p.k_pos, vpos = io.p.v_pos;
+    fetch(0);
     for (int j0 = 0; j0 < nf; j0 += TK) {
         const int nt = min(TK, nf - j0);
-        for (int t = tid; t < TK * (D / 4); t += nthr) {
-            const int jj = t / (D / 4), c4 = t - jj * (D / 4);
-            float4 x = jj < nt ? reinterpret_cast<const float4 *>(K + (int64_t)(j0 + jj) * kpos)[c4]
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-            k_lds[jj][c4 * 4 + 0] = x.x;
-            k_lds[jj][c4 * 4 + 1] = x.y;
-            k_lds[jj][c4 * 4 + 2] = x.z;
-            k_lds[jj][c4 * 4 + 3] = x.w;
-        }
-        for (int t = tid; t < TK * (DV / 4); t += nthr) {
-            const int jj = t / (DV / 4), c4 = t - jj * (DV / 4);
-            float4 x = jj < nt ? reinterpret_cast<const float4 *>(V + (int64_t)(j0 + jj) * vpos)[c4]
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-            *reinterpret_cast<float4 *>(&v_lds[jj][c4 * 4]) = x;
-        }
+        stage();
         __syncthreads();
+        if (j0 + TK < nf) fetch(j0 + TK);  // the next tile is in flight during the MFMAs
 
         // logits of this landmark block against the tile
         f64x4 L = {0.0, 0.0, 0.0, 0.0}, L2 = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
+#pragma unroll 4
         for (int ks = 0; ks < KS; ks += 2) {
-            L = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q_lds[rb][li][ks * 4 + lk],
-                                                    (double)k_lds[li][ks * 4 + lk], L, 0, 0, 0);
-            L2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q_lds[rb][li][ks * 4 + 4 + lk],
-                                                     (double)k_lds[li][ks * 4 + 4 + lk], L2, 0, 0, 0);
+            // opaque copies: widen Q~ at its use instead of keeping KS doubles live
+            float q0 = qa[ks], q1 = qa[ks + 1];
+            asm volatile("" : "+v"(q0), "+v"(q1));
+            L = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q0, (double)k_lds[li][lk][ks], L, 0, 0, 0);
+            L2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q1, (double)k_lds[li][lk][ks + 1], L2, 0, 0, 0);
         }
         L += L2;
         // lane holds L[row lk + 4 r][key li]
-        const bool live = li < nt;
-        double p[4];
+        const bool kl = li < nt;
+        double p[4], f[4];
+        bool grew = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const double l = live ? L[r] * sc : NEG_INF;
+            const double l = kl ? L[r] * sc : NEG_INF;
             double t = l;
 #pragma unroll
             for (int off = 8; off > 0; off >>= 1) t = fmax(t, __shfl_xor(t, off, 64));
             const double nw = fmax(mx[r], t);
-            const double f = exp(mx[r] - nw);  // 0 on the first tile
+            f[r] = exp(mx[r] - nw);  // 0 on the first tile, exactly 1 when the max holds
+            grew |= f[r] != 1.0;
             mx[r] = nw;
-            p[r] = live ? exp(l - nw) : 0.0;
+            p[r] = kl ? exp(l - nw) : 0.0;
             double ps = p[r];
 #pragma unroll
             for (int off = 8; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 64);
-            zs[r] = zs[r] * f + ps;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) tacc[cb][r] *= f;
+            zs[r] = zs[r] * f[r] + ps;
         }
-        // P from the result layout to the A-operand layout through LDS
+        if (__any(grew)) {  // rescale only when some running max of the wave moved
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p_lds[rb][lk + 4 * r][li] = p[r];
-        __builtin_amdgcn_s_waitcnt(0);
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) tacc[cb][r] *= f[r];
+        }
+        // P from the result layout to the A-operand layout through this wave's LDS rows
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p_lds[wave][lk + 4 * r][li] = p[r];
         __builtin_amdgcn_wave_barrier();
         double pa[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) pa[kk] = p_lds[rb][li][kk * 4 + lk];
+        for (int kk = 0; kk < 4; ++kk) pa[kk] = p_lds[wave][li][kk * 4 + lk];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB; ++cb) {
+            float vb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) vb[kk] = v_lds[kk * 4 + lk][cb * 16 + li];
+            asm volatile("" : "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]));
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                tacc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(
-                    pa[kk], (double)v_lds[kk * 4 + lk][cb * 16 + li], tacc[cb], 0, 0, 0);
-        __syncthreads();
+                tacc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(pa[kk], (double)vb[kk], tacc[cb], 0, 0, 0);
+        }
+        __syncthreads();  // every wave is done with the tile before the next is staged
     }
 
+    if (!live) return;
     // store at the scale of the f32 running max kept in the state
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -360,6 +420,35 @@ __global__ __launch_bounds__(256) void far_mfma_kernel(DevState s, PrefillIO io)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) th[cb * 16 + li] = (float)(tacc[cb][r] * corr);
     }
+}
+
+template <int D, int DV, int MM>
+hipError_t launch_far(const DevState &s, const PrefillIO &io, hipStream_t stream)
+{
+    // heads per work-group: as many as keep it at 512 threads or fewer
+    constexpr int HB_MAX = 8 / (MM / 16);
+    const int hb = s.hpk < HB_MAX ? s.hpk : HB_MAX;
+    const long long nhb = (s.hpk + hb - 1) / hb;
+    const long long grid = 8LL * nhb * ((io.map.count + 7) / 8);
+    switch (hb) {
+    case 1: hipLaunchKernelGGL((far_mfma_kernel<D, DV, MM, 1>), dim3((unsigned)grid), dim3(64 * MM / 16), 0, stream, s, io); break;
+    case 2: hipLaunchKernelGGL((far_mfma_kernel<D, DV, MM, 2>), dim3((unsigned)grid), dim3(128 * MM / 16), 0, stream, s, io); break;
+    case 4:
+        if constexpr (HB_MAX >= 4) {
+            hipLaunchKernelGGL((far_mfma_kernel<D, DV, MM, 4>), dim3((unsigned)grid), dim3(256 * MM / 16), 0, stream, s, io);
+            break;
+        }
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int D, int DV>
+hipError_t launch_far_m(const DevState &s, const PrefillIO &io, hipStream_t stream)
+{
+    if (s.m <= 32) return launch_far<D, DV, 32>(s, io, stream);
+    return launch_far<D, DV, 64>(s, io, stream);
 }
 
 // Frozen M, [count][hpk][m][m] in call order, into the mapped groups' state.
@@ -402,14 +491,9 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
         hipLaunchKernelGGL(gram_pinv_kernel, dim3(n * s.hpk), dim3(kThreads), lds, stream, s, io, kRidgeRel);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const int nrb = (s.m + 15) / 16;
-    if (s.d == 128 && s.dv == 128)
-        hipLaunchKernelGGL((far_mfma_kernel<128, 128>), dim3(n * s.hpk), dim3(64 * nrb), 0, stream, s, io);
-    else if (s.d == 64 && s.dv == 64)
-        hipLaunchKernelGGL((far_mfma_kernel<64, 64>), dim3(n * s.hpk), dim3(64 * nrb), 0, stream, s, io);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (s.d == 128 && s.dv == 128) return launch_far_m<128, 128>(s, io, stream);
+    if (s.d == 64 && s.dv == 64) return launch_far_m<64, 64>(s, io, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace o1
