@@ -52,20 +52,50 @@ __global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, Prefill
         fz = io.fz_qt ? io.fz_qt + ((size_t)ci * H + (src - 1)) * m * d : nullptr;
     }
     double *dst64 = io.lm64 + ((size_t)ci * (1 + H) + src) * m * d;
-    for (int t = threadIdx.x; t < m * d; t += kThreads) {
+    // one thread per (segment, 4 components): the segment's rows are summed in
+    // row order, four rows' loads in flight at a time
+    const int d4 = d / 4;
+    for (int t = threadIdx.x; t < m * d4; t += kThreads) {
+        const int a = t / d4, c = (t - a * d4) * 4;
         if (fz) {
-            const float v = fz[t];
-            dst32[t] = v;
-            dst64[t] = (double)v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = fz[a * d + c + e];
+                dst32[a * d + c + e] = v;
+                dst64[a * d + c + e] = (double)v;
+            }
             continue;
         }
-        const int a = t / d, c = t - a * d;
         const long lo = (long)a * T / m, hi = (long)(a + 1) * T / m;
-        double acc = 0.0;
-        for (long j = lo; j < hi; ++j) acc += (double)x[(int64_t)j * pos + c];
-        const double mean = acc * (1.0 / (double)(hi - lo));
-        dst64[t] = mean;
-        dst32[t] = (float)mean;
+        double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+        const float *col = x + c;
+        long j = lo;
+        for (; j + 4 <= hi; j += 4) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4 *>(col + (int64_t)(j + u) * pos);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                s0 += (double)v[u].x;
+                s1 += (double)v[u].y;
+                s2 += (double)v[u].z;
+                s3 += (double)v[u].w;
+            }
+        }
+        for (; j < hi; ++j) {
+            const float4 v = *reinterpret_cast<const float4 *>(col + (int64_t)j * pos);
+            s0 += (double)v.x;
+            s1 += (double)v.y;
+            s2 += (double)v.z;
+            s3 += (double)v.w;
+        }
+        const double inv = 1.0 / (double)(hi - lo);
+        const double mean[4] = {s0 * inv, s1 * inv, s2 * inv, s3 * inv};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dst64[a * d + c + e] = mean[e];
+            dst32[a * d + c + e] = (float)mean[e];
+        }
     }
 }
 
@@ -172,24 +202,31 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
             L[i * ld + j] = Gm[i * ld + j] + (i == j ? lambda : 0.0);
         }
         __syncthreads();
-        // Cholesky, one column at a time: pivot, then the column below it.
-        for (int j = 0; j < m; ++j) {
-            if (tid == 0) {
-                double p = L[j * ld + j];
-                for (int k = 0; k < j; ++k) p -= L[j * ld + k] * L[j * ld + k];
-                const int bad = !(p > 0.0) || !isfinite(p);
-                if (!bad) L[j * ld + j] = sqrt(p);
-                fail_s = bad;
+        if (wave == 0) {
+            // Left-looking Cholesky in one wave, lane i owning row i: for column
+            // j every lane i >= j forms s_i = L[i][j] - sum_{k<j} L[i][k] L[j][k];
+            // lane j's s is the pivot (a failed pivot is <= 0 or not finite).
+            int bad = 0;
+            for (int j = 0; j < m; ++j) {
+                double sv = 0.0;
+                if (lane >= j && lane < m) {
+                    double v = L[lane * ld + j];
+                    for (int k = 0; k < j; ++k) v -= L[lane * ld + k] * L[j * ld + k];
+                    sv = v;
+                }
+                const double p = lane_value(sv, j);
+                if (!(p > 0.0) || !isfinite(p)) {
+                    bad = 1;
+                    break;
+                }
+                const double dj = sqrt(p);
+                if (lane == j) L[j * ld + j] = dj;
+                else if (lane > j && lane < m) L[lane * ld + j] = sv / dj;
+                __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
             }
-            __syncthreads();
-            if (fail_s) break;
-            for (int i = j + 1 + tid; i < m; i += kThreads) {
-                double v = L[i * ld + j];
-                for (int k = 0; k < j; ++k) v -= L[i * ld + k] * L[j * ld + k];
-                L[i * ld + j] = v / L[j * ld + j];
-            }
-            __syncthreads();
+            if (lane == 0) fail_s = bad;
         }
+        __syncthreads();
         const int failed = fail_s;
         __syncthreads();
         if (!failed) {
