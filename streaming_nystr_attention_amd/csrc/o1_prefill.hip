@@ -161,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
         const double *qrow = qt + (size_t)(qi < m ? qi : 0) * d;
         const double *krow = kt + (size_t)(kj < m ? kj : 0) * d;
         f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
         for (int ks = 0; ks < d / 4; ks += 2) {
             acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + lk] : 0.0,
                                                       kj < m ? krow[ks * 4 + lk] : 0.0, acc, 0, 0, 0);
@@ -211,6 +212,9 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
                 double sv = 0.0;
                 if (lane >= j && lane < m) {
                     double v = L[lane * ld + j];
+                    // unrolled so eight steps' LDS reads are in flight; the
+                    // subtractions keep their order
+#pragma unroll 8
                     for (int k = 0; k < j; ++k) v -= L[lane * ld + k] * L[j * ld + k];
                     sv = v;
                 }
@@ -243,11 +247,13 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
             double *x = A + (size_t)b * ld;
             for (int i = 0; i < m; ++i) {
                 double v = x[i];
+#pragma unroll 8
                 for (int k = 0; k < i; ++k) v -= L[i * ld + k] * x[k];
                 x[i] = v / L[i * ld + i];
             }
             for (int i = m - 1; i >= 0; --i) {
                 double v = x[i];
+#pragma unroll 8
                 for (int k = i + 1; k < m; ++k) v -= L[k * ld + i] * x[k];
                 x[i] = v / L[i * ld + i];
             }
