@@ -45,19 +45,25 @@ DECODE_SRC = [os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", f)
 # HBM bytes per decode launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by
 # a 1 GiB copy in the same process), keyed by (workload, sha256 prefix of the decode
 # kernel's sources).
-# A changed kernel source has no entry, and the roofline's traffic is then reported as null.
+# A changed kernel (comments aside) has no entry, and the roofline's traffic is then null.
 MEASURED_TRAFFIC = {
-    ("qwen3_stack_b64", "bc7b04061cda5bec"): 3788477009,
+    ("qwen3_stack_b64", "dc0d67c452e070d5"): 3788477009,
 }
 
 
 def decode_source_sha() -> str:
+    """Hash of the decode kernel's sources with comments and whitespace removed,
+    so the key changes with the code, not with its comments."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for path in DECODE_SRC:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

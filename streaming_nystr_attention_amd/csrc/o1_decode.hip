@@ -6,9 +6,11 @@
 // work-group's time is mostly memory latency.  The kernel is organised to keep
 // few dependent round trips per group and many bytes in flight:
 //
-//   0. prologue, one round of loads into LDS: the ring head e = win_head, the
+//   0. prologue, small loads staged into LDS: the ring head e = win_head, the
 //      queries, the new k/v, the evicted ring row (row sink+e), each head's
 //      running max and Z^, and (small shapes) each head's mixing matrix M.
+//      (Each staging loop waits for its own loads; issuing them all first
+//      measured slower on large launches, whose work-groups overlap anyway.)
 //      Then row sink+e is overwritten by the new k/v (advance); nothing reads
 //      that row from global memory afterwards.
 //   1. row-dot pass, f64 accumulation, each row split over LPR lanes and UNR
@@ -28,7 +30,7 @@
 //      weights p = e^{lg - shift} and the joint denominator.
 //   3. column pass, one float4 column chunk per lane: T^ <- T^ r + e v_e written
 //      back and contracted with gain in the same pass; V rows contracted with p.
-//   4. reduce the row lanes (shuffles within a wave, LDS across waves), one
+//   4. reduce the row lanes (lane swaps within a wave, LDS across waves), one
 //      division per output, counters.
 // HBM traffic: each group's state read once and its modified part (one ring
 // row, T^, Z^, m_max, counters) written once.
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
     float4 *nk = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * R * C::CH;
     float4 *nv = reinterpret_cast<float4 *>(s.near_v) + (size_t)g * R * C::VCH;
 
-    // ---- 0. prologue: one round of small loads into LDS --------------------
+    // ---- 0. prologue: small loads staged into LDS ---------------------------
     {
         const float4 *qg = reinterpret_cast<const float4 *>(io.q) + (size_t)ci * HPK * C::CH;
         for (int i = tid; i < HPK * C::CH; i += NT) (&q_s[0][0])[i] = qg[i];
