@@ -14,8 +14,7 @@ import oracle as O
 import streaming_nystr_attention_amd as P
 from streaming_nystr_attention_amd import workloads as W
 
-from parity_util import (DECODE_TOL, DecodeRun, cpu, frozen_tensors_with_oracle, oracle_decode,
-                         oracle_prefill, row_errors, say)
+from parity_util import decode_parity
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,68 +27,6 @@ def gpu_ready():
     P.lib()  # raises when the HIP library is missing
     yield
     torch.cuda.synchronize()
-
-
-def stack_frozen(orc_groups):
-    sts = [g.state() for g in orc_groups]
-    kt = torch.from_numpy(np.stack([s["k_tilde"] for s in sts])).to(DEV)
-    qt = torch.from_numpy(np.stack([s["q_tilde"] for s in sts])).to(DEV)
-    mu = torch.from_numpy(np.stack([s["mu"] for s in sts])).to(DEV)
-    return kt, qt, mu
-
-
-def decode_parity(wl, sample=None, steps=None, rect=O.RECT_AGGREGATE, frozen_override=None):
-    steps = wl.steps if steps is None else steps
-    G = wl.groups
-    sample = list(range(G)) if sample is None else sample
-    say(f"[decode] {wl.name}: G={G} hpk={wl.hpk} d={wl.d} m={wl.m} w={wl.w} sink={wl.sink} "
-        f"T={wl.T} steps={steps} rect={rect} sampled={len(sample)}")
-    q, k, v = W.prompt(wl, DEV)
-    si = torch.tensor(sample, device=DEV)
-    qh, kh, vh = cpu(q[si]), cpu(k[si]), cpu(v[si])
-    fz_orc = None
-    if frozen_override is not None:
-        fz_orc = [O.Frozen(mu=frozen_override) for _ in sample]
-    orc = oracle_prefill(wl, qh, kh, vh, frozen=fz_orc, rect=rect)
-    cfg = wl.config
-    cfg = P.Config(**{**cfg.__dict__, "rect": rect})
-    grp = P.O1Groups(cfg)
-    if len(sample) == G:
-        frozen = stack_frozen(orc)
-    else:
-        grp.prefill(q, k, v)
-        frozen = frozen_tensors_with_oracle(grp, wl, sample, orc)
-    grp.prefill(q, k, v, frozen=frozen)
-    del q, k, v, frozen
-    run = DecodeRun(wl, sample, steps)
-    qs, ks, vs, gout = run.run(grp)
-    out, alt, amb = oracle_decode(orc, qs, ks, vs)
-    err = row_errors(gout, out, alt, amb)
-    say(f"  rows={err.size} max_err={err.max():.3e} median={np.median(err):.3e} "
-        f"ambiguous={int(amb.sum())}")
-
-    # counters of every group, bit-exact
-    E = wl.T - wl.sink - wl.w + steps
-    far_len = grp.read(P.FIELD_FAR_LEN).numpy()
-    win_head = grp.read(P.FIELD_WIN_HEAD).numpy()
-    assert (far_len == E).all(), "far_len must equal the eviction count for every head"
-    assert (win_head == E % wl.w).all()
-    for i in range(len(sample)):
-        assert orc[i].far_len(0) == E and orc[i].win_head == E % wl.w
-
-    # ring and sink rows of the sampled groups, bit-exact
-    R = wl.sink + wl.w
-    nk = grp.read(P.FIELD_NEAR_K).view(G, R, wl.d)[sample].numpy()
-    nv = grp.read(P.FIELD_NEAR_V).view(G, R, wl.dv)[sample].numpy()
-    for i in range(len(sample)):
-        st = orc[i].state()
-        np.testing.assert_array_equal(nk[i, : wl.sink], st["sink_k"])
-        np.testing.assert_array_equal(nv[i, : wl.sink], st["sink_v"])
-        np.testing.assert_array_equal(nk[i, wl.sink:], st["win_k"])
-        np.testing.assert_array_equal(nv[i, wl.sink:], st["win_v"])
-    grp.close()
-    assert err.max() <= DECODE_TOL, f"max row error {err.max():.3e}"
-    return err
 
 
 def test_decode_single_head():

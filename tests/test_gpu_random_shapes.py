@@ -1,0 +1,56 @@
+"""GPU parity at seeded random shapes: each case draws the query heads per group,
+the head width, the landmark budget, window, sinks, prompt length, rectifier,
+input scale and group counts within the compiled limits (d = dv in {64, 128},
+hpk in {1, 2, 4, 8}, m <= 64, sink + w <= 1024 with hpk * (sink + w) * 8 <= 32 KB),
+then checks the prefill freeze and the decode steps against the oracle exactly
+as the fixed-shape tests do."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import streaming_nystr_attention_amd as P
+from streaming_nystr_attention_amd import workloads as W
+
+from parity_util import decode_parity, prefill_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    P.lib()
+    yield
+
+
+def draw(case: int):
+    r = np.random.default_rng(7000 + case)
+    while True:
+        hpk = int(r.choice([1, 2, 4, 8]))
+        d = int(r.choice([64, 128]))
+        m = int(r.integers(4, 65))
+        sink = int(r.integers(0, 17))
+        w = int(r.integers(1, 300))
+        if hpk * (sink + w) * 8 > 32 * 1024 or sink + w > 1024:
+            continue
+        T = int(r.integers(w + sink + 9, w + sink + 400))  # skeleton mode: T > w + sink + 8
+        n_seq, n_layer, n_kv = (int(x) for x in r.integers(1, 4, size=3))
+        std = float(r.choice([1.0, 2.0, 3.0]))
+        rect = int(r.integers(0, 2))
+        steps = int(r.integers(5, 40))
+        wl = W.Workload(f"rand{case}", n_seq, n_layer, n_kv, hpk, d, d, m, w, sink, T=T, steps=steps,
+                        q_std=std, k_std=std, seed=900 + case)
+        return wl, (O.RECT_AGGREGATE, O.RECT_FM)[rect]
+
+
+CASES = [draw(i) for i in range(10)]
+
+
+@pytest.mark.parametrize("wl,rect", CASES,
+                         ids=[f"{w.name}-h{w.hpk}-d{w.d}-m{w.m}-w{w.w}-s{w.sink}-T{w.T}-r{r}"
+                              for w, r in CASES])
+def test_random_shape_prefill_and_decode(wl, rect):
+    prefill_parity(wl)
+    decode_parity(wl, rect=rect)
