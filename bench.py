@@ -325,7 +325,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; every group is independent, so more "
+        print("bench.py: runs on one GPU only; every group is independent, so more "
               "GPUs would each run the same kernel on their own share of the groups. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

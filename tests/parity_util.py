@@ -1,7 +1,7 @@
 """Helpers of the GPU parity tests: run the HIP path and the CPU oracle on the
 same seeded inputs and compare them row by row.
 
-Row error (the benchmark spec tolerance): max_c |o_gpu[c] - o_orc[c]| / ||o_orc||_2 <= 1e-4
+Row error (the decode tolerance): max_c |o_gpu[c] - o_orc[c]| / ||o_orc||_2 <= 1e-4
 for every (group, head, step) row.  Rows where the aggregate rectifier's
 decision sits within rounding of its threshold (|far_den| < 1e-5 * sum|gain Z^|)
 may take either branch: there the GPU row must match the oracle's output under

@@ -1,7 +1,7 @@
 """GPU parity of the decode step (o1_step) against the CPU oracle.
 
 The GPU prefill runs with the oracle's frozen K~, Q~ and M (the `frozen` hook of
-o1_prefill), so the decode outputs are compared at the benchmark spec tolerance
+o1_prefill), so the decode outputs are compared at the decode tolerance
 (1e-4 of the row norm) without the ill-conditioned pinv's elementwise spread.
 Counters (far_len, win_head) are compared bit-exactly for every group, ring and
 sink rows bit-exactly for the sampled groups.
