@@ -161,12 +161,18 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
         const double *qrow = qt + (size_t)(qi < m ? qi : 0) * d;
         const double *krow = kt + (size_t)(kj < m ? kj : 0) * d;
         f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
-        for (int ks = 0; ks < d / 4; ks += 2) {
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + lk] : 0.0,
-                                                      kj < m ? krow[ks * 4 + lk] : 0.0, acc, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + 4 + lk] : 0.0,
-                                                       kj < m ? krow[ks * 4 + 4 + lk] : 0.0, acc2, 0, 0, 0);
+        // d / 4 is a multiple of 16: a fixed-count inner loop unrolls (MFMA is
+        // convergent, so a runtime count leaves the loop rolled), issuing the
+        // loads of sixteen steps together
+        for (int k0 = 0; k0 < d / 4; k0 += 16) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const int ks = k0 + e;
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + lk] : 0.0,
+                                                          kj < m ? krow[ks * 4 + lk] : 0.0, acc, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + 4 + lk] : 0.0,
+                                                           kj < m ? krow[ks * 4 + 4 + lk] : 0.0, acc2, 0, 0, 0);
+            }
         }
         acc += acc2;
 #pragma unroll
