@@ -68,6 +68,11 @@ struct DecodeShape {
     static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
     static constexpr int MB = NT == 256 ? 16 : 32;                     // M rows in flight (unstaged M)
     static constexpr bool NTL = NT == 256;                             // streaming accesses (large grids)
+    // Few groups per CU and registers to spare (one work-group per CU): the
+    // row pass runs as one pipelined stream over every row it reads.
+    static constexpr bool PIPE = NT == 512 && HPK * D >= 512;
+    // at least three waves per SIMD on large grids (at most 168 VGPRs)
+    static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
     static constexpr int RED_CAP = 16384 / (NW * DV * 8);              // heads per LDS round
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
@@ -78,7 +83,7 @@ struct DecodeShape {
 };
 
 template <int D, int DV, int HPK, int MM, int NT>
-__global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
+__global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) void decode_kernel(DevState s, DecodeIO io)
 {
     using C = DecodeShape<D, DV, HPK, MM, NT>;
     const int ci = blockIdx.x;            // call index: inputs and outputs
@@ -151,62 +156,150 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
         const bool writer = (sub % HSTRIDE) == 0;
         const float4 *kt = reinterpret_cast<const float4 *>(s.k_tilde) + (size_t)g * m * C::CH;
         const int NA = R + m;  // near rows, then landmark rows
-        for (int base = wave * C::RPW; base < NA; base += C::UNR * C::RPB) {
-            float4 x[C::UNR][C::CPL];
+        if constexpr (C::PIPE) {
+            const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
+            const int NQ = HPK * m;
+            // One row space, aligned so that a block row never mixes kinds:
+            // [0, NA) key rows, [NA, Q0) padding, [Q0, Q0 + NQ) query-landmark
+            // rows (far-insert logits against the evicted key).  Batch b + 1
+            // is in flight while batch b is reduced.
+            const int Q0 = (NA + C::RPB - 1) / C::RPB * C::RPB;
+            const int NTOT = Q0 + NQ;
+            constexpr int BR = C::UNR * C::RPB;  // rows per batch
+            const int NB = (NTOT + BR - 1) / BR;
+            const int r0 = wave * C::RPW + rsub;
+            // this lane's columns of every query and of the evicted key, in f64
+            // registers for the whole pass (one work-group per CU leaves room)
+            double qd[HPK][C::CPL][4], kd[C::CPL][4];
 #pragma unroll
-            for (int u = 0; u < C::UNR; ++u) {
-                const int r = min(base + u * C::RPB + rsub, NA - 1);
-                const float4 *row = (r < R) ? nk + (size_t)r * C::CH : kt + (size_t)(r - R) * C::CH;
-#pragma unroll
-                for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
-            }
-#pragma unroll
-            for (int u = 0; u < C::UNR; ++u) {
-                const int r = base + u * C::RPB + rsub;
-                if (r == slot_row) {  // the ring slot already holds the new key
-#pragma unroll
-                    for (int k = 0; k < C::CPL; ++k) x[u][k] = kn_s[sub + C::LPR * k];
-                }
-                double part[HPK];
+            for (int k = 0; k < C::CPL; ++k) {
 #pragma unroll
                 for (int h = 0; h < HPK; ++h) {
-                    // keep q in LDS: re-read per row instead of pinning it in registers
-                    asm volatile("" ::: "memory");
+                    const float4 t = q_s[h][sub + C::LPR * k];
+                    qd[h][k][0] = t.x, qd[h][k][1] = t.y, qd[h][k][2] = t.z, qd[h][k][3] = t.w;
+                }
+                const float4 t = ke_s[sub + C::LPR * k];
+                kd[k][0] = t.x, kd[k][1] = t.y, kd[k][2] = t.z, kd[k][3] = t.w;
+            }
+            auto dotd = [](const double (&a)[4], const float4 x) {
+                double s = a[0] * (double)x.x;
+                s = fma(a[1], (double)x.y, s);
+                s = fma(a[2], (double)x.z, s);
+                s = fma(a[3], (double)x.w, s);
+                return s;
+            };
+            auto load = [&](float4 (&x)[C::UNR][C::CPL], int b) {
+#pragma unroll
+                for (int u = 0; u < C::UNR; ++u) {
+                    const int r = min(b * BR + u * C::RPB + r0, NTOT - 1);
+                    const float4 *row = r < R    ? nk + (size_t)r * C::CH
+                                        : r < Q0 ? kt + (size_t)(min(r, NA - 1) - R) * C::CH
+                                                 : qt + (size_t)(r - Q0) * C::CH;
+#pragma unroll
+                    for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
+                }
+            };
+            auto reduce = [&](float4 (&x)[C::UNR][C::CPL], int b) {
+#pragma unroll
+                for (int u = 0; u < C::UNR; ++u) {
+                    const int rb = b * BR + u * C::RPB;  // first row of the block row (wave-uniform)
+                    if (rb < Q0) {
+                        const int r = rb + r0;
+                        if (r == slot_row) {  // the ring slot already holds the new key
+#pragma unroll
+                            for (int k = 0; k < C::CPL; ++k) x[u][k] = kn_s[sub + C::LPR * k];
+                        }
+                        double part[HPK];
+#pragma unroll
+                        for (int h = 0; h < HPK; ++h) {
+                            double acc = 0.0;
+#pragma unroll
+                            for (int k = 0; k < C::CPL; ++k) acc += dotd(qd[h][k], x[u][k]);
+                            part[h] = acc;
+                        }
+                        const double tot = head_reduce<C::LPR, HPK>(part, lane) * scale;
+                        if (writer) {
+                            if (r < R) lg_s[my_head * R + r] = tot;
+                            else if (r < NA) land_s[my_head][r - R] = tot;
+                        }
+                    } else if (rb < NTOT) {
+                        double acc = 0.0;
+#pragma unroll
+                        for (int k = 0; k < C::CPL; ++k) acc += dotd(kd[k], x[u][k]);
+                        acc = group_sum<C::LPR>(acc);
+                        const int rq = rb + r0 - Q0;
+                        if (sub == 0 && rq < NQ) lf_s[rq / m][rq % m] = acc * scale;
+                    }
+                }
+            };
+            float4 xa[C::UNR][C::CPL], xb[C::UNR][C::CPL];
+            load(xa, 0);
+            for (int b = 0; b < NB; b += 2) {
+                if (b + 1 < NB) load(xb, b + 1);
+                reduce(xa, b);
+                if (b + 1 < NB) {
+                    if (b + 2 < NB) load(xa, b + 2);
+                    reduce(xb, b + 1);
+                }
+            }
+        } else {
+            for (int base = wave * C::RPW; base < NA; base += C::UNR * C::RPB) {
+                float4 x[C::UNR][C::CPL];
+#pragma unroll
+                for (int u = 0; u < C::UNR; ++u) {
+                    const int r = min(base + u * C::RPB + rsub, NA - 1);
+                    const float4 *row = (r < R) ? nk + (size_t)r * C::CH : kt + (size_t)(r - R) * C::CH;
+#pragma unroll
+                    for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
+                }
+#pragma unroll
+                for (int u = 0; u < C::UNR; ++u) {
+                    const int r = base + u * C::RPB + rsub;
+                    if (r == slot_row) {  // the ring slot already holds the new key
+#pragma unroll
+                        for (int k = 0; k < C::CPL; ++k) x[u][k] = kn_s[sub + C::LPR * k];
+                    }
+                    double part[HPK];
+#pragma unroll
+                    for (int h = 0; h < HPK; ++h) {
+                        // keep q in LDS: re-read per row instead of pinning it in registers
+                        asm volatile("" ::: "memory");
+                        double acc = 0.0;
+#pragma unroll
+                        for (int k = 0; k < C::CPL; ++k) acc += dot4(q_s[h][sub + C::LPR * k], x[u][k]);
+                        part[h] = acc;
+                    }
+                    const double tot = head_reduce<C::LPR, HPK>(part, lane) * scale;
+                    if (writer) {
+                        if (r < R) lg_s[my_head * R + r] = tot;
+                        else if (r < NA) land_s[my_head][r - R] = tot;
+                    }
+                }
+            }
+
+            // far-insert logits of the evicted key against every query landmark
+            float4 kr[C::CPL];
+#pragma unroll
+            for (int k = 0; k < C::CPL; ++k) kr[k] = ke_s[sub + C::LPR * k];
+            const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
+            const int NQ = HPK * m;
+            for (int base = wave * C::RPW; base < NQ; base += C::UNR * C::RPB) {
+                float4 x[C::UNR][C::CPL];
+#pragma unroll
+                for (int u = 0; u < C::UNR; ++u) {
+                    const int r = min(base + u * C::RPB + rsub, NQ - 1);
+#pragma unroll
+                    for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(qt + (size_t)r * C::CH + sub + C::LPR * k);
+                }
+#pragma unroll
+                for (int u = 0; u < C::UNR; ++u) {
+                    const int r = base + u * C::RPB + rsub;
                     double acc = 0.0;
 #pragma unroll
-                    for (int k = 0; k < C::CPL; ++k) acc += dot4(q_s[h][sub + C::LPR * k], x[u][k]);
-                    part[h] = acc;
+                    for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kr[k]);
+                    acc = group_sum<C::LPR>(acc);
+                    if (sub == 0 && r < NQ) lf_s[r / m][r % m] = acc * scale;
                 }
-                const double tot = head_reduce<C::LPR, HPK>(part, lane) * scale;
-                if (writer) {
-                    if (r < R) lg_s[my_head * R + r] = tot;
-                    else if (r < NA) land_s[my_head][r - R] = tot;
-                }
-            }
-        }
-
-        // far-insert logits of the evicted key against every query landmark
-        float4 kr[C::CPL];
-#pragma unroll
-        for (int k = 0; k < C::CPL; ++k) kr[k] = ke_s[sub + C::LPR * k];
-        const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
-        const int NQ = HPK * m;
-        for (int base = wave * C::RPW; base < NQ; base += C::UNR * C::RPB) {
-            float4 x[C::UNR][C::CPL];
-#pragma unroll
-            for (int u = 0; u < C::UNR; ++u) {
-                const int r = min(base + u * C::RPB + rsub, NQ - 1);
-#pragma unroll
-                for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(qt + (size_t)r * C::CH + sub + C::LPR * k);
-            }
-#pragma unroll
-            for (int u = 0; u < C::UNR; ++u) {
-                const int r = base + u * C::RPB + rsub;
-                double acc = 0.0;
-#pragma unroll
-                for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kr[k]);
-                acc = group_sum<C::LPR>(acc, lane);
-                if (sub == 0 && r < NQ) lf_s[r / m][r % m] = acc * scale;
             }
         }
 
@@ -233,11 +326,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
     for (int h = wave; h < HPK; h += C::NW) {
         double c = NEG_INF;
         for (int r = lane; r < R; r += 64) c = fmax(c, lg_s[h * R + r]);
-        c = wave_max(c, lane);
+        c = wave_max(c);
 
         const bool act = lane < m;
         const double sa = act ? land_s[h][lane] : NEG_INF;
-        const double f = wave_max(sa, lane);
+        const double f = wave_max(sa);
         const double fh = act ? exp(sa - f) : 0.0;
 
         // NystromHead::far_insert for landmark i = lane: strict ">" growth of
@@ -293,9 +386,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
         }
         if (s.rect == 1) u = fmax(u, 0.0);  // O1Rect::Fm
 
-        const double call = fmax(c, wave_max(act ? f + mn : NEG_INF, lane));
+        const double call = fmax(c, wave_max(act ? f + mn : NEG_INF));
         const double gain = act ? u * exp(f + mn - call) : 0.0;
-        const double far_den = wave_sum(gain * zn, lane);
+        const double far_den = wave_sum(gain * zn);
         const bool keep = far_den >= 0.0;  // aggregate rectifier (0 keeps)
         if (act) gain_s[h][lane] = keep ? gain : 0.0;
         const double shift = keep ? call : c;  // dropped far field: near-only shift
@@ -306,7 +399,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
             lg_s[h * R + r] = p;
             acc += p;
         }
-        acc = wave_sum(acc, lane);
+        acc = wave_sum(acc);
         if (lane == 0) den_s[h] = (keep ? far_den : 0.0) + acc;
     }
     __syncthreads();
@@ -383,7 +476,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DevState s, DecodeIO io)
 #pragma unroll
     for (int h = 0; h < HPK; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCH>(acc[h][c], lane);
+        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCH>(acc[h][c]);
     float4 *outp = reinterpret_cast<float4 *>(io.out) + (size_t)ci * HPK * C::VCH;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {

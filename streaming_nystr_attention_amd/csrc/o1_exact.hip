@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
             if (h >= HPK) break;
             double cm = NEG_INF;
             for (int r = lane; r < nr; r += 64) cm = fmax(cm, lg_s[h][r]);
-            cm = wave_max(cm, lane);
+            cm = wave_max(cm);
             const double nm = fmax(run_max[j], cm);
             const double f = exp(run_max[j] - nm);  // 0 on the first chunk
             double ps = 0.0;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
                 lg_s[h][r] = p;
                 ps += p;
             }
-            ps = wave_sum(ps, lane);
+            ps = wave_sum(ps);
             run_sum[j] = run_sum[j] * f + ps;
             run_max[j] = nm;
             if (lane == 0) fac_s[h] = f;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
 #pragma unroll
     for (int h = 0; h < HPK; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCH>(acc[h][c], lane);
+        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCH>(acc[h][c]);
     const bool final_out = gridDim.y == 1;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {

@@ -109,13 +109,14 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
 
 // ---- wavefront helpers (wave64) ------------------------------------------
 //
-// Cross-lane exchanges of f64 values on the vector ALU (no LDS crossbar): the
-// value of a partner lane whose lane bit `OFF` is flipped.  Within 16-lane rows
-// the partners come from DPP (lane ^ 1 and lane ^ 2 by quad permutes, 7 - i in
-// each 8-lane half row and 15 - i in each row by the mirrors); across rows and
-// wave halves from v_permlane16_swap / v_permlane32_swap (lane ^ 16, lane ^ 32).
-// A reduction that pairs every lane with one lane of the other half at each
-// level sums every lane exactly once, whichever partner of that half it is.
+// Cross-lane exchanges of f64 values on the vector ALU (no LDS crossbar).
+// Within 16-lane rows a partner lane whose lane bit OFF is flipped comes from
+// DPP (lane ^ 1 and lane ^ 2 by quad permutes, 7 - i in each 8-lane half row
+// and 15 - i in each row by the mirrors).  Across rows and wave halves
+// (lane ^ 16, lane ^ 32) v_permlane16_swap / v_permlane32_swap exchange two
+// registers at once.  A reduction that pairs every lane with one lane of the
+// other half at each level sums every lane exactly once, whichever partner of
+// that half it is.
 namespace lanes {
 
 __device__ __forceinline__ unsigned lo32(double x) { return (unsigned)__double_as_longlong(x); }
@@ -135,65 +136,91 @@ __device__ __forceinline__ double dpp(double x)
 }  // namespace lanes
 
 template <int OFF>
-__device__ __forceinline__ double partner(double x, int lane)
+__device__ __forceinline__ double partner(double x)
 {
-    static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "lane bit");
+    static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8, "lane bit within a row");
     if constexpr (OFF == 1) {
         return lanes::dpp<0xB1>(x);   // quad_perm [1,0,3,2]
     } else if constexpr (OFF == 2) {
         return lanes::dpp<0x4E>(x);   // quad_perm [2,3,0,1]
     } else if constexpr (OFF == 4) {
         return lanes::dpp<0x141>(x);  // row_half_mirror: 7 - i within 8 lanes
-    } else if constexpr (OFF == 8) {
-        return lanes::dpp<0x140>(x);  // row_mirror: 15 - i within 16 lanes
-    } else if constexpr (OFF == 16) {
-        // swap odd rows of the first operand with even rows of the second
-        const auto a = __builtin_amdgcn_permlane16_swap(lanes::lo32(x), lanes::lo32(x), false, false);
-        const auto b = __builtin_amdgcn_permlane16_swap(lanes::hi32(x), lanes::hi32(x), false, false);
-        return (lane & 16) ? lanes::join(a[0], b[0]) : lanes::join(a[1], b[1]);
     } else {
-        // swap the upper half of the first operand with the lower half of the second
-        const auto a = __builtin_amdgcn_permlane32_swap(lanes::lo32(x), lanes::lo32(x), false, false);
-        const auto b = __builtin_amdgcn_permlane32_swap(lanes::hi32(x), lanes::hi32(x), false, false);
-        return (lane & 32) ? lanes::join(a[0], b[0]) : lanes::join(a[1], b[1]);
+        return lanes::dpp<0x140>(x);  // row_mirror: 15 - i within 16 lanes
+    }
+}
+
+// Halving exchange across 16-lane rows (OFF = 16) or wave halves (OFF = 32):
+// lanes with lane bit OFF clear return a + a(lane ^ OFF), lanes with it set
+// b + b(lane ^ OFF).  One swap of (a, b) leaves, in every lane, its own kept
+// value in one output and its partner's in the other, so no select is needed
+// (the sum is exact in either order).
+template <int OFF>
+__device__ __forceinline__ double swap_sum(double a, double b)
+{
+    static_assert(OFF == 16 || OFF == 32, "whole-row exchanges only");
+    if constexpr (OFF == 16) {
+        const auto lo = __builtin_amdgcn_permlane16_swap(lanes::lo32(a), lanes::lo32(b), false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(lanes::hi32(a), lanes::hi32(b), false, false);
+        return lanes::join(lo[0], hi[0]) + lanes::join(lo[1], hi[1]);
+    } else {
+        const auto lo = __builtin_amdgcn_permlane32_swap(lanes::lo32(a), lanes::lo32(b), false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(lanes::hi32(a), lanes::hi32(b), false, false);
+        return lanes::join(lo[0], hi[0]) + lanes::join(lo[1], hi[1]);
+    }
+}
+
+// max(x, x(lane ^ OFF)) for OFF = 16 or 32, from one swap as in swap_sum
+template <int OFF>
+__device__ __forceinline__ double swap_max(double x)
+{
+    static_assert(OFF == 16 || OFF == 32, "whole-row exchanges only");
+    if constexpr (OFF == 16) {
+        const auto lo = __builtin_amdgcn_permlane16_swap(lanes::lo32(x), lanes::lo32(x), false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(lanes::hi32(x), lanes::hi32(x), false, false);
+        return fmax(lanes::join(lo[0], hi[0]), lanes::join(lo[1], hi[1]));
+    } else {
+        const auto lo = __builtin_amdgcn_permlane32_swap(lanes::lo32(x), lanes::lo32(x), false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(lanes::hi32(x), lanes::hi32(x), false, false);
+        return fmax(lanes::join(lo[0], hi[0]), lanes::join(lo[1], hi[1]));
     }
 }
 
 // Sum over aligned groups of W lanes (W a power of two <= 64); every lane of
 // the group receives the group total.
 template <int W>
-__device__ __forceinline__ double group_sum(double x, int lane)
+__device__ __forceinline__ double group_sum(double x)
 {
-    if constexpr (W >= 64) x += partner<32>(x, lane);
-    if constexpr (W >= 32) x += partner<16>(x, lane);
-    if constexpr (W >= 16) x += partner<8>(x, lane);
-    if constexpr (W >= 8) x += partner<4>(x, lane);
-    if constexpr (W >= 4) x += partner<2>(x, lane);
-    if constexpr (W >= 2) x += partner<1>(x, lane);
+    if constexpr (W >= 64) x = swap_sum<32>(x, x);
+    if constexpr (W >= 32) x = swap_sum<16>(x, x);
+    if constexpr (W >= 16) x += partner<8>(x);
+    if constexpr (W >= 8) x += partner<4>(x);
+    if constexpr (W >= 4) x += partner<2>(x);
+    if constexpr (W >= 2) x += partner<1>(x);
     return x;
 }
 
-__device__ __forceinline__ double wave_sum(double x, int lane) { return group_sum<64>(x, lane); }
+__device__ __forceinline__ double wave_sum(double x) { return group_sum<64>(x); }
 
-__device__ __forceinline__ double wave_max(double x, int lane)
+__device__ __forceinline__ double wave_max(double x)
 {
-    x = fmax(x, partner<32>(x, lane));
-    x = fmax(x, partner<16>(x, lane));
-    x = fmax(x, partner<8>(x, lane));
-    x = fmax(x, partner<4>(x, lane));
-    x = fmax(x, partner<2>(x, lane));
-    return fmax(x, partner<1>(x, lane));
+    x = swap_max<32>(x);
+    x = swap_max<16>(x);
+    x = fmax(x, partner<8>(x));
+    x = fmax(x, partner<4>(x));
+    x = fmax(x, partner<2>(x));
+    return fmax(x, partner<1>(x));
 }
 
 // Sum over the lanes that differ from this one only in lane bits >= FROM: the
 // partners are exact (lane ^ 16, lane ^ 32), so the lower lane bits -- a column
 // index, say -- are kept.
 template <int FROM>
-__device__ __forceinline__ double sum_high_lanes(double x, int lane)
+__device__ __forceinline__ double sum_high_lanes(double x)
 {
     static_assert(FROM == 16 || FROM == 32 || FROM == 64, "only whole 16-lane rows are exchanged exactly");
-    if constexpr (FROM <= 16) x += partner<16>(x, lane);
-    if constexpr (FROM <= 32) x += partner<32>(x, lane);
+    if constexpr (FROM <= 16) x = swap_sum<16>(x, x);
+    if constexpr (FROM <= 32) x = swap_sum<32>(x, x);
     return x;
 }
 
@@ -249,16 +276,20 @@ template <int W, int N>
 __device__ __forceinline__ double head_reduce(const double *v, int lane)
 {
     if constexpr (N == 1) {
-        return group_sum<W>(v[0], lane);
+        return group_sum<W>(v[0]);
     } else {
         constexpr int off = W / 2;
         const bool hi = (lane & off) != 0;
         double nv[N / 2];
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) {
-            const double mine = hi ? v[N / 2 + i] : v[i];
-            const double send = hi ? v[i] : v[N / 2 + i];
-            nv[i] = mine + partner<off>(send, lane);
+            if constexpr (off >= 16) {
+                nv[i] = swap_sum<off>(v[i], v[N / 2 + i]);
+            } else {
+                const double mine = hi ? v[N / 2 + i] : v[i];
+                const double send = hi ? v[i] : v[N / 2 + i];
+                nv[i] = mine + partner<off>(send);
+            }
         }
         return head_reduce<W / 2, N / 2>(nv, lane);
     }
