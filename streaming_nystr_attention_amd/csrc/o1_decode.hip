@@ -157,13 +157,16 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
         const float4 *kt = reinterpret_cast<const float4 *>(s.k_tilde) + (size_t)g * m * C::CH;
         const int NA = R + m;  // near rows, then landmark rows
         if constexpr (C::PIPE) {
+            // One row space in which each kind of row starts on a block row, so
+            // the source of every load and the work on it are uniform across
+            // the wave: [0, RP) near keys (R used), [RP, Q0) key landmarks (m
+            // used), [Q0, NTOT) query landmarks (far-insert logits against the
+            // evicted key).  Unused rows load a clamped row and are discarded.
+            // Batch b + 1 is in flight while batch b is reduced.
             const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
             const int NQ = HPK * m;
-            // One row space, aligned so that a block row never mixes kinds:
-            // [0, NA) key rows, [NA, Q0) padding, [Q0, Q0 + NQ) query-landmark
-            // rows (far-insert logits against the evicted key).  Batch b + 1
-            // is in flight while batch b is reduced.
-            const int Q0 = (NA + C::RPB - 1) / C::RPB * C::RPB;
+            const int RP = (R + C::RPB - 1) / C::RPB * C::RPB;
+            const int Q0 = (RP + m + C::RPB - 1) / C::RPB * C::RPB;
             const int NTOT = Q0 + NQ;
             constexpr int BR = C::UNR * C::RPB;  // rows per batch
             const int NB = (NTOT + BR - 1) / BR;
@@ -191,10 +194,11 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
             auto load = [&](float4 (&x)[C::UNR][C::CPL], int b) {
 #pragma unroll
                 for (int u = 0; u < C::UNR; ++u) {
-                    const int r = min(b * BR + u * C::RPB + r0, NTOT - 1);
-                    const float4 *row = r < R    ? nk + (size_t)r * C::CH
-                                        : r < Q0 ? kt + (size_t)(min(r, NA - 1) - R) * C::CH
-                                                 : qt + (size_t)(r - Q0) * C::CH;
+                    const int rb = b * BR + u * C::RPB;  // first row of the block row (wave-uniform)
+                    const int r = rb + r0;
+                    const float4 *row = rb < RP ? nk + (size_t)min(r, R - 1) * C::CH
+                                        : rb < Q0 ? kt + (size_t)min(r - RP, m - 1) * C::CH
+                                                  : qt + (size_t)min(r - Q0, NQ - 1) * C::CH;
 #pragma unroll
                     for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
                 }
@@ -202,10 +206,10 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
             auto reduce = [&](float4 (&x)[C::UNR][C::CPL], int b) {
 #pragma unroll
                 for (int u = 0; u < C::UNR; ++u) {
-                    const int rb = b * BR + u * C::RPB;  // first row of the block row (wave-uniform)
+                    const int rb = b * BR + u * C::RPB;
+                    const int r = rb + r0;
                     if (rb < Q0) {
-                        const int r = rb + r0;
-                        if (r == slot_row) {  // the ring slot already holds the new key
+                        if (rb < RP && r == slot_row) {  // the ring slot already holds the new key
 #pragma unroll
                             for (int k = 0; k < C::CPL; ++k) x[u][k] = kn_s[sub + C::LPR * k];
                         }
@@ -219,28 +223,31 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
                         }
                         const double tot = head_reduce<C::LPR, HPK>(part, lane) * scale;
                         if (writer) {
-                            if (r < R) lg_s[my_head * R + r] = tot;
-                            else if (r < NA) land_s[my_head][r - R] = tot;
+                            if (rb < RP) {
+                                if (r < R) lg_s[my_head * R + r] = tot;
+                            } else if (r - RP < m) {
+                                land_s[my_head][r - RP] = tot;
+                            }
                         }
-                    } else if (rb < NTOT) {
+                    } else {
                         double acc = 0.0;
 #pragma unroll
                         for (int k = 0; k < C::CPL; ++k) acc += dotd(kd[k], x[u][k]);
                         acc = group_sum<C::LPR>(acc);
-                        const int rq = rb + r0 - Q0;
+                        const int rq = r - Q0;
                         if (sub == 0 && rq < NQ) lf_s[rq / m][rq % m] = acc * scale;
                     }
                 }
             };
+            // two batches per round trip; no load stays in flight across the
+            // loop's back edge, where the compiler's wait counting turns
+            // conservative
             float4 xa[C::UNR][C::CPL], xb[C::UNR][C::CPL];
-            load(xa, 0);
             for (int b = 0; b < NB; b += 2) {
+                load(xa, b);
                 if (b + 1 < NB) load(xb, b + 1);
                 reduce(xa, b);
-                if (b + 1 < NB) {
-                    if (b + 2 < NB) load(xa, b + 2);
-                    reduce(xb, b + 1);
-                }
+                if (b + 1 < NB) reduce(xb, b + 1);
             }
         } else {
             for (int base = wave * C::RPW; base < NA; base += C::UNR * C::RPB) {
