@@ -20,7 +20,8 @@
 //        far insert   l[h][i]  = q~_{h,i} . k_e * scale  (hpk * m rows)
 //      The hpk partial dots of a row are reduced over the row's lanes by
 //      halving exchanges (each step keeps half the heads), so the lanes of a
-//      row end with one head's total each.  T^ rows and the first V rows this
+//      row end with one head's total each.  Shapes with one work-group per
+//      CU read the three kinds of rows as one block-aligned stream instead.  T^ rows and the first V rows this
 //      thread contracts later are loaded at the end of the pass, so their
 //      latency overlaps step 2.
 //   2. per head (one wave): c = max lg, f = max s, fh = e^{s - f}; running-max
@@ -68,8 +69,9 @@ struct DecodeShape {
     static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
     static constexpr int MB = NT == 256 ? 16 : 32;                     // M rows in flight (unstaged M)
     static constexpr bool NTL = NT == 256;                             // streaming accesses (large grids)
-    // Few groups per CU and registers to spare (one work-group per CU): the
-    // row pass runs as one pipelined stream over every row it reads.
+    // One work-group per CU and registers to spare: the row pass runs as one
+    // stream over every row it reads, two batches per round trip, with the
+    // queries in f64 registers.
     static constexpr bool PIPE = NT == 512 && HPK * D >= 512;
     // at least three waves per SIMD on large grids (at most 168 VGPRs)
     static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
@@ -162,7 +164,6 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
             // the wave: [0, RP) near keys (R used), [RP, Q0) key landmarks (m
             // used), [Q0, NTOT) query landmarks (far-insert logits against the
             // evicted key).  Unused rows load a clamped row and are discarded.
-            // Batch b + 1 is in flight while batch b is reduced.
             const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
             const int NQ = HPK * m;
             const int RP = (R + C::RPB - 1) / C::RPB * C::RPB;
