@@ -11,7 +11,9 @@
 //   gram_pinv_kernel   grid G * hpk: A = exp(Q~ K~^T * scale) and G = A^T A on f64
 //                      MFMA, lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
 //                      G + lambda I in LDS (lambda x10 on a failed pivot, up to 12
-//                      attempts, then diag(1/mean diag)), M = (G + lambda I)^-1 A^T.
+//                      attempts, then diag(1/mean diag)), M = (G + lambda I)^-1 A^T
+//                      by substitutions spread over lane groups.  Two m x m f64
+//                      matrices of LDS per head.
 //   far_mfma_kernel    grid G * ceil(hpk / HB): the far field of keys sink .. T-w-1, i.e. the
 //                      state the page's sequential replay through far_insert
 //                      reaches, computed in 16-key tiles on f64 MFMA with an
@@ -136,16 +138,48 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i % 4),
 // element i / 4); the Cholesky with its retries and the triangular solves run on
 // the vector units from LDS.
-__global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, PrefillIO io, double ridge_rel)
+// Forward then back substitution with the Cholesky factor L for every row b <
+// m of X (in place): X[b] <- (L L^T)^-1 X[b].  P lanes share a row: each sums
+// every P-th term of a step's dot product, the P partial sums are added across
+// the lanes (an aligned lane group of one wave), and the group's first lane
+// stores the step's result, which later steps read back from LDS (the LDS
+// operations of a wave complete in order).
+template <int P>
+__device__ void solve_rows(double *X, const double *L, int m, int ld, int tid)
+{
+    static_assert(P >= 2 && P <= 16 && (P & (P - 1)) == 0, "lane group within a DPP row");
+    const int b = tid / P, sub = tid % P;
+    if (b >= m) return;  // whole lane groups leave together
+    double *x = X + (size_t)b * ld;
+    for (int i = 0; i < m; ++i) {
+        double part = 0.0;
+#pragma unroll 4
+        for (int k = sub; k < i; k += P) part = fma(L[i * ld + k], x[k], part);
+        const double tot = group_sum<P>(part);
+        if (sub == 0) x[i] = (x[i] - tot) / L[i * ld + i];
+        __builtin_amdgcn_wave_barrier();
+    }
+    for (int i = m - 1; i >= 0; --i) {
+        double part = 0.0;
+#pragma unroll 4
+        for (int k = i + 1 + sub; k < m; k += P) part = fma(L[k * ld + i], x[k], part);
+        const double tot = group_sum<P>(part);
+        if (sub == 0) x[i] = (x[i] - tot) / L[i * ld + i];
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Eight waves per SIMD (at most 64 registers): with two matrices of LDS per
+// head, eight work-groups of the m <= 32 shapes fit on a CU.
+__global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, PrefillIO io, double ridge_rel)
 {
     const int H = s.hpk, ci = blockIdx.x / H, h = blockIdx.x - ci * H;
     const size_t gh = (size_t)io.map.state(ci) * H + h;  // state head
     const int m = s.m, d = s.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = (m + 15) / 16, mp = nb * 16, ld = mp + 1;
     extern __shared__ double lds[];
-    double *A = lds;
-    double *Gm = lds + (size_t)mp * ld;
-    double *L = lds + 2 * (size_t)mp * ld;
+    double *A = lds;                      // exp-Gram; then row b holds column b of M
+    double *L = lds + (size_t)mp * ld;    // G = A^T A + lambda I, factored in place
     __shared__ double mean_diag_s;
     __shared__ int fail_s;
 
@@ -182,20 +216,24 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
         }
     }
     __syncthreads();
-    // G = A^T A (padding rows of A are zero)
-    for (int blk = wave; blk < nb * nb; blk += kThreads / 64) {
-        const int bi = blk / nb, bj = blk - bi * nb;
-        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-        for (int ks = 0; ks < mp / 4; ++ks)
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A[(ks * 4 + lk) * ld + bi * 16 + li],
-                                                      A[(ks * 4 + lk) * ld + bj * 16 + li], acc, 0, 0, 0);
+    // G = A^T A into L (padding rows of A are zero).  G is not kept apart from
+    // its factor: a retry recomputes it, bit for bit, from A.
+    auto gram = [&]() {
+        for (int blk = wave; blk < nb * nb; blk += kThreads / 64) {
+            const int bi = blk / nb, bj = blk - bi * nb;
+            f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+            for (int ks = 0; ks < mp / 4; ++ks)
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A[(ks * 4 + lk) * ld + bi * 16 + li],
+                                                          A[(ks * 4 + lk) * ld + bj * 16 + li], acc, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Gm[(bi * 16 + lk + 4 * r) * ld + bj * 16 + li] = acc[r];
-    }
+            for (int r = 0; r < 4; ++r) L[(bi * 16 + lk + 4 * r) * ld + bj * 16 + li] = acc[r];
+        }
+    };
+    gram();
     __syncthreads();
     if (tid == 0) {
         double md = 0.0;
-        for (int i = 0; i < m; ++i) md += Gm[i * ld + i];
+        for (int i = 0; i < m; ++i) md += L[i * ld + i];
         mean_diag_s = md / (double)m;
     }
     __syncthreads();
@@ -204,10 +242,11 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
     int result = kRidgeTries + 1;
 
     for (int attempt = 1; attempt <= kRidgeTries; ++attempt) {
-        for (int t = tid; t < m * m; t += kThreads) {
-            const int i = t / m, j = t - i * m;
-            L[i * ld + j] = Gm[i * ld + j] + (i == j ? lambda : 0.0);
+        if (attempt > 1) {
+            gram();
+            __syncthreads();
         }
+        for (int i = tid; i < m; i += kThreads) L[i * ld + i] += lambda;  // G + lambda I
         __syncthreads();
         if (wave == 0) {
             // Left-looking Cholesky in one wave, lane i owning row i: for column
@@ -248,22 +287,10 @@ __global__ __launch_bounds__(kThreads) void gram_pinv_kernel(DevState s, Prefill
 
     float *mu = s.mu + gh * m * m;
     if (result <= kRidgeTries) {
-        // Column b of M solves (L L^T) x = (row b of A); done in place in row b.
-        for (int b = tid; b < m; b += kThreads) {
-            double *x = A + (size_t)b * ld;
-            for (int i = 0; i < m; ++i) {
-                double v = x[i];
-#pragma unroll 8
-                for (int k = 0; k < i; ++k) v -= L[i * ld + k] * x[k];
-                x[i] = v / L[i * ld + i];
-            }
-            for (int i = m - 1; i >= 0; --i) {
-                double v = x[i];
-#pragma unroll 8
-                for (int k = i + 1; k < m; ++k) v -= L[k * ld + i] * x[k];
-                x[i] = v / L[i * ld + i];
-            }
-        }
+        // Column b of M solves (L L^T) x = (row b of A), in place in row b.
+        if (mp <= 16) solve_rows<16>(A, L, m, ld, tid);
+        else if (mp <= 32) solve_rows<8>(A, L, m, ld, tid);
+        else solve_rows<4>(A, L, m, ld, tid);
         __syncthreads();
         for (int t = tid; t < m * m; t += kThreads) {
             const int a = t / m, b = t - a * m;
@@ -533,7 +560,7 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
         hipLaunchKernelGGL(copy_mu_kernel, dim3(1024), dim3(kThreads), 0, stream, s, io.map, io.fz_mu);
     } else {
         const size_t mp = (size_t)((s.m + 15) / 16) * 16;
-        const size_t lds = sizeof(double) * 3 * mp * (mp + 1);
+        const size_t lds = sizeof(double) * 2 * mp * (mp + 1);
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gram_pinv_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
