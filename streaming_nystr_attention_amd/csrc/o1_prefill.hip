@@ -139,15 +139,15 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // element i / 4); the Cholesky with its retries and the triangular solves run on
 // the vector units from LDS.
 // Forward then back substitution with the Cholesky factor L for every row b <
-// m of X (in place): X[b] <- (L L^T)^-1 X[b].  P lanes share a row: each sums
-// every P-th term of a step's dot product, the P partial sums are added across
-// the lanes (an aligned lane group of one wave), and the group's first lane
-// stores the step's result, which later steps read back from LDS (the LDS
-// operations of a wave complete in order).
+// m of X (in place): X[b] <- (L L^T)^-1 X[b], with inv[i] = 1 / L[i][i].  P
+// lanes share a row: each sums every P-th term of a step's dot product, the P
+// partial sums are added across the lanes (an aligned lane group of one wave),
+// and the group's first lane stores the step's result, which later steps read
+// back from LDS (the LDS operations of a wave complete in order).
 template <int P>
-__device__ void solve_rows(double *X, const double *L, int m, int ld, int tid)
+__device__ void solve_rows(double *X, const double *L, const double *inv, int m, int ld, int tid)
 {
-    static_assert(P >= 2 && P <= 16 && (P & (P - 1)) == 0, "lane group within a DPP row");
+    static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "lane group within a DPP row");
     const int b = tid / P, sub = tid % P;
     if (b >= m) return;  // whole lane groups leave together
     double *x = X + (size_t)b * ld;
@@ -155,16 +155,16 @@ __device__ void solve_rows(double *X, const double *L, int m, int ld, int tid)
         double part = 0.0;
 #pragma unroll 4
         for (int k = sub; k < i; k += P) part = fma(L[i * ld + k], x[k], part);
-        const double tot = group_sum<P>(part);
-        if (sub == 0) x[i] = (x[i] - tot) / L[i * ld + i];
+        const double tot = P > 1 ? group_sum<P>(part) : part;
+        if (sub == 0) x[i] = (x[i] - tot) * inv[i];
         __builtin_amdgcn_wave_barrier();
     }
     for (int i = m - 1; i >= 0; --i) {
         double part = 0.0;
 #pragma unroll 4
         for (int k = i + 1 + sub; k < m; k += P) part = fma(L[k * ld + i], x[k], part);
-        const double tot = group_sum<P>(part);
-        if (sub == 0) x[i] = (x[i] - tot) / L[i * ld + i];
+        const double tot = P > 1 ? group_sum<P>(part) : part;
+        if (sub == 0) x[i] = (x[i] - tot) * inv[i];
         __builtin_amdgcn_wave_barrier();
     }
 }
@@ -182,6 +182,7 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
     double *L = lds + (size_t)mp * ld;    // G = A^T A + lambda I, factored in place
     __shared__ double mean_diag_s;
     __shared__ int fail_s;
+    __shared__ double inv_s[kMaxLandmarks];
 
     const double *kt = io.lm64 + ((size_t)ci * (1 + H)) * m * d;
     const double *qt = io.lm64 + ((size_t)ci * (1 + H) + 1 + h) * m * d;
@@ -287,10 +288,14 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
 
     float *mu = s.mu + gh * m * m;
     if (result <= kRidgeTries) {
+        for (int i = tid; i < m; i += kThreads) inv_s[i] = 1.0 / L[i * ld + i];
+        __syncthreads();
         // Column b of M solves (L L^T) x = (row b of A), in place in row b.
-        if (mp <= 16) solve_rows<16>(A, L, m, ld, tid);
-        else if (mp <= 32) solve_rows<8>(A, L, m, ld, tid);
-        else solve_rows<4>(A, L, m, ld, tid);
+        // one wave (P * mp = 64) while m <= 32, four lanes per row over the
+        // whole work-group beyond (measured best of the two at each size)
+        if (mp <= 16) solve_rows<4>(A, L, inv_s, m, ld, tid);
+        else if (mp <= 32) solve_rows<2>(A, L, inv_s, m, ld, tid);
+        else solve_rows<4>(A, L, inv_s, m, ld, tid);
         __syncthreads();
         for (int t = tid; t < m * m; t += kThreads) {
             const int a = t / m, b = t - a * m;
