@@ -132,25 +132,33 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// One block per (group, head), 256 threads.  Dynamic LDS: A, G and L, each
-// [mp][mp + 1] f64 with mp = m rounded up to 16 (padding rows/columns of A are 0).
-// The exp-Gram and A^T A run on v_mfma_f64_16x16x4f64 (operand layout: A[i][k] in
-// lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i % 4),
-// element i / 4); the Cholesky with its retries and the triangular solves run on
-// the vector units from LDS.
-// Forward then back substitution with the Cholesky factor L for every row b <
-// m of X (in place): X[b] <- (L L^T)^-1 X[b], with inv[i] = 1 / L[i][i].  P
-// lanes share a row: each sums every P-th term of a step's dot product, the P
-// partial sums are added across the lanes (an aligned lane group of one wave),
-// and the group's first lane stores the step's result, which later steps read
-// back from LDS (the LDS operations of a wave complete in order).
+// One block per (group, head), 256 threads.  Dynamic LDS: A [mp][gram_lda(mp)]
+// and L [mp][mp + 1], f64, with mp = m rounded up to 16 (padding rows/columns of
+// A are 0).  The exp-Gram and A^T A run on v_mfma_f64_16x16x4f64 (operand layout:
+// A[i][k] in lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i %
+// 4), element i / 4); the Cholesky with its retries and the triangular solves run
+// on the vector units from LDS.
+//
+// A's row stride is mp + P for the P lanes per row of the substitutions: the 16
+// lanes an LDS access serves per cycle (rows b.. and their P columns) then fall
+// in distinct banks.  L keeps stride mp + 1, which the lane-per-row Cholesky
+// reads without conflicts.
+__host__ __device__ constexpr int gram_lda(int mp) { return mp <= 16 ? mp + 4 : (mp <= 32 ? mp + 2 : mp + 4); }
+
+// Forward then back substitution with the Cholesky factor L (row stride ld)
+// for every row b < m of X (row stride ldx), in place: X[b] <- (L L^T)^-1 X[b],
+// with inv[i] = 1 / L[i][i].  P lanes share a row: each sums every P-th term of
+// a step's dot product, the P partial sums are added across the lanes (an
+// aligned lane group of one wave), and the group's first lane stores the step's
+// result, which later steps read back from LDS (the LDS operations of a wave
+// complete in order).
 template <int P>
-__device__ void solve_rows(double *X, const double *L, const double *inv, int m, int ld, int tid)
+__device__ void solve_rows(double *X, int ldx, const double *L, int ld, const double *inv, int m, int tid)
 {
     static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "lane group within a DPP row");
     const int b = tid / P, sub = tid % P;
     if (b >= m) return;  // whole lane groups leave together
-    double *x = X + (size_t)b * ld;
+    double *x = X + (size_t)b * ldx;
     for (int i = 0; i < m; ++i) {
         double part = 0.0;
 #pragma unroll 4
@@ -176,10 +184,10 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
     const int H = s.hpk, ci = blockIdx.x / H, h = blockIdx.x - ci * H;
     const size_t gh = (size_t)io.map.state(ci) * H + h;  // state head
     const int m = s.m, d = s.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nb = (m + 15) / 16, mp = nb * 16, ld = mp + 1;
+    const int nb = (m + 15) / 16, mp = nb * 16, ld = mp + 1, lda = gram_lda(mp);
     extern __shared__ double lds[];
     double *A = lds;                      // exp-Gram; then row b holds column b of M
-    double *L = lds + (size_t)mp * ld;    // G = A^T A + lambda I, factored in place
+    double *L = lds + (size_t)mp * lda;   // G = A^T A + lambda I, factored in place
     __shared__ double mean_diag_s;
     __shared__ int fail_s;
     __shared__ double inv_s[kMaxLandmarks];
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = bi * 16 + lk + 4 * r, j = bj * 16 + li;
-            A[i * ld + j] = (i < m && j < m) ? exp(acc[r] * sc) : 0.0;
+            A[i * lda + j] = (i < m && j < m) ? exp(acc[r] * sc) : 0.0;
         }
     }
     __syncthreads();
@@ -224,8 +232,8 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
             const int bi = blk / nb, bj = blk - bi * nb;
             f64x4 acc = {0.0, 0.0, 0.0, 0.0};
             for (int ks = 0; ks < mp / 4; ++ks)
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A[(ks * 4 + lk) * ld + bi * 16 + li],
-                                                          A[(ks * 4 + lk) * ld + bj * 16 + li], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A[(ks * 4 + lk) * lda + bi * 16 + li],
+                                                          A[(ks * 4 + lk) * lda + bj * 16 + li], acc, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) L[(bi * 16 + lk + 4 * r) * ld + bj * 16 + li] = acc[r];
         }
@@ -293,13 +301,13 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
         // Column b of M solves (L L^T) x = (row b of A), in place in row b.
         // one wave (P * mp = 64) while m <= 32, four lanes per row over the
         // whole work-group beyond (measured best of the two at each size)
-        if (mp <= 16) solve_rows<4>(A, L, inv_s, m, ld, tid);
-        else if (mp <= 32) solve_rows<2>(A, L, inv_s, m, ld, tid);
-        else solve_rows<4>(A, L, inv_s, m, ld, tid);
+        if (mp <= 16) solve_rows<4>(A, lda, L, ld, inv_s, m, tid);
+        else if (mp <= 32) solve_rows<2>(A, lda, L, ld, inv_s, m, tid);
+        else solve_rows<4>(A, lda, L, ld, inv_s, m, tid);
         __syncthreads();
         for (int t = tid; t < m * m; t += kThreads) {
             const int a = t / m, b = t - a * m;
-            mu[t] = (float)A[(size_t)b * ld + a];
+            mu[t] = (float)A[(size_t)b * lda + a];
         }
     } else {
         for (int t = tid; t < m * m; t += kThreads) {
@@ -565,7 +573,7 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
         hipLaunchKernelGGL(copy_mu_kernel, dim3(1024), dim3(kThreads), 0, stream, s, io.map, io.fz_mu);
     } else {
         const size_t mp = (size_t)((s.m + 15) / 16) * 16;
-        const size_t lds = sizeof(double) * 2 * mp * (mp + 1);
+        const size_t lds = sizeof(double) * mp * (gram_lda((int)mp) + mp + 1);
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gram_pinv_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
