@@ -212,6 +212,19 @@ __device__ __forceinline__ double wave_max(double x)
     return fmax(x, partner<1>(x));
 }
 
+// Max over aligned groups of W lanes within a 16-lane row (W <= 16); every lane
+// of the group receives the group maximum.
+template <int W>
+__device__ __forceinline__ double group_max(double x)
+{
+    static_assert(W >= 1 && W <= 16 && (W & (W - 1)) == 0, "group within a DPP row");
+    if constexpr (W >= 16) x = fmax(x, partner<8>(x));
+    if constexpr (W >= 8) x = fmax(x, partner<4>(x));
+    if constexpr (W >= 4) x = fmax(x, partner<2>(x));
+    if constexpr (W >= 2) x = fmax(x, partner<1>(x));
+    return x;
+}
+
 // Sum over the lanes that differ from this one only in lane bits >= FROM: the
 // partners are exact (lane ^ 16, lane ^ 32), so the lower lane bits -- a column
 // index, say -- are kept.

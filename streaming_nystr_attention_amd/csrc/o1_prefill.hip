@@ -437,41 +437,43 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
         if (j0 + TK < nf) fetch(j0 + TK);  // the next tile is in flight during the MFMAs
 
         // logits of this landmark block against the tile
-        f64x4 L = {0.0, 0.0, 0.0, 0.0}, L2 = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-        for (int ks = 0; ks < KS; ks += 2) {
+        f64x4 L = {0.0, 0.0, 0.0, 0.0}, L2 = {0.0, 0.0, 0.0, 0.0}, L3 = L, L4 = L;
+#pragma unroll 2
+        for (int ks = 0; ks < KS; ks += 4) {
             // opaque copies: widen Q~ at its use instead of keeping KS doubles live
-            float q0 = qa[ks], q1 = qa[ks + 1];
-            asm volatile("" : "+v"(q0), "+v"(q1));
+            float q0 = qa[ks], q1 = qa[ks + 1], q2 = qa[ks + 2], q3 = qa[ks + 3];
+            asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3));
             L = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q0, (double)k_lds[li][lk][ks], L, 0, 0, 0);
             L2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q1, (double)k_lds[li][lk][ks + 1], L2, 0, 0, 0);
+            L3 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q2, (double)k_lds[li][lk][ks + 2], L3, 0, 0, 0);
+            L4 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q3, (double)k_lds[li][lk][ks + 3], L4, 0, 0, 0);
         }
-        L += L2;
+        L = (L + L2) + (L3 + L4);
         // lane holds L[row lk + 4 r][key li]
+        // (the 16 keys of a row sit in one 16-lane row: DPP reductions)
         const bool kl = li < nt;
-        double p[4], f[4];
+        double p[4], nw[4];
         bool grew = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const double l = kl ? L[r] * sc : NEG_INF;
-            double t = l;
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) t = fmax(t, __shfl_xor(t, off, 64));
-            const double nw = fmax(mx[r], t);
-            f[r] = exp(mx[r] - nw);  // 0 on the first tile, exactly 1 when the max holds
-            grew |= f[r] != 1.0;
-            mx[r] = nw;
-            p[r] = kl ? exp(l - nw) : 0.0;
-            double ps = p[r];
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 64);
-            zs[r] = zs[r] * f[r] + ps;
+            nw[r] = fmax(mx[r], group_max<16>(l));
+            grew |= nw[r] != mx[r];
+            p[r] = kl ? exp(l - nw[r]) : 0.0;
         }
         if (__any(grew)) {  // rescale only when some running max of the wave moved
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r) {
+                const double f = exp(mx[r] - nw[r]);  // 0 on the first tile, 1 where the max held
+                zs[r] *= f;
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) tacc[cb][r] *= f[r];
+                for (int cb = 0; cb < CB; ++cb) tacc[cb][r] *= f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            mx[r] = nw[r];
+            zs[r] += group_sum<16>(p[r]);
         }
         // P from the result layout to the A-operand layout through this wave's LDS rows
 #pragma unroll
@@ -481,14 +483,14 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) pa[kk] = p_lds[wave][li][kk * 4 + lk];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            float vb[4];
+        for (int kk = 0; kk < 4; ++kk) {
+            // consecutive MFMAs go to different accumulators
+            float vb[CB];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) vb[kk] = v_lds[kk * 4 + lk][cb * 16 + li];
-            asm volatile("" : "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]));
+            for (int cb = 0; cb < CB; ++cb) vb[cb] = v_lds[kk * 4 + lk][cb * 16 + li];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                tacc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(pa[kk], (double)vb[kk], tacc[cb], 0, 0, 0);
+            for (int cb = 0; cb < CB; ++cb)
+                tacc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(pa[kk], (double)vb[cb], tacc[cb], 0, 0, 0);
         }
         __syncthreads();  // every wave is done with the tile before the next is staged
     }
