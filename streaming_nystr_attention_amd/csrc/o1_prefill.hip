@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, Prefill
     }
     double *dst64 = io.lm64 + ((size_t)ci * (1 + H) + src) * m * d;
     // one thread per (segment, 4 components): the segment's rows are summed in
-    // row order, four rows' loads in flight at a time
+    // row order, eight rows' loads in flight at a time (then four, then one)
     const int d4 = d / 4;
     for (int t = threadIdx.x; t < m * d4; t += kThreads) {
         const int a = t / d4, c = (t - a * d4) * 4;
@@ -72,6 +72,18 @@ __global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, Prefill
         double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
         const float *col = x + c;
         long j = lo;
+        for (; j + 8 <= hi; j += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4 *>(col + (int64_t)(j + u) * pos);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                s0 += (double)v[u].x;
+                s1 += (double)v[u].y;
+                s2 += (double)v[u].z;
+                s3 += (double)v[u].w;
+            }
+        }
         for (; j + 4 <= hi; j += 4) {
             float4 v[4];
 #pragma unroll
