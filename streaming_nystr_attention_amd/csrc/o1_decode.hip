@@ -21,9 +21,9 @@
 //      The hpk partial dots of a row are reduced over the row's lanes by
 //      halving exchanges (each step keeps half the heads), so the lanes of a
 //      row end with one head's total each.  Shapes with one work-group per
-//      CU read the three kinds of rows as one block-aligned stream instead.  T^ rows and the first V rows this
-//      thread contracts later are loaded at the end of the pass, so their
-//      latency overlaps step 2.
+//      CU read the three kinds of rows as one block-aligned stream instead.
+//      T^ rows and the first V rows this thread contracts later are loaded at
+//      the end of the pass, so their latency overlaps step 2.
 //   2. per head (one wave): c = max lg, f = max s, fh = e^{s - f}; running-max
 //      update for the evicted key (NystromHead::far_insert): r_i, e_i, Z^ and
 //      m_max written back; u = fh . M; c_all = max(c, f + m_max); gain =
@@ -72,7 +72,7 @@ struct DecodeShape {
     // One work-group per CU and registers to spare: the row pass runs as one
     // stream over every row it reads, two batches per round trip, with the
     // queries in f64 registers.
-    static constexpr bool PIPE = NT == 512 && HPK * D >= 512;
+    static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512;
     // at least three waves per SIMD on large grids (at most 168 VGPRs)
     static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
     static constexpr int RED_CAP = 16384 / (NW * DV * 8);              // heads per LDS round
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
         const bool writer = (sub % HSTRIDE) == 0;
         const float4 *kt = reinterpret_cast<const float4 *>(s.k_tilde) + (size_t)g * m * C::CH;
         const int NA = R + m;  // near rows, then landmark rows
-        if constexpr (C::PIPE) {
+        if constexpr (C::STREAM_ROWS) {
             // One row space in which each kind of row starts on a block row, so
             // the source of every load and the work on it are uniform across
             // the wave: [0, RP) near keys (R used), [RP, Q0) key landmarks (m

@@ -6,6 +6,8 @@ o1_prefill), so the decode outputs are compared at the decode tolerance
 Counters (far_len, win_head) are compared bit-exactly for every group, ring and
 sink rows bit-exactly for the sampled groups.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -142,5 +144,13 @@ def test_entry_point_errors_on_device():
     with pytest.raises(P.O1Error) as e:
         grp.write(P.FIELD_T_HAT, torch.zeros(4, device=DEV))
     assert e.value.status == P.O1_ESTATE
+    # an empty prompt is refused through the C ABI itself (valid device buffers)
+    L = P.lib()
+    pv = P.o1_prompt_view()
+    pv.q, pv.k, pv.v = qp.data_ptr(), kp.data_ptr(), kp.data_ptr()
+    for T0 in (0, -3):
+        assert L.o1_prefill(grp._h, qp.data_ptr(), kp.data_ptr(), kp.data_ptr(), T0, None, None) == P.O1_EINVAL
+        assert L.o1_prefill_layer(grp._h, 0, ctypes.byref(pv), T0, None, None) == P.O1_EINVAL
+        assert b"prompt length" in L.o1_last_error()
     info = grp.info()
     assert info.sealed == 0 and info.n_groups == G
