@@ -22,7 +22,9 @@
 namespace o1 {
 namespace {
 
-constexpr int kNT = 256, kNW = kNT / 64, kChunk = 128;
+constexpr int kNT = 256, kNW = kNT / 64;
+constexpr int kChunk = 256;     // keys a work-group walks per step of its online softmax
+constexpr int kSplitKeys = 128; // fewest keys per work-group when a range is split
 
 template <int D, int DV, int HPK>
 struct ExactShape {
@@ -309,9 +311,9 @@ hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const Group
 
 int exact_splits(int G, int n_visible)
 {
-    // enough work-groups to cover the CUs several times, at least one chunk each
+    // enough work-groups to cover the CUs several times, at least kSplitKeys keys each
     const int want = (4 * 256 + G - 1) / G;
-    const int most = (n_visible + kChunk - 1) / kChunk;
+    const int most = (n_visible + kSplitKeys - 1) / kSplitKeys;
     int s = want < most ? want : most;
     return s < 1 ? 1 : s;
 }
