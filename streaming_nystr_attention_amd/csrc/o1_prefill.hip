@@ -450,7 +450,7 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
 
         // logits of this landmark block against the tile
         f64x4 L = {0.0, 0.0, 0.0, 0.0}, L2 = {0.0, 0.0, 0.0, 0.0}, L3 = L, L4 = L;
-#pragma unroll 2
+#pragma unroll
         for (int ks = 0; ks < KS; ks += 4) {
             // opaque copies: widen Q~ at its use instead of keeping KS doubles live
             float q0 = qa[ks], q1 = qa[ks + 1], q2 = qa[ks + 2], q3 = qa[ks + 3];
