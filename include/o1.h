@@ -160,9 +160,8 @@ void o1_destroy_groups(o1_groups *g);
  * (which may then be NULL) and `frozen` are not read.
  * Every tensor must be 16-byte aligned.
  * Errors: O1_EINVAL (null or misaligned tensor, T < 1, T * G * hpk * d > 2^40),
- * O1_EEXACT (exact-only prompt and
- * exact_cap = 0), O1_EFULL (exact-only prompt longer than exact_cap),
- * O1_ENOMEM (work buffers), O1_EHIP. */
+ * O1_EEXACT (exact-only prompt and exact_cap = 0), O1_EFULL (exact-only prompt
+ * longer than exact_cap), O1_ENOMEM (work buffers), O1_EHIP. */
 int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int32_t T,
                const o1_frozen *frozen, void *stream);
 
@@ -183,9 +182,8 @@ int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int
  * only.  An exact-only step fixes its key count at capture, so it must not be
  * replayed.
  * Errors: O1_EINVAL (null or misaligned tensor), O1_ESTATE (a layer without a
- * successful prefill), O1_EFULL
- * (exact-only group already holding exact_cap keys; nothing is changed),
- * O1_EHIP. */
+ * successful prefill), O1_EFULL (exact-only group already holding exact_cap
+ * keys; nothing is changed), O1_EHIP. */
 int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float *out,
             void *stream);
 
