@@ -375,8 +375,12 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
     const double NEG_INF = -__builtin_inf();
     const int li = lane & 15, lk = lane >> 4;
 
-    __shared__ float k_lds[TK][4][KS + 1];
-    __shared__ float v_lds[TK][DV + 4];
+    // K and V tiles widened to f64 once, as they are staged: the MFMA operand
+    // reads need no conversion.  K is [k quarter][key][component] with an odd
+    // row length, so the 16 keys of a logit operand read fall in distinct bank
+    // pairs.
+    __shared__ double k_lds[4][TK][KS + 1];
+    __shared__ double v_lds[TK][DV + 2];
     __shared__ double p_lds[NW][16][17];
 
     // Q~ fragment of this wave: row rb * 16 + li, components lk * KS .. lk * KS + KS - 1
@@ -419,14 +423,16 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
             const int idx = tid + p * NT;
             if (idx < K4) {
                 const int key = idx / (D / 4), c = (idx % (D / 4)) * 4;  // component of .x
-                float *dst = &k_lds[key][c / KS][c % KS];
+                double *dst = &k_lds[c / KS][key][c % KS];
                 dst[0] = pre[p].x;
                 dst[1] = pre[p].y;
                 dst[2] = pre[p].z;
                 dst[3] = pre[p].w;
             } else if (idx < KV4) {
                 const int e = idx - K4, key = e / (DV / 4), c4 = e % (DV / 4);
-                *reinterpret_cast<float4 *>(&v_lds[key][c4 * 4]) = pre[p];
+                double2 *dst = reinterpret_cast<double2 *>(&v_lds[key][c4 * 4]);
+                dst[0] = make_double2(pre[p].x, pre[p].y);
+                dst[1] = make_double2(pre[p].z, pre[p].w);
             }
         }
     };
@@ -455,10 +461,10 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
             // opaque copies: widen Q~ at its use instead of keeping KS doubles live
             float q0 = qa[ks], q1 = qa[ks + 1], q2 = qa[ks + 2], q3 = qa[ks + 3];
             asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3));
-            L = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q0, (double)k_lds[li][lk][ks], L, 0, 0, 0);
-            L2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q1, (double)k_lds[li][lk][ks + 1], L2, 0, 0, 0);
-            L3 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q2, (double)k_lds[li][lk][ks + 2], L3, 0, 0, 0);
-            L4 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q3, (double)k_lds[li][lk][ks + 3], L4, 0, 0, 0);
+            L = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q0, k_lds[lk][li][ks], L, 0, 0, 0);
+            L2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q1, k_lds[lk][li][ks + 1], L2, 0, 0, 0);
+            L3 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q2, k_lds[lk][li][ks + 2], L3, 0, 0, 0);
+            L4 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q3, k_lds[lk][li][ks + 3], L4, 0, 0, 0);
         }
         L = (L + L2) + (L3 + L4);
         // lane holds L[row lk + 4 r][key li]
@@ -497,12 +503,12 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             // consecutive MFMAs go to different accumulators
-            float vb[CB];
+            double vb[CB];
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) vb[cb] = v_lds[kk * 4 + lk][cb * 16 + li];
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
-                tacc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(pa[kk], (double)vb[cb], tacc[cb], 0, 0, 0);
+                tacc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(pa[kk], vb[cb], tacc[cb], 0, 0, 0);
         }
         __syncthreads();  // every wave is done with the tile before the next is staged
     }
