@@ -182,7 +182,8 @@ int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int
  * only.  An exact-only step fixes its key count at capture, so it must not be
  * replayed.
  * Errors: O1_EINVAL (null or misaligned tensor), O1_ESTATE (a layer without a
- * successful prefill), O1_EFULL (exact-only group already holding exact_cap
+ * successful prefill; or, in the exact-only mode, layers stepped one by one to
+ * different key counts), O1_EFULL (exact-only group already holding exact_cap
  * keys; nothing is changed), O1_EHIP. */
 int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float *out,
             void *stream);

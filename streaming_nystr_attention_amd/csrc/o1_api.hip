@@ -265,6 +265,13 @@ int step_groups(o1_groups *g, int layer, const float *q, const float *k, const f
     const o1::GroupMap map = layer < 0 ? whole_map(g) : layer_map(g, layer);
     hipError_t err;
     if (g->exact) {
+        // One key count per launch: a whole-handle step needs every layer to
+        // hold the same number of keys (layers stepped one by one may differ).
+        if (layer < 0 && g->steps_extreme(true) != g->steps_extreme(false))
+            return fail(O1_ESTATE,
+                        "exact-only o1_step: the layers hold different key counts (%lld .. %lld steps); "
+                        "step them with o1_step_layer",
+                        (long long)g->steps_extreme(false), (long long)g->steps_extreme(true));
         const long long held =
             (long long)g->T + (layer < 0 ? g->steps_extreme(true) : g->layer_steps[layer]);
         if (held >= g->cfg.exact_cap)

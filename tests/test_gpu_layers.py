@@ -225,6 +225,44 @@ def test_layer_path_exact_only_equals_whole_handle():
     layered.close()
 
 
+def test_exact_only_whole_step_refuses_unequal_layers():
+    """In the exact-only mode a whole-handle step appends at one key count for
+    every group; after layers were stepped one by one to different counts it is
+    refused (O1_ESTATE) and changes nothing, and it works again once the layers
+    are level."""
+    wl = WL.with_(T=30, steps=3, seed=64)
+    cfg = dataclasses.replace(wl.config, exact_cap=wl.T + 8)
+    q, k, v = W.prompt(wl, DEV)
+    grp = P.O1Groups(cfg)
+    grp.prefill(q, k, v)
+    B, K, H, L, G = wl.n_seq, wl.n_kv, wl.hpk, wl.n_layer, wl.groups
+    ql = torch.randn(B, K * H, wl.d, device=DEV)
+    kl = torch.randn(B, K, wl.d, device=DEV)
+    vl = torch.randn(B, K, wl.dv, device=DEV)
+    ol = torch.empty(B, K * H, wl.dv, device=DEV)
+    grp.step_layer(0, ql, kl, vl, ol)  # layer 0 now holds one key more
+    before = [grp.read(f, DEV) for f in (P.FIELD_EXACT_K, P.FIELD_EXACT_V)]
+    qw = torch.randn(G, H, wl.d, device=DEV)
+    kw = torch.randn(G, wl.d, device=DEV)
+    vw = torch.randn(G, wl.dv, device=DEV)
+    out = torch.zeros(G, H, wl.dv, device=DEV)
+    with pytest.raises(P.O1Error) as e:
+        grp.step(qw, kw, vw, out)
+    assert e.value.status == P.O1_ESTATE
+    torch.cuda.synchronize()
+    for b, f in zip(before, (P.FIELD_EXACT_K, P.FIELD_EXACT_V)):
+        assert torch.equal(grp.read(f, DEV), b), f
+    assert not out.any()
+    for l in range(1, L):  # level the other layers, then a whole step is valid
+        grp.step_layer(l, ql, kl, vl, ol)
+    grp.step(qw, kw, vw, out)
+    torch.cuda.synchronize()
+    info = grp.info()
+    assert info.exact_keys == wl.T + 2 and info.steps == 2 and info.max_steps == 2
+    assert torch.isfinite(out).all()
+    grp.close()
+
+
 def test_graph_replay_of_layer_steps_matches_eager():
     """One token's o1_step_layer launches captured in a HIP graph and replayed
     several times, with eager input copies and synchronisation between the
