@@ -173,17 +173,21 @@ int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int
  *   out [G][hpk][dv]   outputs (may not alias the inputs)
  * In the exact-only mode the step appends (k, v) as key n = T + steps and
  * writes, per head, softmax attention over keys 0 .. n (NystromHead::step with
- * no sinks and no far field); one launch, two when a group's keys are split
- * across work-groups.
- * No allocation, no host synchronisation; one kernel launch.
- * Graph capture: in the skeleton mode a step (and o1_step_layer) may be
- * captured into a HIP graph and replayed; each replay advances the device
- * state as a call does, but the step counts o1_get_info reports count calls
- * only.  An exact-only step fixes its key count at capture, so it must not be
- * replayed.
+ * no sinks and no far field).  Each group's key count is its layer's count,
+ * kept on the device, so layers stepped one by one to different counts are
+ * stepped correctly by o1_step as well.  Launches: the attention (plus a
+ * merge when a group's keys are split across work-groups) and a one-block
+ * kernel that advances the counts.
+ * No allocation, no host synchronisation; one kernel launch in the skeleton
+ * mode.
+ * Graph capture: a step (and o1_step_layer) may be captured into a HIP graph
+ * and replayed, in either mode; each replay advances the device state as a
+ * call does.  The step counts o1_get_info reports count calls only.  A replay
+ * that finds an exact-only group already holding exact_cap keys changes
+ * nothing for that group and writes none of its outputs (an eager call
+ * returns O1_EFULL instead).
  * Errors: O1_EINVAL (null or misaligned tensor), O1_ESTATE (a layer without a
- * successful prefill; or, in the exact-only mode, layers stepped one by one to
- * different key counts), O1_EFULL (exact-only group already holding exact_cap
+ * successful prefill), O1_EFULL (exact-only group already holding exact_cap
  * keys; nothing is changed), O1_EHIP. */
 int o1_step(o1_groups *g, const float *q, const float *k, const float *v, float *out,
             void *stream);

@@ -55,6 +55,7 @@ struct o1_groups {
     float *exact_k, *exact_v;
     double *exact_ws;
     size_t exact_ws_bytes;
+    int32_t *exact_held;  // keys held per layer [n_layer], kept on the device
 
     bool any_sealed() const
     {
@@ -129,7 +130,7 @@ void free_state(o1_groups *g)
     o1::DevState &s = g->st;
     void *ptrs[] = {s.near_k, s.near_v, s.k_tilde, s.q_tilde, s.mu,     s.t_hat,
                     s.z_hat,  s.m_max,  s.win_head, s.far_len, s.lambda, s.tries,
-                    g->lm64,  g->exact_k, g->exact_v, g->exact_ws};
+                    g->lm64,  g->exact_k, g->exact_v, g->exact_ws, g->exact_held};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
 }
@@ -229,8 +230,9 @@ int prefill_groups(o1_groups *g, int layer, const o1::PromptView &pv, int32_t T,
 
     hipError_t err;
     if (exact) {
+        const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c.n_layer : layer + 1;
         err = o1::launch_exact_seal(g->st, pv, map, T, g->exact_k, g->exact_v, c.exact_cap,
-                                    (hipStream_t)stream);
+                                    g->exact_held, l0, l1, (hipStream_t)stream);
     } else {
         o1::PrefillIO io;
         io.p = pv;
@@ -265,20 +267,16 @@ int step_groups(o1_groups *g, int layer, const float *q, const float *k, const f
     const o1::GroupMap map = layer < 0 ? whole_map(g) : layer_map(g, layer);
     hipError_t err;
     if (g->exact) {
-        // One key count per launch: a whole-handle step needs every layer to
-        // hold the same number of keys (layers stepped one by one may differ).
-        if (layer < 0 && g->steps_extreme(true) != g->steps_extreme(false))
-            return fail(O1_ESTATE,
-                        "exact-only o1_step: the layers hold different key counts (%lld .. %lld steps); "
-                        "step them with o1_step_layer",
-                        (long long)g->steps_extreme(false), (long long)g->steps_extreme(true));
+        // Each group's key count is read on the device (its layer's count), so
+        // layers stepped one by one may hold different counts and a captured
+        // step replays correctly; the host mirror serves the checks below.
         const long long held =
             (long long)g->T + (layer < 0 ? g->steps_extreme(true) : g->layer_steps[layer]);
         if (held >= g->cfg.exact_cap)
             return fail(O1_EFULL, "exact-only groups already hold exact_cap = %d keys", g->cfg.exact_cap);
         DeviceScope dev(g);
         if (int rc = dev.status()) return rc;
-        const int n = (int)held + 1;  // keys 0 .. n-1 after appending this step's key
+        const int n = (int)held + 1;  // the fullest group's keys after this step's append
         o1::ExactIO io{};
         io.q = q;
         io.k = g->exact_k;
@@ -305,7 +303,14 @@ int step_groups(o1_groups *g, int layer, const float *q, const float *k, const f
         io.v_new = v;
         io.k_dst = g->exact_k;
         io.v_dst = g->exact_v;
+        io.held = g->exact_held;
+        io.n_kv = g->cfg.n_kv;
+        io.n_layer = g->cfg.n_layer;
         err = o1::launch_exact(io, splits, (hipStream_t)stream);
+        if (err == hipSuccess) {
+            const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? g->cfg.n_layer : layer + 1;
+            err = o1::launch_exact_advance(g->exact_held, l0, l1, g->cfg.exact_cap, (hipStream_t)stream);
+        }
     } else {
         DeviceScope dev(g);
         if (int rc = dev.status()) return rc;
@@ -368,6 +373,7 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     g->exact_k = g->exact_v = nullptr;
     g->exact_ws = nullptr;
     g->exact_ws_bytes = 0;
+    g->exact_held = nullptr;
     if (hipGetDevice(&g->device) != hipSuccess) {
         delete g;
         return fail(O1_EHIP, "hipGetDevice failed");
@@ -410,6 +416,7 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         {(void **)&g->exact_k, Gs * E * c.d * sizeof(float)},
         {(void **)&g->exact_v, Gs * E * c.dv * sizeof(float)},
         {(void **)&g->exact_ws, ws_bytes},
+        {(void **)&g->exact_held, E ? (size_t)c.n_layer * sizeof(int32_t) : 0},
     };
     size_t total = 0;
     for (auto &a : allocs) {

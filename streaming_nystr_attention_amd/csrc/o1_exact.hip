@@ -49,8 +49,15 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
     const int ci = blockIdx.x, sp = blockIdx.y;  // call index (q, out, new key, partials)
     const int g = a.map.state(ci);              // cache group
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int k0 = a.first + sp * a.per_split;
-    const int k1 = min(k0 + a.per_split, a.n_keys);
+    int n_keys = a.n_keys, per_split = a.per_split;
+    if (a.held) {  // exact-only decode: this group's key count from the device
+        const int held = a.held[(g / a.n_kv) % a.n_layer];
+        if (held >= a.cap) return;  // full: the step changes nothing here
+        n_keys = held + 1;
+        per_split = (n_keys - a.first + (int)gridDim.y - 1) / (int)gridDim.y;
+    }
+    const int k0 = a.first + sp * per_split;
+    const int k1 = min(k0 + per_split, n_keys);
     const double scale = (double)a.scale;
     const double NEG_INF = -__builtin_inf();
 
@@ -64,7 +71,7 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
     for (int i = tid; i < HPK * C::CH; i += kNT) (&q_s[0][0])[i] = qg[i];
     const float4 *kc = reinterpret_cast<const float4 *>(a.k) + (size_t)g * a.cap * C::CH;
     const float4 *vc = reinterpret_cast<const float4 *>(a.v) + (size_t)g * a.cap * C::VCH;
-    const int new_row = a.k_new ? a.n_keys - 1 : -1;  // absolute index of the appended key
+    const int new_row = a.k_new ? n_keys - 1 : -1;  // absolute index of the appended key
     const float4 *kn = reinterpret_cast<const float4 *>(a.k_new) + (size_t)ci * C::CH;
     const float4 *vn = reinterpret_cast<const float4 *>(a.v_new) + (size_t)ci * C::VCH;
     if (new_row >= k0 && new_row < k1) {
@@ -238,6 +245,7 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
 __global__ void exact_combine_kernel(ExactIO a, int splits)
 {
     const int gh = blockIdx.x, H = a.hpk, g = gh / H, h = gh - g * H, c = threadIdx.x;
+    if (a.held && a.held[(a.map.state(g) / a.n_kv) % a.n_layer] >= a.cap) return;  // as the attention
     double mx = -__builtin_inf();
     for (int s = 0; s < splits; ++s) mx = fmax(mx, a.ws_max[((size_t)g * splits + s) * H + h]);
     double den = 0.0, num = 0.0;
@@ -275,9 +283,12 @@ hipError_t launch_exact_hpk(const ExactIO &a, int splits, hipStream_t stream)
 // One work-group per call index: copy the prompt rows into the mapped group's
 // exact buffers and clear the counters the skeleton mode would have set.
 __global__ __launch_bounds__(256) void exact_seal_kernel(DevState s, PromptView p, GroupMap map, int T,
-                                                         float4 *ek, float4 *ev, int cap)
+                                                         float4 *ek, float4 *ev, int cap, int32_t *held,
+                                                         int l0, int l1)
 {
     const int ci = blockIdx.x, g = map.state(ci), tid = threadIdx.x;
+    if (ci == 0)
+        for (int l = l0 + tid; l < l1; l += 256) held[l] = T;
     const int ck = s.d / 4, cv = s.dv / 4;
     const float4 *k = reinterpret_cast<const float4 *>(p.k_row(map, ci, 0));
     const float4 *v = reinterpret_cast<const float4 *>(p.v_row(map, ci, 0));
@@ -299,13 +310,28 @@ __global__ __launch_bounds__(256) void exact_seal_kernel(DevState s, PromptView 
     }
 }
 
+// The key counts of layers l0 .. l1-1 after an exact-only step: one more key,
+// except for layers already at cap (their step changed nothing).
+__global__ __launch_bounds__(256) void exact_advance_kernel(int32_t *held, int l0, int l1, int cap)
+{
+    for (int l = l0 + (int)threadIdx.x; l < l1; l += 256)
+        if (held[l] < cap) held[l] += 1;
+}
+
 }  // namespace
 
 hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const GroupMap &map, int T,
-                             float *ek, float *ev, int cap, hipStream_t stream)
+                             float *ek, float *ev, int cap, int32_t *held, int l0, int l1,
+                             hipStream_t stream)
 {
     hipLaunchKernelGGL(exact_seal_kernel, dim3(map.count), dim3(256), 0, stream, s, p, map, T,
-                       reinterpret_cast<float4 *>(ek), reinterpret_cast<float4 *>(ev), cap);
+                       reinterpret_cast<float4 *>(ek), reinterpret_cast<float4 *>(ev), cap, held, l0, l1);
+    return hipGetLastError();
+}
+
+hipError_t launch_exact_advance(int32_t *held, int l0, int l1, int cap, hipStream_t stream)
+{
+    hipLaunchKernelGGL(exact_advance_kernel, dim3(1), dim3(256), 0, stream, held, l0, l1, cap);
     return hipGetLastError();
 }
 

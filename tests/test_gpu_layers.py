@@ -5,6 +5,7 @@ sequence.  Both run the same kernels as the whole-handle entry points with a
 different group map, so their outputs and state must equal the whole-handle
 path's bit for bit; a sampled group is also checked against the oracle."""
 import dataclasses
+import gc
 
 import numpy as np
 import pytest
@@ -225,42 +226,100 @@ def test_layer_path_exact_only_equals_whole_handle():
     layered.close()
 
 
-def test_exact_only_whole_step_refuses_unequal_layers():
-    """In the exact-only mode a whole-handle step appends at one key count for
-    every group; after layers were stepped one by one to different counts it is
-    refused (O1_ESTATE) and changes nothing, and it works again once the layers
-    are level."""
-    wl = WL.with_(T=30, steps=3, seed=64)
+def _layer_slices(wl, layer, q, k, v):
+    B, K, H = wl.n_seq, wl.n_kv, wl.hpk
+    idx = torch.tensor(_layer_groups(wl, layer), device=DEV)
+    return (idx, q.index_select(0, idx).view(B, K * H, wl.d).contiguous(),
+            k.index_select(0, idx).view(B, K, wl.d).contiguous(),
+            v.index_select(0, idx).view(B, K, wl.dv).contiguous())
+
+
+def test_exact_only_whole_steps_after_unequal_layers():
+    """Exact-only mode: each group's key count lives on the device, so after
+    layer 0 alone took a step, whole-handle steps append every group at its own
+    count.  They must equal stepping every layer on its own, bit for bit."""
+    wl = WL.with_(T=30, steps=4, seed=64)
     cfg = dataclasses.replace(wl.config, exact_cap=wl.T + 8)
     q, k, v = W.prompt(wl, DEV)
-    grp = P.O1Groups(cfg)
-    grp.prefill(q, k, v)
+    qs, ks, vs = _step_inputs(wl)
+    whole, layered = P.O1Groups(cfg), P.O1Groups(cfg)
     B, K, H, L, G = wl.n_seq, wl.n_kv, wl.hpk, wl.n_layer, wl.groups
-    ql = torch.randn(B, K * H, wl.d, device=DEV)
-    kl = torch.randn(B, K, wl.d, device=DEV)
-    vl = torch.randn(B, K, wl.dv, device=DEV)
-    ol = torch.empty(B, K * H, wl.dv, device=DEV)
-    grp.step_layer(0, ql, kl, vl, ol)  # layer 0 now holds one key more
-    before = [grp.read(f, DEV) for f in (P.FIELD_EXACT_K, P.FIELD_EXACT_V)]
-    qw = torch.randn(G, H, wl.d, device=DEV)
-    kw = torch.randn(G, wl.d, device=DEV)
-    vw = torch.randn(G, wl.dv, device=DEV)
-    out = torch.zeros(G, H, wl.dv, device=DEV)
-    with pytest.raises(P.O1Error) as e:
-        grp.step(qw, kw, vw, out)
-    assert e.value.status == P.O1_ESTATE
+    ob = torch.empty(B, K * H, wl.dv, device=DEV)
+    for grp in (whole, layered):
+        grp.prefill(q, k, v)
+        _, a, b, c = _layer_slices(wl, 0, qs[0], ks[0], vs[0])
+        grp.step_layer(0, a, b, c, ob)  # layer 0 now holds one key more
+    out_w = torch.empty(wl.steps, G, H, wl.dv, device=DEV)
+    out_l = torch.empty_like(out_w)
+    for t in range(1, wl.steps):
+        whole.step(qs[t], ks[t], vs[t], out_w[t])
+        for layer in range(L):
+            idx, a, b, c = _layer_slices(wl, layer, qs[t], ks[t], vs[t])
+            layered.step_layer(layer, a, b, c, ob)
+            out_l[t].index_copy_(0, idx, ob.view(B * K, H, wl.dv))
     torch.cuda.synchronize()
-    for b, f in zip(before, (P.FIELD_EXACT_K, P.FIELD_EXACT_V)):
-        assert torch.equal(grp.read(f, DEV), b), f
-    assert not out.any()
-    for l in range(1, L):  # level the other layers, then a whole step is valid
-        grp.step_layer(l, ql, kl, vl, ol)
-    grp.step(qw, kw, vw, out)
-    torch.cuda.synchronize()
-    info = grp.info()
-    assert info.exact_keys == wl.T + 2 and info.steps == 2 and info.max_steps == 2
-    assert torch.isfinite(out).all()
-    grp.close()
+    assert torch.equal(out_w[1:], out_l[1:])
+    cap = cfg.exact_cap
+    for f, width in ((P.FIELD_EXACT_K, wl.d), (P.FIELD_EXACT_V, wl.dv)):
+        a, b = (h.read(f, DEV).view(G, cap, width) for h in (whole, layered))
+        for layer in range(L):  # rows past a group's keys were never written
+            held = wl.T + wl.steps - (0 if layer == 0 else 1)
+            idx = torch.tensor(_layer_groups(wl, layer), device=DEV)
+            assert torch.equal(a.index_select(0, idx)[:, :held], b.index_select(0, idx)[:, :held]), (f, layer)
+    info = whole.info()
+    assert (info.steps, info.max_steps, info.exact_keys) == (wl.steps - 1, wl.steps, wl.T + wl.steps)
+    whole.close()
+    layered.close()
+
+
+def test_exact_only_graph_replays_match_eager_and_stop_at_cap():
+    """A whole-handle exact-only step captured in a HIP graph: every replay
+    reads the key count from the device, so replays with eager input copies
+    and synchronisation between them equal the eager steps of a twin handle;
+    once the groups hold exact_cap keys a replay changes nothing and writes no
+    output (the eager twin is refused with O1_EFULL)."""
+    wl = WL.with_(T=30, steps=5, seed=65)
+    room = 3  # keys the cap leaves after the prompt
+    cfg = dataclasses.replace(wl.config, exact_cap=wl.T + room)
+    q, k, v = W.prompt(wl, DEV)
+    qs, ks, vs = _step_inputs(wl)
+    G, H = wl.groups, wl.hpk
+    eager, graphed = P.O1Groups(cfg), P.O1Groups(cfg)
+    eager.prefill(q, k, v)
+    graphed.prefill(q, k, v)
+    sq, sk, sv = torch.empty_like(qs[0]), torch.empty_like(ks[0]), torch.empty_like(vs[0])
+    out_g = torch.empty(G, H, wl.dv, device=DEV)
+    out_e = torch.empty_like(out_g)
+    with P.O1Groups(cfg) as warm:  # first launch of this shape outside the capture
+        warm.prefill(q, k, v)
+        warm.step(qs[0], ks[0], vs[0], out_e)
+        torch.cuda.synchronize()
+    gc.collect()  # finalise leftover objects now: destroying a graph during a capture aborts
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graphed.step(sq, sk, sv, out_g)
+    for t in range(wl.steps):
+        status = P.O1_OK
+        try:  # (the except target is unbound on exit: no frame cycle keeps the graph alive)
+            eager.step(qs[t], ks[t], vs[t], out_e)
+        except P.O1Error as err:
+            status = err.status
+        assert status == (P.O1_OK if t < room else P.O1_EFULL), t
+        sq.copy_(qs[t])
+        sk.copy_(ks[t])
+        sv.copy_(vs[t])
+        out_g.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        if t < room:
+            assert torch.equal(out_g, out_e), t
+        else:
+            assert (out_g == 7.0).all(), t
+    for f in (P.FIELD_EXACT_K, P.FIELD_EXACT_V):
+        assert torch.equal(graphed.read(f, DEV), eager.read(f, DEV)), f
+    del graph  # destroyed here, outside any capture
+    eager.close()
+    graphed.close()
 
 
 def test_graph_replay_of_layer_steps_matches_eager():
@@ -289,6 +348,7 @@ def test_graph_replay_of_layer_steps_matches_eager():
         a, b, c = token_inputs(0)
         warm.step_layer(0, a[0], b[0], c[0], out_e[0])
         torch.cuda.synchronize()
+    gc.collect()  # finalise leftover objects now: destroying a graph during a capture aborts
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for l in range(L):
