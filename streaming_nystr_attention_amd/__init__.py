@@ -163,6 +163,27 @@ def o1_destroy_groups(handle):
     lib().o1_destroy_groups(handle)
 
 
+# Handles released while the current stream was capturing a HIP graph: freeing
+# device memory then would invalidate the capture (a garbage-collection pass can
+# run a finaliser at any point), so they are destroyed later, outside a capture.
+_DEFERRED_HANDLES: list = []
+
+
+def _capturing() -> bool:
+    import torch
+
+    try:
+        return torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
+    except Exception:
+        return False
+
+
+def _drain_deferred():
+    if _DEFERRED_HANDLES and not _capturing():
+        while _DEFERRED_HANDLES:
+            o1_destroy_groups(_DEFERRED_HANDLES.pop())
+
+
 def o1_prefill(handle, cfg, q, k, v, T: int, frozen=None, stream=None):
     G = cfg.groups
     # an exact-only prefill does not read q; None is accepted for it
@@ -351,14 +372,20 @@ class O1Groups:
     """Owns one library handle: the state of cfg.groups independent groups."""
 
     def __init__(self, cfg: Config):
+        _drain_deferred()
         self.cfg = cfg
         self._h = o1_create_groups(cfg)
         self.T = None
 
     def close(self):
-        if getattr(self, "_h", None) is not None and self._h.value:
-            o1_destroy_groups(self._h)
+        h = getattr(self, "_h", None)
         self._h = None
+        if h is not None and h.value:
+            if _capturing():
+                _DEFERRED_HANDLES.append(h)  # destroyed once no capture is running
+            else:
+                o1_destroy_groups(h)
+        _drain_deferred()
 
     def __del__(self):
         try:

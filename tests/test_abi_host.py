@@ -145,3 +145,28 @@ def test_exact_comparator_validation_without_device():
     assert n.value == 8 * (4 * 8 * 2 * (128 + 2))
     assert L.o1_exact_attend(ctypes.byref(desc), None, None, None, None, None, 0, None) == 1
     assert L.o1_exact_workspace_bytes(None, ctypes.byref(n)) == 1
+
+
+def test_handle_released_during_a_capture_is_destroyed_later(monkeypatch):
+    """A handle closed (or finalised by a garbage-collection pass) while the
+    current stream is capturing a HIP graph is queued instead of freed, and
+    destroyed at the next close or create outside a capture."""
+    import ctypes
+
+    import streaming_nystr_attention_amd as P
+
+    destroyed = []
+    monkeypatch.setattr(P, "o1_destroy_groups", lambda h: destroyed.append(h.value))
+    capturing = [True]
+    monkeypatch.setattr(P, "_capturing", lambda: capturing[0])
+    grp = object.__new__(P.O1Groups)
+    grp._h = ctypes.c_void_p(0x1234)
+    grp.close()
+    assert destroyed == [] and [h.value for h in P._DEFERRED_HANDLES] == [0x1234]
+    grp.close()  # closing again neither frees nor queues twice
+    assert destroyed == [] and len(P._DEFERRED_HANDLES) == 1
+    capturing[0] = False
+    other = object.__new__(P.O1Groups)
+    other._h = ctypes.c_void_p(0x5678)
+    other.close()
+    assert destroyed == [0x5678, 0x1234] and P._DEFERRED_HANDLES == []
