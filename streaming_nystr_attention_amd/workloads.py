@@ -159,8 +159,8 @@ def decode_inputs(wl: Workload, step: int, device, out=None):
 
 def sample_groups(wl: Workload, extra: int = 4) -> list[int]:
     """Groups whose outputs the oracle recomputes at full size: sequences
-    {0, 1, B/2, B-1} x layers {0, L/2, L-1} x KV heads {0, K-1} (first, middle
-    and last of each axis), plus `extra` seeded groups."""
+    {0, 1, B/2, B-1} x layers {0, L/2, L-1} x KV heads {0, K-1}, plus `extra`
+    seeded groups."""
     B, L, K = wl.n_seq, wl.n_layer, wl.n_kv
     seqs = sorted({0, min(1, B - 1), B // 2, B - 1})
     picks = []
