@@ -75,7 +75,8 @@ struct DecodeShape {
     static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512;
     // at least three waves per SIMD on large grids (at most 168 VGPRs)
     static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
-    static constexpr int RED_CAP = 16384 / (NW * DV * 8);              // heads per LDS round
+    // heads per LDS round of the final reduction (one work-group per CU: room for all)
+    static constexpr int RED_CAP = (STREAM_ROWS ? 65536 : 16384) / (NW * DV * 8);
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
     static_assert(HPK <= LPR, "the head reduction needs at least hpk lanes per row");
