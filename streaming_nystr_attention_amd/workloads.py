@@ -171,3 +171,23 @@ def sample_groups(wl: Workload, extra: int = 4) -> list[int]:
     g = torch.Generator().manual_seed(wl.seed * 7919 + 17)
     picks += torch.randint(0, wl.groups, (extra,), generator=g).tolist()
     return sorted(set(picks))
+
+
+def sample_sequences(wl: Workload, extra: int = 4) -> list[int]:
+    """Sequences {0, 1, B/2, B-1} plus `extra` further seeded sequences (fewer when
+    the batch has no more)."""
+    B = wl.n_seq
+    seqs = {0, min(1, B - 1), B // 2, B - 1}
+    want = min(B, len(seqs) + extra)
+    g = torch.Generator().manual_seed(wl.seed * 7919 + 29)
+    for s in torch.randperm(B, generator=g).tolist():
+        if len(seqs) >= want:
+            break
+        seqs.add(s)
+    return sorted(seqs)
+
+
+def groups_of_sequences(wl: Workload, seqs) -> list[int]:
+    """Every group (all layers and KV heads) of the given sequences, in group order."""
+    per = wl.n_layer * wl.n_kv
+    return [s * per + i for s in sorted(seqs) for i in range(per)]

@@ -103,7 +103,9 @@ class DecodeRun:
         self.v = torch.empty(steps, n, wl.dv, device=dev)
         self.out = torch.empty(steps, n, wl.hpk, wl.dv, device=dev)
 
-    def run(self, grp, dev="cuda"):
+    def run(self, grp, dev="cuda", to_host=True):
+        """Step `grp` through every step's inputs, keeping the sampled groups' inputs
+        and outputs on the device; with `to_host` returns them all as host arrays."""
         wl = self.wl
         G = wl.groups
         qb = torch.empty(G, wl.hpk, wl.d, device=dev)
@@ -120,7 +122,14 @@ class DecodeRun:
             self.out[t] = ob.index_select(0, self.idx)
         torch.cuda.synchronize()
         say(f"  gpu decode {self.steps} steps x {G} groups: {time.time() - t0:.2f}s")
-        return cpu(self.q), cpu(self.k), cpu(self.v), cpu(self.out).astype(np.float64)
+        if to_host:
+            return self.host(0, len(self.sample))
+
+    def host(self, c0, c1):
+        """Host copies of sampled groups c0..c1-1: q, k, v (f32) and the outputs (f64)."""
+        s = slice(c0, c1)
+        return (cpu(self.q[:, s]), cpu(self.k[:, s]), cpu(self.v[:, s]),
+                cpu(self.out[:, s]).astype(np.float64))
 
 
 def frozen_tensors_with_oracle(grp, wl, sample, orc_groups, dev="cuda"):
@@ -142,6 +151,7 @@ def frozen_tensors_with_oracle(grp, wl, sample, orc_groups, dev="cuda"):
 
 DEV = "cuda"
 RESID_TOL = 1e-3
+CHUNK_BYTES = 1 << 29
 
 
 def stack_frozen(orc_groups):
@@ -176,11 +186,23 @@ def decode_parity(wl, sample=None, steps=None, rect=O.RECT_AGGREGATE, frozen_ove
     grp.prefill(q, k, v, frozen=frozen)
     del q, k, v, frozen
     run = DecodeRun(wl, sample, steps)
-    qs, ks, vs, gout = run.run(grp)
-    out, alt, amb = oracle_decode(orc, qs, ks, vs)
-    err = row_errors(gout, out, alt, amb)
+    run.run(grp, to_host=False)
+    # compare in chunks of groups so the host holds at most ~CHUNK_BYTES of f64 outputs
+    n = len(sample)
+    per_group = max(1, steps * wl.hpk * wl.dv * 8)
+    cg = max(1, min(n, CHUNK_BYTES // per_group))
+    errs, n_amb, t0 = [], 0, time.time()
+    for c0 in range(0, n, cg):
+        c1 = min(n, c0 + cg)
+        qs, ks, vs, gout = run.host(c0, c1)
+        out, alt, amb = oracle_decode(orc[c0:c1], qs, ks, vs)
+        errs.append(row_errors(gout, out, alt, amb))
+        n_amb += int(amb.sum())
+        del qs, ks, vs, gout, out, alt, amb
+    del run
+    err = np.concatenate(errs, axis=1)
     say(f"  rows={err.size} max_err={err.max():.3e} median={np.median(err):.3e} "
-        f"ambiguous={int(amb.sum())}")
+        f"ambiguous={n_amb} oracle decode {time.time() - t0:.1f}s")
 
     # counters of every group, bit-exact
     E = wl.T - wl.sink - wl.w + steps

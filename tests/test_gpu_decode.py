@@ -39,21 +39,31 @@ def test_decode_qwen3_layer():
     decode_parity(W.WORKLOADS["qwen3_layer"])
 
 
+def seq_sample(wl):
+    """Every group of sequences {0, 1, B/2, B-1} and 4 seeded ones: all layers, KV
+    heads, query heads and steps of those sequences."""
+    return W.groups_of_sequences(wl, W.sample_sequences(wl))
+
+
 @pytest.mark.parametrize("name", [f"stress_m{m}_s{s}" for m in (8, 16, 32) for s in (0, 4)])
 def test_decode_stress(name):
+    # 64 of 2048 groups, 8192 steps each
     wl = W.WORKLOADS[name]
-    decode_parity(wl, sample=W.sample_groups(wl, extra=2))
+    decode_parity(wl, sample=seq_sample(wl))
 
 
-def test_decode_wide_gqa():
+@pytest.mark.parametrize("part", range(4))
+def test_decode_wide_gqa_all_groups(part):
+    # every group of the wide GQA workload, all 2048 steps, in four parts of 8 sequences
     wl = W.WORKLOADS["wide_gqa"]
-    decode_parity(wl, sample=[0, 1, 7, 8, 128, 200, 255])
+    n = wl.groups // 4
+    decode_parity(wl, sample=list(range(part * n, (part + 1) * n)))
 
 
 def test_decode_qwen3_stack_full_size():
-    # the bench workload: 64 x 28 x 8 groups, 1024 steps, sampled outputs
+    # the bench workload: 64 x 28 x 8 groups, 1024 steps; 8 whole sequences (1792 groups)
     wl = W.WORKLOADS["qwen3_stack_b64"]
-    decode_parity(wl, sample=W.sample_groups(wl, extra=4))
+    decode_parity(wl, sample=seq_sample(wl))
 
 
 # ---- edge cases ----------------------------------------------------------

@@ -37,19 +37,25 @@ def test_prefill_qwen3_layer():
     prefill_parity(W.WORKLOADS["qwen3_layer"])
 
 
+def seq_sample(wl):
+    """Every group of sequences {0, 1, B/2, B-1} and 4 seeded ones."""
+    return W.groups_of_sequences(wl, W.sample_sequences(wl))
+
+
 @pytest.mark.parametrize("name", ["stress_m8_s0", "stress_m16_s4", "stress_m32_s4"])
 def test_prefill_stress(name):
     wl = W.WORKLOADS[name]
-    prefill_parity(wl, sample=W.sample_groups(wl, extra=2))
+    prefill_parity(wl, sample=seq_sample(wl))
 
 
 def test_prefill_wide_gqa():
-    prefill_parity(W.WORKLOADS["wide_gqa"], sample=[0, 5, 131, 255])
+    # every group
+    prefill_parity(W.WORKLOADS["wide_gqa"])
 
 
 def test_prefill_qwen3_stack_full_size():
     wl = W.WORKLOADS["qwen3_stack_b64"]
-    prefill_parity(wl, sample=W.sample_groups(wl, extra=4))
+    prefill_parity(wl, sample=seq_sample(wl))
 
 
 def test_prefill_ragged_segments():
