@@ -42,13 +42,13 @@ if ROOT not in sys.path:
 METRIC = "Nyström decode group-steps/sec & tokens/s at 1 GPU; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 DECODE_SRC = [os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", f)
-              for f in ("o1_decode.hip", "o1_internal.h")]
+              for f in ("o1_decode.hip", "o1_internal.h")] + [os.path.join(ROOT, "include", "o1.h")]
 # HBM bytes per decode launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by
 # a 1 GiB copy in the same process), keyed by (workload, sha256 prefix of the decode
 # kernel's sources).
 # A changed kernel (comments aside) has no entry, and the roofline's traffic is then null.
 MEASURED_TRAFFIC = {
-    ("qwen3_stack_b64", "ce9476b7dbe46b9c"): 3788472057,
+    ("qwen3_stack_b64", "115163c5bde795d6"): 3448464059,
 }
 
 
@@ -68,18 +68,31 @@ def decode_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def decode_bytes_per_group_step(wl) -> tuple[int, int]:
-    """Algorithmic HBM bytes of one group-step: each stored value read once,
-    each modified value written once (f32 state, Z^ f64, far_len i64)."""
+def decode_bytes_per_group_step(wl) -> tuple[float, float]:
+    """Algorithmic HBM bytes of one group-step, averaged over a fold period:
+    each stored value read once, each modified value written once (f32 state,
+    Z^ and held logits f64, far_len i64).
+
+    T^ is read every step and written on the fold step only (once per
+    FOLD_PERIOD = K steps).  A step with P evictions held (P = 0 .. K-1, each
+    equally often) reads their value rows and logits; a step that does not fold
+    writes its own eviction's row and logits into the held set."""
+    from streaming_nystr_attention_amd import FOLD_PERIOD as K
+
     S, w, d, dv, m, H = wl.sink, wl.w, wl.d, wl.dv, wl.m_eff, wl.hpk
+    held = dv * 4 + H * m * 8                # one held eviction: value row, logits per head
     read = ((S + w) * (d + dv) * 4           # sinks + ring rows
             + m * d * 4                      # key landmarks
             + H * (m * d * 4 + m * m * 4     # per head: query landmarks, M
-                   + m * dv * 4 + m * 8 + m * 4)  # T^, Z^ (f64), running max
+                   + m * dv * 4 + m * 8      # T^, Z^ (f64)
+                   + m * 4 + m * 4)          # running max, its value at the last fold
+            + (K - 1) / 2 * held             # the held evictions
             + (H * d + d + dv) * 4           # inputs q, k, v
             + 4 + H * 8)                     # win_head, far_len
     write = ((d + dv) * 4                    # the new ring row
-             + H * (m * dv * 4 + m * 8 + m * 4)  # T^, Z^, running max
+             + H * (m * 8 + m * 4)           # Z^, running max
+             + H * (m * dv * 4 + m * 4) / K  # T^ and its max, on the fold step
+             + (K - 1) / K * held            # this eviction joins the held set
              + H * dv * 4                    # outputs
              + 4 + H * 8)
     return read, write

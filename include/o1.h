@@ -49,6 +49,15 @@ enum o1_status {
     O1_EFULL = 7         /* an exact-only group would exceed exact_cap keys           */
 };
 
+/* The decode step keeps the value row and per-landmark logits of up to
+ * O1_FOLD_PERIOD - 1 evicted keys apart from each head's far numerator T^
+ * (NystromHead::far_insert on the nystrom.rs source page adds every evicted key
+ * to T^ at once) and adds them all to T^ with every O1_FOLD_PERIOD-th eviction,
+ * so T^, otherwise the step's largest write, is rewritten once per
+ * O1_FOLD_PERIOD steps.  Outputs are those of the per-eviction update up to
+ * rounding.  A group's held count is its far_len mod O1_FOLD_PERIOD. */
+#define O1_FOLD_PERIOD 8
+
 /* O1Rect of the nystrom.rs source page: how the indefinite skeleton is
  * rectified.  AGGREGATE (the page's default) drops a row's far field when its
  * far denominator is negative; FM clamps the mixing row u = F M at zero. */
@@ -251,8 +260,13 @@ int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes);
 
 /* Copy a whole state field to `dst` / from `src` (host or device memory;
  * `bytes` must equal o1_field_bytes), enqueued on `stream`.  For tests and
- * state transfer; the decode path never needs them.  Writing requires a
- * sealed layer.  Errors: O1_EINVAL, O1_ESTATE, O1_EHIP. */
+ * state transfer; the decode path never needs them.  Reading O1_FIELD_T_HAT
+ * returns T^ with the held evictions (O1_FOLD_PERIOD) added, built in a
+ * stream-ordered temporary; the state is left as it is.  Every write first
+ * adds the held evictions to the stored T^ (none are held afterwards), and a
+ * write of O1_FIELD_M_MAX takes the stored T^ to be at the new running max.
+ * Writing requires a sealed layer.
+ * Errors: O1_EINVAL, O1_ESTATE, O1_ENOMEM (the T^ temporary), O1_EHIP. */
 int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, void *stream);
 int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, void *stream);
 

@@ -21,6 +21,8 @@ RECT_AGGREGATE, RECT_FM = 0, 1
  FIELD_M_MAX, FIELD_WIN_HEAD, FIELD_FAR_LEN, FIELD_LAMBDA, FIELD_TRIES, FIELD_EXACT_K,
  FIELD_EXACT_V) = range(14)
 FIELD_COUNT = 14
+# evictions are added to T^ together, once per FOLD_PERIOD decode steps (O1_FOLD_PERIOD)
+FOLD_PERIOD = 8
 
 _STATUS_NAMES = {0: "O1_OK", 1: "O1_EINVAL", 2: "O1_ESTATE", 3: "O1_EEXACT", 4: "O1_ENOMEM",
                  5: "O1_EHIP", 6: "O1_EUNSUPPORTED", 7: "O1_EFULL"}

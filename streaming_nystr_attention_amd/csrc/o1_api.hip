@@ -2,7 +2,8 @@
 // allocation (once, at o1_create_groups), stream-ordered launches, and field
 // copies for tests.  No entry point synchronises with the host, except that a
 // prefill needing a larger work buffer than it holds waits for its stream
-// before freeing the old one.
+// before freeing the old one, and o1_create_groups waits for the clearing of
+// its new state's held value rows.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -128,9 +129,10 @@ bool landmark_shaped(int32_t field)
 void free_state(o1_groups *g)
 {
     o1::DevState &s = g->st;
-    void *ptrs[] = {s.near_k, s.near_v, s.k_tilde, s.q_tilde, s.mu,     s.t_hat,
-                    s.z_hat,  s.m_max,  s.win_head, s.far_len, s.lambda, s.tries,
-                    g->lm64,  g->exact_k, g->exact_v, g->exact_ws, g->exact_held};
+    void *ptrs[] = {s.near_k, s.near_v,   s.k_tilde,  s.q_tilde,  s.mu,       s.t_hat,
+                    s.z_hat,  s.m_max,    s.win_head, s.far_len,  s.lambda,   s.tries,
+                    s.pend_v, s.pend_l,   s.m_ref,    g->lm64,    g->exact_k, g->exact_v,
+                    g->exact_ws, g->exact_held};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
 }
@@ -413,6 +415,9 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         {(void **)&s.far_len, Gs * H * sizeof(int64_t)},
         {(void **)&s.lambda, Gs * H * sizeof(double)},
         {(void **)&s.tries, Gs * H * sizeof(int32_t)},
+        {(void **)&s.pend_v, Gs * o1::kPend * c.dv * sizeof(float)},
+        {(void **)&s.pend_l, Gs * H * o1::kPend * M * sizeof(double)},
+        {(void **)&s.m_ref, Gs * H * M * sizeof(float)},
         {(void **)&g->exact_k, Gs * E * c.d * sizeof(float)},
         {(void **)&g->exact_v, Gs * E * c.dv * sizeof(float)},
         {(void **)&g->exact_ws, ws_bytes},
@@ -428,6 +433,16 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
             return fail(O1_ENOMEM, "hipMalloc of %zu bytes failed", a.bytes);
         }
         total += a.bytes;
+    }
+    // held value rows start at zero: a slot the held count does not cover is
+    // never read, and an empty covered slot (logits -inf) weighs 0, which must
+    // not meet a non-finite row
+    if (hipMemsetAsync(s.pend_v, 0, Gs * o1::kPend * c.dv * sizeof(float), nullptr) != hipSuccess ||
+        hipStreamSynchronize(nullptr) != hipSuccess) {
+        (void)hipGetLastError();
+        free_state(g);
+        delete g;
+        return fail(O1_EHIP, "clearing the held value rows failed");
     }
     g->state_bytes = total;
     *out = g;
@@ -552,8 +567,24 @@ int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, vo
     if (bytes != want) return fail(O1_EINVAL, "field %d holds %zu bytes, not %zu", field, want, bytes);
     DeviceScope dev(g);
     if ((rc = dev.status())) return rc;
-    hipError_t err = hipMemcpyAsync(dst, field_info(g, field).ptr, bytes, hipMemcpyDefault,
-                                    (hipStream_t)stream);
+    const hipStream_t st = (hipStream_t)stream;
+    if (field == O1_FIELD_T_HAT) {
+        // T^ with the held evictions folded in, built in a stream-ordered
+        // temporary; the state itself is left as it is
+        void *tmp = nullptr;
+        hipError_t err = hipMallocAsync(&tmp, bytes, st);
+        if (err != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(O1_ENOMEM, "hipMallocAsync of %zu bytes failed: %s", bytes, hipGetErrorString(err));
+        }
+        err = o1::launch_fold(g->st, static_cast<float *>(tmp), false, st);
+        if (err == hipSuccess) err = hipMemcpyAsync(dst, tmp, bytes, hipMemcpyDefault, st);
+        const hipError_t ferr = hipFreeAsync(tmp, st);
+        if (err == hipSuccess) err = ferr;
+        if (err != hipSuccess) return fail(O1_EHIP, "reading T^ failed: %s", hipGetErrorString(err));
+        return ok();
+    }
+    hipError_t err = hipMemcpyAsync(dst, field_info(g, field).ptr, bytes, hipMemcpyDefault, st);
     if (err != hipSuccess) return fail(O1_EHIP, "hipMemcpyAsync failed: %s", hipGetErrorString(err));
     return ok();
 }
@@ -568,9 +599,17 @@ int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, v
     if (bytes != want) return fail(O1_EINVAL, "field %d holds %zu bytes, not %zu", field, want, bytes);
     DeviceScope dev(g);
     if ((rc = dev.status())) return rc;
-    hipError_t err = hipMemcpyAsync(field_info(g, field).ptr, src, bytes, hipMemcpyDefault,
-                                    (hipStream_t)stream);
-    if (err != hipSuccess) return fail(O1_EHIP, "hipMemcpyAsync failed: %s", hipGetErrorString(err));
+    const hipStream_t st = (hipStream_t)stream;
+    o1::DevState &s = g->st;
+    hipError_t err = hipSuccess;
+    // fold the held evictions into T^ first, so that what is written meets a
+    // state with none held (T^ at scale e^{-m_max})
+    if (s.m > 0) err = o1::launch_fold(s, s.t_hat, true, st);
+    if (err == hipSuccess) err = hipMemcpyAsync(field_info(g, field).ptr, src, bytes, hipMemcpyDefault, st);
+    // T^ is stored at the scale of the running max it was written against
+    if (err == hipSuccess && field == O1_FIELD_M_MAX)
+        err = hipMemcpyAsync(s.m_ref, s.m_max, bytes, hipMemcpyDeviceToDevice, st);
+    if (err != hipSuccess) return fail(O1_EHIP, "writing field %d failed: %s", field, hipGetErrorString(err));
     return ok();
 }
 

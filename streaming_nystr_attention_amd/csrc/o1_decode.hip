@@ -8,11 +8,14 @@
 //
 //   0. prologue, small loads staged into LDS: the ring head e = win_head, the
 //      queries, the new k/v, the evicted ring row (row sink+e), each head's
-//      running max and Z^, and (small shapes) each head's mixing matrix M.
-//      (Each staging loop waits for its own loads; issuing them all first
-//      measured slower on large launches, whose work-groups overlap anyway.)
-//      Then row sink+e is overwritten by the new k/v (advance); nothing reads
-//      that row from global memory afterwards.
+//      running max, its value at the last fold and Z^, (small shapes) each
+//      head's mixing matrix M, and the held evictions (kPend): with P =
+//      far_len mod kPend, the value rows and logits of slots j < P, whose
+//      logits become weights e^{l - m_max} against the running max before
+//      this step.  (Each staging loop waits for its own loads; issuing them
+//      all first measured slower on large launches, whose work-groups overlap
+//      anyway.)  Then row sink+e is overwritten by the new k/v (advance); the
+//      evicted value row joins the held set (slot P) unless this step folds.
 //   1. row-dot pass, f64 accumulation, each row split over LPR lanes and UNR
 //      rows per lane in flight:
 //        near logits  lg[h][r] = q_h . k_r * scale       (sink + w rows, all heads)
@@ -25,19 +28,26 @@
 //      T^ rows and the first V rows this thread contracts later are loaded at
 //      the end of the pass, so their latency overlaps step 2.
 //   2. per head (one wave): c = max lg, f = max s, fh = e^{s - f}; running-max
-//      update for the evicted key (NystromHead::far_insert): r_i, e_i, Z^ and
-//      m_max written back; u = fh . M; c_all = max(c, f + m_max); gain =
-//      u e^{f + m_max - c_all}; far_den = gain . Z^; aggregate rectifier; near
-//      weights p = e^{lg - shift} and the joint denominator.
-//   3. column pass, one float4 column chunk per lane: T^ <- T^ r + e v_e written
-//      back and contracted with gain in the same pass; V rows contracted with p.
+//      update for the evicted key (NystromHead::far_insert): Z^ and m_max
+//      written back, the held weights moved to the new max, the eviction's
+//      logit stored in slot P (or, on a fold, m_ref = m_max); u = fh . M;
+//      c_all = max(c, f + m_max); gain = u e^{f + m_max - c_all}; far_den =
+//      gain . Z^; aggregate rectifier; near weights p = e^{lg - shift} and the
+//      joint denominator.  Between folds each held row and the eviction's row
+//      get one coefficient sum_i gain_i w_ij (a wave sum per row).
+//   3. column pass, one float4 column chunk per lane: the far numerator
+//      gain . T^ with T^ = e^{m_ref - m_max} t_hat + sum_j w_j v_j -- between
+//      folds t_hat is only read and the held rows are contracted with their
+//      coefficients; on a fold t_hat is rebuilt at the new max and written
+//      back -- then the V rows contracted with p.
 //   4. reduce the row lanes (lane swaps within a wave, LDS across waves), one
 //      division per output, counters.
-// HBM traffic: each group's state read once and its modified part (one ring
-// row, T^, Z^, m_max, counters) written once.
+// HBM traffic: each group's state read once; the ring row, Z^, m_max, the held
+// slot and the counters written every step, t_hat once per kPend steps.
 //
 // Work-group size: 256 threads when the launch has many groups (several
-// work-groups per CU hide each other's latency), 512 when it has few.
+// work-groups per CU hide each other's latency), 512 when it has few or when
+// the shape's LDS allows only one work-group per CU anyway (hpk * m >= 512).
 // A launch covers the groups of a GroupMap: the whole handle, or one layer of
 // every sequence; inputs and outputs are indexed by the launch's own index.
 #include <atomic>
@@ -65,7 +75,8 @@ struct DecodeShape {
     static constexpr int TPT = (MM + RL - 1) / RL;                     // T^ rows per lane per head
     static constexpr bool STAGE_M = HPK * MM * MM <= 2048;             // M staged in LDS
     static constexpr bool PRE_T = HPK * TPT <= (NT == 256 ? 8 : 32);   // T^ prefetched in registers
-    static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : 8;    // V rows prefetched per lane
+    // V rows prefetched per lane (6 where 8 would spill at 256 VGPRs)
+    static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : (HPK * MM >= 512 ? 6 : 8);
     static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
     static constexpr int MB = NT == 256 ? 16 : 32;                     // M rows in flight (unstaged M)
     static constexpr bool NTL = NT == 256;                             // streaming accesses (large grids)
@@ -73,16 +84,22 @@ struct DecodeShape {
     // stream over every row it reads, two batches per round trip, with the
     // queries in f64 registers.
     static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512;
+    static constexpr int HL = (HPK * kPend * MM + NT - 1) / NT;       // held logits per thread
     // at least three waves per SIMD on large grids (at most 168 VGPRs)
     static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
     // heads per LDS round of the final reduction (one work-group per CU: room for all)
     static constexpr int RED_CAP = (STREAM_ROWS ? 65536 : 16384) / (NW * DV * 8);
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
+    // the final reduction's buffer also holds the held weights (steps 0-3)
+    static constexpr int RED_N = NW * RED_H * DV, WF_N = HPK * kPend * MM;
+    static constexpr int SHARE_N = RED_N > WF_N ? RED_N : WF_N;
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
     static_assert(HPK <= LPR, "the head reduction needs at least hpk lanes per row");
     static_assert(64 % VCH == 0, "value rows must tile a wave");
     static_assert(CH <= 64 && VCH <= 64, "rows wider than 256 floats are not compiled");
     static_assert(RED_H >= 1 && HPK % RED_H == 0, "heads must split into reduction rounds");
+    static_assert(RL >= kPend, "each held value row needs a row lane of its own");
+    static_assert((kPend - 1) * VCH <= NT, "one held value float4 per thread");
 };
 
 template <int D, int DV, int HPK, int MM, int NT>
@@ -99,28 +116,50 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
     __shared__ float4 q_s[HPK][C::CH];
     __shared__ float4 kn_s[C::CH], ke_s[C::CH];
     __shared__ float4 vn_s[C::VCH], ve_s[C::VCH];
+    __shared__ float4 hv_s[kPend - 1][C::VCH];     // value rows of the held evictions (slots j < P)
     __shared__ float mo_s[HPK][MM];                // running max before this step
+    __shared__ float mr_s[HPK][MM];                // running max at the last fold (scale of t_hat)
     __shared__ double zo_s[HPK][MM];               // Z^ before this step
     __shared__ float mu_s[C::STAGE_M ? HPK * MM * MM : 1];
     __shared__ double land_s[HPK][MM];             // landmark logits
     __shared__ double lf_s[HPK][MM];               // far-insert logits
-    __shared__ double r_s[HPK][MM];                // T^ rescale factor per landmark
-    __shared__ double e_s[HPK][MM];                // weight of the evicted key per landmark
-    __shared__ double gain_s[HPK][MM];             // far mixing gains (0 when dropped)
+    __shared__ double r_s[HPK][MM];                // fold: stored t_hat -> new max, per landmark
+    __shared__ double cj_s[HPK][kPend];            // held slot j (and this eviction, slot P): sum_i gain_i w_ij
+    __shared__ double gain_s[HPK][MM];             // far mixing gains (0 when dropped), times r between folds
     __shared__ double fh_s[C::STAGE_M ? HPK : 1][MM];  // landmark weights e^{s - f} (0 past m)
     __shared__ double den_s[HPK];
-    __shared__ double red_s[C::NW][C::RED_H * DV];
+    // held logits, then their weights at the new max, [HPK][kPend][MM] (steps 0-3);
+    // then the reduction across waves, [NW][RED_H * DV] (step 4)
+    __shared__ double share_s[C::SHARE_N];
+    auto wf_s = reinterpret_cast<double (*)[kPend][MM]>(share_s);
+    auto red_s = reinterpret_cast<double (*)[C::RED_H * DV]>(share_s);
     extern __shared__ double lg_s[];               // [HPK][R] near logits, then weights
 
     const size_t gh0 = (size_t)g * HPK;  // first head of this group
     const int e = s.win_head[g];
     const int slot_row = S + e;
+    // evictions held apart from t_hat before this step, and whether this
+    // step's eviction completes the set (then all are folded into t_hat)
+    const int P = (int)((uint64_t)s.far_len[gh0] % kPend);
+    const bool fold = P == kPend - 1;
 
     float4 *nk = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * R * C::CH;
     float4 *nv = reinterpret_cast<float4 *>(s.near_v) + (size_t)g * R * C::VCH;
 
     // ---- 0. prologue: small loads staged into LDS ---------------------------
     {
+        // held evictions, slots j < P: loads issued first, stored at the end
+        float4 hvr = make_float4(0.f, 0.f, 0.f, 0.f);
+        const bool hv_mine = tid < P * C::VCH;
+        if (hv_mine) hvr = ld4<C::NTL>(reinterpret_cast<const float4 *>(s.pend_v) + (size_t)g * kPend * C::VCH + tid);
+        double hlr[C::HL];
+        const int nl = HPK * kPend * m;  // [h][j][a] block of this group
+#pragma unroll
+        for (int u = 0; u < C::HL; ++u) {
+            const int i = tid + u * NT;
+            hlr[u] = 0.0;
+            if (i < nl && (i / m) % kPend < P) hlr[u] = s.pend_l[gh0 * kPend * m + i];
+        }
         const float4 *qg = reinterpret_cast<const float4 *>(io.q) + (size_t)ci * HPK * C::CH;
         for (int i = tid; i < HPK * C::CH; i += NT) (&q_s[0][0])[i] = qg[i];
         if (tid < C::CH) {
@@ -135,16 +174,31 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
         for (int i = tid; i < HPK * m; i += NT) {
             const int h = i / m, a = i - h * m;
             mo_s[h][a] = s.m_max[gh0 * m + i];
+            mr_s[h][a] = s.m_ref[gh0 * m + i];
             zo_s[h][a] = s.z_hat[gh0 * m + i];
         }
         if constexpr (C::STAGE_M) {
             const float *mu = s.mu + gh0 * (size_t)m * m;
             for (int i = tid; i < HPK * m * m; i += NT) mu_s[i] = mu[i];
         }
+        if (hv_mine) (&hv_s[0][0])[tid] = hvr;
+        __syncthreads();
+        // held weights at the running max before this step (at most 1: the
+        // max covers every held logit); step 2 rescales them to the new max
+#pragma unroll
+        for (int u = 0; u < C::HL; ++u) {
+            const int i = tid + u * NT;
+            const int hj = i / m, a = i - hj * m;
+            if (i < nl && hj % kPend < P)
+                wf_s[hj / kPend][hj % kPend][a] = exp(hlr[u] - (double)mo_s[hj / kPend][a]);
+        }
     }
-    __syncthreads();
     if (tid < C::CH) nk[(size_t)slot_row * C::CH + tid] = kn_s[tid];
-    if (tid >= 128 && tid < 128 + C::VCH) nv[(size_t)slot_row * C::VCH + tid - 128] = vn_s[tid - 128];
+    if (tid >= 128 && tid < 128 + C::VCH) {
+        nv[(size_t)slot_row * C::VCH + tid - 128] = vn_s[tid - 128];
+        // the evicted value row joins the held set (slot P) unless this step folds
+        if (!fold) reinterpret_cast<float4 *>(s.pend_v)[((size_t)g * kPend + P) * C::VCH + tid - 128] = ve_s[tid - 128];
+    }
 
     // ---- 1. row-dot pass ----------------------------------------------------
     // Loads are unconditional (row indices clamped into range, results of
@@ -333,36 +387,43 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
 
     // ---- 2. per-head landmark work and near weights (one wave per head) ----
     for (int h = wave; h < HPK; h += C::NW) {
+        const bool act = lane < m;
+        const size_t hi = (gh0 + h) * m + lane;
         double c = NEG_INF;
         for (int r = lane; r < R; r += 64) c = fmax(c, lg_s[h * R + r]);
         c = wave_max(c);
 
-        const bool act = lane < m;
         const double sa = act ? land_s[h][lane] : NEG_INF;
         const double f = wave_max(sa);
         const double fh = act ? exp(sa - f) : 0.0;
 
         // NystromHead::far_insert for landmark i = lane: strict ">" growth of
-        // the running max; T^ and Z^ stay at scale e^{-m_max} with m_max kept
-        // as the f32 value actually stored.
-        const size_t hi = (gh0 + h) * m + lane;
+        // the running max; Z^ stays at scale e^{-m_max} with m_max kept as the
+        // f32 value actually stored.  T^ gets the same update through the held
+        // set: this eviction's weight is ee at the new max.
         double mn = NEG_INF, zn = 0.0;
         if (act) {
-            const double l = lf_s[h][lane];
+            const double lnew = lf_s[h][lane];
             const float mo = mo_s[h][lane];
             float mnf = mo;
             double r = 1.0;
-            if (l > (double)mo) {
-                mnf = (float)l;
+            if (lnew > (double)mo) {
+                mnf = (float)lnew;
                 r = exp((double)mo - (double)mnf);
             }
             mn = (double)mnf;
-            const double ee = exp(l - mn);
+            const double ee = exp(lnew - mn);
             zn = zo_s[h][lane] * r + ee;
             s.m_max[hi] = mnf;
             s.z_hat[hi] = zn;
-            r_s[h][lane] = r;
-            e_s[h][lane] = ee;
+            // T^_i = rf_i t_hat_i + sum_{j<P} w_ij v_j + ee_i v_e at the new max:
+            // the held weights move from the old max to the new one, and this
+            // eviction's weight takes slot P (on a fold, slot kPend - 1)
+            r_s[h][lane] = exp((double)mr_s[h][lane] - mn);
+            for (int j = 0; j < P; ++j) wf_s[h][j][lane] *= r;
+            wf_s[h][fold ? kPend - 1 : P][lane] = ee;
+            if (fold) s.m_ref[hi] = mnf;
+            else s.pend_l[(gh0 + h) * kPend * (size_t)m + (size_t)P * m + lane] = lnew;
         }
 
         // u_b = sum_a fh_a M[a][b]  (lane = b)
@@ -399,8 +460,21 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
         const double gain = act ? u * exp(f + mn - call) : 0.0;
         const double far_den = wave_sum(gain * zn);
         const bool keep = far_den >= 0.0;  // aggregate rectifier (0 keeps)
-        if (act) gain_s[h][lane] = keep ? gain : 0.0;
+        const double gk = keep ? gain : 0.0;
         const double shift = keep ? call : c;  // dropped far field: near-only shift
+
+        if (fold) {
+            // the column pass rebuilds t_hat at the new max
+            if (act) gain_s[h][lane] = gk;
+        } else {
+            // t_hat stays as stored: its gains carry rf, and each held row and
+            // this eviction's row (slot P) gets one coefficient sum_i gain_i w_ij
+            if (act) gain_s[h][lane] = gk * r_s[h][lane];
+            for (int j = 0; j <= P; ++j) {
+                const double cj = wave_sum(act ? gk * wf_s[h][j][lane] : 0.0);
+                if (lane == 0) cj_s[h][j] = cj;
+            }
+        }
 
         double acc = 0.0;
         for (int r = lane; r < R; r += 64) {
@@ -413,33 +487,72 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
     }
     __syncthreads();
 
-    // ---- 3. column pass: T^ update + far contraction, V contraction --------
+    // ---- 3. column pass: far contraction (t_hat rebuilt on a fold), V contraction
     double acc[HPK][4];
 #pragma unroll
     for (int h = 0; h < HPK; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.0;
     {
         float4 *th = reinterpret_cast<float4 *>(s.t_hat) + gh0 * m * C::VCH;
-        const float4 vev = ve_s[cc];
+        if (fold) {
+            // t_hat <- r t_hat + sum_j w_j v_j over the held rows and this
+            // eviction's, written back once for kPend steps
 #pragma unroll
-        for (int h = 0; h < HPK; ++h) {
+            for (int h = 0; h < HPK; ++h) {
 #pragma unroll
-            for (int j = 0; j < C::TPT; ++j) {
-                const int b = rl + j * C::RL;
-                if (b >= m) break;
-                const size_t idx = ((size_t)h * m + b) * C::VCH + cc;
-                float4 t;
-                if constexpr (C::PRE_T) t = tpre[h][j];
-                else t = ld4<C::NTL>(th + idx);
-                const double rb = r_s[h][b], eb = e_s[h][b], gb = gain_s[h][b];
-                const double t0 = fma((double)t.x, rb, eb * (double)vev.x);
-                const double t1 = fma((double)t.y, rb, eb * (double)vev.y);
-                const double t2 = fma((double)t.z, rb, eb * (double)vev.z);
-                const double t3 = fma((double)t.w, rb, eb * (double)vev.w);
-                st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
-                acc[h][0] = fma(gb, t0, acc[h][0]);
-                acc[h][1] = fma(gb, t1, acc[h][1]);
-                acc[h][2] = fma(gb, t2, acc[h][2]);
-                acc[h][3] = fma(gb, t3, acc[h][3]);
+                for (int j = 0; j < C::TPT; ++j) {
+                    const int b = rl + j * C::RL;
+                    if (b >= m) break;
+                    const size_t idx = ((size_t)h * m + b) * C::VCH + cc;
+                    float4 t;
+                    if constexpr (C::PRE_T) t = tpre[h][j];
+                    else t = ld4<C::NTL>(th + idx);
+                    const double rb = r_s[h][b], gb = gain_s[h][b];
+                    double t0 = (double)t.x * rb, t1 = (double)t.y * rb;
+                    double t2 = (double)t.z * rb, t3 = (double)t.w * rb;
+#pragma unroll 1
+                    for (int k = 0; k < kPend; ++k) {
+                        const double wk = wf_s[h][k][b];
+                        const float4 x = k < kPend - 1 ? hv_s[k][cc] : ve_s[cc];
+                        t0 = fma(wk, (double)x.x, t0);
+                        t1 = fma(wk, (double)x.y, t1);
+                        t2 = fma(wk, (double)x.z, t2);
+                        t3 = fma(wk, (double)x.w, t3);
+                    }
+                    st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
+                    acc[h][0] = fma(gb, t0, acc[h][0]);
+                    acc[h][1] = fma(gb, t1, acc[h][1]);
+                    acc[h][2] = fma(gb, t2, acc[h][2]);
+                    acc[h][3] = fma(gb, t3, acc[h][3]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) {
+#pragma unroll
+                for (int j = 0; j < C::TPT; ++j) {
+                    const int b = rl + j * C::RL;
+                    if (b >= m) break;
+                    float4 t;
+                    if constexpr (C::PRE_T) t = tpre[h][j];
+                    else t = ld4<C::NTL>(th + ((size_t)h * m + b) * C::VCH + cc);
+                    const double gb = gain_s[h][b];
+                    acc[h][0] = fma(gb, (double)t.x, acc[h][0]);
+                    acc[h][1] = fma(gb, (double)t.y, acc[h][1]);
+                    acc[h][2] = fma(gb, (double)t.z, acc[h][2]);
+                    acc[h][3] = fma(gb, (double)t.w, acc[h][3]);
+                }
+            }
+            // row lane j < P: held slot j; row lane P: this eviction
+            if (rl <= P) {
+                const float4 x = rl < P ? hv_s[rl][cc] : ve_s[cc];
+#pragma unroll
+                for (int h = 0; h < HPK; ++h) {
+                    const double cj = cj_s[h][rl];
+                    acc[h][0] = fma(cj, (double)x.x, acc[h][0]);
+                    acc[h][1] = fma(cj, (double)x.y, acc[h][1]);
+                    acc[h][2] = fma(cj, (double)x.z, acc[h][2]);
+                    acc[h][3] = fma(cj, (double)x.w, acc[h][3]);
+                }
             }
         }
     }
@@ -481,6 +594,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
     }
 
     // ---- 4. reduce row lanes, joint division, counters ---------------------
+    if (fold) __syncthreads();  // every wave is done with the fold weights
     // within a wave: the RLW row lanes sit VCH lanes apart
 #pragma unroll
     for (int h = 0; h < HPK; ++h)
@@ -544,14 +658,20 @@ hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t strea
 }
 
 // Few groups per launch leave CUs with a single work-group, whose latency is
-// then exposed: use 512 threads per group there.
+// then exposed: use 512 threads per group there.  Shapes with hpk * m >= 512
+// (e.g. 8 heads, 64 landmarks) need so much LDS that 256-thread work-groups
+// would also run one per CU, so they take 512 threads at every grid size.
 constexpr int kSmallGrid = 1024;
 
 template <int D, int DV, int HPK, int MM>
 hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    if (io.map.count < kSmallGrid) return launch_shape<D, DV, HPK, MM, 512>(s, io, stream);
-    return launch_shape<D, DV, HPK, MM, 256>(s, io, stream);
+    if constexpr (HPK * MM >= 512) {
+        return launch_shape<D, DV, HPK, MM, 512>(s, io, stream);
+    } else {
+        if (io.map.count < kSmallGrid) return launch_shape<D, DV, HPK, MM, 512>(s, io, stream);
+        return launch_shape<D, DV, HPK, MM, 256>(s, io, stream);
+    }
 }
 
 template <int D, int DV, int HPK>
@@ -573,7 +693,57 @@ hipError_t launch_hpk(const DevState &s, const DecodeIO &io, hipStream_t stream)
     }
 }
 
+// One work-group per (group, head): T^ with the held evictions folded in, at
+// the current running max, written to dst; with `reset` the held set is then
+// emptied (m_ref = m_max, every slot's logits -inf).  Not on the decode path:
+// state reads and writes use it.
+__global__ __launch_bounds__(256) void fold_kernel(DevState s, float *dst, int reset)
+{
+    const int g = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int m = s.m, VCH = s.dv / 4;
+    const size_t gh = (size_t)g * s.hpk + h;
+    const int P = (int)((uint64_t)s.far_len[gh] % kPend);
+    __shared__ double w_s[kPend][kMaxLandmarks], r_s[kMaxLandmarks];
+    for (int a = tid; a < m; a += 256) {
+        const double mx = (double)s.m_max[gh * m + a];
+        r_s[a] = exp((double)s.m_ref[gh * m + a] - mx);
+        for (int j = 0; j < kPend; ++j)
+            w_s[j][a] = j < P ? exp(s.pend_l[(gh * kPend + j) * m + a] - mx) : 0.0;
+    }
+    __syncthreads();
+    const float4 *th = reinterpret_cast<const float4 *>(s.t_hat) + gh * m * VCH;
+    const float4 *pv = reinterpret_cast<const float4 *>(s.pend_v) + (size_t)g * kPend * VCH;
+    float4 *out = reinterpret_cast<float4 *>(dst) + gh * m * VCH;
+    for (int i = tid; i < m * VCH; i += 256) {
+        const int a = i / VCH, c = i - a * VCH;
+        const float4 t = th[i];
+        const double rb = r_s[a];
+        double t0 = (double)t.x * rb, t1 = (double)t.y * rb, t2 = (double)t.z * rb, t3 = (double)t.w * rb;
+        for (int j = 0; j < P; ++j) {
+            const float4 v = pv[(size_t)j * VCH + c];
+            const double wj = w_s[j][a];
+            t0 = fma(wj, (double)v.x, t0);
+            t1 = fma(wj, (double)v.y, t1);
+            t2 = fma(wj, (double)v.z, t2);
+            t3 = fma(wj, (double)v.w, t3);
+        }
+        out[i] = make_float4((float)t0, (float)t1, (float)t2, (float)t3);
+    }
+    if (!reset) return;
+    for (int a = tid; a < m; a += 256) {
+        s.m_ref[gh * m + a] = s.m_max[gh * m + a];
+        for (int j = 0; j < kPend; ++j) s.pend_l[(gh * kPend + j) * m + a] = -__builtin_inf();
+    }
+}
+
 }  // namespace
+
+hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t stream)
+{
+    if (s.m < 1 || s.m > kMaxLandmarks || s.dv % 4 || (reset && dst != s.t_hat)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fold_kernel, dim3(s.G, s.hpk), dim3(256), 0, stream, s, dst, reset ? 1 : 0);
+    return hipGetLastError();
+}
 
 bool decode_supported(int d, int dv, int hpk, int m, int R)
 {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "o1.h"
+
 namespace o1 {
 
 constexpr int kMaxLandmarks = 64;      // largest m_eff the kernels are compiled for
@@ -12,6 +14,12 @@ constexpr double kDenEps = 1e-30;      // DEN_EPS of the nystrom.rs source page
 constexpr double kRidgeRel = 1e-6;     // RIDGE_REL of the nystrom.rs source page
 constexpr int kRidgeTries = 12;        // ridge_pinv: attempts before the fallback
 constexpr int kExactSlack = 8;         // EXACT_SLACK of the nystrom.rs source page
+// Evictions held apart from T^: the value row and per-landmark logits of up to
+// kPend - 1 evicted keys wait in small per-group buffers, and every kPend-th
+// eviction folds them all into T^ at once, so T^ is rewritten once per kPend
+// steps instead of every step.  A group's held count is far_len mod kPend.
+constexpr int kPend = O1_FOLD_PERIOD;
+static_assert(kPend >= 2, "a fold period of 1 holds nothing");
 
 // Device state of G independent groups (one GQA group each).  Layout, with
 // R = sink + w near rows and m = m_eff:
@@ -21,6 +29,12 @@ constexpr int kExactSlack = 8;         // EXACT_SLACK of the nystrom.rs source p
 //   mu      [G][hpk][m][m]                mixing matrix, row = key landmark
 //   t_hat   [G][hpk][m][dv] (f32), z_hat [G][hpk][m] (f64), m_max [G][hpk][m] (f32)
 //   win_head [G] (i32), far_len [G][hpk] (i64), lambda [G][hpk] (f64), tries [G][hpk] (i32)
+// Held evictions (see kPend): with P = far_len mod kPend evictions held,
+//   pend_v [G][kPend][dv] (f32)           value rows of the held evictions, slot j < P
+//   pend_l [G][hpk][kPend][m] (f64)       their logits q~_i . k * scale (-inf: empty slot)
+//   m_ref  [G][hpk][m] (f32)              the running max at the last fold: the stored
+//                                         t_hat is at scale e^{-m_ref}; the far numerator is
+//   T^_i = e^{m_ref_i - m_max_i} t_hat_i + sum_{j<P} e^{pend_l_ij - m_max_i} pend_v_j
 struct DevState {
     int G, hpk, d, dv, w, sink, R, rect;
     int m;        // m_eff of the current prefill
@@ -29,6 +43,8 @@ struct DevState {
     double *z_hat, *lambda;
     int32_t *win_head, *tries;
     int64_t *far_len;
+    float *pend_v, *m_ref;
+    double *pend_l;
 };
 
 // The groups one call covers.  Its inputs and outputs are indexed by the call's
@@ -117,6 +133,10 @@ hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const Group
 // True when the decode kernel is compiled for this shape.
 bool decode_supported(int d, int dv, int hpk, int m, int R);
 hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stream);
+// T^ with the held evictions folded in, for every group, into dst ([G][hpk][m][dv]
+// f32; may be s.t_hat).  With `reset` the state's held set is then emptied
+// (m_ref = m_max, every slot's logits -inf); dst must then be s.t_hat.
+hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t stream);
 hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t stream);
 
 // ---- wavefront helpers (wave64) ------------------------------------------

@@ -7,7 +7,8 @@
 //                      stored f32 (state) and f64 (work, for the exp-Gram).
 //   scatter_kernel     grid G: sinks (prompt rows 0..sink-1) and the ring (the
 //                      last w prompt keys, key j in slot (j - sink) mod w), the
-//                      ring head and far_len after the replay.
+//                      ring head and far_len after the replay, and an empty set
+//                      of evictions held apart from T^ (logits -inf).
 //   gram_pinv_kernel   grid G * hpk: A = exp(Q~ K~^T * scale) and G = A^T A on f64
 //                      MFMA, lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
 //                      G + lambda I in LDS (lambda x10 on a failed pivot, up to 12
@@ -140,6 +141,10 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO
     const int evictions = T - S - w;
     if (threadIdx.x == 0) s.win_head[g] = evictions % w;
     for (int h = threadIdx.x; h < s.hpk; h += kThreads) s.far_len[(size_t)g * s.hpk + h] = evictions;
+    // no evictions held apart from T^ yet: every slot's logits -inf (weight 0;
+    // the value rows stay finite from the handle's creation or earlier use)
+    double *pl = s.pend_l + (size_t)g * s.hpk * kPend * s.m;
+    for (int t = threadIdx.x; t < s.hpk * kPend * s.m; t += kThreads) pl[t] = -__builtin_inf();
 }
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -523,6 +528,7 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
         const double corr = exp(mx[r] - (double)mf);
         if (li == 0) {
             s.m_max[gh * m + i] = mf;
+            s.m_ref[gh * m + i] = mf;
             s.z_hat[gh * m + i] = zs[r] * corr;
         }
         float *th = s.t_hat + (gh * m + i) * DV;

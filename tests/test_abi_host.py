@@ -67,6 +67,8 @@ def test_binding_constants_match_the_header():
     fields = _header_enum("O1_FIELD_")
     for name, val in fields.items():
         assert getattr(P, name[3:]) == val, name
+    fold = re.search(r"#define\s+O1_FOLD_PERIOD\s+(\d+)", open(HEADER).read())
+    assert fold and int(fold.group(1)) == P.FOLD_PERIOD
     cfg_fields = re.search(r"typedef struct o1_config \{(.*?)\} o1_config;", open(HEADER).read(), re.S)
     names = re.findall(r"int32_t\s+(\w+);", cfg_fields.group(1))
     assert names == [f for f, _ in P.o1_config._fields_]

@@ -121,3 +121,86 @@ def test_reprefill_resets_state_and_info():
     fresh.prefill(q2, k2, v2)
     for field in range(12):
         assert torch.equal(grp.read(field), fresh.read(field)), field
+
+
+def _stepped(wl, steps, dev=DEV):
+    """A prefilled handle stepped `steps` times, with every step's output."""
+    q, k, v = W.prompt(wl, dev)
+    grp = P.O1Groups(wl.config)
+    grp.prefill(q, k, v)
+    outs = []
+    for t in range(steps):
+        out = torch.empty(wl.groups, wl.hpk, wl.dv, device=dev)
+        grp.step(*W.decode_inputs(wl, t, dev), out)
+        outs.append(out)
+    return grp, outs
+
+
+def test_t_hat_read_between_folds_matches_oracle_and_changes_nothing():
+    """Read while evictions are held (far_len mod FOLD_PERIOD != 0), T^ is the
+    oracle's far numerator (compared at a common scale, as for the prefill),
+    and the read leaves the state as it was: later outputs equal, bit for bit,
+    those of an identical handle that was not read."""
+    wl = WL
+    G, H, m, dv = wl.groups, wl.hpk, wl.m_eff, wl.dv
+    n1, n2 = 13, 2 * P.FOLD_PERIOD + 3
+    E = wl.T - wl.sink - wl.w + n1
+    assert E % P.FOLD_PERIOD != 0, "the read must see held evictions"
+    a, _ = _stepped(wl, n1)
+    b, _ = _stepped(wl, n1)
+    th = a.read(P.FIELD_T_HAT).view(G, H, m, dv).numpy().astype(np.float64)
+    mx = a.read(P.FIELD_M_MAX).view(G, H, m).numpy().astype(np.float64)
+
+    q, k, v = W.prompt(wl, DEV)
+    orc = oracle_prefill(wl, cpu(q), cpu(k), cpu(v))
+    qs = np.stack([cpu(W.decode_inputs(wl, t, DEV)[0]) for t in range(n1)])
+    ks = np.stack([cpu(W.decode_inputs(wl, t, DEV)[1]) for t in range(n1)])
+    vs = np.stack([cpu(W.decode_inputs(wl, t, DEV)[2]) for t in range(n1)])
+    oracle_decode(orc, qs, ks, vs)
+    worst = 0.0
+    for i, g in enumerate(orc):
+        st = g.state()
+        for h in range(H):
+            tg = th[i, h] * np.exp(mx[i, h] - st["m_max"][h])[:, None]
+            ref = st["t_hat"][h]
+            rel = np.abs(tg - ref).max(1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+            worst = max(worst, rel.max())
+    say(f"  T^ read between folds: max row error {worst:.3e}")
+    assert worst <= 1e-5
+
+    # the read changed nothing: both handles continue identically past a fold
+    for t in range(n1, n1 + n2):
+        oa = torch.empty(G, H, dv, device=DEV)
+        ob = torch.empty(G, H, dv, device=DEV)
+        qq, kk, vv = W.decode_inputs(wl, t, DEV)
+        a.step(qq, kk, vv, oa)
+        b.step(qq, kk, vv, ob)
+        assert torch.equal(oa, ob), t
+    for f in range(12):
+        assert torch.equal(a.read(f), b.read(f)), f
+
+
+def test_state_upload_between_folds_continues_the_same_outputs():
+    """Every field read from a handle with evictions held, written into a fresh
+    sealed handle (each write first adds that handle's own held evictions to
+    its T^), continues with the same outputs to within rounding."""
+    wl = WL
+    G, H, dv = wl.groups, wl.hpk, wl.dv
+    n1, n2 = 13, 2 * P.FOLD_PERIOD + 3
+    a, _ = _stepped(wl, n1)
+    b, _ = _stepped(wl.with_(seed=wl.seed + 100), 5)  # another state, its own held set
+    for f in range(12):
+        b.write(f, a.read(f))
+    for f in range(12):
+        assert torch.equal(a.read(f), b.read(f)), f
+    worst = 0.0
+    for t in range(n1, n1 + n2):
+        oa = torch.empty(G, H, dv, device=DEV)
+        ob = torch.empty(G, H, dv, device=DEV)
+        qq, kk, vv = W.decode_inputs(wl, t, DEV)
+        a.step(qq, kk, vv, oa)
+        b.step(qq, kk, vv, ob)
+        oa64, ob64 = oa.double(), ob.double()
+        worst = max(worst, ((oa64 - ob64).abs().amax(-1) / oa64.norm(dim=-1)).max().item())
+    say(f"  uploaded state: max row difference {worst:.3e}")
+    assert worst <= 1e-5
