@@ -8,8 +8,9 @@
 // exact_attend_kernel: grid (G, splits), 256 threads.  A work-group owns one
 // key range of one group and walks it in chunks of kChunk keys with an online
 // per-head max: row-dot pass (f64, the decode kernel's lane split and head
-// reduction) -> per-head chunk max, weights and running sum -> V pass with the
-// running rescale.  With one split it writes the normalised output; otherwise
+// reduction; the chunk's first V rows of each lane are loaded at its end, so
+// they arrive during the softmax) -> per-head chunk max, weights and running
+// sum -> V pass with the running rescale.  With one split it writes the normalised output; otherwise
 // it writes (max, sum, numerator) partials that exact_combine_kernel merges.
 // Bound: HBM (n_keys * (d + dv) * 4 B per group, read once, nontemporal).
 //
@@ -39,6 +40,9 @@ struct ExactShape {
     static constexpr int RL = kNT / VCH;
     static constexpr int RED_CAP = 16384 / (kNW * DV * 8);
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
+    // V rows per lane loaded before the chunk's softmax (more would cost a wave
+    // per SIMD at hpk >= 4)
+    static constexpr int VPRE = HPK <= 2 ? 8 : 4;
     static_assert(HPK <= LPR && HPK % RED_H == 0, "unsupported head count");
 };
 
@@ -126,6 +130,13 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
                 if (writer && r < nr) lg_s[my_head][r] = tot;
             }
         }
+        // the chunk's first V rows of this lane, in flight across the softmax
+        float4 vp[C::VPRE];
+#pragma unroll
+        for (int j = 0; j < C::VPRE; ++j) {
+            const int r = c0 + min(rl + j * C::RL, nr - 1);
+            vp[j] = ld4<true>(((r == new_row) ? vn : vc + (size_t)r * C::VCH) + cc);
+        }
         __syncthreads();
         // per head: chunk max, running rescale, weights
 #pragma unroll
@@ -158,8 +169,21 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
             acc[h][2] *= f;
             acc[h][3] *= f;
         }
+#pragma unroll
+        for (int j = 0; j < C::VPRE; ++j) {
+            const int r = rl + j * C::RL;
+            if (r >= nr) break;
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) {
+                const double p = lg_s[h][r];
+                acc[h][0] = fma(p, (double)vp[j].x, acc[h][0]);
+                acc[h][1] = fma(p, (double)vp[j].y, acc[h][1]);
+                acc[h][2] = fma(p, (double)vp[j].z, acc[h][2]);
+                acc[h][3] = fma(p, (double)vp[j].w, acc[h][3]);
+            }
+        }
         constexpr int VU = 8;
-        for (int r0 = rl; r0 < nr; r0 += VU * C::RL) {
+        for (int r0 = rl + C::VPRE * C::RL; r0 < nr; r0 += VU * C::RL) {
             float4 x[VU];
 #pragma unroll
             for (int j = 0; j < VU; ++j) {
