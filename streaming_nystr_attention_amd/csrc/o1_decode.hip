@@ -183,8 +183,9 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
         }
         if (hv_mine) (&hv_s[0][0])[tid] = hvr;
         __syncthreads();
-        // held weights at the running max before this step (at most 1: the
-        // max covers every held logit); step 2 rescales them to the new max
+        // held weights at the running max before this step (at most 1 up to
+        // the f32 rounding of the stored max, which covers every held logit);
+        // step 2 rescales them to the new max
 #pragma unroll
         for (int u = 0; u < C::HL; ++u) {
             const int i = tid + u * NT;
