@@ -182,11 +182,10 @@ int o1_prefill(o1_groups *g, const float *q, const float *k, const float *v, int
  *   out [G][hpk][dv]   outputs (may not alias the inputs)
  * In the exact-only mode the step appends (k, v) as key n = T + steps and
  * writes, per head, softmax attention over keys 0 .. n (NystromHead::step with
- * no sinks and no far field).  Each group's key count is its layer's count,
- * kept on the device, so layers stepped one by one to different counts are
- * stepped correctly by o1_step as well.  Launches: the attention (plus a
- * merge when a group's keys are split across work-groups) and a one-block
- * kernel that advances the counts.
+ * no sinks and no far field).  Each group's key count is kept on the device
+ * and advanced by the step itself, so layers stepped one by one to different
+ * counts are stepped correctly by o1_step as well.  Launches: the attention,
+ * plus a merge when a group's keys are split across work-groups.
  * No allocation, no host synchronisation; one kernel launch in the skeleton
  * mode.
  * Graph capture: a step (and o1_step_layer) may be captured into a HIP graph

@@ -56,7 +56,7 @@ struct o1_groups {
     float *exact_k, *exact_v;
     double *exact_ws;
     size_t exact_ws_bytes;
-    int32_t *exact_held;  // keys held per layer [n_layer], kept on the device
+    int32_t *exact_held;  // keys held per group [G], kept on the device
 
     bool any_sealed() const
     {
@@ -232,9 +232,8 @@ int prefill_groups(o1_groups *g, int layer, const o1::PromptView &pv, int32_t T,
 
     hipError_t err;
     if (exact) {
-        const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c.n_layer : layer + 1;
         err = o1::launch_exact_seal(g->st, pv, map, T, g->exact_k, g->exact_v, c.exact_cap,
-                                    g->exact_held, l0, l1, (hipStream_t)stream);
+                                    g->exact_held, (hipStream_t)stream);
     } else {
         o1::PrefillIO io;
         io.p = pv;
@@ -269,7 +268,7 @@ int step_groups(o1_groups *g, int layer, const float *q, const float *k, const f
     const o1::GroupMap map = layer < 0 ? whole_map(g) : layer_map(g, layer);
     hipError_t err;
     if (g->exact) {
-        // Each group's key count is read on the device (its layer's count), so
+        // Each group's key count is read on the device (and advanced there), so
         // layers stepped one by one may hold different counts and a captured
         // step replays correctly; the host mirror serves the checks below.
         const long long held =
@@ -306,13 +305,7 @@ int step_groups(o1_groups *g, int layer, const float *q, const float *k, const f
         io.k_dst = g->exact_k;
         io.v_dst = g->exact_v;
         io.held = g->exact_held;
-        io.n_kv = g->cfg.n_kv;
-        io.n_layer = g->cfg.n_layer;
         err = o1::launch_exact(io, splits, (hipStream_t)stream);
-        if (err == hipSuccess) {
-            const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? g->cfg.n_layer : layer + 1;
-            err = o1::launch_exact_advance(g->exact_held, l0, l1, g->cfg.exact_cap, (hipStream_t)stream);
-        }
     } else {
         DeviceScope dev(g);
         if (int rc = dev.status()) return rc;
@@ -421,7 +414,7 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         {(void **)&g->exact_k, Gs * E * c.d * sizeof(float)},
         {(void **)&g->exact_v, Gs * E * c.dv * sizeof(float)},
         {(void **)&g->exact_ws, ws_bytes},
-        {(void **)&g->exact_held, E ? (size_t)c.n_layer * sizeof(int32_t) : 0},
+        {(void **)&g->exact_held, E ? Gs * sizeof(int32_t) : 0},
     };
     size_t total = 0;
     for (auto &a : allocs) {

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int n_keys = a.n_keys, per_split = a.per_split;
     if (a.held) {  // exact-only decode: this group's key count from the device
-        const int held = a.held[(g / a.n_kv) % a.n_layer];
+        const int held = a.held[g];
         if (held >= a.cap) return;  // full: the step changes nothing here
         n_keys = held + 1;
         per_split = (n_keys - a.first + (int)gridDim.y - 1) / (int)gridDim.y;
@@ -263,23 +263,39 @@ __global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
         }
         if (h0 + C::RED_H < HPK) __syncthreads();
     }
+    // exact-only decode with one work-group per group: it alone read the count
+    // (at its start), so it advances it; split ranges leave that to the merge
+    if (a.held && final_out && tid == 0) a.held[g] = n_keys;
 }
 
-// One block of dv threads per (call index, head): merge the key-range partials.
+// One block of dv threads per call index: merge the key-range partials of
+// every head.  In the exact-only decode the block also advances the group's
+// key count, after every thread has read it.
 __global__ void exact_combine_kernel(ExactIO a, int splits)
 {
-    const int gh = blockIdx.x, H = a.hpk, g = gh / H, h = gh - g * H, c = threadIdx.x;
-    if (a.held && a.held[(a.map.state(g) / a.n_kv) % a.n_layer] >= a.cap) return;  // as the attention
-    double mx = -__builtin_inf();
-    for (int s = 0; s < splits; ++s) mx = fmax(mx, a.ws_max[((size_t)g * splits + s) * H + h]);
-    double den = 0.0, num = 0.0;
-    for (int s = 0; s < splits; ++s) {
-        const size_t part = ((size_t)g * splits + s) * H + h;
-        const double w = exp(a.ws_max[part] - mx);  // empty ranges carry -inf -> 0
-        den += a.ws_sum[part] * w;
-        num += a.ws_num[part * a.dv + c] * w;
+    const int ci = blockIdx.x, H = a.hpk, c = threadIdx.x;
+    const int g = a.map.state(ci);
+    int held = 0;
+    if (a.held) {
+        held = a.held[g];
+        if (held >= a.cap) return;  // as the attention: full, nothing changes
     }
-    a.out[(size_t)gh * a.dv + c] = (float)(num / den);
+    for (int h = 0; h < H; ++h) {
+        double mx = -__builtin_inf();
+        for (int s = 0; s < splits; ++s) mx = fmax(mx, a.ws_max[((size_t)ci * splits + s) * H + h]);
+        double den = 0.0, num = 0.0;
+        for (int s = 0; s < splits; ++s) {
+            const size_t part = ((size_t)ci * splits + s) * H + h;
+            const double w = exp(a.ws_max[part] - mx);  // empty ranges carry -inf -> 0
+            den += a.ws_sum[part] * w;
+            num += a.ws_num[part * a.dv + c] * w;
+        }
+        a.out[((size_t)ci * H + h) * a.dv + c] = (float)(num / den);
+    }
+    if (a.held) {
+        __syncthreads();  // every thread has read the count
+        if (c == 0) a.held[g] = held + 1;
+    }
 }
 
 template <int D, int DV, int HPK>
@@ -288,7 +304,7 @@ hipError_t launch_exact_shape(const ExactIO &a, int splits, hipStream_t stream)
     hipLaunchKernelGGL((exact_attend_kernel<D, DV, HPK>), dim3(a.map.count, splits), dim3(kNT), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || splits == 1) return err;
-    hipLaunchKernelGGL(exact_combine_kernel, dim3(a.map.count * a.hpk), dim3(a.dv), 0, stream, a, splits);
+    hipLaunchKernelGGL(exact_combine_kernel, dim3(a.map.count), dim3(a.dv), 0, stream, a, splits);
     return hipGetLastError();
 }
 
@@ -307,12 +323,10 @@ hipError_t launch_exact_hpk(const ExactIO &a, int splits, hipStream_t stream)
 // One work-group per call index: copy the prompt rows into the mapped group's
 // exact buffers and clear the counters the skeleton mode would have set.
 __global__ __launch_bounds__(256) void exact_seal_kernel(DevState s, PromptView p, GroupMap map, int T,
-                                                         float4 *ek, float4 *ev, int cap, int32_t *held,
-                                                         int l0, int l1)
+                                                         float4 *ek, float4 *ev, int cap, int32_t *held)
 {
     const int ci = blockIdx.x, g = map.state(ci), tid = threadIdx.x;
-    if (ci == 0)
-        for (int l = l0 + tid; l < l1; l += 256) held[l] = T;
+    if (tid == 0) held[g] = T;
     const int ck = s.d / 4, cv = s.dv / 4;
     const float4 *k = reinterpret_cast<const float4 *>(p.k_row(map, ci, 0));
     const float4 *v = reinterpret_cast<const float4 *>(p.v_row(map, ci, 0));
@@ -334,28 +348,13 @@ __global__ __launch_bounds__(256) void exact_seal_kernel(DevState s, PromptView 
     }
 }
 
-// The key counts of layers l0 .. l1-1 after an exact-only step: one more key,
-// except for layers already at cap (their step changed nothing).
-__global__ __launch_bounds__(256) void exact_advance_kernel(int32_t *held, int l0, int l1, int cap)
-{
-    for (int l = l0 + (int)threadIdx.x; l < l1; l += 256)
-        if (held[l] < cap) held[l] += 1;
-}
-
 }  // namespace
 
 hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const GroupMap &map, int T,
-                             float *ek, float *ev, int cap, int32_t *held, int l0, int l1,
-                             hipStream_t stream)
+                             float *ek, float *ev, int cap, int32_t *held, hipStream_t stream)
 {
     hipLaunchKernelGGL(exact_seal_kernel, dim3(map.count), dim3(256), 0, stream, s, p, map, T,
-                       reinterpret_cast<float4 *>(ek), reinterpret_cast<float4 *>(ev), cap, held, l0, l1);
-    return hipGetLastError();
-}
-
-hipError_t launch_exact_advance(int32_t *held, int l0, int l1, int cap, hipStream_t stream)
-{
-    hipLaunchKernelGGL(exact_advance_kernel, dim3(1), dim3(256), 0, stream, held, l0, l1, cap);
+                       reinterpret_cast<float4 *>(ek), reinterpret_cast<float4 *>(ev), cap, held);
     return hipGetLastError();
 }
 

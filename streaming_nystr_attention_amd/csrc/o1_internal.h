@@ -110,25 +110,21 @@ struct ExactIO {
     // n_keys-1 of k_dst / v_dst (the same buffers as k / v).
     const float *k_new, *v_new;
     float *k_dst, *v_dst;
-    // Exact-only decode: keys held per layer, read on the device (so a graph
-    // replay sees the current count) -- state group g of layer (g / n_kv) %
-    // n_layer holds held[layer] keys and gets n_keys = held + 1 after the
-    // append; a group already holding cap keys is left untouched.  The key
-    // range of a split is then ceil(n_keys / splits) keys.  Null otherwise.
-    const int32_t *held;
-    int n_kv, n_layer;
+    // Exact-only decode: keys held per state group, read on the device (so a
+    // graph replay sees the current count) -- group g holds held[g] keys and
+    // gets n_keys = held[g] + 1 after the append; a group already holding cap
+    // keys is left untouched.  The key range of a split is then
+    // ceil(n_keys / splits) keys.  The step advances held[g] itself (its one
+    // work-group, or the merge of its split ranges).  Null otherwise.
+    int32_t *held;
 };
 int exact_splits(int G, int n_visible);
 hipError_t launch_exact(const ExactIO &io, int splits, hipStream_t stream);
-// held[l] += 1 for the layers l0 .. l1-1 that hold fewer than cap keys: the
-// count an exact-only step advances, after its attention (stream order).
-hipError_t launch_exact_advance(int32_t *held, int l0, int l1, int cap, hipStream_t stream);
 // Exact-only prefill of the groups in `map`: prompt rows 0..T-1 into rows
 // 0..T-1 of ek [G][cap][d], ev [G][cap][dv]; win_head, far_len, lambda, tries
-// cleared; held[l] = T for the layers l0 .. l1-1.
+// cleared; held[g] = T for each mapped group g.
 hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const GroupMap &map, int T,
-                             float *ek, float *ev, int cap, int32_t *held, int l0, int l1,
-                             hipStream_t stream);
+                             float *ek, float *ev, int cap, int32_t *held, hipStream_t stream);
 
 // True when the decode kernel is compiled for this shape.
 bool decode_supported(int d, int dv, int hpk, int m, int R);
