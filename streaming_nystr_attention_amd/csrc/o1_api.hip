@@ -438,6 +438,9 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         return fail(O1_EHIP, "clearing the held value rows failed");
     }
     g->state_bytes = total;
+    // the decode streams its state from HBM when the state outgrows the cache
+    const size_t exact_bytes = Gs * E * (c.d + c.dv) * sizeof(float) + ws_bytes;
+    s.stream_state = total - std::min(total, exact_bytes) > o1::kInfinityCacheBytes ? 1 : 0;
     *out = g;
     return ok();
 }

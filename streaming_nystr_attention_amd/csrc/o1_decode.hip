@@ -48,6 +48,7 @@
 // Work-group size: 256 threads when the launch has many groups (several
 // work-groups per CU hide each other's latency), 512 when it has few or when
 // the shape's LDS allows only one work-group per CU anyway (hpk * m >= 512).
+// State loads and stores are nontemporal when the state is streamed from HBM.
 // A launch covers the groups of a GroupMap: the whole handle, or one layer of
 // every sequence; inputs and outputs are indexed by the launch's own index.
 #include <atomic>
@@ -59,7 +60,7 @@ namespace {
 
 constexpr int kMaxDynLds = 32 * 1024;  // near logits: hpk * (sink + w) doubles
 
-template <int D, int DV, int HPK, int MM, int NT>
+template <int D, int DV, int HPK, int MM, int NT, bool STREAM>
 struct DecodeShape {
     static constexpr int NW = NT / 64;                                 // waves
     static constexpr int CH = D / 4;                                   // float4 per key row
@@ -79,7 +80,7 @@ struct DecodeShape {
     static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : (HPK * MM >= 512 ? 6 : 8);
     static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
     static constexpr int MB = NT == 256 ? 16 : 32;                     // M rows in flight (unstaged M)
-    static constexpr bool NTL = NT == 256;                             // streaming accesses (large grids)
+    static constexpr bool NTL = STREAM;                                // nontemporal state accesses
     // One work-group per CU and registers to spare: the row pass runs as one
     // stream over every row it reads, two batches per round trip, with the
     // queries in f64 registers.
@@ -102,10 +103,10 @@ struct DecodeShape {
     static_assert((kPend - 1) * VCH <= NT, "one held value float4 per thread");
 };
 
-template <int D, int DV, int HPK, int MM, int NT>
-__global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) void decode_kernel(DevState s, DecodeIO io)
+template <int D, int DV, int HPK, int MM, int NT, bool STREAM>
+__global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_WAVES)) void decode_kernel(DevState s, DecodeIO io)
 {
-    using C = DecodeShape<D, DV, HPK, MM, NT>;
+    using C = DecodeShape<D, DV, HPK, MM, NT, STREAM>;
     const int ci = blockIdx.x;            // call index: inputs and outputs
     const int g = io.map.state(ci);       // state group
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT>::MIN_WAVES)) v
     if (tid < HPK) s.far_len[gh0 + tid] += 1;
 }
 
-template <int D, int DV, int HPK, int MM, int NT>
+template <int D, int DV, int HPK, int MM, int NT, bool STREAM>
 hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     // Static LDS of the wide shapes plus the near logits can pass 64 KB; raise
@@ -648,13 +649,13 @@ hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t strea
     if (err != hipSuccess) return err;
     const uint64_t bit = dev < 64 ? 1ull << dev : 0;
     if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, HPK, MM, NT>),
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, HPK, MM, NT, STREAM>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
         if (err != hipSuccess) return err;
         done.fetch_or(bit, std::memory_order_release);
     }
     const size_t dyn = sizeof(double) * (size_t)HPK * s.R;
-    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM, NT>), dim3(io.map.count), dim3(NT), dyn, stream, s, io);
+    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM, NT, STREAM>), dim3(io.map.count), dim3(NT), dyn, stream, s, io);
     return hipGetLastError();
 }
 
@@ -662,17 +663,21 @@ hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t strea
 // then exposed: use 512 threads per group there.  Shapes with hpk * m >= 512
 // (e.g. 8 heads, 64 landmarks) need so much LDS that 256-thread work-groups
 // would also run one per CU, so they take 512 threads at every grid size.
+// State accesses are nontemporal when the handle's state is larger than the
+// Infinity Cache (it is then streamed from HBM at every step, also one layer at
+// a time), and cached when it fits there; 256-thread launches (>= 1024 groups)
+// always stream.
 constexpr int kSmallGrid = 1024;
 
 template <int D, int DV, int HPK, int MM>
 hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    if constexpr (HPK * MM >= 512) {
-        return launch_shape<D, DV, HPK, MM, 512>(s, io, stream);
-    } else {
-        if (io.map.count < kSmallGrid) return launch_shape<D, DV, HPK, MM, 512>(s, io, stream);
-        return launch_shape<D, DV, HPK, MM, 256>(s, io, stream);
+    const bool big = s.stream_state != 0;
+    if constexpr (HPK * MM < 512) {
+        if (io.map.count >= kSmallGrid) return launch_shape<D, DV, HPK, MM, 256, true>(s, io, stream);
     }
+    if (big) return launch_shape<D, DV, HPK, MM, 512, true>(s, io, stream);
+    return launch_shape<D, DV, HPK, MM, 512, false>(s, io, stream);
 }
 
 template <int D, int DV, int HPK>

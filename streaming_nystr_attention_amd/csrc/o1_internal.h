@@ -14,6 +14,7 @@ constexpr double kDenEps = 1e-30;      // DEN_EPS of the nystrom.rs source page
 constexpr double kRidgeRel = 1e-6;     // RIDGE_REL of the nystrom.rs source page
 constexpr int kRidgeTries = 12;        // ridge_pinv: attempts before the fallback
 constexpr int kExactSlack = 8;         // EXACT_SLACK of the nystrom.rs source page
+constexpr size_t kInfinityCacheBytes = size_t(256) << 20;  // MI355X memory-side cache
 // Evictions held apart from T^: the value row and per-landmark logits of up to
 // kPend - 1 evicted keys wait in small per-group buffers, and every kPend-th
 // eviction folds them all into T^ at once, so T^ is rewritten once per kPend
@@ -45,6 +46,7 @@ struct DevState {
     int64_t *far_len;
     float *pend_v, *m_ref;
     double *pend_l;
+    int stream_state;  // 1 when the state is larger than the Infinity Cache (decode streams it)
 };
 
 // The groups one call covers.  Its inputs and outputs are indexed by the call's
