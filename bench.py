@@ -48,7 +48,7 @@ DECODE_SRC = [os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", f)
 # kernel's sources).
 # A changed kernel (comments aside) has no entry, and the roofline's traffic is then null.
 MEASURED_TRAFFIC = {
-    ("qwen3_stack_b64", "0656300b9870fa65"): 3448562367,
+    ("qwen3_stack_b64", "b47341adeff7d7c7"): 3051599349,
 }
 
 
@@ -76,14 +76,20 @@ def decode_bytes_per_group_step(wl) -> tuple[float, float]:
     T^ is read every step and written on the fold step only (once per
     FOLD_PERIOD = K steps).  A step with P evictions held (P = 0 .. K-1, each
     equally often) reads their value rows and logits; a step that does not fold
-    writes its own eviction's row and logits into the held set."""
+    writes its own eviction's row and logits into the held set.  With w >= K
+    the far-insert logits are kept per ring slot: the query landmarks are read
+    on the fold step only, when the logits of the K keys that arrived since the
+    previous fold are written, and every step reads its evicted key's logits."""
     from streaming_nystr_attention_amd import FOLD_PERIOD as K
 
     S, w, d, dv, m, H = wl.sink, wl.w, wl.d, wl.dv, wl.m_eff, wl.hpk
     held = dv * 4 + H * m * 8                # one held eviction: value row, logits per head
+    ring = w >= K                            # far-insert logits kept per ring slot
+    q_tilde = H * m * d * 4                  # every head's query landmarks
     read = ((S + w) * (d + dv) * 4           # sinks + ring rows
             + m * d * 4                      # key landmarks
-            + H * (m * d * 4 + m * m * 4     # per head: query landmarks, M
+            + (q_tilde / K + H * m * 8 if ring else q_tilde)
+            + H * (m * m * 4                 # per head: M
                    + m * dv * 4 + m * 8      # T^, Z^ (f64)
                    + m * 4 + m * 4)          # running max, its value at the last fold
             + (K - 1) / 2 * held             # the held evictions
@@ -93,6 +99,7 @@ def decode_bytes_per_group_step(wl) -> tuple[float, float]:
              + H * (m * 8 + m * 4)           # Z^, running max
              + H * (m * dv * 4 + m * 4) / K  # T^ and its max, on the fold step
              + (K - 1) / K * held            # this eviction joins the held set
+             + (H * m * 8 if ring else 0)    # logits of the arrivals, on the fold step
              + H * dv * 4                    # outputs
              + 4 + H * 8)
     return read, write

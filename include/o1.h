@@ -54,8 +54,11 @@ enum o1_status {
  * (NystromHead::far_insert on the nystrom.rs source page adds every evicted key
  * to T^ at once) and adds them all to T^ with every O1_FOLD_PERIOD-th eviction,
  * so T^, otherwise the step's largest write, is rewritten once per
- * O1_FOLD_PERIOD steps.  Outputs are those of the per-eviction update up to
- * rounding.  A group's held count is its far_len mod O1_FOLD_PERIOD. */
+ * O1_FOLD_PERIOD steps.  With w >= O1_FOLD_PERIOD the far-insert logits
+ * q~ . k * scale of each key are computed on the fold that follows its arrival
+ * (one pass over q~ per O1_FOLD_PERIOD steps) and kept with its ring slot until
+ * it leaves.  Outputs are those of the per-eviction update up to rounding.  A
+ * group's held count is its far_len mod O1_FOLD_PERIOD. */
 #define O1_FOLD_PERIOD 8
 
 /* O1Rect of the nystrom.rs source page: how the indefinite skeleton is
@@ -262,8 +265,10 @@ int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes);
  * state transfer; the decode path never needs them.  Reading O1_FIELD_T_HAT
  * returns T^ with the held evictions (O1_FOLD_PERIOD) added, built in a
  * stream-ordered temporary; the state is left as it is.  Every write first
- * adds the held evictions to the stored T^ (none are held afterwards), and a
- * write of O1_FIELD_M_MAX takes the stored T^ to be at the new running max.
+ * adds the held evictions to the stored T^ (none are held afterwards), a
+ * write of O1_FIELD_M_MAX takes the stored T^ to be at the new running max, and
+ * a write of O1_FIELD_NEAR_K or O1_FIELD_Q_TILDE recomputes the ring keys'
+ * far-insert logits.
  * Writing requires a sealed layer.
  * Errors: O1_EINVAL, O1_ESTATE, O1_ENOMEM (the T^ temporary), O1_EHIP. */
 int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, void *stream);

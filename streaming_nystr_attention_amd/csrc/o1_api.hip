@@ -131,8 +131,8 @@ void free_state(o1_groups *g)
     o1::DevState &s = g->st;
     void *ptrs[] = {s.near_k, s.near_v,   s.k_tilde,  s.q_tilde,  s.mu,       s.t_hat,
                     s.z_hat,  s.m_max,    s.win_head, s.far_len,  s.lambda,   s.tries,
-                    s.pend_v, s.pend_l,   s.m_ref,    g->lm64,    g->exact_k, g->exact_v,
-                    g->exact_ws, g->exact_held};
+                    s.pend_v, s.pend_l,   s.m_ref,    s.ring_l,   g->lm64,    g->exact_k,
+                    g->exact_v, g->exact_ws, g->exact_held};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
 }
@@ -411,6 +411,7 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         {(void **)&s.pend_v, Gs * o1::kPend * c.dv * sizeof(float)},
         {(void **)&s.pend_l, Gs * H * o1::kPend * M * sizeof(double)},
         {(void **)&s.m_ref, Gs * H * M * sizeof(float)},
+        {(void **)&s.ring_l, c.w >= o1::kPend ? Gs * c.w * H * M * sizeof(double) : 0},
         {(void **)&g->exact_k, Gs * E * c.d * sizeof(float)},
         {(void **)&g->exact_v, Gs * E * c.dv * sizeof(float)},
         {(void **)&g->exact_ws, ws_bytes},
@@ -605,6 +606,9 @@ int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, v
     // T^ is stored at the scale of the running max it was written against
     if (err == hipSuccess && field == O1_FIELD_M_MAX)
         err = hipMemcpyAsync(s.m_ref, s.m_max, bytes, hipMemcpyDeviceToDevice, st);
+    // the far-insert logits kept per ring slot follow the ring's keys and q~
+    if (err == hipSuccess && s.m > 0 && (field == O1_FIELD_NEAR_K || field == O1_FIELD_Q_TILDE))
+        err = o1::launch_ring_logits(s, whole_map(g), st);
     if (err != hipSuccess) return fail(O1_EHIP, "writing field %d failed: %s", field, hipGetErrorString(err));
     return ok();
 }

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     __shared__ float4 kn_s[C::CH], ke_s[C::CH];
     __shared__ float4 vn_s[C::VCH], ve_s[C::VCH];
     __shared__ float4 hv_s[kPend - 1][C::VCH];     // value rows of the held evictions (slots j < P)
+    __shared__ float4 kb_s[kPend][C::CH];          // fold with ring logits: the keys that arrived since the last fold
     __shared__ float mo_s[HPK][MM];                // running max before this step
     __shared__ float mr_s[HPK][MM];                // running max at the last fold (scale of t_hat)
     __shared__ double zo_s[HPK][MM];               // Z^ before this step
@@ -137,12 +138,17 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     extern __shared__ double lg_s[];               // [HPK][R] near logits, then weights
 
     const size_t gh0 = (size_t)g * HPK;  // first head of this group
-    const int e = s.win_head[g];
+    const int e = min(max(s.win_head[g], 0), s.w - 1);  // (in range unless written out of range)
     const int slot_row = S + e;
     // evictions held apart from t_hat before this step, and whether this
     // step's eviction completes the set (then all are folded into t_hat)
     const int P = (int)((uint64_t)s.far_len[gh0] % kPend);
     const bool fold = P == kPend - 1;
+    // far-insert logits kept per ring slot (w >= kPend): the evicted key's are
+    // read, and a fold computes those of the keys that arrived since the last
+    // one (slots e, e-1, ..., e-kPend+1), so q~ is read once per kPend steps
+    const bool ring = s.ring_l != nullptr;
+    const int w = s.w;
 
     float4 *nk = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * R * C::CH;
     float4 *nv = reinterpret_cast<float4 *>(s.near_v) + (size_t)g * R * C::VCH;
@@ -164,8 +170,17 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         const float4 *qg = reinterpret_cast<const float4 *>(io.q) + (size_t)ci * HPK * C::CH;
         for (int i = tid; i < HPK * C::CH; i += NT) (&q_s[0][0])[i] = qg[i];
         if (tid < C::CH) {
-            kn_s[tid] = reinterpret_cast<const float4 *>(io.k)[(size_t)ci * C::CH + tid];
-            ke_s[tid] = nk[(size_t)slot_row * C::CH + tid];
+            const float4 kin = reinterpret_cast<const float4 *>(io.k)[(size_t)ci * C::CH + tid];
+            kn_s[tid] = kin;
+            if (!ring) ke_s[tid] = nk[(size_t)slot_row * C::CH + tid];
+            else if (fold) kb_s[0][tid] = kin;
+        }
+        if (ring && fold) {
+            // the keys of the last kPend - 1 arrivals, in slots e-1 .. e-kPend+1
+            for (int i = tid; i < (kPend - 1) * C::CH; i += NT) {
+                const int j = 1 + i / C::CH, c = i - (j - 1) * C::CH;
+                kb_s[j][c] = nk[(size_t)(S + (e - j + w) % w) * C::CH + c];
+            }
         }
         if (tid >= 128 && tid < 128 + C::VCH) {
             const int c = tid - 128;
@@ -177,6 +192,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             mo_s[h][a] = s.m_max[gh0 * m + i];
             mr_s[h][a] = s.m_ref[gh0 * m + i];
             zo_s[h][a] = s.z_hat[gh0 * m + i];
+            if (ring) lf_s[h][a] = s.ring_l[((size_t)g * w + e) * HPK * m + i];
         }
         if constexpr (C::STAGE_M) {
             const float *mu = s.mu + gh0 * (size_t)m * m;
@@ -219,13 +235,15 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             // One row space in which each kind of row starts on a block row, so
             // the source of every load and the work on it are uniform across
             // the wave: [0, RP) near keys (R used), [RP, Q0) key landmarks (m
-            // used), [Q0, NTOT) query landmarks (far-insert logits against the
-            // evicted key).  Unused rows load a clamped row and are discarded.
+            // used), [Q0, NTOT) query landmarks (far-insert logits of the
+            // evicted key, or with ring logits, on a fold only, of the keys that
+            // arrived since the last fold).  Unused rows load a clamped row and
+            // are discarded.
             const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
             const int NQ = HPK * m;
             const int RP = (R + C::RPB - 1) / C::RPB * C::RPB;
             const int Q0 = (RP + m + C::RPB - 1) / C::RPB * C::RPB;
-            const int NTOT = Q0 + NQ;
+            const int NTOT = Q0 + (!ring || fold ? NQ : 0);
             constexpr int BR = C::UNR * C::RPB;  // rows per batch
             const int NB = (NTOT + BR - 1) / BR;
             const int r0 = wave * C::RPW + rsub;
@@ -239,7 +257,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                     const float4 t = q_s[h][sub + C::LPR * k];
                     qd[h][k][0] = t.x, qd[h][k][1] = t.y, qd[h][k][2] = t.z, qd[h][k][3] = t.w;
                 }
-                const float4 t = ke_s[sub + C::LPR * k];
+                const float4 t = ring ? make_float4(0.f, 0.f, 0.f, 0.f) : ke_s[sub + C::LPR * k];
                 kd[k][0] = t.x, kd[k][1] = t.y, kd[k][2] = t.z, kd[k][3] = t.w;
             }
             auto dotd = [](const double (&a)[4], const float4 x) {
@@ -287,13 +305,26 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                                 land_s[my_head][r - RP] = tot;
                             }
                         }
-                    } else {
+                    } else if (rb >= NTOT) {
+                        // past the row space (the last batch's tail): nothing
+                    } else if (!ring) {
                         double acc = 0.0;
 #pragma unroll
                         for (int k = 0; k < C::CPL; ++k) acc += dotd(kd[k], x[u][k]);
                         acc = group_sum<C::LPR>(acc);
                         const int rq = r - Q0;
                         if (sub == 0 && rq < NQ) lf_s[rq / m][rq % m] = acc * scale;
+                    } else {
+                        const int rq = r - Q0;
+#pragma unroll 1
+                        for (int j = 0; j < kPend; ++j) {
+                            double acc = 0.0;
+#pragma unroll
+                            for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kb_s[j][sub + C::LPR * k]);
+                            acc = group_sum<C::LPR>(acc);
+                            if (sub == 0 && rq < NQ)
+                                s.ring_l[((size_t)g * w + (e - j + w) % w) * NQ + rq] = acc * scale;
+                        }
                     }
                 }
             };
@@ -342,28 +373,55 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 }
             }
 
-            // far-insert logits of the evicted key against every query landmark
-            float4 kr[C::CPL];
-#pragma unroll
-            for (int k = 0; k < C::CPL; ++k) kr[k] = ke_s[sub + C::LPR * k];
+            // far-insert logits against every query landmark: of the evicted key
+            // (no ring logits), or, on a fold with ring logits, of the keys
+            // that arrived since the last fold (stored per ring slot)
             const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
             const int NQ = HPK * m;
-            for (int base = wave * C::RPW; base < NQ; base += C::UNR * C::RPB) {
-                float4 x[C::UNR][C::CPL];
+            if (!ring) {
+                float4 kr[C::CPL];
 #pragma unroll
-                for (int u = 0; u < C::UNR; ++u) {
-                    const int r = min(base + u * C::RPB + rsub, NQ - 1);
+                for (int k = 0; k < C::CPL; ++k) kr[k] = ke_s[sub + C::LPR * k];
+                for (int base = wave * C::RPW; base < NQ; base += C::UNR * C::RPB) {
+                    float4 x[C::UNR][C::CPL];
 #pragma unroll
-                    for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(qt + (size_t)r * C::CH + sub + C::LPR * k);
+                    for (int u = 0; u < C::UNR; ++u) {
+                        const int r = min(base + u * C::RPB + rsub, NQ - 1);
+#pragma unroll
+                        for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(qt + (size_t)r * C::CH + sub + C::LPR * k);
+                    }
+#pragma unroll
+                    for (int u = 0; u < C::UNR; ++u) {
+                        const int r = base + u * C::RPB + rsub;
+                        double acc = 0.0;
+#pragma unroll
+                        for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kr[k]);
+                        acc = group_sum<C::LPR>(acc);
+                        if (sub == 0 && r < NQ) lf_s[r / m][r % m] = acc * scale;
+                    }
                 }
+            } else if (fold) {
+                for (int base = wave * C::RPW; base < NQ; base += C::UNR * C::RPB) {
+                    float4 x[C::UNR][C::CPL];
 #pragma unroll
-                for (int u = 0; u < C::UNR; ++u) {
-                    const int r = base + u * C::RPB + rsub;
-                    double acc = 0.0;
+                    for (int u = 0; u < C::UNR; ++u) {
+                        const int r = min(base + u * C::RPB + rsub, NQ - 1);
 #pragma unroll
-                    for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kr[k]);
-                    acc = group_sum<C::LPR>(acc);
-                    if (sub == 0 && r < NQ) lf_s[r / m][r % m] = acc * scale;
+                        for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(qt + (size_t)r * C::CH + sub + C::LPR * k);
+                    }
+#pragma unroll
+                    for (int u = 0; u < C::UNR; ++u) {
+                        const int r = base + u * C::RPB + rsub;
+#pragma unroll 1
+                        for (int j = 0; j < kPend; ++j) {
+                            double acc = 0.0;
+#pragma unroll
+                            for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kb_s[j][sub + C::LPR * k]);
+                            acc = group_sum<C::LPR>(acc);
+                            if (sub == 0 && r < NQ)
+                                s.ring_l[((size_t)g * w + (e - j + w) % w) * NQ + r] = acc * scale;
+                        }
+                    }
                 }
             }
         }
@@ -742,7 +800,107 @@ __global__ __launch_bounds__(256) void fold_kernel(DevState s, float *dst, int r
     }
 }
 
+// One work-group per (call index, head): the far-insert logits of every ring
+// slot's key, ring_l[g][s][h][i] = q~_{h,i} . k_{sink+s} * scale, f64 sums of
+// f32 products in component order.  q~ of the head and a tile of TS ring rows
+// sit in LDS, rows padded to an odd number of 16-byte units; each thread
+// computes 4 x 4 (slot, landmark) dots, its slots SG rows apart and its
+// landmarks LG rows apart, so the lanes of a wave read distinct banks.
+template <int MM>
+struct RingShape {
+    static constexpr int LG = MM / 4;      // landmark groups of 4
+    static constexpr int SG = 16;          // slot groups of 4
+    static constexpr int TS = 4 * SG;      // slots per tile
+    static constexpr int NTH = LG * SG;    // threads (LDS of 51 / 68 KB: 3 / 2 work-groups per CU)
+};
+
+template <int MM>
+__global__ __launch_bounds__(RingShape<MM>::NTH) void ring_logits_kernel(DevState s, GroupMap map)
+{
+    using C = RingShape<MM>;
+    const int g = map.state(blockIdx.x), h = blockIdx.y, tid = threadIdx.x;
+    const int m = s.m, d = s.d, w = s.w, H = s.hpk, ld = d + 4, d4 = d / 4;
+    extern __shared__ float4 ring_smem[];
+    float *qs = reinterpret_cast<float *>(ring_smem);  // [MM][ld]
+    float *ks = qs + MM * ld;                          // [TS][ld]
+    const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde + ((size_t)g * H + h) * m * d);
+    for (int t = tid; t < MM * d4; t += C::NTH) {
+        const int i = t / d4, c = t - i * d4;
+        reinterpret_cast<float4 *>(qs + i * ld)[c] = i < m ? qt[(size_t)i * d4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int sg = tid % C::SG, lg = tid / C::SG;
+    const float4 *ring = reinterpret_cast<const float4 *>(s.near_k + ((size_t)g * s.R + s.sink) * d);
+    const double scale = (double)s.scale;
+    for (int s0 = 0; s0 < w; s0 += C::TS) {
+        __syncthreads();  // q~ staged; the previous tile consumed
+        for (int t = tid; t < C::TS * d4; t += C::NTH) {
+            const int r = t / d4, c = t - r * d4;
+            reinterpret_cast<float4 *>(ks + r * ld)[c] = ring[(size_t)min(s0 + r, w - 1) * d4 + c];
+        }
+        __syncthreads();
+        double acc[4][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+        const float *kr = ks + sg * ld, *qr = qs + lg * ld;
+        for (int c = 0; c < d; c += 4) {
+            float4 kv[4], qv[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) kv[a] = *reinterpret_cast<const float4 *>(kr + a * C::SG * ld + c);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) qv[b] = *reinterpret_cast<const float4 *>(qr + b * C::LG * ld + c);
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    double t = fma((double)kv[a].x, (double)qv[b].x, acc[a][b]);
+                    t = fma((double)kv[a].y, (double)qv[b].y, t);
+                    t = fma((double)kv[a].z, (double)qv[b].z, t);
+                    acc[a][b] = fma((double)kv[a].w, (double)qv[b].w, t);
+                }
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int slot = s0 + sg + a * C::SG;
+            if (slot >= w) continue;
+            double *dst = s.ring_l + (((size_t)g * w + slot) * H + h) * m;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (lg + b * C::LG < m) dst[lg + b * C::LG] = acc[a][b] * scale;
+        }
+    }
+}
+
+template <int MM>
+hipError_t launch_ring(const DevState &s, const GroupMap &map, hipStream_t stream)
+{
+    const size_t lds = sizeof(float) * (size_t)(MM + RingShape<MM>::TS) * (s.d + 4);
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    const uint64_t bit = dev < 64 ? 1ull << dev : 0;
+    if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&ring_logits_kernel<MM>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(sizeof(float) * (MM + RingShape<MM>::TS) * (128 + 4)));
+        if (err != hipSuccess) return err;
+        done.fetch_or(bit, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(ring_logits_kernel<MM>, dim3(map.count, s.hpk), dim3(RingShape<MM>::NTH), lds, stream, s, map);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_t stream)
+{
+    if (!s.ring_l) return hipSuccess;
+    if (s.m < 1 || s.m > kMaxLandmarks || s.d > 128 || s.d % 4) return hipErrorInvalidValue;
+    if (s.m <= 32) return launch_ring<32>(s, map, stream);
+    return launch_ring<kMaxLandmarks>(s, map, stream);
+}
 
 hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t stream)
 {

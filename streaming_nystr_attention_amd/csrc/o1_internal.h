@@ -36,6 +36,10 @@ static_assert(kPend >= 2, "a fold period of 1 holds nothing");
 //   m_ref  [G][hpk][m] (f32)              the running max at the last fold: the stored
 //                                         t_hat is at scale e^{-m_ref}; the far numerator is
 //   T^_i = e^{m_ref_i - m_max_i} t_hat_i + sum_{j<P} e^{pend_l_ij - m_max_i} pend_v_j
+// Far-insert logits of the keys in the ring (only when w >= kPend):
+//   ring_l [G][w][hpk][m] (f64)           q~_{h,i} . k * scale for the key in ring slot s,
+//                                         computed within kPend steps of the key's arrival
+//                                         (one pass over q~ per fold) and read when it leaves
 struct DevState {
     int G, hpk, d, dv, w, sink, R, rect;
     int m;        // m_eff of the current prefill
@@ -46,6 +50,7 @@ struct DevState {
     int64_t *far_len;
     float *pend_v, *m_ref;
     double *pend_l;
+    double *ring_l;    // null when w < kPend (the step then reads q~ at every eviction)
     int stream_state;  // 1 when the state is larger than the Infinity Cache (decode streams it)
 };
 
@@ -131,6 +136,9 @@ hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const Group
 // True when the decode kernel is compiled for this shape.
 bool decode_supported(int d, int dv, int hpk, int m, int R);
 hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stream);
+// ring_l of every ring slot of the groups in `map` from their ring rows and q~
+// (after a prefill, or a write of the ring or of q~).  No-op when ring_l is null.
+hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_t stream);
 // T^ with the held evictions folded in, for every group, into dst ([G][hpk][m][dv]
 // f32; may be s.t_hat).  With `reset` the state's held set is then emptied
 // (m_ref = m_max, every slot's logits -inf); dst must then be s.t_hat.

@@ -606,6 +606,8 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
         hipLaunchKernelGGL(gram_pinv_kernel, dim3(n * s.hpk), dim3(kThreads), lds, stream, s, io, kRidgeRel);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    // far-insert logits of the ring's keys (the landmarks and ring are in place)
+    if ((err = launch_ring_logits(s, io.map, stream)) != hipSuccess) return err;
     if (s.d == 128 && s.dv == 128) return launch_far_m<128, 128>(s, io, stream);
     if (s.d == 64 && s.dv == 64) return launch_far_m<64, 64>(s, io, stream);
     return hipErrorInvalidValue;
