@@ -92,6 +92,16 @@ def test_decode_negative_mixing_drops_far_field():
     decode_parity(wl, frozen_override=mu)
 
 
+@pytest.mark.parametrize("w", [P.FOLD_PERIOD - 1, P.FOLD_PERIOD, P.FOLD_PERIOD + 1])
+def test_decode_windows_around_the_fold_period(w):
+    # w = FOLD_PERIOD is the shortest window whose keys get their far-insert
+    # logits on a fold and keep them per ring slot (every slot is rewritten by
+    # each fold); one less takes them from q~ at every eviction
+    wl = W.Workload(f"w{w}", 2, 1, 2, 2, 128, 128, 16, w, 2, T=133 + w, steps=3 * P.FOLD_PERIOD + 5,
+                    q_std=2.0, k_std=2.0, seed=40 + w)
+    decode_parity(wl)
+
+
 def test_decode_hpk1_window1():
     wl = W.Workload("w1", 2, 1, 1, 1, 128, 128, 4, 1, 0, T=40, steps=30, seed=15)
     decode_parity(wl)
