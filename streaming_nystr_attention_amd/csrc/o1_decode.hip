@@ -800,96 +800,60 @@ __global__ __launch_bounds__(256) void fold_kernel(DevState s, float *dst, int r
     }
 }
 
-// One work-group per (call index, head): the far-insert logits of every ring
-// slot's key, ring_l[g][s][h][i] = q~_{h,i} . k_{sink+s} * scale, f64 sums of
-// f32 products in component order.  q~ of the head and a tile of TS ring rows
-// sit in LDS, rows padded to an odd number of 16-byte units; each thread
-// computes 4 x 4 (slot, landmark) dots, its slots SG rows apart and its
-// landmarks LG rows apart, so the lanes of a wave read distinct banks.
-template <int MM>
-struct RingShape {
-    static constexpr int LG = MM / 4;      // landmark groups of 4
-    static constexpr int SG = 16;          // slot groups of 4
-    static constexpr int TS = 4 * SG;      // slots per tile
-    static constexpr int NTH = LG * SG;    // threads (LDS of 51 / 68 KB: 3 / 2 work-groups per CU)
-};
+// One work-group (4 waves) per (call index, head): the far-insert logits of
+// every ring slot's key, ring_l[g][s][h][i] = q~_{h,i} . k_{sink+s} * scale, a
+// dense [w x d] x [d x m] product on f64 MFMA (v_mfma_f64_16x16x4f64: f32
+// inputs widened to f64, so every product is exact and the sums are f64).
+// q~ of the head (rows past m zero) and a chunk of 64 ring rows sit in LDS,
+// rows padded to an odd length; each wave takes 16 x 16 (slot, landmark) tiles.
+// Operand layout: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in
+// lane j + 16 (i mod 4), element i / 4.
+constexpr int kRingChunk = 64;
 
-template <int MM>
-__global__ __launch_bounds__(RingShape<MM>::NTH) void ring_logits_kernel(DevState s, GroupMap map)
+__global__ __launch_bounds__(256) void ring_logits_kernel(DevState s, GroupMap map)
 {
-    using C = RingShape<MM>;
-    const int g = map.state(blockIdx.x), h = blockIdx.y, tid = threadIdx.x;
-    const int m = s.m, d = s.d, w = s.w, H = s.hpk, ld = d + 4, d4 = d / 4;
-    extern __shared__ float4 ring_smem[];
-    float *qs = reinterpret_cast<float *>(ring_smem);  // [MM][ld]
-    float *ks = qs + MM * ld;                          // [TS][ld]
+    const int g = map.state(blockIdx.x), h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = s.m, d = s.d, w = s.w, H = s.hpk, ld = d + 1, d4 = d / 4;
+    const int mt = (m + 15) / 16;  // landmark tiles
+    extern __shared__ float ring_smem[];
+    float *qs = ring_smem;         // [16 mt][ld]
+    float *ks = qs + 16 * mt * ld; // [kRingChunk][ld]
     const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde + ((size_t)g * H + h) * m * d);
-    for (int t = tid; t < MM * d4; t += C::NTH) {
+    for (int t = tid; t < 16 * mt * d4; t += 256) {
         const int i = t / d4, c = t - i * d4;
-        reinterpret_cast<float4 *>(qs + i * ld)[c] = i < m ? qt[(size_t)i * d4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 v = i < m ? qt[(size_t)i * d4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float *dst = qs + i * ld + 4 * c;
+        dst[0] = v.x, dst[1] = v.y, dst[2] = v.z, dst[3] = v.w;
     }
-    const int sg = tid % C::SG, lg = tid / C::SG;
     const float4 *ring = reinterpret_cast<const float4 *>(s.near_k + ((size_t)g * s.R + s.sink) * d);
     const double scale = (double)s.scale;
-    for (int s0 = 0; s0 < w; s0 += C::TS) {
-        __syncthreads();  // q~ staged; the previous tile consumed
-        for (int t = tid; t < C::TS * d4; t += C::NTH) {
+    const int li = lane & 15, lk = lane >> 4;
+    for (int s0 = 0; s0 < w; s0 += kRingChunk) {
+        __syncthreads();  // q~ staged; the previous chunk consumed
+        for (int t = tid; t < kRingChunk * d4; t += 256) {
             const int r = t / d4, c = t - r * d4;
-            reinterpret_cast<float4 *>(ks + r * ld)[c] = ring[(size_t)min(s0 + r, w - 1) * d4 + c];
+            const float4 v = ring[(size_t)min(s0 + r, w - 1) * d4 + c];
+            float *dst = ks + r * ld + 4 * c;
+            dst[0] = v.x, dst[1] = v.y, dst[2] = v.z, dst[3] = v.w;
         }
         __syncthreads();
-        double acc[4][4];
+        const int st = min(kRingChunk, w - s0 + 15) / 16;  // slot tiles in this chunk
+        for (int t = wave; t < st * mt; t += 4) {
+            const int a = t / mt, b = t - a * mt;
+            const float *kr = ks + (16 * a + li) * ld + lk;  // A[i][k] = k_slot[c + k]
+            const float *qr = qs + (16 * b + li) * ld + lk;  // B[k][j] = q~_j[c + k]
+            __attribute__((ext_vector_type(4))) double acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+            for (int c = 0; c < d; c += 4)
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[c], (double)qr[c], acc, 0, 0, 0);
+            const int i = 16 * b + li;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-        const float *kr = ks + sg * ld, *qr = qs + lg * ld;
-        for (int c = 0; c < d; c += 4) {
-            float4 kv[4], qv[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) kv[a] = *reinterpret_cast<const float4 *>(kr + a * C::SG * ld + c);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) qv[b] = *reinterpret_cast<const float4 *>(qr + b * C::LG * ld + c);
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    double t = fma((double)kv[a].x, (double)qv[b].x, acc[a][b]);
-                    t = fma((double)kv[a].y, (double)qv[b].y, t);
-                    t = fma((double)kv[a].z, (double)qv[b].z, t);
-                    acc[a][b] = fma((double)kv[a].w, (double)qv[b].w, t);
-                }
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int slot = s0 + sg + a * C::SG;
-            if (slot >= w) continue;
-            double *dst = s.ring_l + (((size_t)g * w + slot) * H + h) * m;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (lg + b * C::LG < m) dst[lg + b * C::LG] = acc[a][b] * scale;
+            for (int e = 0; e < 4; ++e) {
+                const int slot = s0 + 16 * a + 4 * e + lk;
+                if (slot < w && i < m) s.ring_l[(((size_t)g * w + slot) * H + h) * m + i] = acc[e] * scale;
+            }
         }
     }
-}
-
-template <int MM>
-hipError_t launch_ring(const DevState &s, const GroupMap &map, hipStream_t stream)
-{
-    const size_t lds = sizeof(float) * (size_t)(MM + RingShape<MM>::TS) * (s.d + 4);
-    static std::atomic<uint64_t> done{0};
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    const uint64_t bit = dev < 64 ? 1ull << dev : 0;
-    if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&ring_logits_kernel<MM>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)(sizeof(float) * (MM + RingShape<MM>::TS) * (128 + 4)));
-        if (err != hipSuccess) return err;
-        done.fetch_or(bit, std::memory_order_release);
-    }
-    hipLaunchKernelGGL(ring_logits_kernel<MM>, dim3(map.count, s.hpk), dim3(RingShape<MM>::NTH), lds, stream, s, map);
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -898,8 +862,22 @@ hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_
 {
     if (!s.ring_l) return hipSuccess;
     if (s.m < 1 || s.m > kMaxLandmarks || s.d > 128 || s.d % 4) return hipErrorInvalidValue;
-    if (s.m <= 32) return launch_ring<32>(s, map, stream);
-    return launch_ring<kMaxLandmarks>(s, map, stream);
+    // LDS: q~ rows of the padded landmark tiles and one chunk of ring rows
+    const size_t lds = sizeof(float) * (size_t)(16 * ((s.m + 15) / 16) + kRingChunk) * (s.d + 1);
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    const uint64_t bit = dev < 64 ? 1ull << dev : 0;
+    if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&ring_logits_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(sizeof(float) * (kMaxLandmarks + kRingChunk) * (128 + 1)));
+        if (err != hipSuccess) return err;
+        done.fetch_or(bit, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(ring_logits_kernel, dim3(map.count, s.hpk), dim3(256), lds, stream, s, map);
+    return hipGetLastError();
 }
 
 hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t stream)
