@@ -236,14 +236,13 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             // the source of every load and the work on it are uniform across
             // the wave: [0, RP) near keys (R used), [RP, Q0) key landmarks (m
             // used), [Q0, NTOT) query landmarks (far-insert logits of the
-            // evicted key, or with ring logits, on a fold only, of the keys that
-            // arrived since the last fold).  Unused rows load a clamped row and
-            // are discarded.
+            // evicted key; none with ring logits).  Unused rows load a clamped
+            // row and are discarded.
             const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
             const int NQ = HPK * m;
             const int RP = (R + C::RPB - 1) / C::RPB * C::RPB;
             const int Q0 = (RP + m + C::RPB - 1) / C::RPB * C::RPB;
-            const int NTOT = Q0 + (!ring || fold ? NQ : 0);
+            const int NTOT = Q0 + (ring ? 0 : NQ);
             constexpr int BR = C::UNR * C::RPB;  // rows per batch
             const int NB = (NTOT + BR - 1) / BR;
             const int r0 = wave * C::RPW + rsub;
@@ -307,24 +306,13 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                         }
                     } else if (rb >= NTOT) {
                         // past the row space (the last batch's tail): nothing
-                    } else if (!ring) {
+                    } else {
                         double acc = 0.0;
 #pragma unroll
                         for (int k = 0; k < C::CPL; ++k) acc += dotd(kd[k], x[u][k]);
                         acc = group_sum<C::LPR>(acc);
                         const int rq = r - Q0;
                         if (sub == 0 && rq < NQ) lf_s[rq / m][rq % m] = acc * scale;
-                    } else {
-                        const int rq = r - Q0;
-#pragma unroll 1
-                        for (int j = 0; j < kPend; ++j) {
-                            double acc = 0.0;
-#pragma unroll
-                            for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kb_s[j][sub + C::LPR * k]);
-                            acc = group_sum<C::LPR>(acc);
-                            if (sub == 0 && rq < NQ)
-                                s.ring_l[((size_t)g * w + (e - j + w) % w) * NQ + rq] = acc * scale;
-                        }
                     }
                 }
             };
@@ -421,6 +409,38 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                             if (sub == 0 && r < NQ)
                                 s.ring_l[((size_t)g * w + (e - j + w) % w) * NQ + r] = acc * scale;
                         }
+                    }
+                }
+            }
+        }
+
+        // on a fold with ring logits, shapes with the streamed row pass (many
+        // heads): the far-insert logits of the kPend latest keys against every
+        // query landmark, a [hpk m x D] x [D x kPend] product on f64 MFMA in
+        // 16-row tiles (the other shapes take them in the row pass, whose rows
+        // span few lanes) (A[i][k] = q~ row i, component c + k, read
+        // through the cache; B[k][j] = key j, component c + k, from LDS, zero for
+        // j >= kPend; D[i][j] in lane j + 16 (i mod 4), element i / 4)
+        if (C::STREAM_ROWS && ring && fold) {
+            const int NQ = HPK * m;
+            const int li = lane & 15, lk = lane >> 4;
+            const float *kbf = reinterpret_cast<const float *>(&kb_s[0][0]);  // [kPend][D]
+            const float *qtf = s.q_tilde + gh0 * m * D;                       // [NQ][D]
+            for (int t = wave; t < (NQ + 15) / 16; t += C::NW) {
+                const float *qa = qtf + (size_t)min(16 * t + li, NQ - 1) * D + lk;
+                const float *kb = kbf + min(li, kPend - 1) * D + lk;
+                __attribute__((ext_vector_type(4))) double acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+                for (int c = 0; c < D; c += 4) {
+                    const double bv = li < kPend ? (double)kb[c] : 0.0;
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[c], bv, acc, 0, 0, 0);
+                }
+                if (li < kPend) {
+                    double *dst = s.ring_l + ((size_t)g * w + (e - li + w) % w) * NQ;
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int r = 16 * t + 4 * r4 + lk;
+                        if (r < NQ) dst[r] = acc[r4] * scale;
                     }
                 }
             }
