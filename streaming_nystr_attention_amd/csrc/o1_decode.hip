@@ -12,9 +12,8 @@
 //      head's mixing matrix M, and the held evictions (kPend): with P =
 //      far_len mod kPend, the value rows and logits of slots j < P, whose
 //      logits become weights e^{l - m_max} against the running max before
-//      this step.  (Each staging loop waits for its own loads; issuing them
-//      all first measured slower on large launches, whose work-groups overlap
-//      anyway.)  Then row sink+e is overwritten by the new k/v (advance); the
+//      this step.  Every load is issued before any is stored (one round
+//      trip).  Then row sink+e is overwritten by the new k/v (advance); the
 //      evicted value row joins the held set (slot P) unless this step folds.
 //   1. row-dot pass, f64 accumulation, each row split over LPR lanes and UNR
 //      rows per lane in flight:
@@ -101,8 +100,8 @@ struct DecodeShape {
     static_assert(RED_H >= 1 && HPK % RED_H == 0, "heads must split into reduction rounds");
     static_assert(RL >= kPend, "each held value row needs a row lane of its own");
     static_assert((kPend - 1) * VCH <= NT, "one held value float4 per thread");
-    static_assert(NT != 512 || (HPK * CH <= NT && (kPend - 1) * CH <= NT && HPK * MM <= NT && 128 + VCH <= NT),
-                  "the 512-thread prologue loads at most one element of each kind per thread");
+    static_assert(HPK * CH <= NT && (kPend - 1) * CH <= NT && HPK * MM <= NT && 128 + VCH <= NT,
+                  "the prologue loads at most one element of each kind per thread");
 };
 
 template <int D, int DV, int HPK, int MM, int NT, bool STREAM>
@@ -170,99 +169,66 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             if (i < nl && (i / m) % kPend < P) hlr[u] = s.pend_l[gh0 * kPend * m + i];
         }
         const float4 *qg = reinterpret_cast<const float4 *>(io.q) + (size_t)ci * HPK * C::CH;
-        if constexpr (NT == 512) {
-            // few work-groups per CU: every load is issued before any is
-            // stored, so the prologue costs one round trip (each thread has at
-            // most one element of each kind)
-            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            const bool q_mine = tid < HPK * C::CH, k_mine = tid < C::CH;
-            const bool v_mine = tid >= 128 && tid < 128 + C::VCH, st_mine = tid < HPK * m;
-            const bool kb_mine = ring && fold && tid < (kPend - 1) * C::CH;
-            const int kbj = 1 + tid / C::CH, kbc = tid - (kbj - 1) * C::CH;
-            float4 qv = z4, kin = z4, kev = z4, vin = z4, vev = z4, kbv = z4;
-            if (q_mine) qv = qg[tid];
-            if (k_mine) {
-                kin = reinterpret_cast<const float4 *>(io.k)[(size_t)ci * C::CH + tid];
-                if (!ring) kev = nk[(size_t)slot_row * C::CH + tid];
-            }
-            if (kb_mine) kbv = nk[(size_t)(S + (e - kbj + w) % w) * C::CH + kbc];
-            if (v_mine) {
-                vin = reinterpret_cast<const float4 *>(io.v)[(size_t)ci * C::VCH + tid - 128];
-                vev = nv[(size_t)slot_row * C::VCH + tid - 128];
-            }
-            float mo = 0.f, mr = 0.f;
-            double zo = 0.0, lr = 0.0;
-            if (st_mine) {
-                mo = s.m_max[gh0 * m + tid];
-                mr = s.m_ref[gh0 * m + tid];
-                zo = s.z_hat[gh0 * m + tid];
-                if (ring) lr = s.ring_l[((size_t)g * w + e) * HPK * m + tid];
-            }
-            constexpr int MUP = C::STAGE_M ? (HPK * MM * MM + NT - 1) / NT : 1;
-            float muv[MUP];
-            if constexpr (C::STAGE_M) {
-                const float *mu = s.mu + gh0 * (size_t)m * m;
+        // every load is issued before any is stored, so the prologue costs
+        // one round trip (each thread has at most one element of each kind,
+        // a few of M)
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const bool q_mine = tid < HPK * C::CH, k_mine = tid < C::CH;
+        const bool v_mine = tid >= 128 && tid < 128 + C::VCH, st_mine = tid < HPK * m;
+        const bool kb_mine = ring && fold && tid < (kPend - 1) * C::CH;
+        const int kbj = 1 + tid / C::CH, kbc = tid - (kbj - 1) * C::CH;
+        float4 qv = z4, kin = z4, kev = z4, vin = z4, vev = z4, kbv = z4;
+        if (q_mine) qv = qg[tid];
+        if (k_mine) {
+            kin = reinterpret_cast<const float4 *>(io.k)[(size_t)ci * C::CH + tid];
+            if (!ring) kev = nk[(size_t)slot_row * C::CH + tid];
+        }
+        if (kb_mine) kbv = nk[(size_t)(S + (e - kbj + w) % w) * C::CH + kbc];
+        if (v_mine) {
+            vin = reinterpret_cast<const float4 *>(io.v)[(size_t)ci * C::VCH + tid - 128];
+            vev = nv[(size_t)slot_row * C::VCH + tid - 128];
+        }
+        float mo = 0.f, mr = 0.f;
+        double zo = 0.0, lr = 0.0;
+        if (st_mine) {
+            mo = s.m_max[gh0 * m + tid];
+            mr = s.m_ref[gh0 * m + tid];
+            zo = s.z_hat[gh0 * m + tid];
+            if (ring) lr = s.ring_l[((size_t)g * w + e) * HPK * m + tid];
+        }
+        constexpr int MUP = C::STAGE_M ? (HPK * MM * MM + NT - 1) / NT : 1;
+        float muv[MUP];
+        if constexpr (C::STAGE_M) {
+            const float *mu = s.mu + gh0 * (size_t)m * m;
 #pragma unroll
-                for (int u = 0; u < MUP; ++u) {
-                    const int i = tid + u * NT;
-                    muv[u] = i < HPK * m * m ? mu[i] : 0.f;
-                }
+            for (int u = 0; u < MUP; ++u) {
+                const int i = tid + u * NT;
+                muv[u] = i < HPK * m * m ? mu[i] : 0.f;
             }
-            if (q_mine) (&q_s[0][0])[tid] = qv;
-            if (k_mine) {
-                kn_s[tid] = kin;
-                if (!ring) ke_s[tid] = kev;
-                else if (fold) kb_s[0][tid] = kin;
-            }
-            if (kb_mine) kb_s[kbj][kbc] = kbv;
-            if (v_mine) {
-                vn_s[tid - 128] = vin;
-                ve_s[tid - 128] = vev;
-            }
-            if (st_mine) {
-                const int h = tid / m, a = tid - h * m;
-                mo_s[h][a] = mo;
-                mr_s[h][a] = mr;
-                zo_s[h][a] = zo;
-                if (ring) lf_s[h][a] = lr;
-            }
-            if constexpr (C::STAGE_M) {
+        }
+        if (q_mine) (&q_s[0][0])[tid] = qv;
+        if (k_mine) {
+            kn_s[tid] = kin;
+            if (!ring) ke_s[tid] = kev;
+            else if (fold) kb_s[0][tid] = kin;
+        }
+        if (kb_mine) kb_s[kbj][kbc] = kbv;
+        if (v_mine) {
+            vn_s[tid - 128] = vin;
+            ve_s[tid - 128] = vev;
+        }
+        if (st_mine) {
+            const int h = tid / m, a = tid - h * m;
+            mo_s[h][a] = mo;
+            mr_s[h][a] = mr;
+            zo_s[h][a] = zo;
+            if (ring) lf_s[h][a] = lr;
+        }
+        if constexpr (C::STAGE_M) {
 #pragma unroll
-                for (int u = 0; u < MUP; ++u) {
-                    const int i = tid + u * NT;
-                    if (i < HPK * m * m) mu_s[i] = muv[u];
-                }
-            }
-        } else {
-                for (int i = tid; i < HPK * C::CH; i += NT) (&q_s[0][0])[i] = qg[i];
-            if (tid < C::CH) {
-                const float4 kin = reinterpret_cast<const float4 *>(io.k)[(size_t)ci * C::CH + tid];
-                kn_s[tid] = kin;
-                if (!ring) ke_s[tid] = nk[(size_t)slot_row * C::CH + tid];
-                else if (fold) kb_s[0][tid] = kin;
-            }
-            if (ring && fold) {
-                // the keys of the last kPend - 1 arrivals, in slots e-1 .. e-kPend+1
-                for (int i = tid; i < (kPend - 1) * C::CH; i += NT) {
-                    const int j = 1 + i / C::CH, c = i - (j - 1) * C::CH;
-                    kb_s[j][c] = nk[(size_t)(S + (e - j + w) % w) * C::CH + c];
-                }
-            }
-            if (tid >= 128 && tid < 128 + C::VCH) {
-                const int c = tid - 128;
-                vn_s[c] = reinterpret_cast<const float4 *>(io.v)[(size_t)ci * C::VCH + c];
-                ve_s[c] = nv[(size_t)slot_row * C::VCH + c];
-            }
-            for (int i = tid; i < HPK * m; i += NT) {
-                const int h = i / m, a = i - h * m;
-                mo_s[h][a] = s.m_max[gh0 * m + i];
-                mr_s[h][a] = s.m_ref[gh0 * m + i];
-                zo_s[h][a] = s.z_hat[gh0 * m + i];
-                if (ring) lf_s[h][a] = s.ring_l[((size_t)g * w + e) * HPK * m + i];
-            }
-            if constexpr (C::STAGE_M) {
-                const float *mu = s.mu + gh0 * (size_t)m * m;
-                for (int i = tid; i < HPK * m * m; i += NT) mu_s[i] = mu[i];
+            for (int u = 0; u < MUP; ++u) {
+                const int i = tid + u * NT;
+                if (i < HPK * m * m) mu_s[i] = muv[u];
             }
         }
         if (hv_mine) (&hv_s[0][0])[tid] = hvr;
