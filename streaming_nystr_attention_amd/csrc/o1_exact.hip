@@ -5,7 +5,8 @@
 //
 //   out_h = sum_{j in [first, n_keys)} softmax_j(q_h . k_j * scale) v_j
 //
-// exact_attend_kernel: grid (G, splits), 256 threads.  A work-group owns one
+// exact_attend_kernel: grid (G, splits), 512 threads for one or two query heads,
+// 256 for more.  A work-group owns one
 // key range of one group and walks it in chunks of kChunk keys with an online
 // per-head max: row-dot pass (f64, the decode kernel's lane split and head
 // reduction; the chunk's first V rows of each lane are loaded at its end, so
@@ -23,22 +24,27 @@
 namespace o1 {
 namespace {
 
-constexpr int kNT = 256, kNW = kNT / 64;
 constexpr int kChunk = 256;     // keys a work-group walks per step of its online softmax
 constexpr int kSplitKeys = 128; // fewest keys per work-group when a range is split
 
 template <int D, int DV, int HPK>
 struct ExactShape {
+    // one or two query heads: 512 threads (twice the rows per round trip on
+    // short key ranges) held to 128 VGPRs so that two work-groups share a CU's
+    // SIMDs; more heads need the registers of a 256-thread work-group
+    static constexpr int NT = HPK <= 2 ? 512 : 256;
+    static constexpr int NW = NT / 64;
+    static constexpr int WAVES_PER_SIMD = HPK <= 2 ? 4 : 1;
     static constexpr int CH = D / 4;
     static constexpr int LPR_WANT = HPK <= 2 ? 8 : (HPK <= 4 ? 16 : 32);
     static constexpr int LPR = LPR_WANT < CH ? LPR_WANT : CH;
     static constexpr int CPL = CH / LPR;
     static constexpr int RPW = 64 / LPR;
-    static constexpr int RPB = RPW * kNW;
+    static constexpr int RPB = RPW * NW;
     static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 2 ? 4 : 8);
     static constexpr int VCH = DV / 4;
-    static constexpr int RL = kNT / VCH;
-    static constexpr int RED_CAP = 16384 / (kNW * DV * 8);
+    static constexpr int RL = NT / VCH;
+    static constexpr int RED_CAP = 16384 / (NW * DV * 8);
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     // V rows per lane loaded before the chunk's softmax (more would cost a wave
     // per SIMD at hpk >= 4)
@@ -47,9 +53,11 @@ struct ExactShape {
 };
 
 template <int D, int DV, int HPK>
-__global__ __launch_bounds__(kNT) void exact_attend_kernel(ExactIO a)
+__global__ __launch_bounds__((ExactShape<D, DV, HPK>::NT))
+__attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) void exact_attend_kernel(ExactIO a)
 {
     using C = ExactShape<D, DV, HPK>;
+    constexpr int kNT = C::NT, kNW = C::NW;
     const int ci = blockIdx.x, sp = blockIdx.y;  // call index (q, out, new key, partials)
     const int g = a.map.state(ci);              // cache group
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -301,7 +309,8 @@ __global__ void exact_combine_kernel(ExactIO a, int splits)
 template <int D, int DV, int HPK>
 hipError_t launch_exact_shape(const ExactIO &a, int splits, hipStream_t stream)
 {
-    hipLaunchKernelGGL((exact_attend_kernel<D, DV, HPK>), dim3(a.map.count, splits), dim3(kNT), 0, stream, a);
+    hipLaunchKernelGGL((exact_attend_kernel<D, DV, HPK>), dim3(a.map.count, splits),
+                       dim3(ExactShape<D, DV, HPK>::NT), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || splits == 1) return err;
     hipLaunchKernelGGL(exact_combine_kernel, dim3(a.map.count), dim3(a.dv), 0, stream, a, splits);
