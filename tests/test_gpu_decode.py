@@ -117,6 +117,21 @@ MAX_SIZES = [
 ]
 
 
+LARGE_GRIDS = [
+    # 2048 groups: 256-thread decode work-groups, and the prefill's ring-key
+    # logits take all of a group's heads in one work-group (4 and 8 heads)
+    W.Workload("grid_hpk4", 256, 1, 8, 4, 128, 128, 32, 64, 4, T=300, steps=20, q_std=2.0,
+               k_std=2.0, seed=18),
+    W.Workload("grid_hpk8_d64", 256, 1, 8, 8, 64, 64, 16, 32, 2, T=200, steps=20, seed=19),
+]
+
+
+@pytest.mark.parametrize("wl", LARGE_GRIDS, ids=[w.name for w in LARGE_GRIDS])
+def test_decode_large_grid_many_heads(wl):
+    assert wl.groups >= 2048
+    decode_parity(wl, sample=W.sample_groups(wl))
+
+
 @pytest.mark.parametrize("wl", MAX_SIZES, ids=[w.name for w in MAX_SIZES])
 def test_decode_maximum_sizes(wl):
     assert wl.hpk * (wl.sink + wl.w) * 8 == 32 * 1024 and wl.m_eff == 64
