@@ -75,8 +75,9 @@ struct DecodeShape {
     static constexpr int TPT = (MM + RL - 1) / RL;                     // T^ rows per lane per head
     static constexpr bool STAGE_M = HPK * MM * MM <= 2048;             // M staged in LDS
     static constexpr bool PRE_T = HPK * TPT <= (NT == 256 ? 8 : 32);   // T^ prefetched in registers
-    // V rows prefetched per lane (6 where 8 would spill at 256 VGPRs)
-    static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : (HPK * MM >= 512 ? 6 : 8);
+    // V rows prefetched per lane (6 where 8 would spill at 256 VGPRs; 9 at 512
+    // threads covers a 128-key window plus 4 sinks, so no V batch follows)
+    static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : (HPK * MM >= 512 ? 6 : 9);
     static constexpr int VU = HPK <= 2 ? 9 : 8;                        // V rows per lane per batch
     static constexpr int MB = NT == 256 ? 16 : 32;                     // M rows in flight (unstaged M)
     static constexpr bool NTL = STREAM;                                // nontemporal state accesses
@@ -622,15 +623,24 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                     const double rb = r_s[h][b], gb = gain_s[h][b];
                     double t0 = (double)t.x * rb, t1 = (double)t.y * rb;
                     double t2 = (double)t.z * rb, t3 = (double)t.w * rb;
+                    // held row k + 1 loaded while row k is added in
+                    double wk = wf_s[h][0][b];
+                    float4 x = hv_s[0][cc];
 #pragma unroll 1
-                    for (int k = 0; k < kPend; ++k) {
-                        const double wk = wf_s[h][k][b];
-                        const float4 x = k < kPend - 1 ? hv_s[k][cc] : ve_s[cc];
+                    for (int k = 1; k < kPend; ++k) {
+                        const double wn = wf_s[h][k][b];
+                        const float4 xn = k < kPend - 1 ? hv_s[k][cc] : ve_s[cc];
                         t0 = fma(wk, (double)x.x, t0);
                         t1 = fma(wk, (double)x.y, t1);
                         t2 = fma(wk, (double)x.z, t2);
                         t3 = fma(wk, (double)x.w, t3);
+                        wk = wn;
+                        x = xn;
                     }
+                    t0 = fma(wk, (double)x.x, t0);
+                    t1 = fma(wk, (double)x.y, t1);
+                    t2 = fma(wk, (double)x.z, t2);
+                    t3 = fma(wk, (double)x.w, t3);
                     st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
                     acc[h][0] = fma(gb, t0, acc[h][0]);
                     acc[h][1] = fma(gb, t1, acc[h][1]);
