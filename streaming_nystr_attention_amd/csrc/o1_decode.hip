@@ -452,22 +452,29 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         // heads): the far-insert logits of the kPend latest keys against every
         // query landmark, a [hpk m x D] x [D x kPend] product on f64 MFMA in
         // 16-row tiles (the other shapes take them in the row pass, whose rows
-        // span few lanes) (A[i][k] = q~ row i, component c + k, read
-        // through the cache; B[k][j] = key j, component c + k, from LDS, zero for
-        // j >= kPend; D[i][j] in lane j + 16 (i mod 4), element i / 4)
+        // span few lanes).  A = q~ rows, read through the cache; B = the keys,
+        // from LDS, zero for j >= kPend.  The reduction index is permuted so the
+        // four k-lanes of a row read 64 contiguous bytes per load: in MFMA step
+        // (jj, c), k-lane kk stands for component 16 jj + 4 kk + c of A and B.
+        // (D[i][j] in lane j + 16 (i mod 4), element i / 4)
         if (C::STREAM_ROWS && ring && fold) {
             const int NQ = HPK * m;
             const int li = lane & 15, lk = lane >> 4;
-            const float *kbf = reinterpret_cast<const float *>(&kb_s[0][0]);  // [kPend][D]
-            const float *qtf = s.q_tilde + gh0 * m * D;                       // [NQ][D]
+            const float4 *qt4 = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH + lk;
+            const float4 *kb4 = &kb_s[min(li, kPend - 1)][lk];
+            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int t = wave; t < (NQ + 15) / 16; t += C::NW) {
-                const float *qa = qtf + (size_t)min(16 * t + li, NQ - 1) * D + lk;
-                const float *kb = kbf + min(li, kPend - 1) * D + lk;
+                const float4 *qa = qt4 + (size_t)min(16 * t + li, NQ - 1) * C::CH;
                 __attribute__((ext_vector_type(4))) double acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
-                for (int c = 0; c < D; c += 4) {
-                    const double bv = li < kPend ? (double)kb[c] : 0.0;
-                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[c], bv, acc, 0, 0, 0);
+#pragma unroll
+                for (int jj = 0; jj < D / 16; ++jj) {
+                    const float4 a = qa[4 * jj];
+                    float4 b = z4;
+                    if (li < kPend) b = kb4[4 * jj];
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.x, (double)b.x, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.y, (double)b.y, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.z, (double)b.z, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.w, (double)b.w, acc, 0, 0, 0);
                 }
                 if (li < kPend) {
                     double *dst = s.ring_l + ((size_t)g * w + (e - li + w) % w) * NQ;
