@@ -221,17 +221,20 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
         const double *qrow = qt + (size_t)(qi < m ? qi : 0) * d;
         const double *krow = kt + (size_t)(kj < m ? kj : 0) * d;
         f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
-        // d / 4 is a multiple of 16: a fixed-count inner loop unrolls (MFMA is
-        // convergent, so a runtime count leaves the loop rolled), issuing the
-        // loads of sixteen steps together
-        for (int k0 = 0; k0 < d / 4; k0 += 16) {
+        // The reduction index is permuted so that each lane loads two adjacent
+        // components at once: in step pair (jj, 0/1), k-lane kk stands for
+        // component 8 jj + 2 kk (+ 1), for both operands.  Rows past m read row
+        // 0; their products reach only entries set to zero below.  d / 8 is a
+        // multiple of 8: a fixed-count inner loop unrolls (MFMA is convergent,
+        // so a runtime count leaves the loop rolled), issuing eight loads together.
+        const double2 *q2 = reinterpret_cast<const double2 *>(qrow) + lk;
+        const double2 *k2 = reinterpret_cast<const double2 *>(krow) + lk;
+        for (int k0 = 0; k0 < d / 8; k0 += 8) {
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                const int ks = k0 + e;
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + lk] : 0.0,
-                                                          kj < m ? krow[ks * 4 + lk] : 0.0, acc, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(qi < m ? qrow[ks * 4 + 4 + lk] : 0.0,
-                                                           kj < m ? krow[ks * 4 + 4 + lk] : 0.0, acc2, 0, 0, 0);
+            for (int e = 0; e < 8; ++e) {
+                const double2 a = q2[(k0 + e) * 4], b = k2[(k0 + e) * 4];
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.x, b.x, acc, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(a.y, b.y, acc2, 0, 0, 0);
             }
         }
         acc += acc2;
