@@ -12,6 +12,7 @@ run on a thread pool.
 
 Parity status of each oracle function (what pins it is in ``tests/test_oracle_*``):
   seg_means, cholesky, ridge_pinv, exact attention      pinned
+  memory_bytes (skeleton and exact-only)                pinned
   prefill (sinks, ring placement, landmarks, replay)    pinned
   decode step (near/far joint division, rectifiers)     pinned
   absolute model quality (perplexity figures)           parity unpinned (needs

@@ -96,6 +96,9 @@ typedef struct orc_group {
     /* scratch, sized at prefill so step allocates nothing in skeleton mode */
     double *scr_s, *scr_fh, *scr_u, *scr_l, *scr_acc;
     int scr_s_cap;
+    /* length the page's per-head score scratch has (what memory_bytes counts):
+     * sink + w after seal, 0 after seal_exact, sink_len + win_len after a step */
+    int scr_s_len;
 } orc_group;
 
 static double f32_scale_of(int d)
@@ -129,82 +132,83 @@ void orc_seg_means(const float *xs, int t, int d, int m, double *out)
     }
 }
 
-/* cholesky (nystrom.rs source page): in-place lower factor of an SPD matrix g
- * [n][n]; entry (i, j<=i) becomes L[i][j].  Returns 1, or 0 when a pivot is
- * <= 0 or not finite.                                                        */
+/* cholesky (nystrom.rs source page): the lower-triangular L with L L^T = G
+ * for a symmetric positive definite G [n][n], written over G's lower triangle
+ * (the strict upper triangle is left as it was).  Column k at a time: the
+ * pivot is what remains of G[k][k] after the earlier columns' contributions;
+ * it must be positive and finite, else the factorisation fails (returns 0).
+ * Then L[k][k] = sqrt(pivot), L[i][k] = (remaining G[i][k]) / L[k][k] for
+ * i > k, and column k's contribution L[i][k] L[j][k] is taken off every
+ * remaining entry (i >= j > k).  Returns 1 on success.                      */
 int orc_cholesky(double *g, int n)
 {
-    for (int i = 0; i < n; ++i) {
-        for (int j = 0; j <= i; ++j) {
-            double s = g[i * n + j];
-            for (int k = 0; k < j; ++k) s -= g[i * n + k] * g[j * n + k];
-            if (i == j) {
-                if (!(s > 0.0) || !isfinite(s)) return 0;
-                g[i * n + i] = sqrt(s);
-            } else {
-                g[i * n + j] = s / g[j * n + j];
-            }
-        }
+    for (int k = 0; k < n; ++k) {
+        const double pivot = g[k * n + k];
+        if (!(pivot > 0.0) || !isfinite(pivot)) return 0;
+        const double lkk = sqrt(pivot);
+        g[k * n + k] = lkk;
+        for (int i = k + 1; i < n; ++i) g[i * n + k] /= lkk;
+        for (int j = k + 1; j < n; ++j)
+            for (int i = j; i < n; ++i) g[i * n + j] -= g[i * n + k] * g[j * n + k];
     }
     return 1;
 }
 
-/* ridge_pinv (nystrom.rs source page): M = (A^T A + lambda I)^-1 A^T for a
- * square a [n][n], lambda = ridge_rel * max(mean diag(A^T A), DBL_MIN).  When the
- * Cholesky factorisation fails, lambda grows tenfold, up to 12 attempts; after
- * that the result is the scaled identity diag(1/max(mean diag, DBL_MIN)).
- * Returns the number of the successful attempt (1..12), or 13 for the fallback.
- * *lambda_out receives the lambda of the successful attempt (or of the last). */
+/* ridge_pinv (nystrom.rs source page): the ridge-regularised pseudo-inverse
+ *   M = (A^T A + lambda I)^-1 A^T
+ * of a square A [n][n], with lambda = ridge_rel * max(tr(A^T A) / n, DBL_MIN).
+ * G = A^T A + lambda I = L L^T (cholesky above), so M follows from two
+ * triangular solves with A^T as the right-hand side: L Y = A^T, then
+ * L^T M = Y.  When the factorisation fails, lambda is multiplied by 10 and G
+ * rebuilt, up to 12 attempts; after that M is the scaled identity
+ * I / max(tr(A^T A) / n, DBL_MIN).
+ * Returns the attempt that factored (1..12), or 13 for the scaled identity.
+ * *lambda_out receives the lambda that factored; after the fallback it is
+ * the initial lambda times 10^12 (the value the growth reached).           */
 int orc_ridge_pinv(const double *a, int n, double ridge_rel, double *out, double *lambda_out)
 {
-    double *ata = (double *)malloc(sizeof(double) * n * n);
-    double *g = (double *)malloc(sizeof(double) * n * n);
-    double *x = (double *)malloc(sizeof(double) * n);
-    for (int i = 0; i < n; ++i)
-        for (int j = 0; j < n; ++j) {
-            double s = 0.0;
-            for (int k = 0; k < n; ++k) s += a[k * n + i] * a[k * n + j];
-            ata[i * n + j] = s;
-        }
-    double mean_diag = 0.0;
-    for (int i = 0; i < n; ++i) mean_diag += ata[i * n + i];
-    mean_diag /= (double)n;
-    double floor_diag = mean_diag > DBL_MIN ? mean_diag : DBL_MIN;
-    double lambda = ridge_rel * floor_diag;
-    int result = ORC_RIDGE_TRIES + 1;
-    for (int attempt = 1; attempt <= ORC_RIDGE_TRIES; ++attempt) {
-        memcpy(g, ata, sizeof(double) * n * n);
-        for (int i = 0; i < n; ++i) g[i * n + i] += lambda;
-        if (orc_cholesky(g, n)) {
-            /* G M = A^T, one column at a time; column j of A^T is row j of A. */
-            for (int j = 0; j < n; ++j) {
-                const double *rhs = a + (size_t)j * n;
-                for (int i = 0; i < n; ++i) { /* L y = rhs */
-                    double s = rhs[i];
-                    for (int k = 0; k < i; ++k) s -= g[i * n + k] * x[k];
-                    x[i] = s / g[i * n + i];
-                }
-                for (int i = n - 1; i >= 0; --i) { /* L^T x = y */
-                    double s = x[i];
-                    for (int k = i + 1; k < n; ++k) s -= g[k * n + i] * x[k];
-                    x[i] = s / g[i * n + i];
-                }
-                for (int i = 0; i < n; ++i) out[i * n + j] = x[i];
-            }
-            result = attempt;
-            break;
-        }
-        lambda *= 10.0;
+    const size_t nn = (size_t)n * n;
+    double *gram = (double *)calloc(nn, sizeof(double)); /* A^T A            */
+    double *fac = (double *)malloc(sizeof(double) * nn);  /* G, then L        */
+    /* A^T A as the sum over rows r of A of the outer product a_r a_r^T. */
+    for (int r = 0; r < n; ++r)
+        for (int i = 0; i < n; ++i)
+            for (int j = 0; j < n; ++j) gram[i * n + j] += a[r * n + i] * a[r * n + j];
+    double trace = 0.0;
+    for (int i = 0; i < n; ++i) trace += gram[i * n + i];
+    const double scale_ref = trace / (double)n > DBL_MIN ? trace / (double)n : DBL_MIN;
+    double lambda = ridge_rel * scale_ref;
+
+    int attempt = 1;
+    for (; attempt <= ORC_RIDGE_TRIES; ++attempt, lambda *= 10.0) {
+        memcpy(fac, gram, sizeof(double) * nn);
+        for (int i = 0; i < n; ++i) fac[i * n + i] += lambda;
+        if (orc_cholesky(fac, n)) break;
     }
-    if (result > ORC_RIDGE_TRIES) {
-        for (int i = 0; i < n * n; ++i) out[i] = 0.0;
-        for (int i = 0; i < n; ++i) out[i * n + i] = 1.0 / floor_diag;
+    if (attempt <= ORC_RIDGE_TRIES) {
+        /* out starts as A^T, becomes Y (forward, rows top-down), then M
+         * (backward, rows bottom-up); each row update runs over every
+         * column of the right-hand side at once. */
+        for (int i = 0; i < n; ++i)
+            for (int c = 0; c < n; ++c) out[i * n + c] = a[c * n + i];
+        for (int i = 0; i < n; ++i) {
+            for (int k = 0; k < i; ++k)
+                for (int c = 0; c < n; ++c) out[i * n + c] -= fac[i * n + k] * out[k * n + c];
+            for (int c = 0; c < n; ++c) out[i * n + c] /= fac[i * n + i];
+        }
+        for (int i = n - 1; i >= 0; --i) {
+            for (int k = i + 1; k < n; ++k)
+                for (int c = 0; c < n; ++c) out[i * n + c] -= fac[k * n + i] * out[k * n + c];
+            for (int c = 0; c < n; ++c) out[i * n + c] /= fac[i * n + i];
+        }
+    } else {
+        for (size_t t = 0; t < nn; ++t) out[t] = 0.0;
+        for (int i = 0; i < n; ++i) out[i * n + i] = 1.0 / scale_ref;
     }
     if (lambda_out) *lambda_out = lambda;
-    free(ata);
-    free(g);
-    free(x);
-    return result;
+    free(gram);
+    free(fac);
+    return attempt;
 }
 
 /* Exact softmax attention over n keys, brute force (the operator the near field
@@ -335,9 +339,10 @@ static void advance(orc_group *g, const float *k, const float *v)
     }
 }
 
-/* NystromHead::step (nystrom.rs source page): head h's output for query q
- * against the current sinks + window and its own far field.  The window
- * insertion for this position has already happened (advance).               */
+/* NystromHead::step (nystrom.rs source page): the output row of head h for
+ * query q.  Near part: exact logits over the sink rows and every window slot;
+ * advance has run before this, so the slots already hold this position's own
+ * key.  Far part: head h's T^, Z^ and running maxima through F M.           */
 static void head_step(orc_group *g, int h, const float *q, double *out, double *out_alt,
                       orc_diag *diag)
 {
@@ -463,6 +468,7 @@ int orc_prefill_group(orc_group *g, const float *qs, const float *ks, const floa
         g->win_len = t;
         g->m_eff = 0;
         ensure_score_cap(g, t + 64);
+        g->scr_s_len = 0; /* seal_exact reserves the scratch but leaves it empty */
         return 0;
     }
 
@@ -492,6 +498,7 @@ int orc_prefill_group(orc_group *g, const float *qs, const float *ks, const floa
     g->win_v = (float *)calloc((size_t)g->w * dv, sizeof(float));
     g->cap = g->w;
     ensure_score_cap(g, g->sink + g->w);
+    g->scr_s_len = g->sink + g->w;
     g->scr_fh = (double *)malloc(sizeof(double) * m);
     g->scr_u = (double *)malloc(sizeof(double) * m);
     g->scr_l = (double *)malloc(sizeof(double) * m);
@@ -559,6 +566,7 @@ int orc_step_group(orc_group *g, const float *q_all, const float *k, const float
 {
     if (!g || !g->sealed) return -1;
     advance(g, k, v);
+    g->scr_s_len = g->sink_len + g->win_len; /* every head's step resizes its scratch */
     for (int h = 0; h < g->hpk; ++h)
         head_step(g, h, q_all + (size_t)h * g->d, out_all + (size_t)h * g->dv,
                   out_alt ? out_alt + (size_t)h * g->dv : NULL, diag ? diag + h : NULL);
@@ -577,19 +585,29 @@ double orc_scale(const orc_group *g) { return g->scale; }
 double orc_lambda(const orc_group *g, int h) { return g->lambda ? g->lambda[h] : 0.0; }
 int orc_ridge_tries(const orc_group *g, int h) { return g->tries ? g->tries[h] : 0; }
 
-/* memory_bytes of the page, counted the way the page counts it: f32 words of
- * window + sinks + K~, plus per head T^, Z^, running max, Q~, M and scratch. */
+/* NystromState::memory_bytes (nystrom.rs source page): f32 words of the
+ * vectors the group holds (window, sinks, K~) and each head holds (T^, Z^,
+ * running max, Q~, M and its four scratch vectors), counted by length, as the
+ * page counts them, times 4 bytes.
+ *   skeleton:   window w (d + dv), sinks sink (d + dv), K~ m d; per head
+ *               m dv + m + m + m d + m m + (sink + w) + 3 m.
+ *   exact-only: window (t + steps)(d + dv); per head only the score scratch,
+ *               empty until the first step and sized to every key after it.
+ * A group never prefilled holds nothing.  (State an earlier prompt left in a
+ * reused group is not counted: this oracle releases it at every prefill.)   */
 size_t orc_memory_bytes(const orc_group *g)
 {
-    size_t m = (size_t)g->m_eff, words = 0;
-    words += (size_t)g->cap * (g->d + g->dv);
-    words += (size_t)g->sink_len * (g->d + g->dv);
-    words += m * g->d;
-    if (!g->exact_only)
-        words += (size_t)g->hpk * (m * g->dv + m + m + m * g->d + m * m + (g->sink + g->w) + 3 * m);
-    else
-        words += (size_t)g->hpk * (size_t)g->scr_s_cap;
-    return words * sizeof(float);
+    if (!g->sealed) return 0;
+    const size_t d = (size_t)g->d, dv = (size_t)g->dv, m = (size_t)g->m_eff;
+    size_t shared, per_head;
+    if (g->exact_only) {
+        shared = (size_t)g->win_len * (d + dv);
+        per_head = (size_t)g->scr_s_len;
+    } else {
+        shared = (size_t)g->w * (d + dv) + (size_t)g->sink_len * (d + dv) + m * d;
+        per_head = m * dv + m + m + m * d + m * m + (size_t)g->scr_s_len + 3 * m;
+    }
+    return (shared + (size_t)g->hpk * per_head) * sizeof(float);
 }
 
 /* Copies of the state.  Any pointer may be NULL.  Shapes: sink [sink_len][d|dv],

@@ -237,6 +237,97 @@ def test_ridge_pinv_grows_lambda_tenfold():
     assert found, "no seed exercised the ridge growth"
 
 
+def zero_one_gram_case(m=16):
+    """A 0/1 matrix A (m = 16) whose A^T A has a rank-deficient 2x2 block: columns
+    0 and 1 of A are both e_0, row 1 is empty, and column j >= 2 is e_j.  Then
+    A^T A has ones on the diagonal, ones at (0, 1) and (1, 0), zeros elsewhere,
+    and tr(A^T A) / m = 1 exactly."""
+    a = np.zeros((m, m))
+    a[0, 0] = a[0, 1] = 1.0
+    for j in range(2, m):
+        a[j, j] = 1.0
+    return a
+
+
+def test_ridge_pinv_retry_fixed_by_rounding():
+    # IEEE arithmetic fixes the attempt: while lambda <= 2^-53, 1 + lambda rounds
+    # to 1, so the second pivot of the block [[1, 1], [1, 1]] is 1 - 1*1 = 0
+    # exactly and the factorisation fails.  With ridge_rel = 8e-19 the ridges are
+    # 8e-19, 8e-18, 8e-17 (all below 2^-53 ~ 1.11e-16), then 8e-16: attempt 4
+    # factors, with a pivot of about 2 * 4 * 2^-52.
+    a = zero_one_gram_case()
+    M, lam, tries = O.ridge_pinv(a, ridge_rel=8e-19)
+    assert tries == 4
+    assert lam == 8e-19 * 10.0 * 10.0 * 10.0
+    G = a.T @ a + lam * np.eye(16)
+    ref = np.linalg.solve(G, a.T)
+    assert np.linalg.norm(M - ref) / np.linalg.norm(ref) < 1e-9
+    # the ridge of attempt 3 is lost when added to 1, that of attempt 4 is not
+    assert 1.0 + lam / 10.0 == 1.0 and 1.0 + lam > 1.0
+    assert O.cholesky(a.T @ a + (lam / 10.0) * np.eye(16)) is None
+
+
+# ------------------------------------------------------------ memory_bytes --
+
+def _state_words(st):
+    return sum(int(np.asarray(st[k]).size) for k in
+               ("sink_k", "sink_v", "win_k", "win_v", "k_tilde", "q_tilde", "mu", "t_hat",
+                "z_hat", "m_max") if k in st)
+
+
+@pytest.mark.parametrize("hpk,T,d,dv,m,w,S", [(2, 256, 128, 128, 32, 128, 4),
+                                             (3, 100, 64, 32, 16, 24, 0),
+                                             (1, 64, 64, 64, 8, 16, 2)])
+def test_memory_bytes_skeleton_counts_state_vectors(hpk, T, d, dv, m, w, S):
+    # NystromState::memory_bytes counts f32 words of the window (w rows), sinks,
+    # K~, and per head T^, Z^, running max, Q~, M plus the score scratch (sink + w)
+    # and three m-vectors of scratch.  The state arrays' own sizes give all but
+    # the scratch; the count does not change while stepping.
+    rng = np.random.default_rng(T + hpk)
+    g, *_ = run_group(rng, hpk, T, d, dv, m, w, S, steps=0)
+    st = g.state()
+    me = st["m_eff"]
+    expect = 4 * (_state_words(st) + hpk * ((S + w) + 3 * me))
+    assert g.memory_bytes() == expect
+    for _ in range(3):
+        g.step(rng.standard_normal((hpk, d)).astype(np.float32),
+               rng.standard_normal(d).astype(np.float32), rng.standard_normal(dv).astype(np.float32))
+        assert g.memory_bytes() == expect
+
+
+def test_memory_bytes_qwen3_layer_group_by_hand():
+    # One group of the Qwen3-0.6B-shaped layer (d = dv = 128, m = 32, w = 128,
+    # sink = 4, two query heads), counted field by field from the page's lists:
+    #   shared  128*256 (window) + 4*256 (sinks) + 32*128 (K~)        = 37 888 words
+    #   head    32*128 (T^) + 32 (Z^) + 32 (max) + 32*128 (Q~) + 32*32 (M)
+    #           + 132 (score scratch) + 3*32 (other scratch)           =  9 508 words
+    #   total   37 888 + 2 * 9 508 = 56 904 words = 227 616 bytes
+    rng = np.random.default_rng(5)
+    g, *_ = run_group(rng, 2, 256, 128, 128, 32, 128, 4, steps=2)
+    assert g.memory_bytes() == 227_616
+
+
+def test_memory_bytes_exact_only_counts_lengths():
+    # Exact-only (seal_exact): the window holds every key by length (not by the
+    # capacity reserved for growth); each head's score scratch is reserved but
+    # empty until the first step, then holds one entry per key.  No sinks, K~ or
+    # skeleton vectors.  A group never prefilled holds nothing.
+    hpk, T, d, dv, w, S = 3, 20, 64, 32, 16, 2
+    rng = np.random.default_rng(9)
+    g = O.Group(8, w, S, hpk)
+    assert g.memory_bytes() == 0
+    qs, ks, vs = rand_prompt(rng, hpk, T, d, dv)
+    g.prefill(qs, ks, vs)
+    assert g.exact_only
+    assert g.memory_bytes() == 4 * T * (d + dv)
+    for s in range(1, 40):  # the window grows past its first reserved capacity
+        g.step(rng.standard_normal((hpk, d)).astype(np.float32),
+               rng.standard_normal(d).astype(np.float32), rng.standard_normal(dv).astype(np.float32))
+        n = T + s
+        assert g.win_len == n
+        assert g.memory_bytes() == 4 * (n * (d + dv) + hpk * n)
+
+
 # ------------------------------------------------------- exact attention --
 
 def test_exact_attention_matches_scipy():
