@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define O1_ABI_VERSION 2
+#define O1_ABI_VERSION 3
 
 enum o1_status {
     O1_OK = 0,
@@ -77,7 +77,13 @@ enum o1_rect { O1_RECT_AGGREGATE = 0, O1_RECT_FM = 1 };
  * skeleton; the group keeps every key exactly and each decode step appends one,
  * so the window grows without bound on that page.  Here it grows into buffers
  * of exact_cap keys per group, allocated once by o1_create_groups; 0 allocates
- * nothing and such prompts return O1_EEXACT. */
+ * nothing and such prompts return O1_EEXACT.
+ *
+ * ridge_rel is the relative ridge of the mixing matrix's pseudo-inverse
+ * (RIDGE_REL = 1e-6 on the nystrom.rs source page, used when it is 0):
+ * lambda = ridge_rel * max(mean diag(A^T A), DBL_MIN).  Other values exist to
+ * test the retry path of ridge_pinv (lambda grown tenfold after a failed
+ * Cholesky factorisation); a model has no reason to set it. */
 typedef struct o1_config {
     int32_t n_seq;    /* sequences                         (>= 1) */
     int32_t n_layer;  /* layers per sequence               (>= 1) */
@@ -90,6 +96,7 @@ typedef struct o1_config {
     int32_t sink;     /* permanent exact sink keys         (>= 0) */
     int32_t rect;     /* enum o1_rect                             */
     int32_t exact_cap;/* keys an exact-only group may hold   (>= 0) */
+    double ridge_rel; /* 0 = 1e-6; otherwise finite, > 0           */
 } o1_config;
 
 typedef struct o1_groups o1_groups; /* opaque; owns every state buffer */
@@ -120,6 +127,29 @@ typedef struct o1_info {
     int32_t n_layer;      /* layers per sequence                                 */
     int32_t layers_sealed;/* layers with a successful prefill of the prompt      */
     int64_t max_steps;    /* decode steps of the most advanced sealed layer      */
+    /* NystromState::memory_bytes of the nystrom.rs source page, summed over the
+     * groups of the sealed layers: the f32 words of the vectors the page keeps
+     * per group (window w (d + dv), sinks sink (d + dv), K~ m d) and per head
+     * (T^ m dv, Z^ m, running max m, Q~ m d, M m m, score scratch sink + w and
+     * three m-long scratch vectors), times 4.  In the exact-only mode a group
+     * counts its keys, n (d + dv), and each head a score scratch of n entries
+     * once the layer has stepped (none before).  Steps are counted per call, as
+     * `steps` is.  This is the page's figure, not this library's allocation. */
+    uint64_t page_bytes;
+    uint64_t fold_bytes;       /* device bytes of the held evictions (value rows, their
+                                  logits, T^'s scale): part of state_bytes, not on the page */
+    uint64_t ring_logit_bytes; /* device bytes of the far-insert logits kept per ring
+                                  slot (0 when w < O1_FOLD_PERIOD): part of state_bytes */
+    /* The ridge of every head of the sealed skeleton-mode layers whose M was
+     * computed (not given as frozen): smallest, median and largest lambda, the
+     * largest Cholesky attempt number (13 = the scaled-identity fallback), and
+     * the heads that needed more than one attempt / took the fallback.  All 0
+     * when no such head exists. */
+    double lambda_min, lambda_median, lambda_max;
+    int32_t tries_max;
+    int32_t heads_retried;
+    int32_t heads_fallback;
+    int32_t ridge_heads;       /* heads these figures cover                           */
 } o1_info;
 
 /* Fields of the device state, for o1_field_bytes / o1_read_field /
@@ -251,7 +281,12 @@ int o1_prefill_layer(o1_groups *g, int32_t layer, const o1_prompt_view *p, int32
 int o1_step_layer(o1_groups *g, int32_t layer, const float *q, const float *k, const float *v,
                   float *out, void *stream);
 
-/* Host-side facts about the handle; no device work. Errors: O1_EINVAL. */
+/* Facts about the handle.  The ridge figures are read from the device: the
+ * first call after a prefill (or a write of O1_FIELD_LAMBDA / O1_FIELD_TRIES)
+ * waits for the device to finish its work (hipDeviceSynchronize) and copies
+ * every head's lambda and attempt number to the host; later calls reuse that
+ * copy and do no device work.  Not to be called while a stream of the
+ * device is being captured.  Errors: O1_EINVAL, O1_EHIP. */
 int o1_get_info(const o1_groups *g, o1_info *info);
 
 /* Bytes of one state field at the current m_eff (see enum o1_field).
@@ -267,8 +302,9 @@ int o1_field_bytes(const o1_groups *g, int32_t field, size_t *bytes);
  * stream-ordered temporary; the state is left as it is.  Every write first
  * adds the held evictions to the stored T^ (none are held afterwards), a
  * write of O1_FIELD_M_MAX takes the stored T^ to be at the new running max, and
- * a write of O1_FIELD_NEAR_K or O1_FIELD_Q_TILDE recomputes the ring keys'
- * far-insert logits.
+ * every write recomputes the far-insert logits of all keys in the ring (a write
+ * may change the ring's keys, q~, or the counters that schedule the folds that
+ * would otherwise compute them).
  * Writing requires a sealed layer.
  * Errors: O1_EINVAL, O1_ESTATE, O1_ENOMEM (the T^ temporary), O1_EHIP. */
 int o1_read_field(const o1_groups *g, int32_t field, void *dst, size_t bytes, void *stream);

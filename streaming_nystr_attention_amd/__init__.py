@@ -39,7 +39,7 @@ class O1Error(RuntimeError):
 class o1_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_seq", "n_layer", "n_kv", "hpk", "d", "dv", "m", "w", "sink", "rect",
-                 "exact_cap")]
+                 "exact_cap")] + [("ridge_rel", ctypes.c_double)]
 
 
 class o1_frozen(ctypes.Structure):
@@ -52,7 +52,12 @@ class o1_info(ctypes.Structure):
                 ("steps", ctypes.c_int64), ("state_bytes", ctypes.c_uint64),
                 ("work_bytes", ctypes.c_uint64), ("exact_only", ctypes.c_int32),
                 ("exact_keys", ctypes.c_int32), ("n_layer", ctypes.c_int32),
-                ("layers_sealed", ctypes.c_int32), ("max_steps", ctypes.c_int64)]
+                ("layers_sealed", ctypes.c_int32), ("max_steps", ctypes.c_int64),
+                ("page_bytes", ctypes.c_uint64), ("fold_bytes", ctypes.c_uint64),
+                ("ring_logit_bytes", ctypes.c_uint64), ("lambda_min", ctypes.c_double),
+                ("lambda_median", ctypes.c_double), ("lambda_max", ctypes.c_double),
+                ("tries_max", ctypes.c_int32), ("heads_retried", ctypes.c_int32),
+                ("heads_fallback", ctypes.c_int32), ("ridge_heads", ctypes.c_int32)]
 
 
 class o1_prompt_view(ctypes.Structure):
@@ -155,7 +160,7 @@ def _dev_ptr(t, name, numel, dtype_name="float32"):
 
 def o1_create_groups(cfg: "Config"):
     c = o1_config(cfg.n_seq, cfg.n_layer, cfg.n_kv, cfg.hpk, cfg.d, cfg.dv, cfg.m, cfg.w,
-                  cfg.sink, cfg.rect, cfg.exact_cap)
+                  cfg.sink, cfg.rect, cfg.exact_cap, cfg.ridge_rel)
     h = ctypes.c_void_p()
     _check(lib().o1_create_groups(ctypes.byref(c), ctypes.byref(h)))
     return h
@@ -349,6 +354,7 @@ class Config:
     sink: int = 4
     rect: int = RECT_AGGREGATE
     exact_cap: int = 0  # keys an exact-only group may hold (0: that mode is refused)
+    ridge_rel: float = 0.0  # relative ridge of the pinv; 0 selects the page's 1e-6
 
     @property
     def groups(self) -> int:

@@ -57,6 +57,13 @@ struct o1_groups {
     double *exact_ws;
     size_t exact_ws_bytes;
     int32_t *exact_held;  // keys held per group [G], kept on the device
+    double ridge_rel;     // relative ridge of the pinv (the page's RIDGE_REL unless set)
+    size_t fold_bytes, ring_logit_bytes;  // parts of state_bytes (o1_info)
+    // host copy of every head's ridge record, refreshed by o1_get_info after a
+    // prefill or a write of the record (a diagnostics read, not on the hot path)
+    mutable bool ridge_stale = true;
+    mutable std::vector<double> lambda_host;
+    mutable std::vector<int32_t> tries_host;
 
     bool any_sealed() const
     {
@@ -243,8 +250,10 @@ int prefill_groups(o1_groups *g, int layer, const o1::PromptView &pv, int32_t T,
         io.fz_qt = frozen ? frozen->q_tilde : nullptr;
         io.fz_mu = frozen ? frozen->mu : nullptr;
         io.lm64 = g->lm64;
+        io.ridge_rel = g->ridge_rel;
         err = o1::launch_prefill(g->st, io, (hipStream_t)stream);
     }
+    g->ridge_stale = true;
     if (err != hipSuccess) return fail(O1_EHIP, "prefill launch failed: %s", hipGetErrorString(err));
     for (int l = 0; l < c.n_layer; ++l) {
         if (layer >= 0 && l != layer) continue;
@@ -341,6 +350,8 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     if (c.d < 1 || c.dv < 1) return fail(O1_EINVAL, "d and dv must be >= 1 (d=%d dv=%d)", c.d, c.dv);
     if (c.rect != O1_RECT_AGGREGATE && c.rect != O1_RECT_FM)
         return fail(O1_EINVAL, "unknown rectifier %d", c.rect);
+    if (!(c.ridge_rel >= 0.0) || !isfinite(c.ridge_rel))
+        return fail(O1_EINVAL, "ridge_rel must be finite and >= 0 (0 selects 1e-6), got %g", c.ridge_rel);
     const long long G = (long long)c.n_seq * c.n_layer * c.n_kv;
     if (G > (1LL << 30)) return fail(O1_EINVAL, "too many groups (%lld)", G);
     if (c.exact_cap < 0 || (double)G * c.exact_cap * ((double)c.d + c.dv) * 4.0 > 0x1p50)
@@ -369,6 +380,7 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     g->exact_ws = nullptr;
     g->exact_ws_bytes = 0;
     g->exact_held = nullptr;
+    g->ridge_rel = c.ridge_rel > 0.0 ? c.ridge_rel : o1::kRidgeRel;
     if (hipGetDevice(&g->device) != hipSuccess) {
         delete g;
         return fail(O1_EHIP, "hipGetDevice failed");
@@ -439,6 +451,9 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         return fail(O1_EHIP, "clearing the held value rows failed");
     }
     g->state_bytes = total;
+    g->fold_bytes = Gs * o1::kPend * c.dv * sizeof(float) + Gs * H * o1::kPend * M * sizeof(double) +
+                    Gs * H * M * sizeof(float);
+    g->ring_logit_bytes = c.w >= o1::kPend ? Gs * c.w * H * M * sizeof(double) : 0;
     // the decode streams its state from HBM when the state outgrows the cache
     const size_t exact_bytes = Gs * E * (c.d + c.dv) * sizeof(float) + ws_bytes;
     s.stream_state = total - std::min(total, exact_bytes) > o1::kInfinityCacheBytes ? 1 : 0;
@@ -540,6 +555,68 @@ int o1_get_info(const o1_groups *g, o1_info *info)
     info->n_layer = g->cfg.n_layer;
     info->layers_sealed = (int32_t)std::count(g->layer_sealed.begin(), g->layer_sealed.end(), 1);
     info->max_steps = g->steps_extreme(true);
+    info->fold_bytes = g->fold_bytes;
+    info->ring_logit_bytes = g->ring_logit_bytes;
+
+    // NystromState::memory_bytes (f32 words by vector length) of every sealed group
+    const o1_config &c = g->cfg;
+    const uint64_t per_layer = (uint64_t)c.n_seq * c.n_kv, d = c.d, dv = c.dv, H = c.hpk;
+    uint64_t words = 0;
+    for (int l = 0; l < c.n_layer; ++l) {
+        if (!g->layer_sealed[l]) continue;
+        uint64_t w_group;
+        if (g->exact) {
+            const uint64_t n = (uint64_t)g->T + (uint64_t)g->layer_steps[l];
+            w_group = n * (d + dv) + (g->layer_steps[l] > 0 ? H * n : 0);
+        } else {
+            const uint64_t m = (uint64_t)g->st.m, S = c.sink, W = c.w;
+            w_group = W * (d + dv) + S * (d + dv) + m * d +
+                      H * (m * dv + m + m + m * d + m * m + (S + W) + 3 * m);
+        }
+        words += per_layer * w_group;
+    }
+    info->page_bytes = words * sizeof(float);
+
+    // ridge record of the sealed skeleton layers' computed pinvs
+    info->lambda_min = info->lambda_median = info->lambda_max = 0.0;
+    info->tries_max = info->heads_retried = info->heads_fallback = info->ridge_heads = 0;
+    if (any && !g->exact) {
+        const size_t n = (size_t)g->G * c.hpk;
+        if (g->ridge_stale) {
+            DeviceScope dev(g);
+            if (int rc = dev.status()) return rc;
+            g->lambda_host.resize(n);
+            g->tries_host.resize(n);
+            if (hipDeviceSynchronize() != hipSuccess ||
+                hipMemcpy(g->lambda_host.data(), g->st.lambda, n * sizeof(double), hipMemcpyDeviceToHost) !=
+                    hipSuccess ||
+                hipMemcpy(g->tries_host.data(), g->st.tries, n * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+                    hipSuccess) {
+                (void)hipGetLastError();
+                return fail(O1_EHIP, "o1_get_info: reading the ridge record failed");
+            }
+            g->ridge_stale = false;
+        }
+        std::vector<double> lam;
+        lam.reserve(n);
+        for (size_t i = 0; i < n; ++i) {
+            const int l = (int)((i / c.hpk / c.n_kv) % c.n_layer);
+            const int32_t t = g->tries_host[i];
+            if (!g->layer_sealed[l] || t < 1) continue;  // unsealed layer, or M given frozen
+            lam.push_back(g->lambda_host[i]);
+            info->tries_max = std::max(info->tries_max, t);
+            info->heads_retried += t > 1;
+            info->heads_fallback += t > o1::kRidgeTries;
+        }
+        if (!lam.empty()) {
+            std::sort(lam.begin(), lam.end());
+            const size_t k = lam.size();
+            info->lambda_min = lam.front();
+            info->lambda_max = lam.back();
+            info->lambda_median = k % 2 ? lam[k / 2] : 0.5 * (lam[k / 2 - 1] + lam[k / 2]);
+            info->ridge_heads = (int32_t)k;
+        }
+    }
     return ok();
 }
 
@@ -606,9 +683,11 @@ int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, v
     // T^ is stored at the scale of the running max it was written against
     if (err == hipSuccess && field == O1_FIELD_M_MAX)
         err = hipMemcpyAsync(s.m_ref, s.m_max, bytes, hipMemcpyDeviceToDevice, st);
-    // the far-insert logits kept per ring slot follow the ring's keys and q~
-    if (err == hipSuccess && s.m > 0 && (field == O1_FIELD_NEAR_K || field == O1_FIELD_Q_TILDE))
-        err = o1::launch_ring_logits(s, whole_map(g), st);
+    // the far-insert logits kept per ring slot: recomputed for every key in the
+    // ring, since a write may change the ring's keys or q~, or far_len / win_head,
+    // which schedule the folds that compute the logits of newly arrived keys
+    if (err == hipSuccess && s.m > 0) err = o1::launch_ring_logits(s, whole_map(g), st);
+    if (field == O1_FIELD_LAMBDA || field == O1_FIELD_TRIES) g->ridge_stale = true;
     if (err != hipSuccess) return fail(O1_EHIP, "writing field %d failed: %s", field, hipGetErrorString(err));
     return ok();
 }

@@ -100,6 +100,7 @@ struct PrefillIO {
     int T;
     const float *fz_kt, *fz_qt, *fz_mu;  // optional frozen replacements, [count][...]
     double *lm64;                        // work: [count][1 + hpk][m][d] f64 landmarks
+    double ridge_rel;                    // relative ridge of the pinv (RIDGE_REL unless a test sets it)
 };
 
 // Exact grouped-GQA attention over a stored KV cache: the O(p) comparator, and

@@ -606,7 +606,7 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gram_pinv_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(gram_pinv_kernel, dim3(n * s.hpk), dim3(kThreads), lds, stream, s, io, kRidgeRel);
+        hipLaunchKernelGGL(gram_pinv_kernel, dim3(n * s.hpk), dim3(kThreads), lds, stream, s, io, io.ridge_rel);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // far-insert logits of the ring's keys (the landmarks and ring are in place)

@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version():
     P, L = _lib()
-    assert P.o1_abi_version() == 2
+    assert P.o1_abi_version() == 3
 
 
 def _header_enum(prefix):
@@ -69,17 +69,19 @@ def test_binding_constants_match_the_header():
         assert getattr(P, name[3:]) == val, name
     fold = re.search(r"#define\s+O1_FOLD_PERIOD\s+(\d+)", open(HEADER).read())
     assert fold and int(fold.group(1)) == P.FOLD_PERIOD
-    cfg_fields = re.search(r"typedef struct o1_config \{(.*?)\} o1_config;", open(HEADER).read(), re.S)
-    names = re.findall(r"int32_t\s+(\w+);", cfg_fields.group(1))
-    assert names == [f for f, _ in P.o1_config._fields_]
-    info_fields = re.search(r"typedef struct o1_info \{(.*?)\} o1_info;", open(HEADER).read(), re.S)
-    names = re.findall(r"int\d+_t\s+(\w+);", info_fields.group(1))
-    assert names == [f for f, _ in P.o1_info._fields_]
+    for struct in ("o1_config", "o1_info"):
+        body = re.search(rf"typedef struct {struct} \{{(.*?)\}} {struct};", open(HEADER).read(), re.S)
+        decls = re.findall(r"(u?int\d+_t|double|float)\s+([\w\s,]+);",
+                           re.sub(r"/\*.*?\*/", "", body.group(1), flags=re.S))
+        ctype = {"int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "uint64_t": ctypes.c_uint64,
+                 "double": ctypes.c_double, "float": ctypes.c_float}
+        fields = [(n.strip(), ctype[t]) for t, names in decls for n in names.split(",")]
+        assert fields == list(getattr(P, struct)._fields_), struct
 
 
 def _create(P, L, **kw):
     base = dict(n_seq=1, n_layer=1, n_kv=1, hpk=1, d=64, dv=64, m=8, w=16, sink=2, rect=0,
-                exact_cap=0)
+                exact_cap=0, ridge_rel=0.0)
     base.update(kw)
     cfg = P.o1_config(*[base[f] for f, _ in P.o1_config._fields_])
     h = ctypes.c_void_p()
@@ -92,6 +94,7 @@ def _create(P, L, **kw):
     (dict(dv=0), 1), (dict(n_seq=0), 1), (dict(n_layer=0), 1), (dict(n_kv=0), 1), (dict(rect=7), 1),
     (dict(d=96, dv=96), 6), (dict(hpk=3), 6), (dict(m=65), 6), (dict(d=64, dv=128), 6),
     (dict(w=2000), 6), (dict(exact_cap=-1), 1), (dict(n_seq=1 << 20, exact_cap=1 << 22), 1),
+    (dict(ridge_rel=-1e-6), 1), (dict(ridge_rel=float("inf")), 1), (dict(ridge_rel=float("nan")), 1),
 ])
 def test_create_rejects_before_touching_the_device(kw, code):
     P, L = _lib()

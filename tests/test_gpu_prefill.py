@@ -42,7 +42,7 @@ def seq_sample(wl):
     return W.groups_of_sequences(wl, W.sample_sequences(wl))
 
 
-@pytest.mark.parametrize("name", ["stress_m8_s0", "stress_m16_s4", "stress_m32_s4"])
+@pytest.mark.parametrize("name", ["stress_m8_s0", "stress_m8_s4", "stress_m16_s0", "stress_m16_s4", "stress_m32_s0", "stress_m32_s4"])
 def test_prefill_stress(name):
     wl = W.WORKLOADS[name]
     prefill_parity(wl, sample=seq_sample(wl))
