@@ -343,6 +343,23 @@ int o1_exact_workspace_bytes(const o1_exact_desc *desc, size_t *bytes);
 int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, const float *v,
                     float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* o1_exact_attend for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and results, without the work space: the split
+ * partials go to a static buffer of O1_EXACT_NOALLOC_BYTES in the library's
+ * device memory, one per device, held until the process ends (its device
+ * address is looked up on the first call on each device).  Nothing is
+ * allocated, by the library or by the caller.
+ * Every call on a device shares that device's buffer: calls that may run at
+ * the same time on one device (different streams, or graphs replayed
+ * concurrently) race on it and must be ordered by the caller.
+ * Errors: those of o1_exact_attend; O1_EINVAL also when the launch needs more
+ * work space than the buffer holds (o1_exact_workspace_bytes of `desc` above
+ * O1_EXACT_NOALLOC_BYTES; then use o1_exact_attend). */
+#define O1_EXACT_NOALLOC_BYTES (16u << 20)
+int o1_exact_attend_noalloc(const o1_exact_desc *desc, const float *q, const float *k, const float *v,
+                            float *out, void *stream);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char *o1_last_error(void);
 

@@ -76,7 +76,7 @@ class o1_exact_desc(ctypes.Structure):
 EXPORTS = ("o1_create_groups", "o1_destroy_groups", "o1_prefill", "o1_step", "o1_prefill_layer",
            "o1_step_layer", "o1_get_info",
            "o1_field_bytes", "o1_read_field", "o1_write_field", "o1_exact_workspace_bytes",
-           "o1_exact_attend", "o1_last_error", "o1_abi_version")
+           "o1_exact_attend", "o1_exact_attend_noalloc", "o1_last_error", "o1_abi_version")
 
 _lib = None
 
@@ -118,6 +118,8 @@ def lib():
     L.o1_exact_attend.restype = ctypes.c_int
     L.o1_exact_attend.argtypes = [ctypes.POINTER(o1_exact_desc), vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
+    L.o1_exact_attend_noalloc.restype = ctypes.c_int
+    L.o1_exact_attend_noalloc.argtypes = [ctypes.POINTER(o1_exact_desc), vp, vp, vp, vp, vp]
     L.o1_last_error.restype = ctypes.c_char_p
     L.o1_last_error.argtypes = []
     L.o1_abi_version.restype = ctypes.c_int
@@ -329,6 +331,18 @@ def o1_exact_attend(q, k, v, out, n_keys: int, first: int = 0, scale=None, works
     _check(lib().o1_exact_attend(ctypes.byref(desc), _dev_ptr(q, "q", G * H * d),
                                  _dev_ptr(k, "k", G * cap * d), _dev_ptr(v, "v", G * cap * dv),
                                  _dev_ptr(out, "out", G * H * dv), wp, wb, _stream_handle(stream)))
+
+
+def o1_exact_attend_noalloc(q, k, v, out, n_keys: int, first: int = 0, scale=None, stream=None):
+    """o1_exact_attend without a work space (the library's static per-device
+    buffer holds the split partials); nothing is allocated."""
+    desc = _exact_desc(q, k, n_keys, first, scale)
+    G, H, d = q.shape
+    cap, dv = k.shape[1], v.shape[2]
+    _check(lib().o1_exact_attend_noalloc(ctypes.byref(desc), _dev_ptr(q, "q", G * H * d),
+                                         _dev_ptr(k, "k", G * cap * d),
+                                         _dev_ptr(v, "v", G * cap * dv),
+                                         _dev_ptr(out, "out", G * H * dv), _stream_handle(stream)))
 
 
 def o1_last_error() -> str:

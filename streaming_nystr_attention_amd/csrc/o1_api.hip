@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -692,6 +693,50 @@ int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, v
     return ok();
 }
 
+}  // extern "C"
+
+// ---- the work space of o1_exact_attend_noalloc ---------------------------
+// One array per device, in the code object's device memory: the split
+// partials (max, sum, numerator) of a launch.  In host code `scratch` names a
+// host-side shadow, not device memory: its device address is looked up with
+// hipGetSymbolAddress, per device, on that device's first call, and only that
+// address is passed to kernels.  Every partial a launch reads it has written
+// in the same launch, so nothing needs clearing between calls.
+namespace {
+constexpr size_t kScratchBytes = O1_EXACT_NOALLOC_BYTES;
+constexpr int kMaxDevices = 64;
+}  // namespace
+static __device__ __align__(256) double scratch[kScratchBytes / sizeof(double)];
+
+namespace {
+std::mutex g_scratch_mu;
+double *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, null until looked up
+
+int scratch_of_current_device(double **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(O1_EHIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(O1_EUNSUPPORTED, "o1_exact_attend_noalloc: device %d beyond the %d supported", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(O1_EHIP, "hipGetSymbolAddress of the static work space failed on device %d: %s",
+                        dev, hipGetErrorString(err));
+        }
+        g_scratch_ptr[dev] = static_cast<double *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return O1_OK;
+}
+}  // namespace
+
+extern "C" {
+
 static int exact_check(const o1_exact_desc *x, int *splits, size_t *bytes)
 {
     if (!x) return fail(O1_EINVAL, "o1_exact: null descriptor");
@@ -717,19 +762,11 @@ int o1_exact_workspace_bytes(const o1_exact_desc *desc, size_t *bytes)
     return rc ? rc : ok();
 }
 
-int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, const float *v,
-                    float *out, void *workspace, size_t workspace_bytes, void *stream)
+// The launch shared by o1_exact_attend and o1_exact_attend_noalloc, after
+// their checks: `ws` holds the split partials (null when splits == 1).
+static int exact_launch(const o1_exact_desc &x, int splits, const float *q, const float *k,
+                        const float *v, float *out, double *ws, void *stream)
 {
-    int splits = 0;
-    size_t need = 0;
-    int rc = exact_check(desc, &splits, &need);
-    if (rc) return rc;
-    if (!q || !k || !v || !out) return fail(O1_EINVAL, "o1_exact_attend: null tensor");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-        return fail(O1_EINVAL, "o1_exact_attend: tensors must be 16-byte aligned");
-    if (need && (!workspace || workspace_bytes < need))
-        return fail(O1_EINVAL, "o1_exact_attend: work space of %zu bytes needed", need);
-    const o1_exact_desc &x = *desc;
     o1::ExactIO io{};
     io.q = q;
     io.k = k;
@@ -746,7 +783,6 @@ int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, c
     io.per_split = (visible + splits - 1) / splits;
     splits = (visible + io.per_split - 1) / io.per_split;  // no empty ranges
     io.scale = x.scale > 0.0f ? x.scale : 1.0f / sqrtf((float)x.d);
-    double *ws = static_cast<double *>(workspace);
     const size_t parts = (size_t)x.n_groups * splits * x.hpk;
     io.ws_max = ws;
     io.ws_sum = ws ? ws + parts : nullptr;
@@ -754,6 +790,46 @@ int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, c
     hipError_t err = o1::launch_exact(io, splits, (hipStream_t)stream);
     if (err != hipSuccess) return fail(O1_EHIP, "exact attention launch failed: %s", hipGetErrorString(err));
     return ok();
+}
+
+static int exact_tensors_check(const char *who, const float *q, const float *k, const float *v,
+                               const float *out)
+{
+    if (!q || !k || !v || !out) return fail(O1_EINVAL, "%s: null tensor", who);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(O1_EINVAL, "%s: tensors must be 16-byte aligned", who);
+    return O1_OK;
+}
+
+int o1_exact_attend(const o1_exact_desc *desc, const float *q, const float *k, const float *v,
+                    float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int splits = 0;
+    size_t need = 0;
+    int rc = exact_check(desc, &splits, &need);
+    if (rc) return rc;
+    if ((rc = exact_tensors_check("o1_exact_attend", q, k, v, out))) return rc;
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(O1_EINVAL, "o1_exact_attend: work space of %zu bytes needed", need);
+    return exact_launch(*desc, splits, q, k, v, out, static_cast<double *>(workspace), stream);
+}
+
+int o1_exact_attend_noalloc(const o1_exact_desc *desc, const float *q, const float *k, const float *v,
+                            float *out, void *stream)
+{
+    int splits = 0;
+    size_t need = 0;
+    int rc = exact_check(desc, &splits, &need);
+    if (rc) return rc;
+    if ((rc = exact_tensors_check("o1_exact_attend_noalloc", q, k, v, out))) return rc;
+    if (need > kScratchBytes)
+        return fail(O1_EINVAL,
+                    "o1_exact_attend_noalloc: this launch needs %zu bytes of work space, more than the "
+                    "%zu bytes of its static buffer (o1_exact_attend takes a caller work space)",
+                    need, kScratchBytes);
+    double *ws = nullptr;
+    if (need && (rc = scratch_of_current_device(&ws))) return rc;
+    return exact_launch(*desc, splits, q, k, v, out, ws, stream);
 }
 
 }  // extern "C"

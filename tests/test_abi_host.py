@@ -175,3 +175,21 @@ def test_handle_released_during_a_capture_is_destroyed_later(monkeypatch):
     other._h = ctypes.c_void_p(0x5678)
     other.close()
     assert destroyed == [0x5678, 0x1234] and P._DEFERRED_HANDLES == []
+
+
+def test_exact_noalloc_refuses_launches_beyond_its_buffer_without_device():
+    # 1020 groups of 8 heads over 4096 keys split in two: 1020 * 2 * 8 * (128 + 2)
+    # doubles of partials, 16.9 MB, above the 16 MiB static buffer.  The check
+    # comes before any device work (the tensors are never touched).
+    P, L = _lib()
+    desc = P.o1_exact_desc(1020, 8, 128, 128, 4096, 0, 4096, 0.0)
+    n = ctypes.c_size_t()
+    assert L.o1_exact_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == 0
+    assert n.value > (16 << 20)
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced
+    rc = L.o1_exact_attend_noalloc(ctypes.byref(desc), fake, fake, fake, fake, None)
+    assert rc == P.O1_EINVAL
+    assert "static buffer" in P.o1_last_error()
+    assert L.o1_exact_attend_noalloc(None, fake, fake, fake, fake, None) == P.O1_EINVAL
+    small = P.o1_exact_desc(4, 2, 128, 128, 100, 0, 100, 0.0)
+    assert L.o1_exact_attend_noalloc(ctypes.byref(small), None, fake, fake, fake, None) == P.O1_EINVAL
