@@ -9,11 +9,24 @@ timed job does identical work.
 
 value       decode group-steps per second over the whole timed job (prefill
             time included); tokens_per_s = sequences x decode steps / time.
-roofline    the decode kernel: algorithmic bytes per launch / its average
-            launch time from HIP events on the launch stream, against the
-            MI355X HBM peak of 8 TB/s.
+roofline    the decode kernel against the MI355X HBM peak of 8 TB/s, from its
+            average launch time (HIP events on the launch stream):
+              achieved / frac       algorithmic bytes of the per-eviction step
+                                    (every state value read once, its modified
+                                    part written once, q/k/v in, outputs out)
+              kernel_*              the bytes this kernel's algorithm must move
+                                    (T^ written and q~ read once per fold period),
+                                    averaged over the period
+              traffic / dram_*      HBM bytes the counters measured per launch
+prefill     the prefill freeze: prompt read once and state written once against
+            the HBM peak, and the far field's f64 matrix-core flops over the
+            whole prefill time against the f64 MFMA peak (a lower bound of that
+            kernel's rate).
+workloads   decode launches of other workloads (eviction stress, wide GQA) with
+            the same roofline figures.
 cpu_baseline  the CPU oracle (tests' reference implementation, untuned) on a
-            bounded sample of the same workload, on this host's cores.
+            bounded sample of the same workload, on every CPU this process may
+            use.
 exact_comparator  exact grouped-GQA attention (o1_exact_attend) over the job's
             final context at the same shape: the O(context) decode replaced.
 exact_only_mode  o1_step in the exact-only mode (prompt of w + sink + 8 tokens,
@@ -41,6 +54,7 @@ if ROOT not in sys.path:
 
 METRIC = "Nyström decode group-steps/sec & tokens/s at 1 GPU; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+F64_MFMA_PEAK_TFLOPS = 78.6
 DECODE_SRC = [os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", f)
               for f in ("o1_decode.hip", "o1_internal.h")] + [os.path.join(ROOT, "include", "o1.h")]
 # HBM bytes per decode launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by
@@ -66,6 +80,49 @@ def decode_source_sha() -> str:
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def step_bytes_per_group_step(wl) -> int:
+    """Algorithmic bytes of one group-step of the per-eviction step
+    (NystromState::step_group of the nystrom.rs source page), f32 throughout:
+    read the near rows, K~, and per head Q~, M, T^, Z^ and the running max, plus
+    the inputs q, k, v; write the new ring row, per head T^, Z^ and the running
+    max, and the outputs."""
+    S, w, d, dv, m, H = wl.sink, wl.w, wl.d, wl.dv, wl.m_eff, wl.hpk
+    read = (S + w) * (d + dv) + m * d + H * (m * d + m * m + m * dv + 2 * m) + H * d + d + dv
+    write = (d + dv) + H * (m * dv + 2 * m) + H * dv
+    return 4 * (read + write)
+
+
+def prefill_bytes_and_flops(wl) -> tuple[int, int]:
+    """Algorithmic work of the prefill freeze per launch over every group: the
+    prompt (each head's queries, keys, values) read once and the frozen state
+    written once (near rows, K~, per head Q~, M, T^, Z^, running max), f32; and
+    the far field's matrix products, 2 m T_far (d + dv) flops per head
+    (logits Q~ K_far^T, then weights times V) over the T - sink - w far keys."""
+    S, w, d, dv, m, H, T = wl.sink, wl.w, wl.d, wl.dv, wl.m_eff, wl.hpk, wl.T
+    read = H * T * d + T * d + T * dv
+    write = (S + w) * (d + dv) + m * d + H * (m * d + m * m + m * dv + 2 * m)
+    flops = H * 2 * m * (T - S - w) * (d + dv)
+    return 4 * (read + write) * wl.groups, flops * wl.groups
+
+
+def host_cpu_share() -> tuple[int, str]:
+    """CPUs this process may run on: its affinity set, capped by a cgroup CPU
+    quota when one is set; with how that was found."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    how = f"affinity {n} of {os.cpu_count()} host CPUs"
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            q = max(1, int(float(quota) / float(period)))
+            if q < n:
+                n = q
+                how += f", cgroup quota {quota}/{period}"
+    except (OSError, ValueError):
+        pass
+    return n, how
 
 
 def decode_bytes_per_group_step(wl) -> tuple[float, float]:
@@ -105,8 +162,8 @@ def decode_bytes_per_group_step(wl) -> tuple[float, float]:
     return read, write
 
 
-def cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads, per_thread):
-    """Time the oracle on a bounded sample of groups (whole jobs)."""
+def cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads, n, share):
+    """Time the oracle on a bounded sample of n groups (whole jobs)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -114,7 +171,6 @@ def cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads, per_thread):
 
     import oracle as O
 
-    n = threads * per_thread
     g = torch.Generator().manual_seed(1234)
     idx = torch.randperm(wl.groups, generator=g)[:n].sort().values
     di = idx.to(q.device)
@@ -138,11 +194,75 @@ def cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads, per_thread):
         "value": n * n_dec / dt,
         "unit": "group-steps/s",
         "cores": threads,
+        "host_cpus": os.cpu_count(),
+        "cpu_share": share,
         "kind": "oracle",
         "sample": (f"{n} of the {wl.groups} groups of {wl.name} (seeded pick), each a whole job: "
                    f"prefill of {wl.T} tokens + {n_dec} decode steps; f64 C oracle, "
-                   f"{threads} threads, {dt:.1f} s wall"),
+                   f"{threads} threads (one per CPU this process may use), {dt:.1f} s wall"),
     }
+
+
+def decode_roofline(wl, us_per_launch, traffic=None) -> dict:
+    """Roofline figures of one decode launch over every group of `wl`."""
+    G = wl.groups
+    alg = step_bytes_per_group_step(wl) * G
+    rd, wr = decode_bytes_per_group_step(wl)
+    kern = (rd + wr) * G
+    t = us_per_launch * 1e-6
+    res = {"bound": "hbm", "achieved": alg / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": alg / t / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+           "traffic_unit": "bytes per launch", "bytes_per_launch": alg,
+           "bytes_per_group_step": alg / G,
+           "kernel_bytes_per_group_step": kern / G,
+           "kernel_GBps": kern / t / 1e9, "kernel_frac": kern / t / 1e9 / HBM_PEAK_GBS}
+    if traffic:
+        res["dram_GBps"] = traffic / t / 1e9
+        res["dram_frac"] = traffic / t / 1e9 / HBM_PEAK_GBS
+    return res
+
+
+def other_workload(name, n_steps, dev):
+    """Prefill, then n_steps decode launches of workload `name`, timed with HIP
+    events on the launch stream (inputs generated beforehand)."""
+    import torch
+
+    import streaming_nystr_attention_amd as P
+    from streaming_nystr_attention_amd import workloads as W
+
+    wl = W.WORKLOADS[name]
+    G, H = wl.groups, wl.hpk
+    try:
+        q, k, v = W.prompt(wl, dev)
+        Q = torch.empty(n_steps, G, H, wl.d, device=dev)
+        K = torch.empty(n_steps, G, wl.d, device=dev)
+        V = torch.empty(n_steps, G, wl.dv, device=dev)
+        for t in range(n_steps):
+            W.decode_inputs(wl, t, dev, out=(Q[t], K[t], V[t]))
+        out = torch.empty(G, H, wl.dv, device=dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        with P.O1Groups(wl.config) as grp:
+            for timed in (False, True):  # the first pass warms up, the second is timed
+                e[0].record()
+                grp.prefill(q, k, v)
+                e[1].record()
+                for t in range(n_steps):
+                    grp.step(Q[t], K[t], V[t], out)
+                e[2].record()
+            torch.cuda.synchronize()
+        us = e[1].elapsed_time(e[2]) * 1e3 / n_steps
+        pf_bytes, pf_flops = prefill_bytes_and_flops(wl)
+        pf_ms = e[0].elapsed_time(e[1])
+        del q, k, v, Q, K, V
+        torch.cuda.empty_cache()
+        return {"groups": G, "hpk": H, "m": wl.m_eff, "w": wl.w, "sink": wl.sink,
+                "prompt_len": wl.T, "decode_steps_timed": n_steps, "us_per_launch": us,
+                "group_steps_per_s": G / (us * 1e-6),
+                "roofline": decode_roofline(wl, us, MEASURED_TRAFFIC.get((name, decode_source_sha()))),
+                "prefill_ms": pf_ms, "prefill_frac_hbm": pf_bytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "prefill_far_tflops": pf_flops / (pf_ms * 1e-3) / 1e12}
+    except Exception as exc:  # context, never the headline
+        return {"error": str(exc)[:200]}
 
 
 def exact_comparator(wl, ctx, nystrom_us, dev):
@@ -334,7 +454,12 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="decode steps per job (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-per-thread", type=int, default=32, help="oracle groups per thread")
+    ap.add_argument("--cpu-groups", type=int, default=512,
+                    help="groups (whole jobs) in the oracle's timed sample")
+    ap.add_argument("--other-workloads", default="stress_m32_s4,stress_m8_s0,wide_gqa",
+                    help="comma-separated workloads whose decode launches are also timed ('' skips)")
+    ap.add_argument("--other-steps", type=int, default=256,
+                    help="decode launches timed per other workload")
     ap.add_argument("--exact-context", type=int, default=-1,
                     help="also time the exact grouped-GQA comparator over this many keys per "
                          "group (-1: the job's final context, 0: skip)")
@@ -409,10 +534,10 @@ def main():
     prefill_ms = sum(e[0].elapsed_time(e[1]) for e in events) / len(events)
     decode_ms = sum(e[1].elapsed_time(e[2]) for e in events) / len(events)
     launch_us = decode_ms * 1e3 / n_dec
-    rd, wr = decode_bytes_per_group_step(wl)
-    bytes_per_launch = (rd + wr) * G
-    achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
     group_steps = args.steps * n_dec * G
+    pf_bytes, pf_flops = prefill_bytes_and_flops(wl)
+    roofline = decode_roofline(wl, launch_us, MEASURED_TRAFFIC.get((wl.name, decode_source_sha())))
+    roofline["kernel"] = ("decode_kernel<128,128,2>" if (wl.d == 128 and H == 2) else "decode_kernel")
 
     res = {
         "metric": METRIC,
@@ -438,17 +563,15 @@ def main():
         "decode_group_steps_per_s": n_dec * G / (decode_ms * 1e-3),
         "decode_us_per_launch": launch_us,
         "prefill_ms": prefill_ms,
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "decode_kernel<128,128,2>" if (wl.d == 128 and H == 2) else "decode_kernel",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": MEASURED_TRAFFIC.get((wl.name, decode_source_sha())),
-            "traffic_unit": "bytes per launch",
-            "bytes_per_launch": bytes_per_launch,
-            "bytes_per_group_step": rd + wr,
+        "roofline": roofline,
+        "prefill": {
+            "bound": "hbm", "bytes_per_launch": pf_bytes, "ms": prefill_ms,
+            "achieved": pf_bytes / (prefill_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": pf_bytes / (prefill_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "far_field_gflop": pf_flops / 1e9,
+            "far_field_tflops_over_whole_prefill": pf_flops / (prefill_ms * 1e-3) / 1e12,
+            "f64_mfma_peak_tflops": F64_MFMA_PEAK_TFLOPS,
+            "far_field_frac_f64_mfma": pf_flops / (prefill_ms * 1e-3) / 1e12 / F64_MFMA_PEAK_TFLOPS,
         },
     }
     ctx = wl.T + n_dec if args.exact_context < 0 else args.exact_context
@@ -461,6 +584,12 @@ def main():
         res["exact_only_mode"] = exact_only_mode(wl, args.exact_only_steps, dev)
     if args.per_layer_tokens > 0 and wl.n_layer > 1:
         res["per_layer_mode"] = per_layer_mode(wl, args.per_layer_tokens, dev)
+    others = [n for n in args.other_workloads.split(",") if n and n != wl.name]
+    if others and args.other_steps > 0:
+        del Q, K, V
+        torch.cuda.empty_cache()
+        Q = None
+        res["workloads"] = {n: other_workload(n, args.other_steps, dev) for n in others}
     if not args.no_cpu_baseline:
         if Q is None:
             Q = torch.empty(n_dec, G, H, wl.d, device=dev)
@@ -468,9 +597,9 @@ def main():
             V = torch.empty(n_dec, G, wl.dv, device=dev)
             for t in range(n_dec):
                 W.decode_inputs(wl, t, dev, out=(Q[t], K[t], V[t]))
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads, share = host_cpu_share()
         res["cpu_baseline"] = cpu_baseline(wl, q, k, v, Q, K, V, n_dec, threads,
-                                           args.cpu_per_thread)
+                                           min(args.cpu_groups, G), share)
     else:
         res["cpu_baseline"] = None
     grp.close()
