@@ -341,22 +341,41 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
     }
 }
 
-// ---- far field of the prompt on the matrix cores (f64 MFMA) ---------------
+// ---- far field of the prompt on the matrix cores ---------------------------
 //
 // One work-group per (group, block of HB heads): the far keys' K and V tiles are
 // loaded once and used by every head of the block, and the head blocks of one
 // group run on one XCD (work-group b goes to XCD b mod 8), so they share its L2.
 // One wave per 16-landmark row block of one head, its Q~ rows held in registers.
-// For each tile of 16 far keys (staged in LDS while the next one is in flight):
-//   L   = Q~_blk K_tile^T * scale        16 x 16, D/4 MFMA 16x16x4 f64
-//   online per-landmark max, P = e^{L - max}, Z^ += row sums of P
-//   T^ <- T^ * e^{max_old - max_new} + P V_tile   16 x dv, 4 * dv/16 MFMAs
+// Every product is taken transposed, so that each lane owns one landmark row
+// (row li = lane % 16 of the wave's block) throughout:
+//   L^T = K_tile Q~_blk^T * scale     keys x rows, D/4 MFMA 16x16x4 f64; lane
+//                                     holds keys 4 e + lk (lk = lane / 16) of row li
+//   row max: in the lane over its 4 keys, then across lk (lane ^ 16, ^ 32)
+//   P   = e^{L - max} in f32 (the gap is formed in f64; at most 1 in value, so
+//         its absolute error is that of an f32 rounding), Z^ += row sums (f64)
+//   T^T <- T^T * e^{max_old - max_new} + V_tile^T P^T    dv x rows, 4 * dv/16
+//         MFMA 16x16x4 f32; P's operand for k-step kk is this lane's own weight
+//         e = kk (key 4 kk + lk), so P never leaves the registers
 // The logit product runs over a permuted component order: at step ks, lane
-// (i, k) holds A[i][k] = Q~[i][k * D/4 + ks] and B[k][j] = K[j][k * D/4 + ks],
-// so each lane's Q~ operands are one contiguous run of D/4 components and the
-// sum over k and ks still covers every component once.
-// v_mfma_f64_16x16x4f64 operand layout (wave64): A[i][k] in lane i + 16 k,
-// B[k][j] in lane j + 16 k, and D[i][j] in lane j + 16 (i % 4), element i / 4.
+// (i, k) holds K[i][k * D/4 + ks] and Q~[i][k * D/4 + ks], so each lane's Q~
+// operands are one contiguous run of D/4 components and the sum over k and ks
+// still covers every component once.
+// Operand layout of both MFMAs (wave64): A[i][k] in lane i + 16 k, B[k][j] in
+// lane j + 16 k; results: f64 D[i][j] in lane j + 16 (i % 4), element i / 4; f32
+// D[i][j] in lane j + 16 (i / 4), element i % 4.
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// x + x(lane ^ 16) + x(lane ^ 32) + x(lane ^ 48): the four lanes of one row
+// index li (f32, exact exchanges as in sum_high_lanes)
+__device__ __forceinline__ float sum_over_lk(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // (At least two waves per SIMD: otherwise a 4-wave work-group may take the
 // whole register file, and one work-group per CU leaves the MFMAs idle on loads.)
@@ -369,6 +388,8 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
     constexpr int TK = 16;       // keys per tile
     constexpr int K4 = TK * (D / 4), KV4 = K4 + TK * (DV / 4);  // float4 of a K tile, of K and V
     constexpr int PT = (KV4 + NT - 1) / NT;                     // float4 per thread per tile
+    constexpr int VLD = DV + 16;  // V tile row stride (floats): the 4 rows an operand read touches start 16 banks apart
+    constexpr double LOG2E = 1.4426950408889634;
     const int H = s.hpk, nhb = (H + HB - 1) / HB;
     const int jb = blockIdx.x >> 3;
     const int ci = (jb / nhb) * 8 + (blockIdx.x & 7), hb = jb - (jb / nhb) * nhb;
@@ -383,13 +404,12 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
     const double NEG_INF = -__builtin_inf();
     const int li = lane & 15, lk = lane >> 4;
 
-    // K and V tiles widened to f64 once, as they are staged: the MFMA operand
-    // reads need no conversion.  K is [k quarter][key][component] with an odd
-    // row length, so the 16 keys of a logit operand read fall in distinct bank
-    // pairs.
+    // K tiles widened to f64 once, as they are staged: the MFMA operand reads
+    // need no conversion.  K is [k quarter][key][component] with an odd row
+    // length, so the 16 keys of an operand read fall in distinct bank pairs.
+    // V stays f32 (the weights' product runs on f32 MFMA).
     __shared__ double k_lds[4][TK][KS + 1];
-    __shared__ double v_lds[TK][DV + 2];
-    __shared__ double p_lds[NW][16][17];
+    __shared__ float v_lds[TK][VLD];
 
     // Q~ fragment of this wave: row rb * 16 + li, components lk * KS .. lk * KS + KS - 1
     float qa[KS];
@@ -409,7 +429,7 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
     }
 
     // K and V tiles: thread slot p covers float4 tid + p * NT of [K tile | V tile];
-    // key indices are clamped (dead keys get -inf logits and zero weights below)
+    // key indices are clamped (dead keys get zero weights below)
     const float *K = io.p.k_row(io.map, ci, S);
     const float *V = io.p.v_row(io.map, ci, S);
     const int64_t kpos = io.p.k_pos, vpos = io.p.v_pos;
@@ -438,22 +458,15 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
                 dst[3] = pre[p].w;
             } else if (idx < KV4) {
                 const int e = idx - K4, key = e / (DV / 4), c4 = e % (DV / 4);
-                double2 *dst = reinterpret_cast<double2 *>(&v_lds[key][c4 * 4]);
-                dst[0] = make_double2(pre[p].x, pre[p].y);
-                dst[1] = make_double2(pre[p].z, pre[p].w);
+                *reinterpret_cast<float4 *>(&v_lds[key][c4 * 4]) = pre[p];
             }
         }
     };
 
-    f64x4 tacc[CB];
+    f32x4 tacc[CB];  // T^ transposed: element e of lane (li, lk) is column 4 lk + e of row li
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) tacc[cb] = f64x4{0.0, 0.0, 0.0, 0.0};
-    double mx[4], zs[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        mx[r] = NEG_INF;
-        zs[r] = 0.0;
-    }
+    for (int cb = 0; cb < CB; ++cb) tacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    double mx = NEG_INF, zs = 0.0;  // row li: running max, Z^
 
     fetch(0);
     for (int j0 = 0; j0 < nf; j0 += TK) {
@@ -462,82 +475,68 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
         __syncthreads();
         if (j0 + TK < nf) fetch(j0 + TK);  // the next tile is in flight during the MFMAs
 
-        // logits of this landmark block against the tile
+        // logits of the tile against this landmark block, transposed
         f64x4 L = {0.0, 0.0, 0.0, 0.0}, L2 = {0.0, 0.0, 0.0, 0.0}, L3 = L, L4 = L;
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 4) {
             // opaque copies: widen Q~ at its use instead of keeping KS doubles live
             float q0 = qa[ks], q1 = qa[ks + 1], q2 = qa[ks + 2], q3 = qa[ks + 3];
             asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3));
-            L = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q0, k_lds[lk][li][ks], L, 0, 0, 0);
-            L2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q1, k_lds[lk][li][ks + 1], L2, 0, 0, 0);
-            L3 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q2, k_lds[lk][li][ks + 2], L3, 0, 0, 0);
-            L4 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)q3, k_lds[lk][li][ks + 3], L4, 0, 0, 0);
+            L = __builtin_amdgcn_mfma_f64_16x16x4f64(k_lds[lk][li][ks], (double)q0, L, 0, 0, 0);
+            L2 = __builtin_amdgcn_mfma_f64_16x16x4f64(k_lds[lk][li][ks + 1], (double)q1, L2, 0, 0, 0);
+            L3 = __builtin_amdgcn_mfma_f64_16x16x4f64(k_lds[lk][li][ks + 2], (double)q2, L3, 0, 0, 0);
+            L4 = __builtin_amdgcn_mfma_f64_16x16x4f64(k_lds[lk][li][ks + 3], (double)q3, L4, 0, 0, 0);
         }
         L = (L + L2) + (L3 + L4);
-        // lane holds L[row lk + 4 r][key li]
-        // (the 16 keys of a row sit in one 16-lane row: DPP reductions)
-        const bool kl = li < nt;
-        double p[4], nw[4];
-        bool grew = false;
+        // lane holds L[key 4 e + lk][row li], e = 0..3
+        double l[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const double l = kl ? L[r] * sc : NEG_INF;
-            nw[r] = fmax(mx[r], group_max<16>(l));
-            grew |= nw[r] != mx[r];
-            p[r] = kl ? exp(l - nw[r]) : 0.0;
+        for (int e = 0; e < 4; ++e) l[e] = 4 * e + lk < nt ? L[e] * sc : NEG_INF;
+        double rmax = fmax(fmax(l[0], l[1]), fmax(l[2], l[3]));
+        rmax = swap_max<32>(swap_max<16>(rmax));  // row li over the whole tile
+        const double nw = fmax(mx, rmax);
+        if (__any(nw != mx)) {  // rescale only when some running max of the wave moved
+            const double f = exp(mx - nw);  // 0 on the first tile, 1 where the max held
+            zs *= f;
+            const float ff = (float)f;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) tacc[cb] *= ff;
         }
-        if (__any(grew)) {  // rescale only when some running max of the wave moved
+        mx = nw;
+        float p[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const double f = exp(mx[r] - nw[r]);  // 0 on the first tile, 1 where the max held
-                zs[r] *= f;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) tacc[cb][r] *= f;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            mx[r] = nw[r];
-            zs[r] += group_sum<16>(p[r]);
-        }
-        // P from the result layout to the A-operand layout through this wave's LDS rows
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p_lds[wave][lk + 4 * r][li] = p[r];
-        __builtin_amdgcn_wave_barrier();
-        double pa[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) pa[kk] = p_lds[wave][li][kk * 4 + lk];
+        for (int e = 0; e < 4; ++e)
+            p[e] = 4 * e + lk < nt ? __builtin_amdgcn_exp2f((float)((l[e] - nw) * LOG2E)) : 0.0f;
+        zs += (double)sum_over_lk((p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             // consecutive MFMAs go to different accumulators
-            double vb[CB];
+            float va[CB];
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) vb[cb] = v_lds[kk * 4 + lk][cb * 16 + li];
+            for (int cb = 0; cb < CB; ++cb) va[cb] = v_lds[kk * 4 + lk][cb * 16 + li];
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
-                tacc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(pa[kk], vb[cb], tacc[cb], 0, 0, 0);
+                tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[cb], p[kk], tacc[cb], 0, 0, 0);
         }
         __syncthreads();  // every wave is done with the tile before the next is staged
     }
 
     if (!live) return;
     // store at the scale of the f32 running max kept in the state
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = rb * 16 + lk + 4 * r;
-        if (i >= m) continue;
-        const float mf = (float)mx[r];
-        const double corr = exp(mx[r] - (double)mf);
-        if (li == 0) {
-            s.m_max[gh * m + i] = mf;
-            s.m_ref[gh * m + i] = mf;
-            s.z_hat[gh * m + i] = zs[r] * corr;
-        }
-        float *th = s.t_hat + (gh * m + i) * DV;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) th[cb * 16 + li] = (float)(tacc[cb][r] * corr);
+    const int i = rb * 16 + li;
+    if (i >= m) return;
+    const float mf = (float)mx;
+    const double corr = exp(mx - (double)mf);
+    if (lk == 0) {
+        s.m_max[gh * m + i] = mf;
+        s.m_ref[gh * m + i] = mf;
+        s.z_hat[gh * m + i] = zs * corr;
     }
+    float4 *th = reinterpret_cast<float4 *>(s.t_hat + (gh * m + i) * DV);
+    const float cf = (float)corr;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        th[cb * 4 + lk] = make_float4(tacc[cb][0] * cf, tacc[cb][1] * cf, tacc[cb][2] * cf, tacc[cb][3] * cf);
 }
 
 template <int D, int DV, int MM>

@@ -303,5 +303,9 @@ def prefill_parity(wl, sample=None):
     assert worst["lm_ulp"] <= 1
     assert worst["resid"] <= RESID_TOL
     assert worst["lam"] <= 1e-12
+    # the far weights e^{l - max} are f32 values (an f32 exp, as NystromHead::far_insert
+    # on the nystrom.rs source page takes them; the gap itself is formed in f64) and
+    # T^ is accumulated in f32 as the page accumulates it: T^ rows within 1e-5, Z^
+    # (f64 sums of the f32 weights) within 1e-6 relative
     assert worst["far"] <= 1e-5
-    assert worst["z"] <= 1e-12
+    assert worst["z"] <= 1e-6

@@ -7,7 +7,9 @@ against the CPU oracle on the same prompts.
                  oracle's f64 A, not elementwise (A is ill-conditioned).
   lambda, tries  lambda within 1e-12 relative, attempt number equal.
   far field      T^ e^{m_max} and Z^ e^{m_max} against the oracle's (which uses
-                 the oracle's own landmarks), relative 1e-5 of each landmark row.
+                 the oracle's own landmarks): T^ within 1e-5 of each landmark
+                 row's norm, Z^ within 1e-6 relative (f32 weights, as the page's
+                 far_insert takes them).
   ring, sinks,   bit-exact; counters bit-exact for every group.
 """
 import pytest
