@@ -49,8 +49,8 @@ struct o1_groups {
     std::vector<uint8_t> layer_sealed;
     std::vector<int64_t> layer_steps;  // decode steps since each layer's prefill
     o1::DevState st;                   // m_eff and pointers
-    double *lm64;                      // prefill work buffer
-    size_t lm64_bytes;
+    double *a64;                       // prefill work buffer: every head's exp-Gram
+    size_t a64_bytes;
     size_t state_bytes;
     // exact-only mode: keys [G][exact_cap][d], values [G][exact_cap][dv], and the
     // split partials of its decode step (all allocated at create when exact_cap > 0)
@@ -139,7 +139,7 @@ void free_state(o1_groups *g)
     o1::DevState &s = g->st;
     void *ptrs[] = {s.near_k, s.near_v,   s.k_tilde,  s.q_tilde,  s.mu,       s.t_hat,
                     s.z_hat,  s.m_max,    s.win_head, s.far_len,  s.lambda,   s.tries,
-                    s.pend_v, s.pend_l,   s.m_ref,    s.ring_l,   g->lm64,    g->exact_k,
+                    s.pend_v, s.pend_l,   s.m_ref,    s.ring_l,   g->a64,     g->exact_k,
                     g->exact_v, g->exact_ws, g->exact_held};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -210,21 +210,21 @@ int prefill_groups(o1_groups *g, int layer, const o1::PromptView &pv, int32_t T,
     if (m_eff > c.m) m_eff = c.m;
 
     if (!exact) {
-        const size_t need = sizeof(double) * (size_t)map.count * (1 + c.hpk) * m_eff * c.d;
-        if (need > g->lm64_bytes) {
-            if (g->lm64) {
+        const size_t need = sizeof(double) * (size_t)map.count * c.hpk * m_eff * m_eff;
+        if (need > g->a64_bytes) {
+            if (g->a64) {
                 if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
                     return fail(O1_EHIP, "hipStreamSynchronize failed");
-                (void)hipFree(g->lm64);
-                g->lm64 = nullptr;
-                g->lm64_bytes = 0;
+                (void)hipFree(g->a64);
+                g->a64 = nullptr;
+                g->a64_bytes = 0;
             }
-            if (hipMalloc((void **)&g->lm64, need) != hipSuccess) {
+            if (hipMalloc((void **)&g->a64, need) != hipSuccess) {
                 (void)hipGetLastError();
-                g->lm64 = nullptr;
+                g->a64 = nullptr;
                 return fail(O1_ENOMEM, "hipMalloc of %zu bytes of prefill work space failed", need);
             }
-            g->lm64_bytes = need;
+            g->a64_bytes = need;
         }
     }
 
@@ -250,7 +250,7 @@ int prefill_groups(o1_groups *g, int layer, const o1::PromptView &pv, int32_t T,
         io.fz_kt = frozen ? frozen->k_tilde : nullptr;
         io.fz_qt = frozen ? frozen->q_tilde : nullptr;
         io.fz_mu = frozen ? frozen->mu : nullptr;
-        io.lm64 = g->lm64;
+        io.a64 = g->a64;
         io.ridge_rel = g->ridge_rel;
         err = o1::launch_prefill(g->st, io, (hipStream_t)stream);
     }
@@ -375,8 +375,8 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     g->exact = 0;
     g->layer_sealed.assign(c.n_layer, 0);
     g->layer_steps.assign(c.n_layer, 0);
-    g->lm64 = nullptr;
-    g->lm64_bytes = 0;
+    g->a64 = nullptr;
+    g->a64_bytes = 0;
     g->exact_k = g->exact_v = nullptr;
     g->exact_ws = nullptr;
     g->exact_ws_bytes = 0;
@@ -550,7 +550,7 @@ int o1_get_info(const o1_groups *g, o1_info *info)
     info->m_eff = any ? g->st.m : 0;
     info->steps = g->steps_extreme(false);
     info->state_bytes = g->state_bytes;
-    info->work_bytes = g->lm64_bytes;
+    info->work_bytes = g->a64_bytes;
     info->exact_only = any ? g->exact : 0;
     info->exact_keys = !any ? 0 : g->exact ? (int32_t)(g->T + g->steps_extreme(true)) : g->R;
     info->n_layer = g->cfg.n_layer;

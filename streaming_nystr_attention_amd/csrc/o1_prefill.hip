@@ -2,15 +2,20 @@
 // NystromGroup::prefill_shared, NystromHead::seal, ridge_pinv / cholesky and
 // the replay of NystromState::prefill_group on the nystrom.rs source page.
 //
-//   landmarks_kernel   grid (G, 1 + hpk): segment means of the keys (K~) and of
-//                      each head's queries (Q~), f64 accumulation in row order,
-//                      stored f32 (state) and f64 (work, for the exp-Gram).
-//   scatter_kernel     grid G: sinks (prompt rows 0..sink-1) and the ring (the
-//                      last w prompt keys, key j in slot (j - sink) mod w), the
-//                      ring head and far_len after the replay, and an empty set
-//                      of evictions held apart from T^ (logits -inf).
-//   gram_pinv_kernel   grid G * hpk: A = exp(Q~ K~^T * scale) and G = A^T A on f64
-//                      MFMA, lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
+//   landmarks_kernel   grid G: segment means of the keys (K~) and then of each
+//                      head's queries (Q~), f64 accumulation in row order, stored
+//                      f32 (state) and kept f64 in LDS for the exp-Gram A =
+//                      exp(Q~ K~^T * scale) (f64 MFMA), written per head to the
+//                      work buffer; the key rows of the sinks and the ring are
+//                      copied to the state as the key pass streams them.
+//   scatter_kernel     grid G: the value rows of the sinks (prompt rows
+//                      0..sink-1) and the ring (the last w prompt rows, row j in
+//                      slot (j - sink) mod w) -- the key rows too when frozen key
+//                      landmarks skip the key pass --, the ring head and
+//                      far_len after the replay, and an empty set of evictions
+//                      held apart from T^ (logits -inf).
+//   gram_pinv_kernel   grid G * hpk: G = A^T A on f64 MFMA from the exp-Gram,
+//                      lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
 //                      G + lambda I in LDS (lambda x10 on a failed pivot, up to 12
 //                      attempts, then diag(1/mean diag)), M = (G + lambda I)^-1 A^T
 //                      by substitutions spread over lane groups.  Two m x m f64
@@ -34,45 +39,36 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, PrefillIO io)
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLmThreads = 512;
+
+// Near-state row of prompt key j, or -1: sinks j < sink keep row j, the last w
+// keys go to ring slot (j - sink) mod w (row sink + slot).
+__device__ __forceinline__ int near_row(int j, int S, int w, int T)
 {
-    const int ci = blockIdx.x, src = blockIdx.y;  // src 0 = keys, 1 + h = head h
-    const int g = io.map.state(ci);
-    const int d = s.d, m = s.m, T = io.T, H = s.hpk;
-    const float *x;  // prompt row 0 of the source; rows are `pos` floats apart
-    int64_t pos;
-    float *dst32;
-    const float *fz;
-    if (src == 0) {
-        x = io.p.k_row(io.map, ci, 0);
-        pos = io.p.k_pos;
-        dst32 = s.k_tilde + (size_t)g * m * d;
-        fz = io.fz_kt ? io.fz_kt + (size_t)ci * m * d : nullptr;
-    } else {
-        x = io.p.q_row(io.map, H, ci, src - 1, 0);
-        pos = io.p.q_pos;
-        dst32 = s.q_tilde + ((size_t)g * H + (src - 1)) * m * d;
-        fz = io.fz_qt ? io.fz_qt + ((size_t)ci * H + (src - 1)) * m * d : nullptr;
-    }
-    double *dst64 = io.lm64 + ((size_t)ci * (1 + H) + src) * m * d;
-    // one thread per (segment, 4 components): the segment's rows are summed in
-    // row order, eight rows' loads in flight at a time (then four, then one)
+    if (j < S) return j;
+    if (j >= T - w) return S + (j - S) % w;
+    return -1;
+}
+
+// Segment means of the rows of x (row stride pos floats) into dst32 (state, f32)
+// and l64 (LDS, f64, row stride ld): one thread per (segment, 4 components),
+// the segment's rows summed in row order, eight rows' loads in flight at a
+// time.  With `near`, rows that are sinks or ring keys are also copied there.
+__device__ __forceinline__ void seg_means_pass(const float *x, int64_t pos, int T, int m, int d,
+                                               float *dst32, double *l64, int ld, float4 *near,
+                                               int S, int w)
+{
     const int d4 = d / 4;
-    for (int t = threadIdx.x; t < m * d4; t += kThreads) {
-        const int a = t / d4, c = (t - a * d4) * 4;
-        if (fz) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = fz[a * d + c + e];
-                dst32[a * d + c + e] = v;
-                dst64[a * d + c + e] = (double)v;
-            }
-            continue;
-        }
-        const long lo = (long)a * T / m, hi = (long)(a + 1) * T / m;
+    for (int t = threadIdx.x; t < m * d4; t += kLmThreads) {
+        const int a = t / d4, c4 = t - a * d4, c = c4 * 4;
+        const int lo = (int)((long)a * T / m), hi = (int)((long)(a + 1) * T / m);
         double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
         const float *col = x + c;
-        long j = lo;
+        // only the first and last segments can hold sinks or ring keys
+        const bool copy = near && (lo < S || hi > T - w);
+        int j = lo;
         for (; j + 8 <= hi; j += 8) {
             float4 v[8];
 #pragma unroll
@@ -84,17 +80,12 @@ __global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, Prefill
                 s2 += (double)v[u].z;
                 s3 += (double)v[u].w;
             }
-        }
-        for (; j + 4 <= hi; j += 4) {
-            float4 v[4];
+            if (copy) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4 *>(col + (int64_t)(j + u) * pos);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                s0 += (double)v[u].x;
-                s1 += (double)v[u].y;
-                s2 += (double)v[u].z;
-                s3 += (double)v[u].w;
+                for (int u = 0; u < 8; ++u) {
+                    const int r = near_row(j + u, S, w, T);
+                    if (r >= 0) near[(size_t)r * d4 + c4] = v[u];
+                }
             }
         }
         for (; j < hi; ++j) {
@@ -103,13 +94,90 @@ __global__ __launch_bounds__(kThreads) void landmarks_kernel(DevState s, Prefill
             s1 += (double)v.y;
             s2 += (double)v.z;
             s3 += (double)v.w;
+            if (copy) {
+                const int r = near_row(j, S, w, T);
+                if (r >= 0) near[(size_t)r * d4 + c4] = v;
+            }
         }
         const double inv = 1.0 / (double)(hi - lo);
         const double mean[4] = {s0 * inv, s1 * inv, s2 * inv, s3 * inv};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            dst64[a * d + c + e] = mean[e];
+            l64[a * ld + c + e] = mean[e];
             dst32[a * d + c + e] = (float)mean[e];
+        }
+    }
+}
+
+// Frozen landmarks given by the caller: the state takes them, LDS their f64 values.
+__device__ __forceinline__ void frozen_pass(const float *fz, int m, int d, float *dst32, double *l64, int ld)
+{
+    for (int t = threadIdx.x; t < m * d; t += kLmThreads) {
+        const int a = t / d, c = t - a * d;
+        const float v = fz[t];
+        dst32[t] = v;
+        l64[a * ld + c] = (double)v;
+    }
+}
+
+// One work-group per group, 512 threads (two per CU, as LDS allows at m <= 32,
+// d = 128: four waves per SIMD); dynamic LDS: K~ and one head's Q~ in
+// f64, [mp][d + 1] each (mp = m rounded up to 16, rows past m zero).  The
+// exp-Gram of head h, A[i][j] = exp(q~_i . k~_j * scale), runs on
+// v_mfma_f64_16x16x4f64 from LDS, one 16 x 16 block per wave, and goes to
+// io.a64[call][h][m][m] for gram_pinv_kernel (`gram` = 0: M is given frozen and
+// no A is needed).
+__global__ __launch_bounds__(kLmThreads, 4) void landmarks_kernel(DevState s, PrefillIO io, int gram)
+{
+    const int ci = blockIdx.x, g = io.map.state(ci);
+    const int d = s.d, m = s.m, T = io.T, H = s.hpk, tid = threadIdx.x;
+    const int nb = (m + 15) / 16, mp = nb * 16, ld = d + 1;
+    extern __shared__ double lm_lds[];
+    double *kt64 = lm_lds, *qt64 = lm_lds + (size_t)mp * ld;
+    // rows past m stay zero for every head
+    for (int t = tid; t < (mp - m) * ld; t += kLmThreads) {
+        kt64[m * ld + t] = 0.0;
+        qt64[m * ld + t] = 0.0;
+    }
+
+    float *kt32 = s.k_tilde + (size_t)g * m * d;
+    if (io.fz_kt) {
+        frozen_pass(io.fz_kt + (size_t)ci * m * d, m, d, kt32, kt64, ld);
+    } else {
+        float4 *near = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * s.R * (d / 4);
+        seg_means_pass(io.p.k_row(io.map, ci, 0), io.p.k_pos, T, m, d, kt32, kt64, ld, near, s.sink, s.w);
+    }
+
+    const int lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
+    const double sc = (double)s.scale;
+    for (int h = 0; h < H; ++h) {
+        float *qt32 = s.q_tilde + ((size_t)g * H + h) * m * d;
+        __syncthreads();  // the previous head's exp-Gram is done with qt64
+        if (io.fz_qt)
+            frozen_pass(io.fz_qt + ((size_t)ci * H + h) * m * d, m, d, qt32, qt64, ld);
+        else
+            seg_means_pass(io.p.q_row(io.map, H, ci, h, 0), io.p.q_pos, T, m, d, qt32, qt64, ld, nullptr,
+                           0, 0);
+        if (!gram) continue;
+        __syncthreads();
+        double *a = io.a64 + ((size_t)ci * H + h) * m * m;
+        for (int blk = wave; blk < nb * nb; blk += kLmThreads / 64) {
+            const int bi = blk / nb, bj = blk - bi * nb;
+            const double *qrow = qt64 + (bi * 16 + li) * ld + lk;
+            const double *krow = kt64 + (bj * 16 + li) * ld + lk;
+            f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
+            // k-step ks covers components 4 ks .. 4 ks + 3 (k-lane lk: 4 ks + lk)
+            for (int ks = 0; ks < d / 4; ks += 2) {
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qrow[4 * ks], krow[4 * ks], acc, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(qrow[4 * ks + 4], krow[4 * ks + 4], acc2, 0, 0, 0);
+            }
+            acc += acc2;
+            // lane holds A[bi*16 + lk + 4 r][bj*16 + li]
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = bi * 16 + lk + 4 * r, j = bj * 16 + li;
+                if (i < m && j < m) a[i * m + j] = exp(acc[r] * sc);
+            }
         }
     }
 }
@@ -126,8 +194,11 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO
     float4 *nv = reinterpret_cast<float4 *>(s.near_v) + (size_t)g * R * cv;
     const int base = T - w;          // first prompt key still in the window
     const int shift = base - S;      // >= 9 in skeleton mode
-    for (int t = threadIdx.x; t < R * (ck + cv); t += kThreads) {
-        const int r = t / (ck + cv), c = t - r * (ck + cv);
+    // the key rows come from the landmark kernel's key pass unless frozen key
+    // landmarks replaced it
+    const int kc = io.fz_kt ? ck : 0;
+    for (int t = threadIdx.x; t < R * (kc + cv); t += kThreads) {
+        const int r = t / (kc + cv), c = t - r * (kc + cv);
         int j;
         if (r < S) {
             j = r;
@@ -135,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO
             const int slot = r - S;
             j = base + ((slot - shift) % w + w) % w;  // (j - S) mod w == slot
         }
-        if (c < ck) nk[(size_t)r * ck + c] = kin[(int64_t)j * kp + c];
-        else nv[(size_t)r * cv + (c - ck)] = vin[(int64_t)j * vp + (c - ck)];
+        if (c < kc) nk[(size_t)r * ck + c] = kin[(int64_t)j * kp + c];
+        else nv[(size_t)r * cv + (c - kc)] = vin[(int64_t)j * vp + (c - kc)];
     }
     const int evictions = T - S - w;
     if (threadIdx.x == 0) s.win_head[g] = evictions % w;
@@ -147,13 +218,11 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO
     for (int t = threadIdx.x; t < s.hpk * kPend * s.m; t += kThreads) pl[t] = -__builtin_inf();
 }
 
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
 // One block per (group, head), 256 threads.  Dynamic LDS: A [mp][gram_lda(mp)]
 // and L [mp][mp + 1], f64, with mp = m rounded up to 16 (padding rows/columns of
-// A are 0).  The exp-Gram and A^T A run on v_mfma_f64_16x16x4f64 (operand layout:
-// A[i][k] in lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i %
-// 4), element i / 4); the Cholesky with its retries and the triangular solves run
+// A are 0).  A^T A runs on v_mfma_f64_16x16x4f64 (operand layout: A[i][k] in
+// lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i % 4),
+// element i / 4); the Cholesky with its retries and the triangular solves run
 // on the vector units from LDS.
 //
 // A's row stride is mp + P for the P lanes per row of the substitutions: the 16
@@ -200,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
 {
     const int H = s.hpk, ci = blockIdx.x / H, h = blockIdx.x - ci * H;
     const size_t gh = (size_t)io.map.state(ci) * H + h;  // state head
-    const int m = s.m, d = s.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = s.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = (m + 15) / 16, mp = nb * 16, ld = mp + 1, lda = gram_lda(mp);
     extern __shared__ double lds[];
     double *A = lds;                      // exp-Gram; then row b holds column b of M
@@ -209,40 +278,12 @@ __global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, Pref
     __shared__ int fail_s;
     __shared__ double inv_s[kMaxLandmarks];
 
-    const double *kt = io.lm64 + ((size_t)ci * (1 + H)) * m * d;
-    const double *qt = io.lm64 + ((size_t)ci * (1 + H) + 1 + h) * m * d;
-    const double sc = (double)s.scale;
     const int li = lane & 15, lk = lane >> 4;
-
-    // exp-Gram: A[i][j] = exp(q~_i . k~_j * scale), one 16x16 block per wave pass
-    for (int blk = wave; blk < nb * nb; blk += kThreads / 64) {
-        const int bi = blk / nb, bj = blk - bi * nb;
-        const int qi = bi * 16 + li, kj = bj * 16 + li;
-        const double *qrow = qt + (size_t)(qi < m ? qi : 0) * d;
-        const double *krow = kt + (size_t)(kj < m ? kj : 0) * d;
-        f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
-        // The reduction index is permuted so that each lane loads two adjacent
-        // components at once: in step pair (jj, 0/1), k-lane kk stands for
-        // component 8 jj + 2 kk (+ 1), for both operands.  Rows past m read row
-        // 0; their products reach only entries set to zero below.  d / 8 is a
-        // multiple of 8: a fixed-count inner loop unrolls (MFMA is convergent,
-        // so a runtime count leaves the loop rolled), issuing eight loads together.
-        const double2 *q2 = reinterpret_cast<const double2 *>(qrow) + lk;
-        const double2 *k2 = reinterpret_cast<const double2 *>(krow) + lk;
-        for (int k0 = 0; k0 < d / 8; k0 += 8) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const double2 a = q2[(k0 + e) * 4], b = k2[(k0 + e) * 4];
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.x, b.x, acc, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(a.y, b.y, acc2, 0, 0, 0);
-            }
-        }
-        acc += acc2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = bi * 16 + lk + 4 * r, j = bj * 16 + li;
-            A[i * lda + j] = (i < m && j < m) ? exp(acc[r] * sc) : 0.0;
-        }
+    // the exp-Gram of this head from the landmark kernel, zero-padded to mp x mp
+    const double *a64 = io.a64 + ((size_t)ci * H + h) * m * m;
+    for (int t = tid; t < mp * mp; t += kThreads) {
+        const int i = t / mp, j = t - i * mp;
+        A[i * lda + j] = (i < m && j < m) ? a64[i * m + j] : 0.0;
     }
     __syncthreads();
     // G = A^T A into L (padding rows of A are zero).  G is not kept apart from
@@ -592,16 +633,19 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
 {
     if (s.d > 128 || s.dv > 128 || s.m > kMaxLandmarks) return hipErrorInvalidValue;
     const int n = io.map.count;
-    hipLaunchKernelGGL(landmarks_kernel, dim3(n, 1 + s.hpk), dim3(kThreads), 0, stream, s, io);
-    hipError_t err = hipGetLastError();
+    const int mp = (s.m + 15) / 16 * 16;
+    const size_t lm_lds = sizeof(double) * 2 * mp * (s.d + 1);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&landmarks_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lm_lds);
     if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(landmarks_kernel, dim3(n), dim3(kLmThreads), lm_lds, stream, s, io, io.fz_mu ? 0 : 1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(scatter_kernel, dim3(n), dim3(kThreads), 0, stream, s, io);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (io.fz_mu) {
         hipLaunchKernelGGL(copy_mu_kernel, dim3(1024), dim3(kThreads), 0, stream, s, io.map, io.fz_mu);
     } else {
-        const size_t mp = (size_t)((s.m + 15) / 16) * 16;
-        const size_t lds = sizeof(double) * mp * (gram_lda((int)mp) + mp + 1);
+        const size_t lds = sizeof(double) * mp * (gram_lda(mp) + mp + 1);
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gram_pinv_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
