@@ -69,6 +69,7 @@ struct DecodeShape {
     static constexpr int RPW = 64 / LPR;                               // rows per wave per pass
     static constexpr int RPB = RPW * NW;                               // rows per block per pass
     static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 2 ? 4 : 8);      // rows per lane in flight
+    static constexpr int UNR_NEAR = (NT == 512 && CPL >= 4) ? 3 : UNR;   // near + landmark rows (row pass)
     static constexpr int VCH = DV / 4;                                 // float4 per value row
     static constexpr int RL = NT / VCH;                                // row lanes, column pass
     static constexpr int RLW = 64 / VCH;                               // row lanes per wave
@@ -155,6 +156,14 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     float4 *nk = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * R * C::CH;
     float4 *nv = reinterpret_cast<float4 *>(s.near_v) + (size_t)g * R * C::VCH;
 
+    // 512-thread launches without the streamed row pass: the row pass's first
+    // batch of near and landmark rows is issued with the prologue's loads (the
+    // rows do not depend on them; the ring slot the prologue overwrites is
+    // replaced by the new key when its dot is taken)
+    constexpr bool HOIST = NT == 512 && !C::STREAM_ROWS;
+    const float4 *kt_rows = reinterpret_cast<const float4 *>(s.k_tilde) + (size_t)g * m * C::CH;
+    float4 xh[HOIST ? C::UNR_NEAR : 1][C::CPL];
+
     // ---- 0. prologue: small loads staged into LDS ---------------------------
     {
         // held evictions, slots j < P: loads issued first, stored at the end
@@ -205,6 +214,18 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             for (int u = 0; u < MUP; ++u) {
                 const int i = tid + u * NT;
                 muv[u] = i < HPK * m * m ? mu[i] : 0.f;
+            }
+        }
+        // after the prologue's own loads, so that its stores below wait for
+        // those alone (loads complete in order)
+        if constexpr (HOIST) {
+            const int sub = lane % C::LPR, rsub = lane / C::LPR, NA = R + m;
+#pragma unroll
+            for (int u = 0; u < C::UNR_NEAR; ++u) {
+                const int r = min(wave * C::RPW + u * C::RPB + rsub, NA - 1);
+                const float4 *row = (r < R) ? nk + (size_t)r * C::CH : kt_rows + (size_t)(r - R) * C::CH;
+#pragma unroll
+                for (int k = 0; k < C::CPL; ++k) xh[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
             }
         }
         if (q_mine) (&q_s[0][0])[tid] = qv;
@@ -361,17 +382,24 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 if (b + 1 < NB) reduce(xb, b + 1);
             }
         } else {
-            for (int base = wave * C::RPW; base < NA; base += C::UNR * C::RPB) {
-                float4 x[C::UNR][C::CPL];
+            for (int base = wave * C::RPW; base < NA; base += C::UNR_NEAR * C::RPB) {
+                float4 x[C::UNR_NEAR][C::CPL];
+                if (HOIST && base == wave * C::RPW) {
 #pragma unroll
-                for (int u = 0; u < C::UNR; ++u) {
-                    const int r = min(base + u * C::RPB + rsub, NA - 1);
-                    const float4 *row = (r < R) ? nk + (size_t)r * C::CH : kt + (size_t)(r - R) * C::CH;
+                    for (int u = 0; u < C::UNR_NEAR; ++u)
 #pragma unroll
-                    for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
+                        for (int k = 0; k < C::CPL; ++k) x[u][k] = xh[HOIST ? u : 0][k];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < C::UNR_NEAR; ++u) {
+                        const int r = min(base + u * C::RPB + rsub, NA - 1);
+                        const float4 *row = (r < R) ? nk + (size_t)r * C::CH : kt + (size_t)(r - R) * C::CH;
+#pragma unroll
+                        for (int k = 0; k < C::CPL; ++k) x[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
+                    }
                 }
 #pragma unroll
-                for (int u = 0; u < C::UNR; ++u) {
+                for (int u = 0; u < C::UNR_NEAR; ++u) {
                     const int r = base + u * C::RPB + rsub;
                     if (r == slot_row) {  // the ring slot already holds the new key
 #pragma unroll
