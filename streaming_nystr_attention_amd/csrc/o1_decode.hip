@@ -114,6 +114,11 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     const int g = io.map.state(ci);       // state group
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = s.sink, R = s.R, m = s.m;
+    // query heads of the group: HPK is the compiled count (a power of two), H
+    // the group's own (HPK / 2 < H <= HPK).  Heads H .. HPK-1 are placeholders:
+    // zero queries, no state read or written, no output; their LDS slots hold
+    // values nothing stores.
+    const int H = s.hpk;
     const double scale = (double)s.scale;
     const double NEG_INF = -__builtin_inf();
 
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     auto red_s = reinterpret_cast<double (*)[C::RED_H * DV]>(share_s);
     extern __shared__ double lg_s[];               // [HPK][R] near logits, then weights
 
-    const size_t gh0 = (size_t)g * HPK;  // first head of this group
+    const size_t gh0 = (size_t)g * H;  // first head of this group
     const int e = min(max(s.win_head[g], 0), s.w - 1);  // (in range unless written out of range)
     const int slot_row = S + e;
     // evictions held apart from t_hat before this step, and whether this
@@ -171,20 +176,20 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         const bool hv_mine = tid < P * C::VCH;
         if (hv_mine) hvr = ld4<C::NTL>(reinterpret_cast<const float4 *>(s.pend_v) + (size_t)g * kPend * C::VCH + tid);
         double hlr[C::HL];
-        const int nl = HPK * kPend * m;  // [h][j][a] block of this group
+        const int nl = H * kPend * m;  // [h][j][a] block of this group
 #pragma unroll
         for (int u = 0; u < C::HL; ++u) {
             const int i = tid + u * NT;
             hlr[u] = 0.0;
             if (i < nl && (i / m) % kPend < P) hlr[u] = s.pend_l[gh0 * kPend * m + i];
         }
-        const float4 *qg = reinterpret_cast<const float4 *>(io.q) + (size_t)ci * HPK * C::CH;
+        const float4 *qg = reinterpret_cast<const float4 *>(io.q) + (size_t)ci * H * C::CH;
         // every load is issued before any is stored, so the prologue costs
         // one round trip (each thread has at most one element of each kind,
         // a few of M)
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        const bool q_mine = tid < HPK * C::CH, k_mine = tid < C::CH;
-        const bool v_mine = tid >= 128 && tid < 128 + C::VCH, st_mine = tid < HPK * m;
+        const bool q_mine = tid < H * C::CH, q_slot = tid < HPK * C::CH, k_mine = tid < C::CH;
+        const bool v_mine = tid >= 128 && tid < 128 + C::VCH, st_mine = tid < H * m;
         const bool kb_mine = ring && fold && tid < (kPend - 1) * C::CH;
         const int kbj = 1 + tid / C::CH, kbc = tid - (kbj - 1) * C::CH;
         float4 qv = z4, kin = z4, kev = z4, vin = z4, vev = z4, kbv = z4;
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             mo = s.m_max[gh0 * m + tid];
             mr = s.m_ref[gh0 * m + tid];
             zo = s.z_hat[gh0 * m + tid];
-            if (ring) lr = s.ring_l[((size_t)g * w + e) * HPK * m + tid];
+            if (ring) lr = s.ring_l[((size_t)g * w + e) * H * m + tid];
         }
         constexpr int MUP = C::STAGE_M ? (HPK * MM * MM + NT - 1) / NT : 1;
         float muv[MUP];
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
 #pragma unroll
             for (int u = 0; u < MUP; ++u) {
                 const int i = tid + u * NT;
-                muv[u] = i < HPK * m * m ? mu[i] : 0.f;
+                muv[u] = i < H * m * m ? mu[i] : 0.f;
             }
         }
         // after the prologue's own loads, so that its stores below wait for
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 for (int k = 0; k < C::CPL; ++k) xh[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
             }
         }
-        if (q_mine) (&q_s[0][0])[tid] = qv;
+        if (q_slot) (&q_s[0][0])[tid] = qv;  // placeholder heads: zero
         if (k_mine) {
             kn_s[tid] = kin;
             if (!ring) ke_s[tid] = kev;
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
 #pragma unroll
             for (int u = 0; u < MUP; ++u) {
                 const int i = tid + u * NT;
-                if (i < HPK * m * m) mu_s[i] = muv[u];
+                if (i < H * m * m) mu_s[i] = muv[u];
             }
         }
         if (hv_mine) (&hv_s[0][0])[tid] = hvr;
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             // evicted key; none with ring logits).  Unused rows load a clamped
             // row and are discarded.
             const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
-            const int NQ = HPK * m;
+            const int NQ = H * m;
             const int RP = (R + C::RPB - 1) / C::RPB * C::RPB;
             const int Q0 = (RP + m + C::RPB - 1) / C::RPB * C::RPB;
             const int NTOT = Q0 + (ring ? 0 : NQ);
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             // (no ring logits), or, on a fold with ring logits, of the keys
             // that arrived since the last fold (stored per ring slot)
             const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
-            const int NQ = HPK * m;
+            const int NQ = H * m;
             if (!ring) {
                 float4 kr[C::CPL];
 #pragma unroll
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         // (jj, c), k-lane kk stands for component 16 jj + 4 kk + c of A and B.
         // (D[i][j] in lane j + 16 (i mod 4), element i / 4)
         if (C::STREAM_ROWS && ring && fold) {
-            const int NQ = HPK * m;
+            const int NQ = H * m;
             const int li = lane & 15, lk = lane >> 4;
             const float4 *qt4 = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH + lk;
             const float4 *kb4 = &kb_s[min(li, kPend - 1)][lk];
@@ -523,7 +528,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
 #pragma unroll
                 for (int j = 0; j < C::TPT; ++j) {
                     const int b = min(rl + j * C::RL, m - 1);
-                    tpre[h][j] = ld4<C::NTL>(th + ((size_t)h * m + b) * C::VCH + cc);
+                    tpre[h][j] = ld4<C::NTL>(th + ((size_t)min(h, H - 1) * m + b) * C::VCH + cc);
                 }
         }
 #pragma unroll
@@ -535,7 +540,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     __syncthreads();
 
     // ---- 2. per-head landmark work and near weights (one wave per head) ----
-    for (int h = wave; h < HPK; h += C::NW) {
+    for (int h = wave; h < H; h += C::NW) {
         const bool act = lane < m;
         const size_t hi = (gh0 + h) * m + lane;
         double c = NEG_INF;
@@ -651,7 +656,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 for (int j = 0; j < C::TPT; ++j) {
                     const int b = rl + j * C::RL;
                     if (b >= m) break;
-                    const size_t idx = ((size_t)h * m + b) * C::VCH + cc;
+                    const size_t idx = ((size_t)min(h, H - 1) * m + b) * C::VCH + cc;
                     float4 t;
                     if constexpr (C::PRE_T) t = tpre[h][j];
                     else t = ld4<C::NTL>(th + idx);
@@ -676,7 +681,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                     t1 = fma(wk, (double)x.y, t1);
                     t2 = fma(wk, (double)x.z, t2);
                     t3 = fma(wk, (double)x.w, t3);
-                    st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
+                    if (h < H) st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
                     acc[h][0] = fma(gb, t0, acc[h][0]);
                     acc[h][1] = fma(gb, t1, acc[h][1]);
                     acc[h][2] = fma(gb, t2, acc[h][2]);
@@ -692,7 +697,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                     if (b >= m) break;
                     float4 t;
                     if constexpr (C::PRE_T) t = tpre[h][j];
-                    else t = ld4<C::NTL>(th + ((size_t)h * m + b) * C::VCH + cc);
+                    else t = ld4<C::NTL>(th + ((size_t)min(h, H - 1) * m + b) * C::VCH + cc);
                     const double gb = gain_s[h][b];
                     acc[h][0] = fma(gb, (double)t.x, acc[h][0]);
                     acc[h][1] = fma(gb, (double)t.y, acc[h][1]);
@@ -758,7 +763,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     for (int h = 0; h < HPK; ++h)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCH>(acc[h][c]);
-    float4 *outp = reinterpret_cast<float4 *>(io.out) + (size_t)ci * HPK * C::VCH;
+    float4 *outp = reinterpret_cast<float4 *>(io.out) + (size_t)ci * H * C::VCH;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
         if (lane < C::VCH) {
@@ -772,7 +777,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             }
         }
         __syncthreads();
-        if (tid < C::RED_H * C::VCH) {
+        if (tid < C::RED_H * C::VCH && h0 + tid / C::VCH < H) {
             const int hh = tid / C::VCH, c4 = tid - hh * C::VCH;
             double o0 = 0.0, o1 = 0.0, o2 = 0.0, o3 = 0.0;
 #pragma unroll
@@ -790,7 +795,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         if (h0 + C::RED_H < HPK) __syncthreads();
     }
     if (tid == 0) s.win_head[g] = (e + 1 == s.w) ? 0 : e + 1;
-    if (tid < HPK) s.far_len[gh0 + tid] += 1;
+    if (tid < H) s.far_len[gh0 + tid] += 1;
 }
 
 template <int D, int DV, int HPK, int MM, int NT, bool STREAM>
@@ -846,10 +851,15 @@ hipError_t launch_m(const DevState &s, const DecodeIO &io, hipStream_t stream)
 template <int D, int DV>
 hipError_t launch_hpk(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
+    // a group of hpk heads runs the kernel compiled for the next power of two
     switch (s.hpk) {
     case 1: return launch_m<D, DV, 1>(s, io, stream);
     case 2: return launch_m<D, DV, 2>(s, io, stream);
+    case 3:
     case 4: return launch_m<D, DV, 4>(s, io, stream);
+    case 5:
+    case 6:
+    case 7:
     case 8: return launch_m<D, DV, 8>(s, io, stream);
     default: return hipErrorInvalidValue;
     }
@@ -986,11 +996,13 @@ hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t st
 bool decode_supported(int d, int dv, int hpk, int m, int R)
 {
     if (!(d == dv && (d == 64 || d == 128))) return false;
-    if (!(hpk == 1 || hpk == 2 || hpk == 4 || hpk == 8)) return false;
+    if (hpk < 1 || hpk > 8) return false;
     if (m < 4 || m > kMaxLandmarks) return false;
     if (R < 1 || R > 1024) return false;
-    // dynamic LDS for the near logits stays within 32 KB
-    return (size_t)hpk * R * sizeof(double) <= (size_t)kMaxDynLds;
+    // dynamic LDS for the near logits of the compiled head count (hpk rounded
+    // up to a power of two) stays within 32 KB
+    const int hc = hpk <= 1 ? 1 : hpk <= 2 ? 2 : hpk <= 4 ? 4 : 8;
+    return (size_t)hc * R * sizeof(double) <= (size_t)kMaxDynLds;
 }
 
 hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stream)

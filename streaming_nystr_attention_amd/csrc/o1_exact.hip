@@ -78,9 +78,13 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
     __shared__ double fac_s[HPK];
     __shared__ double red_s[kNW][C::RED_H * DV];
 
-    const size_t gh0 = (size_t)ci * HPK;
+    // query heads: HPK is the compiled count (a power of two), H the group's own
+    // (HPK / 2 < H <= HPK); heads H .. HPK-1 take zero queries and write nothing
+    const int H = a.hpk;
+    const size_t gh0 = (size_t)ci * H;
     const float4 *qg = reinterpret_cast<const float4 *>(a.q) + gh0 * C::CH;
-    for (int i = tid; i < HPK * C::CH; i += kNT) (&q_s[0][0])[i] = qg[i];
+    for (int i = tid; i < HPK * C::CH; i += kNT)
+        (&q_s[0][0])[i] = i < H * C::CH ? qg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 *kc = reinterpret_cast<const float4 *>(a.k) + (size_t)g * a.cap * C::CH;
     const float4 *vc = reinterpret_cast<const float4 *>(a.v) + (size_t)g * a.cap * C::VCH;
     const int new_row = a.k_new ? n_keys - 1 : -1;  // absolute index of the appended key
@@ -244,7 +248,7 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
             }
         }
         __syncthreads();
-        if (tid < C::RED_H * C::VCH) {
+        if (tid < C::RED_H * C::VCH && h0 + tid / C::VCH < H) {
             const int hh = tid / C::VCH, c4 = tid - hh * C::VCH, h = h0 + hh;
             double o[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -257,7 +261,7 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
                     make_float4((float)(o[0] / den), (float)(o[1] / den), (float)(o[2] / den),
                                 (float)(o[3] / den));
             } else {
-                const size_t part = ((size_t)ci * gridDim.y + sp) * HPK + h;
+                const size_t part = ((size_t)ci * gridDim.y + sp) * H + h;
                 double *num = a.ws_num + part * DV + c4 * 4;
                 num[0] = o[0];
                 num[1] = o[1];
@@ -320,10 +324,15 @@ hipError_t launch_exact_shape(const ExactIO &a, int splits, hipStream_t stream)
 template <int D, int DV>
 hipError_t launch_exact_hpk(const ExactIO &a, int splits, hipStream_t stream)
 {
+    // hpk heads run the kernel compiled for the next power of two
     switch (a.hpk) {
     case 1: return launch_exact_shape<D, DV, 1>(a, splits, stream);
     case 2: return launch_exact_shape<D, DV, 2>(a, splits, stream);
+    case 3:
     case 4: return launch_exact_shape<D, DV, 4>(a, splits, stream);
+    case 5:
+    case 6:
+    case 7:
     case 8: return launch_exact_shape<D, DV, 8>(a, splits, stream);
     default: return hipErrorInvalidValue;
     }

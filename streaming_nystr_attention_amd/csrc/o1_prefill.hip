@@ -585,7 +585,8 @@ hipError_t launch_far(const DevState &s, const PrefillIO &io, hipStream_t stream
 {
     // heads per work-group: as many as keep it at 512 threads or fewer
     constexpr int HB_MAX = 8 / (MM / 16);
-    const int hb = s.hpk < HB_MAX ? s.hpk : HB_MAX;
+    int hb = HB_MAX;  // a power of two; the last block of a group may hold fewer heads
+    while (hb > s.hpk) hb /= 2;
     const long long nhb = (s.hpk + hb - 1) / hb;
     const long long grid = 8LL * nhb * ((io.map.count + 7) / 8);
     switch (hb) {

@@ -27,6 +27,10 @@ def gpu_ready():
     (2048, 2, 128, 200, 200, 0, 3.0),     # many groups: one work-group per group
     (5, 4, 128, 64, 1, 0, 1.0),           # a single key
     (7, 1, 64, 3000, 2999, 1234, 2.0),    # long range, odd counts
+    (6, 3, 128, 900, 900, 0, 2.0),        # 3 heads (run as 4): split key range
+    (1500, 6, 64, 150, 150, 10, 1.0),     # 6 heads (run as 8), many groups
+    (2, 7, 128, 300, 257, 3, 1.0),        # 7 heads
+    (4, 5, 64, 2000, 2000, 0, 2.0),       # 5 heads, split key range
 ])
 def test_exact_attend_matches_oracle(G, H, d, cap, n, first, std):
     say(f"[exact] G={G} hpk={H} d={d} cap={cap} n_keys={n} first={first}")

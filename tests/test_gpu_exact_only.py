@@ -42,6 +42,8 @@ CASES = [
     (_wl("x_d128_h2_T140", 1, 2, 4, 2, 128, 32, 128, 4, T=140, steps=24, seed=43), 200),
     (_wl("x_d128_h8_T268", 2, 1, 2, 8, 128, 64, 256, 4, T=268, steps=8, seed=44), 276),
     (_wl("x_d64_h4_split", 1, 1, 1, 4, 64, 16, 1000, 8, T=1010, steps=30, seed=45), 1040),
+    (_wl("x_d128_h3_T100", 2, 1, 3, 3, 128, 16, 96, 4, T=100, steps=12, seed=46), 120),
+    (_wl("x_d64_h6_split", 1, 1, 1, 6, 64, 8, 500, 2, T=505, steps=16, seed=47), 530),
 ]
 
 
