@@ -106,7 +106,7 @@ struct DecodeShape {
                   "the prologue loads at most one element of each kind per thread");
 };
 
-template <int D, int DV, int HPK, int MM, int NT, bool STREAM>
+template <int D, int DV, int HPK, int MM, int NT, bool STREAM, bool PART>
 __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_WAVES)) void decode_kernel(DevState s, DecodeIO io)
 {
     using C = DecodeShape<D, DV, HPK, MM, NT, STREAM>;
@@ -115,10 +115,11 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = s.sink, R = s.R, m = s.m;
     // query heads of the group: HPK is the compiled count (a power of two), H
-    // the group's own (HPK / 2 < H <= HPK).  Heads H .. HPK-1 are placeholders:
-    // zero queries, no state read or written, no output; their LDS slots hold
-    // values nothing stores.
-    const int H = s.hpk;
+    // the group's own.  With PART (HPK / 2 < H < HPK) heads H .. HPK-1 are
+    // placeholders: zero queries, no state read or written, no output; their
+    // LDS slots hold values nothing stores.  Without it H is the compile-time
+    // HPK (full groups keep every index a constant).
+    const int H = PART ? s.hpk : HPK;
     const double scale = (double)s.scale;
     const double NEG_INF = -__builtin_inf();
 
@@ -798,7 +799,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     if (tid < H) s.far_len[gh0 + tid] += 1;
 }
 
-template <int D, int DV, int HPK, int MM, int NT, bool STREAM>
+template <int D, int DV, int HPK, int MM, int NT, bool STREAM, bool PART>
 hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     // Static LDS of the wide shapes plus the near logits can pass 64 KB; raise
@@ -810,13 +811,13 @@ hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t strea
     if (err != hipSuccess) return err;
     const uint64_t bit = dev < 64 ? 1ull << dev : 0;
     if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, HPK, MM, NT, STREAM>),
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, HPK, MM, NT, STREAM, PART>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
         if (err != hipSuccess) return err;
         done.fetch_or(bit, std::memory_order_release);
     }
     const size_t dyn = sizeof(double) * (size_t)HPK * s.R;
-    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM, NT, STREAM>), dim3(io.map.count), dim3(NT), dyn, stream, s, io);
+    hipLaunchKernelGGL((decode_kernel<D, DV, HPK, MM, NT, STREAM, PART>), dim3(io.map.count), dim3(NT), dyn, stream, s, io);
     return hipGetLastError();
 }
 
@@ -830,36 +831,37 @@ hipError_t launch_shape(const DevState &s, const DecodeIO &io, hipStream_t strea
 // always stream.
 constexpr int kSmallGrid = 1024;
 
-template <int D, int DV, int HPK, int MM>
+template <int D, int DV, int HPK, int MM, bool PART>
 hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     const bool big = s.stream_state != 0;
     if constexpr (HPK * MM < 512) {
-        if (io.map.count >= kSmallGrid) return launch_shape<D, DV, HPK, MM, 256, true>(s, io, stream);
+        if (io.map.count >= kSmallGrid) return launch_shape<D, DV, HPK, MM, 256, true, PART>(s, io, stream);
     }
-    if (big) return launch_shape<D, DV, HPK, MM, 512, true>(s, io, stream);
-    return launch_shape<D, DV, HPK, MM, 512, false>(s, io, stream);
+    if (big) return launch_shape<D, DV, HPK, MM, 512, true, PART>(s, io, stream);
+    return launch_shape<D, DV, HPK, MM, 512, false, PART>(s, io, stream);
 }
 
-template <int D, int DV, int HPK>
+template <int D, int DV, int HPK, bool PART = false>
 hipError_t launch_m(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    if (s.m <= 32) return launch_nt<D, DV, HPK, 32>(s, io, stream);
-    return launch_nt<D, DV, HPK, kMaxLandmarks>(s, io, stream);
+    if (s.m <= 32) return launch_nt<D, DV, HPK, 32, PART>(s, io, stream);
+    return launch_nt<D, DV, HPK, kMaxLandmarks, PART>(s, io, stream);
 }
 
 template <int D, int DV>
 hipError_t launch_hpk(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    // a group of hpk heads runs the kernel compiled for the next power of two
+    // a group of hpk heads runs the kernel compiled for the next power of two;
+    // its variant for partial groups takes the head count at run time
     switch (s.hpk) {
     case 1: return launch_m<D, DV, 1>(s, io, stream);
     case 2: return launch_m<D, DV, 2>(s, io, stream);
-    case 3:
+    case 3: return launch_m<D, DV, 4, true>(s, io, stream);
     case 4: return launch_m<D, DV, 4>(s, io, stream);
     case 5:
     case 6:
-    case 7:
+    case 7: return launch_m<D, DV, 8, true>(s, io, stream);
     case 8: return launch_m<D, DV, 8>(s, io, stream);
     default: return hipErrorInvalidValue;
     }
