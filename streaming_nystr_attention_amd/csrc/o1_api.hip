@@ -210,7 +210,8 @@ int prefill_groups(o1_groups *g, int layer, const o1::PromptView &pv, int32_t T,
     if (m_eff > c.m) m_eff = c.m;
 
     if (!exact) {
-        const size_t need = sizeof(double) * (size_t)map.count * c.hpk * m_eff * m_eff;
+        const size_t mp = (size_t)(m_eff + 15) / 16 * 16;  // zero-padded to whole 16 x 16 blocks
+        const size_t need = sizeof(double) * (size_t)map.count * c.hpk * mp * mp;
         if (need > g->a64_bytes) {
             if (g->a64) {
                 if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)

@@ -99,7 +99,7 @@ struct PrefillIO {
     GroupMap map;
     int T;
     const float *fz_kt, *fz_qt, *fz_mu;  // optional frozen replacements, [count][...]
-    double *a64;                         // work: [count][hpk][m][m] f64 exp-Gram of each head
+    double *a64;                         // work: [count][hpk][mp][mp] f64 exp-Gram of each head, zero past m
     double ridge_rel;                    // relative ridge of the pinv (RIDGE_REL unless a test sets it)
 };
 

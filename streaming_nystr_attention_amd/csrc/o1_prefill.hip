@@ -14,12 +14,14 @@
 //                      landmarks skip the key pass --, the ring head and
 //                      far_len after the replay, and an empty set of evictions
 //                      held apart from T^ (logits -inf).
-//   gram_pinv_kernel   grid G * hpk: G = A^T A on f64 MFMA from the exp-Gram,
-//                      lambda = ridge_rel * max(mean diag G, DBL_MIN), Cholesky of
-//                      G + lambda I in LDS (lambda x10 on a failed pivot, up to 12
-//                      attempts, then diag(1/mean diag)), M = (G + lambda I)^-1 A^T
-//                      by substitutions spread over lane groups.  Two m x m f64
-//                      matrices of LDS per head.
+//   gram_pinv_kernel   one wave per 64 / mp heads (mp = m rounded up to 16),
+//                      a lane per matrix row: G = A^T A on f64 MFMA from the
+//                      exp-Gram, lambda = ridge_rel * max(mean diag G, DBL_MIN),
+//                      Cholesky of G + lambda I with the rows in registers
+//                      (lambda x10 on a failed pivot, up to 12 attempts, then
+//                      diag(1/mean diag)), M = (G + lambda I)^-1 A^T by forward
+//                      and back substitution, a right-hand side per lane.  One
+//                      mp x (mp + 1) f64 matrix of LDS per head.
 //   far_mfma_kernel    grid G * ceil(hpk / HB): the far field of keys sink .. T-w-1, i.e. the
 //                      state the page's sequential replay through far_insert
 //                      reaches, computed in 16-key tiles on f64 MFMA with an
@@ -125,7 +127,7 @@ __device__ __forceinline__ void frozen_pass(const float *fz, int m, int d, float
 // f64, [mp][d + 1] each (mp = m rounded up to 16, rows past m zero).  The
 // exp-Gram of head h, A[i][j] = exp(q~_i . k~_j * scale), runs on
 // v_mfma_f64_16x16x4f64 from LDS, one 16 x 16 block per wave, and goes to
-// io.a64[call][h][m][m] for gram_pinv_kernel (`gram` = 0: M is given frozen and
+// io.a64[call][h][mp][mp], zero past m, for gram_pinv_kernel (`gram` = 0: M is given frozen and
 // no A is needed).
 __global__ __launch_bounds__(kLmThreads, 4) void landmarks_kernel(DevState s, PrefillIO io, int gram)
 {
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kLmThreads, 4) void landmarks_kernel(DevState s, Pr
                            0, 0);
         if (!gram) continue;
         __syncthreads();
-        double *a = io.a64 + ((size_t)ci * H + h) * m * m;
+        double *a = io.a64 + ((size_t)ci * H + h) * mp * mp;
         for (int blk = wave; blk < nb * nb; blk += kLmThreads / 64) {
             const int bi = blk / nb, bj = blk - bi * nb;
             const double *qrow = qt64 + (bi * 16 + li) * ld + lk;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kLmThreads, 4) void landmarks_kernel(DevState s, Pr
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = bi * 16 + lk + 4 * r, j = bj * 16 + li;
-                if (i < m && j < m) a[i * m + j] = exp(acc[r] * sc);
+                a[i * mp + j] = (i < m && j < m) ? exp(acc[r] * sc) : 0.0;
             }
         }
     }
@@ -218,167 +220,183 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DevState s, PrefillIO
     for (int t = threadIdx.x; t < s.hpk * kPend * s.m; t += kThreads) pl[t] = -__builtin_inf();
 }
 
-// One block per (group, head), 256 threads.  Dynamic LDS: A [mp][gram_lda(mp)]
-// and L [mp][mp + 1], f64, with mp = m rounded up to 16 (padding rows/columns of
-// A are 0).  A^T A runs on v_mfma_f64_16x16x4f64 (operand layout: A[i][k] in
-// lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i % 4),
-// element i / 4); the Cholesky with its retries and the triangular solves run
-// on the vector units from LDS.
-//
-// A's row stride is mp + P for the P lanes per row of the substitutions: the 16
-// lanes an LDS access serves per cycle (rows b.. and their P columns) then fall
-// in distinct banks.  L keeps stride mp + 1, which the lane-per-row Cholesky
-// reads without conflicts.
-__host__ __device__ constexpr int gram_lda(int mp) { return mp <= 16 ? mp + 4 : (mp <= 32 ? mp + 2 : mp + 4); }
-
-// Forward then back substitution with the Cholesky factor L (row stride ld)
-// for every row b < m of X (row stride ldx), in place: X[b] <- (L L^T)^-1 X[b],
-// with inv[i] = 1 / L[i][i].  P lanes share a row: each sums every P-th term of
-// a step's dot product, the P partial sums are added across the lanes (an
-// aligned lane group of one wave), and the group's first lane stores the step's
-// result, which later steps read back from LDS (the LDS operations of a wave
-// complete in order).
-template <int P>
-__device__ void solve_rows(double *X, int ldx, const double *L, int ld, const double *inv, int m, int tid)
+// Value of lane u * MP + j (head u's lane j) in every lane of head u = sub.
+template <int MP, int HPW>
+__device__ __forceinline__ double head_lane_value(double v, int j, int sub)
 {
-    static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "lane group within a DPP row");
-    const int b = tid / P, sub = tid % P;
-    if (b >= m) return;  // whole lane groups leave together
-    double *x = X + (size_t)b * ldx;
-    for (int i = 0; i < m; ++i) {
-        double part = 0.0;
-#pragma unroll 4
-        for (int k = sub; k < i; k += P) part = fma(L[i * ld + k], x[k], part);
-        const double tot = P > 1 ? group_sum<P>(part) : part;
-        if (sub == 0) x[i] = (x[i] - tot) * inv[i];
-        __builtin_amdgcn_wave_barrier();
-    }
-    for (int i = m - 1; i >= 0; --i) {
-        double part = 0.0;
-#pragma unroll 4
-        for (int k = i + 1 + sub; k < m; k += P) part = fma(L[k * ld + i], x[k], part);
-        const double tot = P > 1 ? group_sum<P>(part) : part;
-        if (sub == 0) x[i] = (x[i] - tot) * inv[i];
-        __builtin_amdgcn_wave_barrier();
-    }
+    double r = lane_value(v, j);
+#pragma unroll
+    for (int u = 1; u < HPW; ++u) r = sub == u ? lane_value(v, u * MP + j) : r;
+    return r;
 }
 
-// Eight waves per SIMD (at most 64 registers): with two matrices of LDS per
-// head, eight work-groups of the m <= 32 shapes fit on a CU.
-__global__ __launch_bounds__(kThreads, 8) void gram_pinv_kernel(DevState s, PrefillIO io, double ridge_rel)
+// HPW = 64 / MP heads per wave, one lane per matrix row: a head's ridge
+// pseudo-inverse needs no more than MP lanes (m <= 64), so the heads run
+// without work-group barriers and interleave on the SIMDs.  MP = m rounded up
+// to 16; each matrix is padded to MP x MP as [G 0; 0 I], whose factor is
+// [L 0; 0 I] and whose padding adds nothing to the solves.  One MP x (MP + 1)
+// f64 matrix of LDS per head holds G, then L^T.
+//
+//   G = A^T A         per head, all lanes: v_mfma_f64_16x16x4f64 straight from
+//                     the exp-Gram in global memory, stored MP x MP with zeros
+//                     past m, so every load is unconditional (operand layout:
+//                     A[i][k] in lane i + 16 k, B[k][j] in lane j + 16 k,
+//                     D[i][j] in lane j + 16 (i % 4), element i / 4); blocks on
+//                     and above the diagonal, each stored with its mirror.  Lane
+//                     i of the head reads row i into registers.
+//   Cholesky          right-looking, as the page's cholesky: the pivot of
+//                     column j is the head's lane j's entry j after the updates
+//                     of columns 0..j-1 (a pivot not > 0 or not finite fails the
+//                     attempt: lambda x10, G recomputed bit for bit from A, up to
+//                     12 attempts); lane i divides its entry j by the pivot's
+//                     root and stores it as L^T[j][i], then subtracts
+//                     L[i][j] L[k][j] (read back from LDS) from its entry k for
+//                     k > j.  Heads of a wave retry independently: the lanes of a
+//                     head that is done run the later attempts too, but store
+//                     into a spare row, so its factor stays.
+//   M = (G + lambda I)^-1 A^T
+//                     lane b solves (L L^T) x = (row b of A) by forward and back
+//                     substitution, x in registers, L from LDS (the same address
+//                     in every lane of a head); x is column b of M.
+// Loops run over the compile-time MP, fully unrolled, so rows stay in registers;
+// after each solve row an empty asm statement that takes the row's result and
+// clobbers memory keeps the next row's LDS reads behind it (else every read of
+// the solve is hoisted to its start and the registers spill).
+template <int MP>
+__global__ __launch_bounds__(64) void gram_pinv_kernel(DevState s, PrefillIO io, double ridge_rel)
 {
-    const int H = s.hpk, ci = blockIdx.x / H, h = blockIdx.x - ci * H;
-    const size_t gh = (size_t)io.map.state(ci) * H + h;  // state head
-    const int m = s.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nb = (m + 15) / 16, mp = nb * 16, ld = mp + 1, lda = gram_lda(mp);
-    extern __shared__ double lds[];
-    double *A = lds;                      // exp-Gram; then row b holds column b of M
-    double *L = lds + (size_t)mp * lda;   // G = A^T A + lambda I, factored in place
-    __shared__ double mean_diag_s;
-    __shared__ int fail_s;
-    __shared__ double inv_s[kMaxLandmarks];
+    static_assert(MP % 16 == 0 && MP <= 64, "one lane per row");
+    constexpr int HPW = 64 / MP, NB = MP / 16, KS = MP / 4, LD = MP + 1;
+    __shared__ double Ws[HPW][(MP + 1) * LD];  // G, then L^T (row j: column j of L); row MP spare
+    __shared__ double inv_s[HPW][MP + 1];      // 1 / L[j][j]; entry MP spare
+    const int H = s.hpk, nh = io.map.count * H, m = s.m;
+    const int lane = threadIdx.x, li = lane & 15, lk = lane >> 4;
+    const int sub = min(lane / MP, HPW - 1), row = lane % MP;  // head in the wave, matrix row
+    // lanes past HPW * MP (MP = 48) shadow a row of head 0 and store nothing
+    const int hidx = blockIdx.x * HPW + sub;  // call-major head index
+    const bool owner = lane < HPW * MP && hidx < nh;
+    const double *a_of = io.a64 + (size_t)blockIdx.x * HPW * MP * MP;  // zero past m
+    const double *a64 = a_of + (size_t)min(sub, nh - 1 - (int)blockIdx.x * HPW) * MP * MP;
+    double *W = Ws[sub];
 
-    const int li = lane & 15, lk = lane >> 4;
-    // the exp-Gram of this head from the landmark kernel, zero-padded to mp x mp
-    const double *a64 = io.a64 + ((size_t)ci * H + h) * m * m;
-    for (int t = tid; t < mp * mp; t += kThreads) {
-        const int i = t / mp, j = t - i * mp;
-        A[i * lda + j] = (i < m && j < m) ? a64[i * m + j] : 0.0;
-    }
-    __syncthreads();
-    // G = A^T A into L (padding rows of A are zero).  G is not kept apart from
-    // its factor: a retry recomputes it, bit for bit, from A.
-    auto gram = [&]() {
-        for (int blk = wave; blk < nb * nb; blk += kThreads / 64) {
-            const int bi = blk / nb, bj = blk - bi * nb;
-            f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-            for (int ks = 0; ks < mp / 4; ++ks)
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A[(ks * 4 + lk) * lda + bi * 16 + li],
-                                                          A[(ks * 4 + lk) * lda + bj * 16 + li], acc, 0, 0, 0);
+    // G of head u of this wave (heads past the last one recompute the last)
+    auto gram = [&](int u) {
+        const double *au = a_of + (size_t)min(u, nh - 1 - (int)blockIdx.x * HPW) * MP * MP;
+        double av[NB][KS];  // A[4 ks + lk][16 b + li]
 #pragma unroll
-            for (int r = 0; r < 4; ++r) L[(bi * 16 + lk + 4 * r) * ld + bj * 16 + li] = acc[r];
-        }
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) av[bi][ks] = au[(4 * ks + lk) * MP + 16 * bi + li];
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+            for (int bj = bi; bj < NB; ++bj) {
+                f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[bi][ks], av[bj][ks], acc, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * bi + lk + 4 * r, j = 16 * bj + li;
+                    Ws[u][i * LD + j] = acc[r];
+                    Ws[u][j * LD + i] = acc[r];
+                }
+            }
+        asm volatile("" ::: "memory");  // the next head's operands load after these
     };
-    gram();
-    __syncthreads();
-    if (tid == 0) {
-        double md = 0.0;
-        for (int i = 0; i < m; ++i) md += L[i * ld + i];
-        mean_diag_s = md / (double)m;
-    }
-    __syncthreads();
-    const double floor_diag = mean_diag_s > DBL_MIN ? mean_diag_s : DBL_MIN;
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) gram(u);
+    __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
+    constexpr int GS = HPW * MP == 64 ? MP : 64;  // lanes summed per head
+    const double mean_diag =
+        group_sum<GS>(lane < HPW * MP && row < m ? W[row * LD + row] : 0.0) / (double)m;
+    const double floor_diag = mean_diag > DBL_MIN ? mean_diag : DBL_MIN;
     double lambda = ridge_rel * floor_diag;
     int result = kRidgeTries + 1;
+    bool done = false;
 
+#pragma unroll 1
     for (int attempt = 1; attempt <= kRidgeTries; ++attempt) {
         if (attempt > 1) {
-            gram();
-            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < HPW; ++u)
+                if (!__builtin_amdgcn_readlane((int)done, u * MP)) gram(u);  // heads still failing
+            __builtin_amdgcn_wave_barrier();
         }
-        for (int i = tid; i < m; i += kThreads) L[i * ld + i] += lambda;  // G + lambda I
-        __syncthreads();
-        if (wave == 0) {
-            // Left-looking Cholesky in one wave, lane i owning row i: for column
-            // j every lane i >= j forms s_i = L[i][j] - sum_{k<j} L[i][k] L[j][k];
-            // lane j's s is the pivot (a failed pivot is <= 0 or not finite).
-            int bad = 0;
-            for (int j = 0; j < m; ++j) {
-                double sv = 0.0;
-                if (lane >= j && lane < m) {
-                    double v = L[lane * ld + j];
-                    // unrolled so eight steps' LDS reads are in flight; the
-                    // subtractions keep their order
-#pragma unroll 8
-                    for (int k = 0; k < j; ++k) v -= L[lane * ld + k] * L[j * ld + k];
-                    sv = v;
-                }
-                const double p = lane_value(sv, j);
-                if (!(p > 0.0) || !isfinite(p)) {
-                    bad = 1;
-                    break;
-                }
-                const double dj = sqrt(p);
-                if (lane == j) L[j * ld + j] = dj;
-                else if (lane > j && lane < m) L[lane * ld + j] = sv / dj;
-                __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
+        // G + lambda I on the m x m block, 1 on the padding diagonal
+        double Lr[MP];
+#pragma unroll
+        for (int k = 0; k < MP; ++k) {
+            const double gk = W[row * LD + k];
+            Lr[k] = k != row ? gk : (row < m ? gk + lambda : 1.0);
+        }
+        __builtin_amdgcn_wave_barrier();  // G read before L^T overwrites it
+        // a failed pivot clears `ok` and the factorization runs on with a
+        // unit pivot (no branch inside the unrolled steps; the result is
+        // discarded); a head already done stores into the spare row
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < MP; ++j) {
+            const double p = head_lane_value<MP, HPW>(Lr[j], j, sub);
+            ok = ok && p > 0.0 && isfinite(p);
+            const double dj = sqrt(ok ? p : 1.0);
+            const double c = row == j ? dj : Lr[j] / dj;  // L[row][j]
+            const int jr = done ? MP : j;
+            W[jr * LD + row] = c;
+            inv_s[sub][jr] = 1.0 / dj;
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int k = j + 1; k < MP; ++k) {
+                Lr[k] = fma(-c, W[j * LD + k], Lr[k]);
+                asm volatile("" : "+v"(Lr[k]));  // updated within step j
             }
-            if (lane == 0) fail_s = bad;
+            asm volatile("" ::: "memory");
         }
-        __syncthreads();
-        const int failed = fail_s;
-        __syncthreads();
-        if (!failed) {
-            result = attempt;
-            break;
-        }
-        lambda *= 10.0;
+        if (!done && ok) result = attempt;
+        done = done || ok;
+        if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+        if (!done) lambda *= 10.0;
+        __builtin_amdgcn_wave_barrier();
     }
 
-    float *mu = s.mu + gh * m * m;
-    if (result <= kRidgeTries) {
-        for (int i = tid; i < m; i += kThreads) inv_s[i] = 1.0 / L[i * ld + i];
-        __syncthreads();
-        // Column b of M solves (L L^T) x = (row b of A), in place in row b.
-        // one wave (P * mp = 64) while m <= 32, four lanes per row over the
-        // whole work-group beyond (measured best of the two at each size)
-        if (mp <= 16) solve_rows<4>(A, lda, L, ld, inv_s, m, tid);
-        else if (mp <= 32) solve_rows<2>(A, lda, L, ld, inv_s, m, tid);
-        else solve_rows<4>(A, lda, L, ld, inv_s, m, tid);
-        __syncthreads();
-        for (int t = tid; t < m * m; t += kThreads) {
-            const int a = t / m, b = t - a * m;
-            mu[t] = (float)A[(size_t)b * lda + a];
+    float *mu = s.mu + ((size_t)io.map.state(min(hidx, nh - 1) / H) * H + min(hidx, nh - 1) % H) * m * m;
+    const bool fallback = result > kRidgeTries;
+    double x[MP];  // row `row` of A: the right-hand side of column `row` of M
+#pragma unroll
+    for (int k = 0; k < MP; ++k) x[k] = a64[row * MP + k];
+#pragma unroll
+    for (int i = 0; i < MP; ++i) {
+        double tot = 0.0;
+#pragma unroll
+        for (int k = 0; k < i; ++k) {
+            tot = fma(W[k * LD + i], x[k], tot);  // L[i][k]
+            if (k % 16 == 15) asm volatile("" : "+v"(tot)::"memory");  // 16 reads in flight
         }
-    } else {
-        for (int t = tid; t < m * m; t += kThreads) {
-            const int a = t / m, b = t - a * m;
-            mu[t] = (a == b) ? (float)(1.0 / floor_diag) : 0.0f;
-        }
+        x[i] = (x[i] - tot) * inv_s[sub][i];
+        asm volatile("" : "+v"(x[i])::"memory");
     }
-    if (tid == 0) {
-        s.lambda[gh] = lambda;
-        s.tries[gh] = result;
+#pragma unroll
+    for (int i = MP - 1; i >= 0; --i) {
+        double tot = 0.0;
+#pragma unroll
+        for (int k = i + 1; k < MP; ++k) {
+            tot = fma(W[i * LD + k], x[k], tot);  // L[k][i]
+            if ((k - i) % 16 == 0) asm volatile("" : "+v"(tot)::"memory");  // 16 reads in flight
+        }
+        x[i] = (x[i] - tot) * inv_s[sub][i];
+        asm volatile("" : "+v"(x[i])::"memory");
+    }
+    // column `row` of M; a head whose attempts all failed takes diag(1 / mean diag)
+    if (owner && row < m) {
+        const float fb = (float)(1.0 / floor_diag);
+#pragma unroll
+        for (int a = 0; a < MP; ++a)
+            if (a < m) mu[a * m + row] = fallback ? (a == row ? fb : 0.0f) : (float)x[a];
+        if (row == 0) {
+            const size_t gh = (size_t)io.map.state(hidx / H) * H + hidx % H;
+            s.lambda[gh] = lambda;
+            s.tries[gh] = result;
+        }
     }
 }
 
@@ -646,11 +664,14 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
     if (io.fz_mu) {
         hipLaunchKernelGGL(copy_mu_kernel, dim3(1024), dim3(kThreads), 0, stream, s, io.map, io.fz_mu);
     } else {
-        const size_t lds = sizeof(double) * mp * (gram_lda(mp) + mp + 1);
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gram_pinv_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(gram_pinv_kernel, dim3(n * s.hpk), dim3(kThreads), lds, stream, s, io, io.ridge_rel);
+        // 64 / mp heads per one-wave work-group
+        const auto grid = [&](int hpw) { return dim3((unsigned)((n * s.hpk + hpw - 1) / hpw)); };
+        switch (mp) {
+        case 16: hipLaunchKernelGGL(gram_pinv_kernel<16>, grid(4), dim3(64), 0, stream, s, io, io.ridge_rel); break;
+        case 32: hipLaunchKernelGGL(gram_pinv_kernel<32>, grid(2), dim3(64), 0, stream, s, io, io.ridge_rel); break;
+        case 48: hipLaunchKernelGGL(gram_pinv_kernel<48>, grid(1), dim3(64), 0, stream, s, io, io.ridge_rel); break;
+        default: hipLaunchKernelGGL(gram_pinv_kernel<64>, grid(1), dim3(64), 0, stream, s, io, io.ridge_rel); break;
+        }
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // far-insert logits of the ring's keys (the landmarks and ring are in place)
