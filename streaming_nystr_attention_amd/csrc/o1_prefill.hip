@@ -436,10 +436,13 @@ __device__ __forceinline__ float sum_over_lk(float x)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// (At least two waves per SIMD: otherwise a 4-wave work-group may take the
-// whole register file, and one work-group per CU leaves the MFMAs idle on loads.)
+// Occupancy: the MFMAs of one wave's tile are a dependent chain, so they stay
+// busy only with other waves to switch to.  Work-groups of four waves run at
+// three waves per SIMD (three work-groups per CU), those of eight at four (two
+// per CU; a few address registers spill), with the logits summed in two
+// accumulator chains to fit.
 template <int D, int DV, int MM, int HB>
-__global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevState s, PrefillIO io)
+__global__ __launch_bounds__(64 * HB * (MM / 16), (HB * (MM / 16) <= 4 ? 3 : 4)) void far_mfma_kernel(DevState s, PrefillIO io)
 {
     constexpr int NRB = MM / 16, NW = HB * NRB, NT = 64 * NW;
     constexpr int KS = D / 4;    // k-steps of the logit product = components per lane
@@ -535,18 +538,16 @@ __global__ __launch_bounds__(64 * HB * (MM / 16), 2) void far_mfma_kernel(DevSta
         if (j0 + TK < nf) fetch(j0 + TK);  // the next tile is in flight during the MFMAs
 
         // logits of the tile against this landmark block, transposed
-        f64x4 L = {0.0, 0.0, 0.0, 0.0}, L2 = {0.0, 0.0, 0.0, 0.0}, L3 = L, L4 = L;
+        f64x4 L = {0.0, 0.0, 0.0, 0.0}, L2 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int ks = 0; ks < KS; ks += 4) {
+        for (int ks = 0; ks < KS; ks += 2) {
             // opaque copies: widen Q~ at its use instead of keeping KS doubles live
-            float q0 = qa[ks], q1 = qa[ks + 1], q2 = qa[ks + 2], q3 = qa[ks + 3];
-            asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3));
+            float q0 = qa[ks], q1 = qa[ks + 1];
+            asm volatile("" : "+v"(q0), "+v"(q1));
             L = __builtin_amdgcn_mfma_f64_16x16x4f64(k_lds[lk][li][ks], (double)q0, L, 0, 0, 0);
             L2 = __builtin_amdgcn_mfma_f64_16x16x4f64(k_lds[lk][li][ks + 1], (double)q1, L2, 0, 0, 0);
-            L3 = __builtin_amdgcn_mfma_f64_16x16x4f64(k_lds[lk][li][ks + 2], (double)q2, L3, 0, 0, 0);
-            L4 = __builtin_amdgcn_mfma_f64_16x16x4f64(k_lds[lk][li][ks + 3], (double)q3, L4, 0, 0, 0);
         }
-        L = (L + L2) + (L3 + L4);
+        L = L + L2;
         // lane holds L[key 4 e + lk][row li], e = 0..3
         double l[4];
 #pragma unroll
