@@ -910,83 +910,7 @@ __global__ __launch_bounds__(256) void fold_kernel(DevState s, float *dst, int r
     }
 }
 
-// One work-group (4 waves) per (call index, block of hb heads): the far-insert
-// logits of every ring slot's key, ring_l[g][s][h][i] = q~_{h,i} . k_{sink+s} * scale,
-// a dense [w x d] x [d x m] product per head on f64 MFMA (v_mfma_f64_16x16x4f64:
-// f32 inputs widened to f64, so every product is exact and the sums are f64).
-// The operands go from global memory straight into registers: a wave holds one
-// 16-slot tile of ring keys (A) and walks the landmark tiles of its heads (B);
-// at 98 VGPRs four waves share a SIMD and hide each other's B loads (a second
-// B buffer in flight measured no faster at three waves per SIMD).  The reduction
-// index is permuted so that the four k-lanes of a row read 64 contiguous bytes
-// per load: in MFMA step (j, c), k-lane kk stands for column 16 j + 4 kk + c, for
-// A and B alike.  Rows past w or m are clamped to the last row; their products
-// reach only outputs that are not stored.
-// Operand layout: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in
-// lane j + 16 (i mod 4), element i / 4.
-template <int D>
-__global__ __launch_bounds__(256) void ring_logits_kernel(DevState s, GroupMap map, int hb)
-{
-    constexpr int NJ = D / 16, D4 = D / 4;
-    const int g = map.state(blockIdx.x), h0 = blockIdx.y * hb;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lk = lane >> 4;
-    const int m = s.m, w = s.w, H = s.hpk;
-    const int st = (w + 15) / 16, mt = (m + 15) / 16, nb = hb * mt;  // slot tiles; (head, landmark tile) pairs
-    const float4 *ring = reinterpret_cast<const float4 *>(s.near_k) + ((size_t)g * s.R + s.sink) * D4 + lk;
-    const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + ((size_t)g * H + h0) * m * D4 + lk;
-    const double scale = (double)s.scale;
-    using d4v = __attribute__((ext_vector_type(4))) double;
-
-    for (int a = wave; a < st; a += 4) {
-        float4 x[NJ];
-        const float4 *kr = ring + (size_t)min(16 * a + li, w - 1) * D4;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) x[j] = kr[4 * j];
-        for (int t = 0; t < nb; ++t) {  // head h0 + t / mt, landmark tile t % mt
-            const int hh = t / mt, i = 16 * (t - hh * mt) + li;
-            const float4 *qr = qt + ((size_t)hh * m + min(i, m - 1)) * D4;
-            float4 y[NJ];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) y[j] = qr[4 * j];
-            d4v acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[j].x, (double)y[j].x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[j].y, (double)y[j].y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[j].z, (double)y[j].z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[j].w, (double)y[j].w, acc, 0, 0, 0);
-            }
-            if (i >= m) continue;
-            double *dst = s.ring_l + ((size_t)g * w * H + h0 + hh) * m + i;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int slot = 16 * a + 4 * e + lk;
-                if (slot < w) dst[(size_t)slot * H * m] = acc[e] * scale;
-            }
-        }
-    }
-}
-
 }  // namespace
-
-hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_t stream)
-{
-    if (!s.ring_l) return hipSuccess;
-    if (s.m < 1 || s.m > kMaxLandmarks || s.w < 1 || s.hpk < 1) return hipErrorInvalidValue;
-    // heads per work-group: all of a group's heads (its ring rows loaded once)
-    // unless that leaves fewer than 2048 work-groups
-    int hb = s.hpk;
-    while (hb > 1 && (long)map.count * (s.hpk / hb) < 2048) hb /= 2;
-    if (s.hpk % hb) hb = 1;
-    const dim3 grid(map.count, s.hpk / hb);
-    if (s.d == 64)
-        hipLaunchKernelGGL(ring_logits_kernel<64>, grid, dim3(256), 0, stream, s, map, hb);
-    else if (s.d == 128)
-        hipLaunchKernelGGL(ring_logits_kernel<128>, grid, dim3(256), 0, stream, s, map, hb);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
-}
 
 hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t stream)
 {

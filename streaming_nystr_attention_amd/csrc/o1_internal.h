@@ -138,7 +138,7 @@ hipError_t launch_exact_seal(const DevState &s, const PromptView &p, const Group
 bool decode_supported(int d, int dv, int hpk, int m, int R);
 hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stream);
 // ring_l of every ring slot of the groups in `map` from their ring rows and q~
-// (after a prefill, or a write of the ring or of q~).  No-op when ring_l is null.
+// (after a prefill, and after every state write).  No-op when ring_l is null.
 hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_t stream);
 // T^ with the held evictions folded in, for every group, into dst ([G][hpk][m][dv]
 // f32; may be s.t_hat).  With `reset` the state's held set is then emptied

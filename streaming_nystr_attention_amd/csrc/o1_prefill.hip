@@ -22,6 +22,10 @@
 //                      diag(1/mean diag)), M = (G + lambda I)^-1 A^T by forward
 //                      and back substitution, a right-hand side per lane.  One
 //                      mp x (mp + 1) f64 matrix of LDS per head.
+//   ring_logits_kernel grid G * hpk / hb: the far-insert logits of every ring
+//                      slot's key against each head's query landmarks (kept per
+//                      slot for the decode's evictions), f64 MFMA with the
+//                      landmark queries staged in LDS; also run after state writes.
 //   far_mfma_kernel    grid G * ceil(hpk / HB): the far field of keys sink .. T-w-1, i.e. the
 //                      state the page's sequential replay through far_insert
 //                      reaches, computed in 16-key tiles on f64 MFMA with an
@@ -629,6 +633,67 @@ hipError_t launch_far_m(const DevState &s, const PrefillIO &io, hipStream_t stre
     return launch_far<D, DV, 64>(s, io, stream);
 }
 
+// One work-group (4 waves) per (call index, block of hb heads): the far-insert
+// logits of every ring slot's key, ring_l[g][s][h][i] = q~_{h,i} . k_{sink+s} * scale,
+// a dense [w x d] x [d x m] product per head on f64 MFMA (v_mfma_f64_16x16x4f64:
+// f32 inputs widened to f64, so every product is exact and the sums are f64).
+// The block's landmark queries (hb * m rows) are staged in LDS once; each wave
+// holds one 16-slot tile of ring keys (A) in registers, loaded straight from
+// global memory, and walks the landmark tiles of its heads (B) from LDS.  The
+// reduction index is permuted so that the four k-lanes of a row read 64
+// contiguous bytes: in MFMA step (j, c), k-lane kk stands for column
+// 16 j + 4 kk + c, for A and B alike.  Rows past w or m are clamped to the last
+// row; their products reach only outputs that are not stored.
+// Operand layout: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in
+// lane j + 16 (i mod 4), element i / 4.
+template <int D>
+__global__ __launch_bounds__(256) void ring_logits_kernel(DevState s, GroupMap map, int hb)
+{
+    constexpr int NJ = D / 16, D4 = D / 4, LDQ = D4 + 1;  // LDS row stride (float4): rows start 4 banks apart
+    extern __shared__ float4 qt_s[];                      // [hb * m][LDQ]
+    const int g = map.state(blockIdx.x), h0 = blockIdx.y * hb;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
+    const int m = s.m, w = s.w, H = s.hpk;
+    const int st = (w + 15) / 16, mt = (m + 15) / 16, nb = hb * mt;  // slot tiles; (head, landmark tile) pairs
+    const float4 *ring = reinterpret_cast<const float4 *>(s.near_k) + ((size_t)g * s.R + s.sink) * D4 + lk;
+    const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + ((size_t)g * H + h0) * m * D4;
+    const double scale = (double)s.scale;
+    using d4v = __attribute__((ext_vector_type(4))) double;
+
+    for (int t = tid; t < hb * m * D4; t += 256) {
+        const int r = t / D4, c = t - r * D4;
+        qt_s[r * LDQ + c] = qt[t];
+    }
+    __syncthreads();
+
+    for (int a = wave; a < st; a += 4) {
+        float4 x[NJ];
+        const float4 *kr = ring + (size_t)min(16 * a + li, w - 1) * D4;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) x[j] = kr[4 * j];
+        for (int t = 0; t < nb; ++t) {  // head h0 + t / mt, landmark tile t % mt
+            const int hh = t / mt, i = 16 * (t - hh * mt) + li;
+            const float4 *qr = qt_s + (hh * m + min(i, m - 1)) * LDQ + lk;
+            d4v acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float4 y = qr[4 * j];
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[j].x, (double)y.x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[j].y, (double)y.y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[j].z, (double)y.z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[j].w, (double)y.w, acc, 0, 0, 0);
+            }
+            if (i >= m) continue;
+            double *dst = s.ring_l + ((size_t)g * w * H + h0 + hh) * m + i;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int slot = 16 * a + 4 * e + lk;
+                if (slot < w) dst[(size_t)slot * H * m] = acc[e] * scale;
+            }
+        }
+    }
+}
+
 // Frozen M, [count][hpk][m][m] in call order, into the mapped groups' state.
 __global__ void copy_mu_kernel(DevState s, GroupMap map, const float *src)
 {
@@ -680,6 +745,27 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
     if (s.d == 128 && s.dv == 128) return launch_far_m<128, 128>(s, io, stream);
     if (s.d == 64 && s.dv == 64) return launch_far_m<64, 64>(s, io, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_t stream)
+{
+    if (!s.ring_l) return hipSuccess;
+    if (s.m < 1 || s.m > kMaxLandmarks || s.w < 1 || s.hpk < 1) return hipErrorInvalidValue;
+    // heads per work-group: all of a group's heads (its ring rows loaded once)
+    // unless that leaves fewer than 2048 work-groups or stages more than 64
+    // landmark rows in LDS
+    int hb = s.hpk;
+    while (hb > 1 && ((long)map.count * (s.hpk / hb) < 2048 || hb * s.m > 64)) hb /= 2;
+    if (s.hpk % hb) hb = 1;
+    const dim3 grid(map.count, s.hpk / hb);
+    const size_t lds = sizeof(float4) * (size_t)hb * s.m * (s.d / 4 + 1);
+    if (s.d == 64)
+        hipLaunchKernelGGL(ring_logits_kernel<64>, grid, dim3(256), lds, stream, s, map, hb);
+    else if (s.d == 128)
+        hipLaunchKernelGGL(ring_logits_kernel<128>, grid, dim3(256), lds, stream, s, map, hb);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace o1
