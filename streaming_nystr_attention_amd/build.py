@@ -26,19 +26,37 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library (always recompiles)."""
-    os.makedirs(LIB_DIR, exist_ok=True)
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-8000:]}")
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (in parallel, one object each) and link them
+    into one shared library (always recompiles)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(LIB_DIR, exist_ok=True)
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tag = f".tmp{os.getpid()}"
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs = [os.path.join(LIB_DIR, os.path.splitext(s)[0] + tag + ".o") for s in SOURCES]
+    jobs = [[hipcc, *compile_flags, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    try:
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as pool:
+            for f in [pool.submit(_run, j, verbose) for j in jobs]:
+                f.result()
+        tmp = LIB + tag
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 
