@@ -64,15 +64,16 @@ struct DecodeShape {
     static constexpr int NW = NT / 64;                                 // waves
     static constexpr int CH = D / 4;                                   // float4 per key row
     static constexpr int LPR_WANT = HPK <= 2 ? 8 : (HPK <= 4 ? 16 : 32);
-    static constexpr int LPR = LPR_WANT < CH ? LPR_WANT : CH;          // lanes per row
+    static constexpr int LPR = pow2_divisor(LPR_WANT, CH);             // lanes per row
     static constexpr int CPL = CH / LPR;                               // float4 per lane per row
     static constexpr int RPW = 64 / LPR;                               // rows per wave per pass
     static constexpr int RPB = RPW * NW;                               // rows per block per pass
-    static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 2 ? 4 : 8);      // rows per lane in flight
+    static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 3 ? 3 : (CPL == 2 ? 4 : 8));  // rows per lane in flight
     static constexpr int UNR_NEAR = (NT == 512 && CPL >= 4) ? 3 : UNR;   // near + landmark rows (row pass)
     static constexpr int VCH = DV / 4;                                 // float4 per value row
-    static constexpr int RL = NT / VCH;                                // row lanes, column pass
-    static constexpr int RLW = 64 / VCH;                               // row lanes per wave
+    static constexpr int VCP = pow2_ceil(VCH);                         // lanes per value row (VCH used)
+    static constexpr int RL = NT / VCP;                                // row lanes, column pass
+    static constexpr int RLW = 64 / VCP;                               // row lanes per wave
     static constexpr int TPT = (MM + RL - 1) / RL;                     // T^ rows per lane per head
     static constexpr bool STAGE_M = HPK * MM * MM <= 2048;             // M staged in LDS
     static constexpr bool PRE_T = HPK * TPT <= (NT == 256 ? 8 : 32);   // T^ prefetched in registers
@@ -85,19 +86,19 @@ struct DecodeShape {
     // One work-group per CU and registers to spare: the row pass runs as one
     // stream over every row it reads, two batches per round trip, with the
     // queries in f64 registers.
-    static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512;
+    static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512 && (CH & (CH - 1)) == 0;
     static constexpr int HL = (HPK * kPend * MM + NT - 1) / NT;       // held logits per thread
     // at least three waves per SIMD on large grids (at most 168 VGPRs)
     static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
     // heads per LDS round of the final reduction (one work-group per CU: room for all)
-    static constexpr int RED_CAP = (STREAM_ROWS ? 65536 : 16384) / (NW * DV * 8);
+    static constexpr int RED_CAP = pow2_floor((STREAM_ROWS ? 65536 : 16384) / (NW * DV * 8));
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     // the final reduction's buffer also holds the held weights (steps 0-3)
     static constexpr int RED_N = NW * RED_H * DV, WF_N = HPK * kPend * MM;
     static constexpr int SHARE_N = RED_N > WF_N ? RED_N : WF_N;
     static_assert(D % (4 * LPR) == 0, "key width must split evenly over the row lanes");
     static_assert(HPK <= LPR, "the head reduction needs at least hpk lanes per row");
-    static_assert(64 % VCH == 0, "value rows must tile a wave");
+    static_assert(64 % VCP == 0, "value rows must tile a wave");
     static_assert(CH <= 64 && VCH <= 64, "rows wider than 256 floats are not compiled");
     static_assert(RED_H >= 1 && HPK % RED_H == 0, "heads must split into reduction rounds");
     static_assert(RL >= kPend, "each held value row needs a row lane of its own");
@@ -282,7 +283,9 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     // ---- 1. row-dot pass ----------------------------------------------------
     // Loads are unconditional (row indices clamped into range, results of
     // out-of-range rows discarded) so each batch issues back to back.
-    const int cc = tid % C::VCH, rl = tid / C::VCH;  // column-pass mapping
+    // column-pass mapping: column lane cp of row lane rl; lanes past a row's VCH
+    // columns (VCH not a power of two) repeat its last column and store nothing
+    const int cp = tid % C::VCP, rl = tid / C::VCP, cc = min(cp, C::VCH - 1);
     float4 tpre[C::PRE_T ? HPK : 1][C::PRE_T ? C::TPT : 1];
     float4 vpre[C::VPRE];
     {
@@ -682,7 +685,8 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                     t1 = fma(wk, (double)x.y, t1);
                     t2 = fma(wk, (double)x.z, t2);
                     t3 = fma(wk, (double)x.w, t3);
-                    if (h < H) st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
+                    if (h < H && cp < C::VCH)
+                        st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
                     acc[h][0] = fma(gb, t0, acc[h][0]);
                     acc[h][1] = fma(gb, t1, acc[h][1]);
                     acc[h][2] = fma(gb, t2, acc[h][2]);
@@ -759,11 +763,11 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
 
     // ---- 4. reduce row lanes, joint division, counters ---------------------
     if (fold) __syncthreads();  // every wave is done with the fold weights
-    // within a wave: the RLW row lanes sit VCH lanes apart
+    // within a wave: the RLW row lanes sit VCP lanes apart
 #pragma unroll
     for (int h = 0; h < HPK; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCH>(acc[h][c]);
+        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCP>(acc[h][c]);
     float4 *outp = reinterpret_cast<float4 *>(io.out) + (size_t)ci * H * C::VCH;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
@@ -921,7 +925,7 @@ hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t st
 
 bool decode_supported(int d, int dv, int hpk, int m, int R)
 {
-    if (!(d == dv && (d == 64 || d == 128))) return false;
+    if (!(d == dv && (d == 64 || d == 96 || d == 128))) return false;
     if (hpk < 1 || hpk > 8) return false;
     if (m < 4 || m > kMaxLandmarks) return false;
     if (R < 1 || R > 1024) return false;
@@ -935,6 +939,7 @@ hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stre
 {
     if (!decode_supported(s.d, s.dv, s.hpk, s.m, s.R)) return hipErrorInvalidValue;
     if (s.d == 64) return launch_hpk<64, 64>(s, io, stream);
+    if (s.d == 96) return launch_hpk<96, 96>(s, io, stream);
     return launch_hpk<128, 128>(s, io, stream);
 }
 

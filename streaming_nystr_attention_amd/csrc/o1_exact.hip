@@ -37,14 +37,15 @@ struct ExactShape {
     static constexpr int WAVES_PER_SIMD = HPK <= 2 ? 4 : 1;
     static constexpr int CH = D / 4;
     static constexpr int LPR_WANT = HPK <= 2 ? 8 : (HPK <= 4 ? 16 : 32);
-    static constexpr int LPR = LPR_WANT < CH ? LPR_WANT : CH;
+    static constexpr int LPR = pow2_divisor(LPR_WANT, CH);
     static constexpr int CPL = CH / LPR;
     static constexpr int RPW = 64 / LPR;
     static constexpr int RPB = RPW * NW;
-    static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 2 ? 4 : 8);
+    static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 3 ? 3 : (CPL == 2 ? 4 : 8));
     static constexpr int VCH = DV / 4;
-    static constexpr int RL = NT / VCH;
-    static constexpr int RED_CAP = 16384 / (NW * DV * 8);
+    static constexpr int VCP = pow2_ceil(VCH);  // lanes per value row (VCH used)
+    static constexpr int RL = NT / VCP;
+    static constexpr int RED_CAP = pow2_floor(16384 / (NW * DV * 8));
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     // V rows per lane loaded before the chunk's softmax (more would cost a wave
     // per SIMD at hpk >= 4)
@@ -100,7 +101,9 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
     constexpr int HSTRIDE = C::LPR / HPK;
     const int my_head = sub / HSTRIDE;
     const bool writer = (sub % HSTRIDE) == 0;
-    const int cc = tid % C::VCH, rl = tid / C::VCH;
+    // V pass: column lane cp of row lane rl; lanes past a row's VCH columns (VCH
+    // not a power of two) repeat its last column and store nothing
+    const int cp = tid % C::VCP, rl = tid / C::VCP, cc = min(cp, C::VCH - 1);
 
     constexpr int HPW = (HPK + kNW - 1) / kNW;  // heads per wave: h = wave + j * kNW
     double run_max[HPW], run_sum[HPW];          // running max / sum of the wave's heads
@@ -233,7 +236,7 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
 #pragma unroll
     for (int h = 0; h < HPK; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCH>(acc[h][c]);
+        for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCP>(acc[h][c]);
     const bool final_out = gridDim.y == 1;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
@@ -388,6 +391,7 @@ int exact_splits(int G, int n_visible)
 hipError_t launch_exact(const ExactIO &a, int splits, hipStream_t stream)
 {
     if (a.d == 64 && a.dv == 64) return launch_exact_hpk<64, 64>(a, splits, stream);
+    if (a.d == 96 && a.dv == 96) return launch_exact_hpk<96, 96>(a, splits, stream);
     if (a.d == 128 && a.dv == 128) return launch_exact_hpk<128, 128>(a, splits, stream);
     return hipErrorInvalidValue;
 }

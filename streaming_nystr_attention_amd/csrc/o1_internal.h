@@ -20,6 +20,27 @@ constexpr size_t kInfinityCacheBytes = size_t(256) << 20;  // MI355X memory-side
 // eviction folds them all into T^ at once, so T^ is rewritten once per kPend
 // steps instead of every step.  A group's held count is far_len mod kPend.
 constexpr int kPend = O1_FOLD_PERIOD;
+
+// Largest power of two not above `want` that divides n; smallest power of two
+// not below n; largest power of two not above n (n >= 1).
+__host__ __device__ constexpr int pow2_divisor(int want, int n)
+{
+    int p = 1;
+    while (2 * p <= want && n % (2 * p) == 0) p *= 2;
+    return p;
+}
+__host__ __device__ constexpr int pow2_ceil(int n)
+{
+    int p = 1;
+    while (p < n) p *= 2;
+    return p;
+}
+__host__ __device__ constexpr int pow2_floor(int n)
+{
+    int p = 1;
+    while (2 * p <= n) p *= 2;
+    return p;
+}
 static_assert(kPend >= 2, "a fold period of 1 holds nothing");
 
 // Device state of G independent groups (one GQA group each).  Layout, with

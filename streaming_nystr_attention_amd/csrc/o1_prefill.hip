@@ -743,6 +743,7 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
     // far-insert logits of the ring's keys (the landmarks and ring are in place)
     if ((err = launch_ring_logits(s, io.map, stream)) != hipSuccess) return err;
     if (s.d == 128 && s.dv == 128) return launch_far_m<128, 128>(s, io, stream);
+    if (s.d == 96 && s.dv == 96) return launch_far_m<96, 96>(s, io, stream);
     if (s.d == 64 && s.dv == 64) return launch_far_m<64, 64>(s, io, stream);
     return hipErrorInvalidValue;
 }
@@ -761,6 +762,8 @@ hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_
     const size_t lds = sizeof(float4) * (size_t)hb * s.m * (s.d / 4 + 1);
     if (s.d == 64)
         hipLaunchKernelGGL(ring_logits_kernel<64>, grid, dim3(256), lds, stream, s, map, hb);
+    else if (s.d == 96)
+        hipLaunchKernelGGL(ring_logits_kernel<96>, grid, dim3(256), lds, stream, s, map, hb);
     else if (s.d == 128)
         hipLaunchKernelGGL(ring_logits_kernel<128>, grid, dim3(256), lds, stream, s, map, hb);
     else

@@ -31,6 +31,9 @@ def gpu_ready():
     (1500, 6, 64, 150, 150, 10, 1.0),     # 6 heads (run as 8), many groups
     (2, 7, 128, 300, 257, 3, 1.0),        # 7 heads
     (4, 5, 64, 2000, 2000, 0, 2.0),       # 5 heads, split key range
+    (3, 2, 96, 1000, 1000, 0, 2.0),       # d = 96: value rows of 24 float4, split key range
+    (2048, 8, 96, 150, 150, 5, 1.0),      # d = 96, 8 heads, many groups
+    (5, 3, 96, 300, 211, 7, 1.0),         # d = 96, 3 heads (run as 4), ragged tail
 ])
 def test_exact_attend_matches_oracle(G, H, d, cap, n, first, std):
     say(f"[exact] G={G} hpk={H} d={d} cap={cap} n_keys={n} first={first}")

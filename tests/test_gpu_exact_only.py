@@ -44,6 +44,8 @@ CASES = [
     (_wl("x_d64_h4_split", 1, 1, 1, 4, 64, 16, 1000, 8, T=1010, steps=30, seed=45), 1040),
     (_wl("x_d128_h3_T100", 2, 1, 3, 3, 128, 16, 96, 4, T=100, steps=12, seed=46), 120),
     (_wl("x_d64_h6_split", 1, 1, 1, 6, 64, 8, 500, 2, T=505, steps=16, seed=47), 530),
+    (_wl("x_d96_h2_T60", 2, 1, 2, 2, 96, 16, 64, 4, T=60, steps=20, seed=48), 80),
+    (_wl("x_d96_h8_split", 1, 1, 1, 8, 96, 32, 500, 4, T=510, steps=12, seed=49), 530),
 ]
 
 

@@ -1,6 +1,6 @@
 """GPU parity at seeded random shapes: each case draws the query heads per group,
 the head width, the landmark budget, window, sinks, prompt length, rectifier,
-input scale and group counts within the compiled limits (d = dv in {64, 128},
+input scale and group counts within the compiled limits (d = dv in {64, 96, 128},
 hpk <= 8, m <= 64, sink + w <= 1024 with hpk' * (sink + w) * 8 <= 32 KB for hpk'
 the head count rounded up to a power of two),
 then checks the prefill freeze and the decode steps against the oracle exactly
@@ -26,13 +26,13 @@ def gpu_ready():
     yield
 
 
-def draw(case: int):
-    r = np.random.default_rng(7000 + case)
+def draw(case: int, widths=(64, 128), base=7000):
+    r = np.random.default_rng(base + case)
     while True:
         # the first ten cases draw power-of-two head counts, the rest any count
         hpk = int(r.choice([1, 2, 4, 8])) if case < 10 else int(r.integers(1, 9))
         hc = 1 << (hpk - 1).bit_length()  # the compiled head count that runs it
-        d = int(r.choice([64, 128]))
+        d = int(r.choice(list(widths)))
         m = int(r.integers(4, 65))
         sink = int(r.integers(0, 17))
         w = int(r.integers(1, 300))
@@ -43,12 +43,15 @@ def draw(case: int):
         std = float(r.choice([1.0, 2.0, 3.0]))
         rect = int(r.integers(0, 2))
         steps = int(r.integers(5, 40))
-        wl = W.Workload(f"rand{case}", n_seq, n_layer, n_kv, hpk, d, d, m, w, sink, T=T, steps=steps,
+        wl = W.Workload(f"rand{case}" if base == 7000 else f"rand{case}_d{d}", n_seq, n_layer, n_kv, hpk, d, d, m, w, sink, T=T, steps=steps,
                         q_std=std, k_std=std, seed=900 + case)
         return wl, (O.RECT_AGGREGATE, O.RECT_FM)[rect]
 
 
 CASES = [draw(i) for i in range(16)]
+# d = 96 (value rows of 24 float4) drawn from their own seeds, so the cases
+# above keep theirs
+CASES += [draw(i, widths=(96,), base=7100) for i in range(6)]
 
 
 @pytest.mark.parametrize("wl,rect", CASES,
