@@ -23,7 +23,9 @@
 //      The hpk partial dots of a row are reduced over the row's lanes by
 //      halving exchanges (each step keeps half the heads), so the lanes of a
 //      row end with one head's total each.  Shapes with one work-group per
-//      CU read the three kinds of rows as one block-aligned stream instead.
+//      CU read the three kinds of rows as one block-aligned stream instead,
+//      and with eight heads take the dots on f64 MFMA (16-row tiles times the
+//      queries and the evicted key as columns).
 //      T^ rows and the first V rows this thread contracts later are loaded at
 //      the end of the pass, so their latency overlaps step 2.
 //   2. per head (one wave): c = max lg, f = max s, fh = e^{s - f}; running-max
@@ -87,6 +89,9 @@ struct DecodeShape {
     // stream over every row it reads, two batches per round trip, with the
     // queries in f64 registers.
     static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512 && (CH & (CH - 1)) == 0;
+    // eight heads: the streamed row pass takes its dots on f64 MFMA (rows x
+    // [queries, evicted key]) instead of per-lane dots and head reductions
+    static constexpr bool MFMA_ROWS = STREAM_ROWS && HPK == 8 && D % 16 == 0;
     static constexpr int HL = (HPK * kPend * MM + NT - 1) / NT;       // held logits per thread
     // at least three waves per SIMD on large grids (at most 168 VGPRs)
     static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
@@ -295,7 +300,72 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         const bool writer = (sub % HSTRIDE) == 0;
         const float4 *kt = reinterpret_cast<const float4 *>(s.k_tilde) + (size_t)g * m * C::CH;
         const int NA = R + m;  // near rows, then landmark rows
-        if constexpr (C::STREAM_ROWS) {
+        if constexpr (C::MFMA_ROWS) {
+            // Row space [0, R) near keys, [R, R + m) key landmarks, [R + m, NR)
+            // query landmarks (far-insert logits of the evicted key; none with
+            // ring logits), in 16-row tiles, times B = [q_0 .. q_7, k_e, 0 ..]:
+            // D[row][j] is the dot of the row with head j's query (j < 8) or
+            // with the evicted key (j = 8).  Operand layout (wave64): A[i][k] in
+            // lane i + 16 k, B[k][j] in lane j + 16 k; f64 D[i][j] in lane
+            // j + 16 (i % 4), element i / 4.  In MFMA step (jj, c), k-lane kk
+            // stands for component 16 jj + 4 kk + c of A and B alike, so a lane's
+            // operands of one row are the D/16 float4 at 4 jj + kk.  Rows past NR
+            // load a clamped row and are discarded.
+            constexpr int NJ = D / 16;
+            using d4v = __attribute__((ext_vector_type(4))) double;
+            const int li = lane & 15, lk = lane >> 4;
+            const float4 *qt = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH;
+            const int NQ = ring ? 0 : H * m, NR = R + m + NQ, NTILE = (NR + 15) / 16;
+            float4 bq[NJ];  // column li of B: head li's query, or the evicted key
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) {
+                const float4 q = q_s[min(li, HPK - 1)][4 * jj + lk], k = ke_s[4 * jj + lk];
+                bq[jj] = li < HPK ? q : (li == HPK && !ring ? k : make_float4(0.f, 0.f, 0.f, 0.f));
+            }
+            auto loadA = [&](float4 (&x)[NJ], int t) {
+                const int r = min(16 * t + li, NR - 1);
+                const float4 *row = r < R ? nk + (size_t)r * C::CH
+                                  : r < R + m ? kt + (size_t)(r - R) * C::CH
+                                              : qt + (size_t)(r - R - m) * C::CH;
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj) x[jj] = ld4<C::NTL>(row + 4 * jj + lk);
+            };
+            auto mma = [&](float4 (&x)[NJ], int t) {
+                if (16 * t + li == slot_row) {  // the ring slot already holds the new key
+#pragma unroll
+                    for (int jj = 0; jj < NJ; ++jj) x[jj] = kn_s[4 * jj + lk];
+                }
+                d4v acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj) {
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[jj].x, (double)bq[jj].x, acc, 0, 0, 0);
+                    acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[jj].y, (double)bq[jj].y, acc2, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[jj].z, (double)bq[jj].z, acc, 0, 0, 0);
+                    acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[jj].w, (double)bq[jj].w, acc2, 0, 0, 0);
+                }
+                acc += acc2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * t + 4 * e + lk;  // D[4 e + lk][li]
+                    const double v = acc[e] * scale;
+                    if (li < HPK) {
+                        if (row < R) lg_s[li * R + row] = v;
+                        else if (row < R + m) land_s[li][row - R] = v;
+                    } else if (li == HPK && row >= R + m && row < NR) {
+                        const int rq = row - R - m;
+                        lf_s[rq / m][rq % m] = v;
+                    }
+                }
+            };
+            // two tiles per round trip
+            float4 xa[NJ], xb[NJ];
+            for (int t = wave; t < NTILE; t += 2 * C::NW) {
+                loadA(xa, t);
+                if (t + C::NW < NTILE) loadA(xb, t + C::NW);
+                mma(xa, t);
+                if (t + C::NW < NTILE) mma(xb, t + C::NW);
+            }
+        } else if constexpr (C::STREAM_ROWS) {
             // One row space in which each kind of row starts on a block row, so
             // the source of every load and the work on it are uniform across
             // the wave: [0, RP) near keys (R used), [RP, Q0) key landmarks (m
