@@ -62,10 +62,10 @@ DECODE_SRC = [os.path.join(ROOT, "streaming_nystr_attention_amd", "csrc", f)
 # kernel's sources).
 # A changed kernel (comments aside) has no entry, and the roofline's traffic is then null.
 MEASURED_TRAFFIC = {
-    ("qwen3_stack_b64", "7ad30069431d3c9c"): 3051887110,
-    ("stress_m32_s4", "7ad30069431d3c9c"): 436418021,
-    ("stress_m8_s0", "7ad30069431d3c9c"): 318928099,
-    ("wide_gqa", "7ad30069431d3c9c"): 214466228,
+    ("qwen3_stack_b64", "3289e4b5a52372fa"): 3051970419,
+    ("stress_m32_s4", "3289e4b5a52372fa"): 436436459,
+    ("stress_m8_s0", "3289e4b5a52372fa"): 318871012,
+    ("wide_gqa", "3289e4b5a52372fa"): 208450724,
 }
 
 
