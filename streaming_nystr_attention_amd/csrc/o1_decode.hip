@@ -70,15 +70,15 @@ struct DecodeShape {
     static constexpr int CPL = CH / LPR;                               // float4 per lane per row
     static constexpr int RPW = 64 / LPR;                               // rows per wave per pass
     static constexpr int RPB = RPW * NW;                               // rows per block per pass
-    static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 3 ? 3 : (CPL == 2 ? 4 : 8));  // rows per lane in flight
-    static constexpr int UNR_NEAR = (NT == 512 && CPL >= 4) ? 3 : UNR;   // near + landmark rows (row pass)
+    static constexpr int UNR = CPL >= 8 ? 1 : (CPL >= 4 ? 2 : (CPL == 3 ? 3 : (CPL == 2 ? 4 : 8)));  // rows per lane in flight
+    static constexpr int UNR_NEAR = (NT == 512 && CPL >= 4 && CPL < 8) ? 3 : UNR;  // near + landmark rows (row pass)
     static constexpr int VCH = DV / 4;                                 // float4 per value row
     static constexpr int VCP = pow2_ceil(VCH);                         // lanes per value row (VCH used)
     static constexpr int RL = NT / VCP;                                // row lanes, column pass
     static constexpr int RLW = 64 / VCP;                               // row lanes per wave
     static constexpr int TPT = (MM + RL - 1) / RL;                     // T^ rows per lane per head
     static constexpr bool STAGE_M = HPK * MM * MM <= 2048;             // M staged in LDS
-    static constexpr bool PRE_T = HPK * TPT <= (NT == 256 ? 8 : 32);   // T^ prefetched in registers
+    static constexpr bool PRE_T = HPK * TPT <= (NT == 256 ? 8 : (DV > 128 ? 16 : 32));  // T^ prefetched in registers
     // V rows prefetched per lane (6 where 8 would spill at 256 VGPRs; 9 at 512
     // threads covers a 128-key window plus 4 sinks, so no V batch follows)
     static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : (HPK * MM >= 512 ? 6 : 9);
@@ -88,7 +88,7 @@ struct DecodeShape {
     // One work-group per CU and registers to spare: the row pass runs as one
     // stream over every row it reads, two batches per round trip, with the
     // queries in f64 registers.
-    static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512 && (CH & (CH - 1)) == 0;
+    static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512 && (CH & (CH - 1)) == 0 && HPK * CPL <= 8;
     // eight heads: the streamed row pass takes its dots on f64 MFMA (rows x
     // [queries, evicted key]) instead of per-lane dots and head reductions
     static constexpr bool MFMA_ROWS = STREAM_ROWS && HPK == 8 && D % 16 == 0;
@@ -909,7 +909,8 @@ template <int D, int DV, int HPK, int MM, bool PART>
 hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     const bool big = s.stream_state != 0;
-    if constexpr (HPK * MM < 512) {
+    // (rows wider than 128 floats: 512 threads keep a row lane per held slot)
+    if constexpr (HPK * MM < 512 && DV <= 128) {
         if (io.map.count >= kSmallGrid) return launch_shape<D, DV, HPK, MM, 256, true, PART>(s, io, stream);
     }
     if (big) return launch_shape<D, DV, HPK, MM, 512, true, PART>(s, io, stream);
@@ -919,8 +920,12 @@ hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 template <int D, int DV, int HPK, bool PART = false>
 hipError_t launch_m(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    if (s.m <= 32) return launch_nt<D, DV, HPK, 32, PART>(s, io, stream);
-    return launch_nt<D, DV, HPK, kMaxLandmarks, PART>(s, io, stream);
+    if constexpr (D > 128) {
+        return launch_nt<D, DV, HPK, 32, PART>(s, io, stream);  // m <= 32 at these widths
+    } else {
+        if (s.m <= 32) return launch_nt<D, DV, HPK, 32, PART>(s, io, stream);
+        return launch_nt<D, DV, HPK, kMaxLandmarks, PART>(s, io, stream);
+    }
 }
 
 template <int D, int DV>
@@ -995,7 +1000,9 @@ hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t st
 
 bool decode_supported(int d, int dv, int hpk, int m, int R)
 {
-    if (!(d == dv && (d == 64 || d == 96 || d == 128))) return false;
+    if (!(d == dv && (d == 64 || d == 96 || d == 128 || d == 256))) return false;
+    // the prefill's landmark pass keeps K~ and one head's Q~ in f64 LDS
+    if (d > 128 && m > 32) return false;
     if (hpk < 1 || hpk > 8) return false;
     if (m < 4 || m > kMaxLandmarks) return false;
     if (R < 1 || R > 1024) return false;
@@ -1010,6 +1017,7 @@ hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stre
     if (!decode_supported(s.d, s.dv, s.hpk, s.m, s.R)) return hipErrorInvalidValue;
     if (s.d == 64) return launch_hpk<64, 64>(s, io, stream);
     if (s.d == 96) return launch_hpk<96, 96>(s, io, stream);
+    if (s.d == 256) return launch_hpk<256, 256>(s, io, stream);
     return launch_hpk<128, 128>(s, io, stream);
 }
 

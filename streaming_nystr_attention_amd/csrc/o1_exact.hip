@@ -41,7 +41,7 @@ struct ExactShape {
     static constexpr int CPL = CH / LPR;
     static constexpr int RPW = 64 / LPR;
     static constexpr int RPB = RPW * NW;
-    static constexpr int UNR = CPL >= 4 ? 2 : (CPL == 3 ? 3 : (CPL == 2 ? 4 : 8));
+    static constexpr int UNR = CPL >= 8 ? 1 : (CPL >= 4 ? 2 : (CPL == 3 ? 3 : (CPL == 2 ? 4 : 8)));
     static constexpr int VCH = DV / 4;
     static constexpr int VCP = pow2_ceil(VCH);  // lanes per value row (VCH used)
     static constexpr int RL = NT / VCP;
@@ -49,7 +49,7 @@ struct ExactShape {
     static constexpr int RED_H = HPK < RED_CAP ? HPK : RED_CAP;
     // V rows per lane loaded before the chunk's softmax (more would cost a wave
     // per SIMD at hpk >= 4)
-    static constexpr int VPRE = HPK <= 2 ? 8 : 4;
+    static constexpr int VPRE = HPK <= 2 && DV <= 128 ? 8 : 4;
     static_assert(HPK <= LPR && HPK % RED_H == 0, "unsupported head count");
 };
 
@@ -393,6 +393,7 @@ hipError_t launch_exact(const ExactIO &a, int splits, hipStream_t stream)
     if (a.d == 64 && a.dv == 64) return launch_exact_hpk<64, 64>(a, splits, stream);
     if (a.d == 96 && a.dv == 96) return launch_exact_hpk<96, 96>(a, splits, stream);
     if (a.d == 128 && a.dv == 128) return launch_exact_hpk<128, 128>(a, splits, stream);
+    if (a.d == 256 && a.dv == 256) return launch_exact_hpk<256, 256>(a, splits, stream);
     return hipErrorInvalidValue;
 }
 

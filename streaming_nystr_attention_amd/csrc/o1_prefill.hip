@@ -444,9 +444,9 @@ __device__ __forceinline__ float sum_over_lk(float x)
 // busy only with other waves to switch to.  Work-groups of four waves run at
 // three waves per SIMD (three work-groups per CU), those of eight at four (two
 // per CU; a few address registers spill), with the logits summed in two
-// accumulator chains to fit.
+// accumulator chains to fit.  Rows of 256 floats run at two per SIMD.
 template <int D, int DV, int MM, int HB>
-__global__ __launch_bounds__(64 * HB * (MM / 16), (HB * (MM / 16) <= 4 ? 3 : 4)) void far_mfma_kernel(DevState s, PrefillIO io)
+__global__ __launch_bounds__(64 * HB * (MM / 16), (D > 128 ? 2 : (HB * (MM / 16) <= 4 ? 3 : 4))) void far_mfma_kernel(DevState s, PrefillIO io)
 {
     constexpr int NRB = MM / 16, NW = HB * NRB, NT = 64 * NW;
     constexpr int KS = D / 4;    // k-steps of the logit product = components per lane
@@ -716,7 +716,7 @@ __global__ void copy_mu_kernel(DevState s, GroupMap map, const float *src)
 
 hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t stream)
 {
-    if (s.d > 128 || s.dv > 128 || s.m > kMaxLandmarks) return hipErrorInvalidValue;
+    if (s.d > 256 || s.dv > 256 || s.m > kMaxLandmarks || (s.d > 128 && s.m > 32)) return hipErrorInvalidValue;
     const int n = io.map.count;
     const int mp = (s.m + 15) / 16 * 16;
     const size_t lm_lds = sizeof(double) * 2 * mp * (s.d + 1);
@@ -744,6 +744,7 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
     if ((err = launch_ring_logits(s, io.map, stream)) != hipSuccess) return err;
     if (s.d == 128 && s.dv == 128) return launch_far_m<128, 128>(s, io, stream);
     if (s.d == 96 && s.dv == 96) return launch_far_m<96, 96>(s, io, stream);
+    if (s.d == 256 && s.dv == 256) return launch_far<256, 256, 32>(s, io, stream);
     if (s.d == 64 && s.dv == 64) return launch_far_m<64, 64>(s, io, stream);
     return hipErrorInvalidValue;
 }
@@ -756,7 +757,8 @@ hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_
     // unless that leaves fewer than 2048 work-groups or stages more than 64
     // landmark rows in LDS
     int hb = s.hpk;
-    while (hb > 1 && ((long)map.count * (s.hpk / hb) < 2048 || hb * s.m > 64)) hb /= 2;
+    const int max_rows = s.d > 128 ? 32 : 64;  // landmark rows staged per work-group (33.8 KB)
+    while (hb > 1 && ((long)map.count * (s.hpk / hb) < 2048 || hb * s.m > max_rows)) hb /= 2;
     if (s.hpk % hb) hb = 1;
     const dim3 grid(map.count, s.hpk / hb);
     const size_t lds = sizeof(float4) * (size_t)hb * s.m * (s.d / 4 + 1);
@@ -766,6 +768,8 @@ hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_
         hipLaunchKernelGGL(ring_logits_kernel<96>, grid, dim3(256), lds, stream, s, map, hb);
     else if (s.d == 128)
         hipLaunchKernelGGL(ring_logits_kernel<128>, grid, dim3(256), lds, stream, s, map, hb);
+    else if (s.d == 256)
+        hipLaunchKernelGGL(ring_logits_kernel<256>, grid, dim3(256), lds, stream, s, map, hb);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

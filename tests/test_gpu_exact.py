@@ -34,6 +34,9 @@ def gpu_ready():
     (3, 2, 96, 1000, 1000, 0, 2.0),       # d = 96: value rows of 24 float4, split key range
     (2048, 8, 96, 150, 150, 5, 1.0),      # d = 96, 8 heads, many groups
     (5, 3, 96, 300, 211, 7, 1.0),         # d = 96, 3 heads (run as 4), ragged tail
+    (3, 2, 256, 700, 700, 0, 1.0),        # d = 256: a value row per wave, split key range
+    (2048, 2, 256, 100, 100, 0, 1.0),     # d = 256, many groups
+    (4, 8, 256, 300, 257, 3, 1.0),        # d = 256, 8 heads
 ])
 def test_exact_attend_matches_oracle(G, H, d, cap, n, first, std):
     say(f"[exact] G={G} hpk={H} d={d} cap={cap} n_keys={n} first={first}")

@@ -1,7 +1,7 @@
 """GPU parity at seeded random shapes: each case draws the query heads per group,
 the head width, the landmark budget, window, sinks, prompt length, rectifier,
-input scale and group counts within the compiled limits (d = dv in {64, 96, 128},
-hpk <= 8, m <= 64, sink + w <= 1024 with hpk' * (sink + w) * 8 <= 32 KB for hpk'
+input scale and group counts within the compiled limits (d = dv in {64, 96, 128, 256},
+hpk <= 8, m <= 64 (32 at d = 256), sink + w <= 1024 with hpk' * (sink + w) * 8 <= 32 KB for hpk'
 the head count rounded up to a power of two),
 then checks the prefill freeze and the decode steps against the oracle exactly
 as the fixed-shape tests do."""
@@ -26,14 +26,14 @@ def gpu_ready():
     yield
 
 
-def draw(case: int, widths=(64, 128), base=7000):
+def draw(case: int, widths=(64, 128), base=7000, max_m=64):
     r = np.random.default_rng(base + case)
     while True:
         # the first ten cases draw power-of-two head counts, the rest any count
         hpk = int(r.choice([1, 2, 4, 8])) if case < 10 else int(r.integers(1, 9))
         hc = 1 << (hpk - 1).bit_length()  # the compiled head count that runs it
         d = int(r.choice(list(widths)))
-        m = int(r.integers(4, 65))
+        m = int(r.integers(4, max_m + 1))
         sink = int(r.integers(0, 17))
         w = int(r.integers(1, 300))
         if hc * (sink + w) * 8 > 32 * 1024 or sink + w > 1024:
@@ -52,6 +52,8 @@ CASES = [draw(i) for i in range(16)]
 # d = 96 (value rows of 24 float4) drawn from their own seeds, so the cases
 # above keep theirs
 CASES += [draw(i, widths=(96,), base=7100) for i in range(6)]
+# d = 256 (a value row per wave; m <= 32)
+CASES += [draw(i, widths=(256,), base=7200, max_m=32) for i in range(4)]
 
 
 @pytest.mark.parametrize("wl,rect", CASES,
