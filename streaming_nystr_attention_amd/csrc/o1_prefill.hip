@@ -444,9 +444,10 @@ __device__ __forceinline__ float sum_over_lk(float x)
 // busy only with other waves to switch to.  Work-groups of four waves run at
 // three waves per SIMD (three work-groups per CU), those of eight at four (two
 // per CU; a few address registers spill), with the logits summed in two
-// accumulator chains to fit.  Rows of 256 floats run at two per SIMD.
+// accumulator chains to fit; two-wave work-groups (one head of m <= 32) and
+// rows of 256 floats, whose tiles need more registers, at two per SIMD.
 template <int D, int DV, int MM, int HB>
-__global__ __launch_bounds__(64 * HB * (MM / 16), (D > 128 ? 2 : (HB * (MM / 16) <= 4 ? 3 : 4))) void far_mfma_kernel(DevState s, PrefillIO io)
+__global__ __launch_bounds__(64 * HB * (MM / 16), (D > 128 || HB * (MM / 16) == 2 ? 2 : (HB * (MM / 16) == 4 ? 3 : 4))) void far_mfma_kernel(DevState s, PrefillIO io)
 {
     constexpr int NRB = MM / 16, NW = HB * NRB, NT = 64 * NW;
     constexpr int KS = D / 4;    // k-steps of the logit product = components per lane
