@@ -89,9 +89,11 @@ struct DecodeShape {
     // stream over every row it reads, two batches per round trip, with the
     // queries in f64 registers.
     static constexpr bool STREAM_ROWS = NT == 512 && HPK * D >= 512 && (CH & (CH - 1)) == 0 && HPK * CPL <= 8;
-    // eight heads: the streamed row pass takes its dots on f64 MFMA (rows x
-    // [queries, evicted key]) instead of per-lane dots and head reductions
-    static constexpr bool MFMA_ROWS = STREAM_ROWS && HPK == 8 && D % 16 == 0;
+    // eight heads: the row pass takes its dots on f64 MFMA (rows x [queries,
+    // evicted key]) instead of per-lane dots and head reductions, in the
+    // streamed form's launches and in 256-thread ones (rows of at most 128
+    // floats: a tile's operands stay in registers)
+    static constexpr bool MFMA_ROWS = HPK == 8 && D % 16 == 0 && D <= 128 && (STREAM_ROWS || NT == 256);
     static constexpr int HL = (HPK * kPend * MM + NT - 1) / NT;       // held logits per thread
     // at least three waves per SIMD on large grids (at most 168 VGPRs)
     static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
@@ -555,8 +557,8 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             }
         }
 
-        // on a fold with ring logits, shapes with the streamed row pass (many
-        // heads): the far-insert logits of the kPend latest keys against every
+        // on a fold with ring logits, shapes with the streamed or MFMA row pass
+        // (many heads): the far-insert logits of the kPend latest keys against every
         // query landmark, a [hpk m x D] x [D x kPend] product on f64 MFMA in
         // 16-row tiles (the other shapes take them in the row pass, whose rows
         // span few lanes).  A = q~ rows, read through the cache; B = the keys,
@@ -564,7 +566,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         // four k-lanes of a row read 64 contiguous bytes per load: in MFMA step
         // (jj, c), k-lane kk stands for component 16 jj + 4 kk + c of A and B.
         // (D[i][j] in lane j + 16 (i mod 4), element i / 4)
-        if (C::STREAM_ROWS && ring && fold) {
+        if ((C::STREAM_ROWS || C::MFMA_ROWS) && ring && fold) {
             const int NQ = H * m;
             const int li = lane & 15, lk = lane >> 4;
             const float4 *qt4 = reinterpret_cast<const float4 *>(s.q_tilde) + gh0 * m * C::CH + lk;
