@@ -79,6 +79,8 @@ struct DecodeShape {
     static constexpr int TPT = (MM + RL - 1) / RL;                     // T^ rows per lane per head
     static constexpr bool STAGE_M = HPK * MM * MM <= 2048;             // M staged in LDS
     static constexpr bool PRE_T = HPK * TPT <= (NT == 256 ? 8 : (DV > 128 ? 16 : 32));  // T^ prefetched in registers
+    // otherwise heads per block of T^ loads in flight (at most 8 rows per lane)
+    static constexpr int TB = TPT >= 8 ? 1 : (8 / TPT < HPK ? 8 / TPT : HPK);
     // V rows prefetched per lane (6 where 8 would spill at 256 VGPRs; 9 at 512
     // threads covers a 128-key window plus 4 sinks, so no V batch follows)
     static constexpr int VPRE = NT == 256 ? (HPK <= 2 ? 8 : 4) : (HPK * MM >= 512 ? 6 : 9);
@@ -726,60 +728,115 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         if (fold) {
             // t_hat <- r t_hat + sum_j w_j v_j over the held rows and this
             // eviction's, written back once for kPend steps
-#pragma unroll
-            for (int h = 0; h < HPK; ++h) {
-#pragma unroll
-                for (int j = 0; j < C::TPT; ++j) {
-                    const int b = rl + j * C::RL;
-                    if (b >= m) break;
-                    const size_t idx = ((size_t)min(h, H - 1) * m + b) * C::VCH + cc;
-                    float4 t;
-                    if constexpr (C::PRE_T) t = tpre[h][j];
-                    else t = ld4<C::NTL>(th + idx);
-                    const double rb = r_s[h][b], gb = gain_s[h][b];
-                    double t0 = (double)t.x * rb, t1 = (double)t.y * rb;
-                    double t2 = (double)t.z * rb, t3 = (double)t.w * rb;
-                    // held row k + 1 loaded while row k is added in
-                    double wk = wf_s[h][0][b];
-                    float4 x = hv_s[0][cc];
+            auto fold_row = [&](int h, int b, float4 t) {
+                const size_t idx = ((size_t)min(h, H - 1) * m + b) * C::VCH + cc;
+                const double rb = r_s[h][b], gb = gain_s[h][b];
+                double t0 = (double)t.x * rb, t1 = (double)t.y * rb;
+                double t2 = (double)t.z * rb, t3 = (double)t.w * rb;
+                // held row k + 1 loaded while row k is added in
+                double wk = wf_s[h][0][b];
+                float4 x = hv_s[0][cc];
 #pragma unroll 1
-                    for (int k = 1; k < kPend; ++k) {
-                        const double wn = wf_s[h][k][b];
-                        const float4 xn = k < kPend - 1 ? hv_s[k][cc] : ve_s[cc];
-                        t0 = fma(wk, (double)x.x, t0);
-                        t1 = fma(wk, (double)x.y, t1);
-                        t2 = fma(wk, (double)x.z, t2);
-                        t3 = fma(wk, (double)x.w, t3);
-                        wk = wn;
-                        x = xn;
-                    }
+                for (int k = 1; k < kPend; ++k) {
+                    const double wn = wf_s[h][k][b];
+                    const float4 xn = k < kPend - 1 ? hv_s[k][cc] : ve_s[cc];
                     t0 = fma(wk, (double)x.x, t0);
                     t1 = fma(wk, (double)x.y, t1);
                     t2 = fma(wk, (double)x.z, t2);
                     t3 = fma(wk, (double)x.w, t3);
-                    if (h < H && cp < C::VCH)
-                        st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
-                    acc[h][0] = fma(gb, t0, acc[h][0]);
-                    acc[h][1] = fma(gb, t1, acc[h][1]);
-                    acc[h][2] = fma(gb, t2, acc[h][2]);
-                    acc[h][3] = fma(gb, t3, acc[h][3]);
+                    wk = wn;
+                    x = xn;
+                }
+                t0 = fma(wk, (double)x.x, t0);
+                t1 = fma(wk, (double)x.y, t1);
+                t2 = fma(wk, (double)x.z, t2);
+                t3 = fma(wk, (double)x.w, t3);
+                if (h < H && cp < C::VCH)
+                    st4<C::NTL>(th + idx, make_float4((float)t0, (float)t1, (float)t2, (float)t3));
+                acc[h][0] = fma(gb, t0, acc[h][0]);
+                acc[h][1] = fma(gb, t1, acc[h][1]);
+                acc[h][2] = fma(gb, t2, acc[h][2]);
+                acc[h][3] = fma(gb, t3, acc[h][3]);
+            };
+            if constexpr (C::PRE_T) {
+#pragma unroll
+                for (int h = 0; h < HPK; ++h) {
+#pragma unroll
+                    for (int j = 0; j < C::TPT; ++j) {
+                        const int b = rl + j * C::RL;
+                        if (b >= m) break;
+                        fold_row(h, b, tpre[h][j]);
+                    }
+                }
+            } else {
+                // T^ rows in blocks of TB heads, each block's loads issued
+                // before its rows are folded (rows past m load row m - 1 and
+                // are skipped)
+#pragma unroll
+                for (int h0 = 0; h0 < HPK; h0 += C::TB) {
+                    float4 t[C::TB][C::TPT];
+#pragma unroll
+                    for (int hh = 0; hh < C::TB; ++hh)
+#pragma unroll
+                        for (int j = 0; j < C::TPT; ++j)
+                            t[hh][j] = ld4<C::NTL>(th + ((size_t)min(h0 + hh, H - 1) * m + min(rl + j * C::RL, m - 1)) * C::VCH + cc);
+#pragma unroll
+                    for (int hh = 0; hh < C::TB; ++hh) {
+                        const int h = h0 + hh;
+#pragma unroll
+                        for (int j = 0; j < C::TPT; ++j) {
+                            const int b = rl + j * C::RL;
+                            if (b < m) fold_row(h, b, t[hh][j]);
+                        }
+                        // as in the step without a fold: one block's rows live at a time
+                        asm volatile("" : "+v"(acc[h][0]), "+v"(acc[h][1]), "+v"(acc[h][2]), "+v"(acc[h][3])::"memory");
+                    }
                 }
             }
         } else {
+            if constexpr (C::PRE_T) {
 #pragma unroll
-            for (int h = 0; h < HPK; ++h) {
+                for (int h = 0; h < HPK; ++h) {
 #pragma unroll
-                for (int j = 0; j < C::TPT; ++j) {
-                    const int b = rl + j * C::RL;
-                    if (b >= m) break;
-                    float4 t;
-                    if constexpr (C::PRE_T) t = tpre[h][j];
-                    else t = ld4<C::NTL>(th + ((size_t)min(h, H - 1) * m + b) * C::VCH + cc);
-                    const double gb = gain_s[h][b];
-                    acc[h][0] = fma(gb, (double)t.x, acc[h][0]);
-                    acc[h][1] = fma(gb, (double)t.y, acc[h][1]);
-                    acc[h][2] = fma(gb, (double)t.z, acc[h][2]);
-                    acc[h][3] = fma(gb, (double)t.w, acc[h][3]);
+                    for (int j = 0; j < C::TPT; ++j) {
+                        const int b = rl + j * C::RL;
+                        if (b >= m) break;
+                        const float4 t = tpre[h][j];
+                        const double gb = gain_s[h][b];
+                        acc[h][0] = fma(gb, (double)t.x, acc[h][0]);
+                        acc[h][1] = fma(gb, (double)t.y, acc[h][1]);
+                        acc[h][2] = fma(gb, (double)t.z, acc[h][2]);
+                        acc[h][3] = fma(gb, (double)t.w, acc[h][3]);
+                    }
+                }
+            } else {
+                // T^ rows in blocks of TB heads, every load of a block issued
+                // before its rows are added in (rows past m load row m - 1 and
+                // weigh 0), so a block costs one round trip
+#pragma unroll
+                for (int h0 = 0; h0 < HPK; h0 += C::TB) {
+                    float4 t[C::TB][C::TPT];
+#pragma unroll
+                    for (int hh = 0; hh < C::TB; ++hh)
+#pragma unroll
+                        for (int j = 0; j < C::TPT; ++j)
+                            t[hh][j] = ld4<C::NTL>(th + ((size_t)min(h0 + hh, H - 1) * m + min(rl + j * C::RL, m - 1)) * C::VCH + cc);
+#pragma unroll
+                    for (int hh = 0; hh < C::TB; ++hh) {
+                        const int h = h0 + hh;
+#pragma unroll
+                        for (int j = 0; j < C::TPT; ++j) {
+                            const int b = rl + j * C::RL;
+                            const double gb = b < m ? gain_s[h][b] : 0.0;
+                            acc[h][0] = fma(gb, (double)t[hh][j].x, acc[h][0]);
+                            acc[h][1] = fma(gb, (double)t[hh][j].y, acc[h][1]);
+                            acc[h][2] = fma(gb, (double)t[hh][j].z, acc[h][2]);
+                            acc[h][3] = fma(gb, (double)t[hh][j].w, acc[h][3]);
+                        }
+                        // the block's sums are complete here and the next block's
+                        // loads stay behind them: one block's rows live at a time
+                        asm volatile("" : "+v"(acc[h][0]), "+v"(acc[h][1]), "+v"(acc[h][2]), "+v"(acc[h][3])::"memory");
+                    }
                 }
             }
             // row lane j < P: held slot j; row lane P: this eviction
