@@ -205,6 +205,14 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
                 const int r = c0 + min(r0 + j * C::RL, nr - 1);
                 x[j] = ld4<true>(((r == new_row) ? vn : vc + (size_t)r * C::VCH) + cc);
             }
+            // many heads or wide rows: the rows are taken as loaded here, as
+            // the compiler otherwise sinks each load past the exit test below
+            // to its use and waits for it alone (with fewer heads it keeps
+            // them in flight and adds each in as it arrives)
+            if constexpr (HPK >= 4 || DV > 128) {
+#pragma unroll
+                for (int j = 0; j < VU; ++j) asm volatile("" : "+v"(x[j].x), "+v"(x[j].y), "+v"(x[j].z), "+v"(x[j].w));
+            }
 #pragma unroll
             for (int j = 0; j < VU; ++j) {
                 const int r = r0 + j * C::RL;
