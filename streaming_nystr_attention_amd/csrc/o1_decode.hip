@@ -130,6 +130,9 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     // LDS slots hold values nothing stores.  Without it H is the compile-time
     // HPK (full groups keep every index a constant).
     const int H = PART ? s.hpk : HPK;
+    // 256-thread launches skip the placeholder heads' column sums and
+    // reductions (uniform branches on H); 512-thread ones would spill for it
+    constexpr bool SKIP_PH = PART && NT == 256;
     const double scale = (double)s.scale;
     const double NEG_INF = -__builtin_inf();
 
@@ -774,6 +777,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 // are skipped)
 #pragma unroll
                 for (int h0 = 0; h0 < HPK; h0 += C::TB) {
+                    if (SKIP_PH && h0 >= H) break;
                     float4 t[C::TB][C::TPT];
 #pragma unroll
                     for (int hh = 0; hh < C::TB; ++hh)
@@ -783,6 +787,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
 #pragma unroll
                     for (int hh = 0; hh < C::TB; ++hh) {
                         const int h = h0 + hh;
+                        if (SKIP_PH && h >= H) break;
 #pragma unroll
                         for (int j = 0; j < C::TPT; ++j) {
                             const int b = rl + j * C::RL;
@@ -815,6 +820,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 // weigh 0), so a block costs one round trip
 #pragma unroll
                 for (int h0 = 0; h0 < HPK; h0 += C::TB) {
+                    if (SKIP_PH && h0 >= H) break;  // placeholder heads only
                     float4 t[C::TB][C::TPT];
 #pragma unroll
                     for (int hh = 0; hh < C::TB; ++hh)
@@ -824,6 +830,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
 #pragma unroll
                     for (int hh = 0; hh < C::TB; ++hh) {
                         const int h = h0 + hh;
+                        if (SKIP_PH && h >= H) break;
 #pragma unroll
                         for (int j = 0; j < C::TPT; ++j) {
                             const int b = rl + j * C::RL;
@@ -844,6 +851,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 const float4 x = rl < P ? hv_s[rl][cc] : ve_s[cc];
 #pragma unroll
                 for (int h = 0; h < HPK; ++h) {
+                    if (SKIP_PH && h >= H) break;
                     const double cj = cj_s[h][rl];
                     acc[h][0] = fma(cj, (double)x.x, acc[h][0]);
                     acc[h][1] = fma(cj, (double)x.y, acc[h][1]);
@@ -862,6 +870,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             const float4 x = (r == slot_row) ? vn_s[cc] : vpre[j];
 #pragma unroll
             for (int h = 0; h < HPK; ++h) {
+                if (SKIP_PH && h >= H) break;  // placeholder heads: nothing to add
                 const double p = lg_s[h * R + r];
                 acc[h][0] = fma(p, (double)x.x, acc[h][0]);
                 acc[h][1] = fma(p, (double)x.y, acc[h][1]);
@@ -880,6 +889,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 if (r == slot_row) x[j] = vn_s[cc];
 #pragma unroll
                 for (int h = 0; h < HPK; ++h) {
+                    if (SKIP_PH && h >= H) break;
                     const double p = lg_s[h * R + r];
                     acc[h][0] = fma(p, (double)x[j].x, acc[h][0]);
                     acc[h][1] = fma(p, (double)x[j].y, acc[h][1]);
@@ -894,12 +904,15 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     if (fold) __syncthreads();  // every wave is done with the fold weights
     // within a wave: the RLW row lanes sit VCP lanes apart
 #pragma unroll
-    for (int h = 0; h < HPK; ++h)
+    for (int h = 0; h < HPK; ++h) {
+        if (SKIP_PH && h >= H) break;
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCP>(acc[h][c]);
+    }
     float4 *outp = reinterpret_cast<float4 *>(io.out) + (size_t)ci * H * C::VCH;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
+        if (SKIP_PH && h0 >= H) break;  // uniform: every thread leaves together
         if (lane < C::VCH) {
 #pragma unroll
             for (int hh = 0; hh < C::RED_H; ++hh) {
