@@ -53,6 +53,7 @@
 // A launch covers the groups of a GroupMap: the whole handle, or one layer of
 // every sequence; inputs and outputs are indexed by the launch's own index.
 #include <atomic>
+#include <type_traits>
 
 #include "o1_internal.h"
 
@@ -97,6 +98,8 @@ struct DecodeShape {
     // floats: a tile's operands stay in registers)
     static constexpr bool MFMA_ROWS = HPK == 8 && D % 16 == 0 && D <= 128 && (STREAM_ROWS || NT == 256);
     static constexpr int HL = (HPK * kPend * MM + NT - 1) / NT;       // held logits per thread
+    // per-head phase: two heads per wave, one per half-wave (m <= 32)
+    static constexpr bool PAIR_HEADS = NT == 256 && HPK == 2 * NW && MM == 32;
     // at least three waves per SIMD on large grids (at most 168 VGPRs)
     static constexpr int MIN_WAVES = NT == 256 ? 3 : 2;
     // heads per LDS round of the final reduction (one work-group per CU: room for all)
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     __shared__ double r_s[HPK][MM];                // fold: stored t_hat -> new max, per landmark
     __shared__ double cj_s[HPK][kPend];            // held slot j (and this eviction, slot P): sum_i gain_i w_ij
     __shared__ double gain_s[HPK][MM];             // far mixing gains (0 when dropped), times r between folds
-    __shared__ double fh_s[C::STAGE_M ? HPK : 1][MM];  // landmark weights e^{s - f} (0 past m)
+    __shared__ double fh_s[C::STAGE_M || C::PAIR_HEADS ? HPK : 1][MM];  // landmark weights e^{s - f} (0 past m)
     __shared__ double den_s[HPK];
     // held logits, then their weights at the new max, [HPK][kPend][MM] (steps 0-3);
     // then the reduction across waves, [NW][RED_H * DV] (step 4)
@@ -620,26 +623,37 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     }
     __syncthreads();
 
-    // ---- 2. per-head landmark work and near weights (one wave per head) ----
-    for (int h = wave; h < H; h += C::NW) {
-        const bool act = lane < m;
-        const size_t hi = (gh0 + h) * m + lane;
+    // ---- 2. per-head landmark work and near weights ------------------------
+    // One head per wave (W = 64 lanes), or, in 256-thread launches of eight
+    // heads with m <= 32, one head per half-wave (W = 32: heads 2 wave and
+    // 2 wave + 1 side by side, so each instruction serves two heads).  Lane la
+    // of the head's W owns landmark la; reductions run over the W lanes.
+    auto per_head = [&](auto width, int h, int la, bool live) {
+        constexpr int W = decltype(width)::value;
+        auto wmax = [](double x) {
+            if constexpr (W == 64) return wave_max(x);
+            else return group_max<16>(swap_max<16>(x));
+        };
+        auto wsum = [](double x) { return group_sum<W>(x); };
+        const bool act = la < m;
+        const bool stores = act && live;  // placeholder halves compute, but store nothing
+        const size_t hi = (gh0 + h) * m + la;
         double c = NEG_INF;
-        for (int r = lane; r < R; r += 64) c = fmax(c, lg_s[h * R + r]);
-        c = wave_max(c);
+        for (int r = la; r < R; r += W) c = fmax(c, lg_s[h * R + r]);
+        c = wmax(c);
 
-        const double sa = act ? land_s[h][lane] : NEG_INF;
-        const double f = wave_max(sa);
+        const double sa = act ? land_s[h][la] : NEG_INF;
+        const double f = wmax(sa);
         const double fh = act ? exp(sa - f) : 0.0;
 
-        // NystromHead::far_insert for landmark i = lane: strict ">" growth of
+        // NystromHead::far_insert for landmark i = la: strict ">" growth of
         // the running max; Z^ stays at scale e^{-m_max} with m_max kept as the
         // f32 value actually stored.  T^ gets the same update through the held
         // set: this eviction's weight is ee at the new max.
         double mn = NEG_INF, zn = 0.0;
         if (act) {
-            const double lnew = lf_s[h][lane];
-            const float mo = mo_s[h][lane];
+            const double lnew = lf_s[h][la];
+            const float mo = mo_s[h][la];
             float mnf = mo;
             double r = 1.0;
             if (lnew > (double)mo) {
@@ -648,77 +662,93 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             }
             mn = (double)mnf;
             const double ee = exp(lnew - mn);
-            zn = zo_s[h][lane] * r + ee;
-            s.m_max[hi] = mnf;
-            s.z_hat[hi] = zn;
-            // T^_i = rf_i t_hat_i + sum_{j<P} w_ij v_j + ee_i v_e at the new max:
-            // the held weights move from the old max to the new one, and this
-            // eviction's weight takes slot P (on a fold, slot kPend - 1)
-            r_s[h][lane] = exp((double)mr_s[h][lane] - mn);
-            for (int j = 0; j < P; ++j) wf_s[h][j][lane] *= r;
-            wf_s[h][fold ? kPend - 1 : P][lane] = ee;
-            if (fold) s.m_ref[hi] = mnf;
-            else s.pend_l[(gh0 + h) * kPend * (size_t)m + (size_t)P * m + lane] = lnew;
+            zn = zo_s[h][la] * r + ee;
+            if (live) {
+                s.m_max[hi] = mnf;
+                s.z_hat[hi] = zn;
+                // T^_i = rf_i t_hat_i + sum_{j<P} w_ij v_j + ee_i v_e at the new
+                // max: the held weights move from the old max to the new one,
+                // and this eviction's weight takes slot P (on a fold, slot
+                // kPend - 1)
+                r_s[h][la] = exp((double)mr_s[h][la] - mn);
+                for (int j = 0; j < P; ++j) wf_s[h][j][la] *= r;
+                wf_s[h][fold ? kPend - 1 : P][la] = ee;
+                if (fold) s.m_ref[hi] = mnf;
+                else s.pend_l[(gh0 + h) * kPend * (size_t)m + (size_t)P * m + la] = lnew;
+            }
         }
 
-        // u_b = sum_a fh_a M[a][b]  (lane = b)
+        // u_b = sum_a fh_a M[a][b]  (la = b)
         double u = 0.0;
         if constexpr (C::STAGE_M) {
             // fh goes through LDS (zero past m): the loop runs over the
             // compile-time bound MM with broadcast reads and clamped rows of
             // the staged M, without branches or cross-lane shuffles.
-            if (lane < MM) fh_s[h][lane] = fh;
+            if (la < MM) fh_s[h][la] = fh;
             __builtin_amdgcn_wave_barrier();
             const float *mu = mu_s + (size_t)h * m * m;
-            const int col = act ? lane : 0;
+            const int col = act ? la : 0;
 #pragma unroll 8
             for (int a = 0; a < MM; ++a) u = fma(fh_s[h][a], (double)mu[min(a, m - 1) * m + col], u);
             if (!act) u = 0.0;
         } else {
-            // M from global memory, MB rows per lane in flight
-            const float *mu = s.mu + (gh0 + h) * (size_t)m * m;
-            const int col = act ? lane : 0;
+            // M from global memory, MB rows per lane in flight; fh_a from
+            // lane a (one head per wave) or through LDS (two per wave)
+            const float *mu = s.mu + (gh0 + (W == 32 ? min(h, H - 1) : h)) * (size_t)m * m;
+            const int col = act ? la : 0;
+            if constexpr (W == 32) {
+                fh_s[h][la] = fh;
+                __builtin_amdgcn_wave_barrier();
+            }
             for (int a0 = 0; a0 < m; a0 += C::MB) {
                 float mv[C::MB];
 #pragma unroll
                 for (int j = 0; j < C::MB; ++j) mv[j] = mu[(size_t)min(a0 + j, m - 1) * m + col];
 #pragma unroll
                 for (int j = 0; j < C::MB; ++j) {
-                    const double fa = lane_value(fh, (a0 + j) & 63);
+                    double fa;
+                    if constexpr (W == 64) fa = lane_value(fh, (a0 + j) & 63);
+                    else fa = fh_s[h][(a0 + j) & 31];
                     if (a0 + j < m && act) u = fma(fa, (double)mv[j], u);
                 }
             }
         }
         if (s.rect == 1) u = fmax(u, 0.0);  // O1Rect::Fm
 
-        const double call = fmax(c, wave_max(act ? f + mn : NEG_INF));
+        const double call = fmax(c, wmax(act ? f + mn : NEG_INF));
         const double gain = act ? u * exp(f + mn - call) : 0.0;
-        const double far_den = wave_sum(gain * zn);
+        const double far_den = wsum(gain * zn);
         const bool keep = far_den >= 0.0;  // aggregate rectifier (0 keeps)
         const double gk = keep ? gain : 0.0;
         const double shift = keep ? call : c;  // dropped far field: near-only shift
 
         if (fold) {
             // the column pass rebuilds t_hat at the new max
-            if (act) gain_s[h][lane] = gk;
+            if (stores) gain_s[h][la] = gk;
         } else {
             // t_hat stays as stored: its gains carry rf, and each held row and
             // this eviction's row (slot P) gets one coefficient sum_i gain_i w_ij
-            if (act) gain_s[h][lane] = gk * r_s[h][lane];
+            if (stores) gain_s[h][la] = gk * r_s[h][la];
             for (int j = 0; j <= P; ++j) {
-                const double cj = wave_sum(act ? gk * wf_s[h][j][lane] : 0.0);
-                if (lane == 0) cj_s[h][j] = cj;
+                const double cj = wsum(act ? gk * wf_s[h][j][la] : 0.0);
+                if (la == 0 && live) cj_s[h][j] = cj;
             }
         }
 
         double acc = 0.0;
-        for (int r = lane; r < R; r += 64) {
+        for (int r = la; r < R; r += W) {
             const double p = exp(lg_s[h * R + r] - shift);
-            lg_s[h * R + r] = p;
+            if (live) lg_s[h * R + r] = p;
             acc += p;
         }
-        acc = wave_sum(acc);
-        if (lane == 0) den_s[h] = (keep ? far_den : 0.0) + acc;
+        acc = wsum(acc);
+        if (la == 0 && live) den_s[h] = (keep ? far_den : 0.0) + acc;
+    };
+    if constexpr (C::PAIR_HEADS) {
+        const int h = 2 * wave + (lane >> 5);
+        if (2 * wave < H) per_head(std::integral_constant<int, 32>{}, h, lane & 31, h < H);
+    } else {
+        for (int h = wave; h < H; h += C::NW) per_head(std::integral_constant<int, 64>{}, h, lane, true);
     }
     __syncthreads();
 

@@ -55,3 +55,16 @@ def test_head_count_3_large_grid_sampled():
     sample = W.groups_of_sequences(wl, W.sample_sequences(wl))
     prefill_parity(wl, sample=sample)
     decode_parity(wl, sample=sample)
+
+
+@pytest.mark.parametrize("hpk,seed", [(5, 68), (7, 69)], ids=["h5", "h7"])
+def test_head_count_large_grid_eight_head_kernel(hpk, seed):
+    """1024 groups of 5 or 7 heads at d = 128: 256-thread work-groups of the
+    8-head kernel, whose per-head phase runs two heads per wave, one per
+    half-wave.  With 7 heads the last wave's second half is a placeholder; with
+    5 one wave holds a head and a placeholder and another only placeholders.  A
+    declared sample of sequences is compared."""
+    wl = _wl(f"h{hpk}_grid1024", 64, 16, hpk, 128, 32, 64, 4, 300, 20, 2.0, seed)
+    sample = W.groups_of_sequences(wl, W.sample_sequences(wl))
+    prefill_parity(wl, sample=sample)
+    decode_parity(wl, sample=sample)
