@@ -34,7 +34,7 @@ struct ExactShape {
     // SIMDs; more heads need the registers of a 256-thread work-group
     static constexpr int NT = HPK <= 2 ? 512 : 256;
     static constexpr int NW = NT / 64;
-    static constexpr int WAVES_PER_SIMD = HPK <= 2 ? 4 : 1;
+    static constexpr int WAVES_PER_SIMD = HPK <= 2 ? 4 : (HPK == 8 && D % 16 == 0 && D <= 128 ? 2 : 1);
     static constexpr int CH = D / 4;
     static constexpr int LPR_WANT = HPK <= 2 ? 8 : (HPK <= 4 ? 16 : 32);
     static constexpr int LPR = pow2_divisor(LPR_WANT, CH);
@@ -50,6 +50,9 @@ struct ExactShape {
     // V rows per lane loaded before the chunk's softmax (more would cost a wave
     // per SIMD at hpk >= 4)
     static constexpr int VPRE = HPK <= 2 && DV <= 128 ? 8 : 4;
+    // eight heads: the key dots on f64 MFMA (16-key tiles times the queries)
+    // instead of per-lane dots and 32-lane head reductions
+    static constexpr bool MFMA_ROWS = HPK == 8 && D % 16 == 0 && D <= 128;
     static_assert(HPK <= LPR && HPK % RED_H == 0, "unsupported head count");
 };
 
@@ -120,6 +123,51 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
     for (int c0 = k0; c0 < k1; c0 += kChunk) {
         const int nr = min(kChunk, k1 - c0);
         // row dots of this chunk's keys
+        if constexpr (C::MFMA_ROWS) {
+            // eight heads: 16-key tiles times B = [q_0 .. q_7, 0 ..] on f64
+            // MFMA.  Operand layout (wave64): A[i][k] in lane i + 16 k, B[k][j]
+            // in lane j + 16 k; f64 D[i][j] in lane j + 16 (i % 4), element
+            // i / 4.  In step (jj, c) k-lane kk stands for component
+            // 16 jj + 4 kk + c of A and B alike, so a lane's operands of one
+            // key are the D/16 float4 at 4 jj + kk.  Keys past the chunk load
+            // its last key and are discarded.
+            constexpr int NJ = D / 16;
+            using d4v = __attribute__((ext_vector_type(4))) double;
+            const int li = lane & 15, lk = lane >> 4;
+            // column li of B: head li's query (read from LDS at each step, so
+            // it holds no registers), zero past the heads
+            const float4 *bq = &q_s[min(li, HPK - 1)][lk];
+            const float bm = li < HPK ? 1.0f : 0.0f;
+            const int ntile = (nr + 15) / 16;
+            auto load = [&](float4 (&x)[NJ], int t) {
+                const int r = c0 + min(16 * t + li, nr - 1);
+                const float4 *row = (r == new_row) ? kn : kc + (size_t)r * C::CH;
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj) x[jj] = ld4<true>(row + 4 * jj + lk);
+            };
+            auto mma = [&](float4 (&x)[NJ], int t) {
+                d4v acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj) {
+                    const float4 b = bq[4 * jj];
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[jj].x, (double)(b.x * bm), acc, 0, 0, 0);
+                    acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[jj].y, (double)(b.y * bm), acc2, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[jj].z, (double)(b.z * bm), acc, 0, 0, 0);
+                    acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x[jj].w, (double)(b.w * bm), acc2, 0, 0, 0);
+                }
+                acc += acc2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * t + 4 * e + lk;  // D[4 e + lk][li]
+                    if (li < HPK && r < nr) lg_s[li][r] = acc[e] * scale;
+                }
+            };
+            for (int t = wave; t < ntile; t += kNW) {
+                float4 xa[NJ];
+                load(xa, t);
+                mma(xa, t);
+            }
+        } else
         for (int base = wave * C::RPW; base < nr; base += C::UNR * C::RPB) {
             float4 x[C::UNR][C::CPL];
 #pragma unroll
