@@ -132,7 +132,10 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     // placeholders: zero queries, no state read or written, no output; their
     // LDS slots hold values nothing stores.  Without it H is the compile-time
     // HPK (full groups keep every index a constant).
-    const int H = PART ? s.hpk : HPK;
+    const int H = PART ? io.hb : HPK;
+    // the group's own head count, the stride of every per-head array, and the
+    // first head of this launch's block
+    const int HG = s.hpk, h0 = io.h0;
     // 256-thread launches skip the placeholder heads' column sums and
     // reductions (uniform branches on H); 512-thread ones would spill for it
     constexpr bool SKIP_PH = PART && NT == 256;
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
     auto red_s = reinterpret_cast<double (*)[C::RED_H * DV]>(share_s);
     extern __shared__ double lg_s[];               // [HPK][R] near logits, then weights
 
-    const size_t gh0 = (size_t)g * H;  // first head of this group
+    const size_t gh0 = (size_t)g * HG + h0;  // first head of this block
     const int e = min(max(s.win_head[g], 0), s.w - 1);  // (in range unless written out of range)
     const int slot_row = S + e;
     // evictions held apart from t_hat before this step, and whether this
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             hlr[u] = 0.0;
             if (i < nl && (i / m) % kPend < P) hlr[u] = s.pend_l[gh0 * kPend * m + i];
         }
-        const float4 *qg = reinterpret_cast<const float4 *>(io.q) + (size_t)ci * H * C::CH;
+        const float4 *qg = reinterpret_cast<const float4 *>(io.q) + ((size_t)ci * HG + h0) * C::CH;
         // every load is issued before any is stored, so the prologue costs
         // one round trip (each thread has at most one element of each kind,
         // a few of M)
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             mo = s.m_max[gh0 * m + tid];
             mr = s.m_ref[gh0 * m + tid];
             zo = s.z_hat[gh0 * m + tid];
-            if (ring) lr = s.ring_l[((size_t)g * w + e) * H * m + tid];
+            if (ring) lr = s.ring_l[(((size_t)g * w + e) * HG + h0) * m + tid];
         }
         constexpr int MUP = C::STAGE_M ? (HPK * MM * MM + NT - 1) / NT : 1;
         float muv[MUP];
@@ -288,11 +291,16 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 wf_s[hj / kPend][hj % kPend][a] = exp(hlr[u] - (double)mo_s[hj / kPend][a]);
         }
     }
-    if (tid < C::CH) nk[(size_t)slot_row * C::CH + tid] = kn_s[tid];
-    if (tid >= 128 && tid < 128 + C::VCH) {
-        nv[(size_t)slot_row * C::VCH + tid - 128] = vn_s[tid - 128];
-        // the evicted value row joins the held set (slot P) unless this step folds
-        if (!fold) reinterpret_cast<float4 *>(s.pend_v)[((size_t)g * kPend + P) * C::VCH + tid - 128] = ve_s[tid - 128];
+    // the group's shared writes (the last head block's launch; every launch
+    // reads the ring slot's old row in its prologue and uses the new key and
+    // value from LDS for that slot)
+    if (io.shared) {
+        if (tid < C::CH) nk[(size_t)slot_row * C::CH + tid] = kn_s[tid];
+        if (tid >= 128 && tid < 128 + C::VCH) {
+            nv[(size_t)slot_row * C::VCH + tid - 128] = vn_s[tid - 128];
+            // the evicted value row joins the held set (slot P) unless this step folds
+            if (!fold) reinterpret_cast<float4 *>(s.pend_v)[((size_t)g * kPend + P) * C::VCH + tid - 128] = ve_s[tid - 128];
+        }
     }
 
     // ---- 1. row-dot pass ----------------------------------------------------
@@ -558,7 +566,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                             for (int k = 0; k < C::CPL; ++k) acc += dot4(x[u][k], kb_s[j][sub + C::LPR * k]);
                             acc = group_sum<C::LPR>(acc);
                             if (sub == 0 && r < NQ)
-                                s.ring_l[((size_t)g * w + (e - j + w) % w) * NQ + r] = acc * scale;
+                                s.ring_l[(((size_t)g * w + (e - j + w) % w) * HG + h0) * m + r] = acc * scale;
                         }
                     }
                 }
@@ -594,7 +602,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                     acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.w, (double)b.w, acc, 0, 0, 0);
                 }
                 if (li < kPend) {
-                    double *dst = s.ring_l + ((size_t)g * w + (e - li + w) % w) * NQ;
+                    double *dst = s.ring_l + (((size_t)g * w + (e - li + w) % w) * HG + h0) * m;
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const int r = 16 * t + 4 * r4 + lk;
@@ -939,7 +947,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[h][c] = sum_high_lanes<C::VCP>(acc[h][c]);
     }
-    float4 *outp = reinterpret_cast<float4 *>(io.out) + (size_t)ci * H * C::VCH;
+    float4 *outp = reinterpret_cast<float4 *>(io.out) + ((size_t)ci * HG + h0) * C::VCH;
 #pragma unroll
     for (int h0 = 0; h0 < HPK; h0 += C::RED_H) {
         if (SKIP_PH && h0 >= H) break;  // uniform: every thread leaves together
@@ -971,7 +979,7 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         }
         if (h0 + C::RED_H < HPK) __syncthreads();
     }
-    if (tid == 0) s.win_head[g] = (e + 1 == s.w) ? 0 : e + 1;
+    if (tid == 0 && io.shared) s.win_head[g] = (e + 1 == s.w) ? 0 : e + 1;
     if (tid < H) s.far_len[gh0 + tid] += 1;
 }
 
@@ -1033,9 +1041,9 @@ hipError_t launch_m(const DevState &s, const DecodeIO &io, hipStream_t stream)
 template <int D, int DV>
 hipError_t launch_hpk(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    // a group of hpk heads runs the kernel compiled for the next power of two;
-    // its variant for partial groups takes the head count at run time
-    switch (s.hpk) {
+    // a block of hb heads runs the kernel compiled for the next power of two;
+    // its variant for partial blocks takes the head count at run time
+    switch (io.hb) {
     case 1: return launch_m<D, DV, 1>(s, io, stream);
     case 2: return launch_m<D, DV, 2>(s, io, stream);
     case 3: return launch_m<D, DV, 4, true>(s, io, stream);
@@ -1105,22 +1113,34 @@ bool decode_supported(int d, int dv, int hpk, int m, int R)
     if (!(d == dv && (d == 64 || d == 96 || d == 128 || d == 256))) return false;
     // the prefill's landmark pass keeps K~ and one head's Q~ in f64 LDS
     if (d > 128 && m > 32) return false;
-    if (hpk < 1 || hpk > 8) return false;
+    if (hpk < 1 || hpk > 2 * kMaxBlockHeads) return false;
     if (m < 4 || m > kMaxLandmarks) return false;
     if (R < 1 || R > 1024) return false;
     // dynamic LDS for the near logits of the compiled head count (hpk rounded
     // up to a power of two) stays within 32 KB
-    const int hc = hpk <= 1 ? 1 : hpk <= 2 ? 2 : hpk <= 4 ? 4 : 8;
+    const int hb = hpk < kMaxBlockHeads ? hpk : kMaxBlockHeads;  // heads of the largest block
+    const int hc = hb <= 1 ? 1 : hb <= 2 ? 2 : hb <= 4 ? 4 : 8;
     return (size_t)hc * R * sizeof(double) <= (size_t)kMaxDynLds;
 }
 
-hipError_t launch_decode(const DevState &s, const DecodeIO &io, hipStream_t stream)
+hipError_t launch_decode(const DevState &s, const DecodeIO &io_in, hipStream_t stream)
 {
     if (!decode_supported(s.d, s.dv, s.hpk, s.m, s.R)) return hipErrorInvalidValue;
-    if (s.d == 64) return launch_hpk<64, 64>(s, io, stream);
-    if (s.d == 96) return launch_hpk<96, 96>(s, io, stream);
-    if (s.d == 256) return launch_hpk<256, 256>(s, io, stream);
-    return launch_hpk<128, 128>(s, io, stream);
+    // groups of more than kMaxBlockHeads heads: one launch per block of heads,
+    // in order on the stream; the last makes the group's shared writes
+    for (int h0 = 0; h0 < s.hpk; h0 += kMaxBlockHeads) {
+        DecodeIO io = io_in;
+        io.h0 = h0;
+        io.hb = min(kMaxBlockHeads, s.hpk - h0);
+        io.shared = h0 + kMaxBlockHeads >= s.hpk;
+        hipError_t err;
+        if (s.d == 64) err = launch_hpk<64, 64>(s, io, stream);
+        else if (s.d == 96) err = launch_hpk<96, 96>(s, io, stream);
+        else if (s.d == 256) err = launch_hpk<256, 256>(s, io, stream);
+        else err = launch_hpk<128, 128>(s, io, stream);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace o1

@@ -85,7 +85,7 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
     // query heads: HPK is the compiled count (a power of two), H the group's own
     // (HPK / 2 < H <= HPK); heads H .. HPK-1 take zero queries and write nothing
     const int H = a.hpk;
-    const size_t gh0 = (size_t)ci * H;
+    const size_t gh0 = (size_t)ci * a.hg + a.h0;  // first head of this block
     const float4 *qg = reinterpret_cast<const float4 *>(a.q) + gh0 * C::CH;
     for (int i = tid; i < HPK * C::CH; i += kNT)
         (&q_s[0][0])[i] = i < H * C::CH ? qg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -94,7 +94,7 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
     const int new_row = a.k_new ? n_keys - 1 : -1;  // absolute index of the appended key
     const float4 *kn = reinterpret_cast<const float4 *>(a.k_new) + (size_t)ci * C::CH;
     const float4 *vn = reinterpret_cast<const float4 *>(a.v_new) + (size_t)ci * C::VCH;
-    if (new_row >= k0 && new_row < k1) {
+    if (a.shared && new_row >= k0 && new_row < k1) {
         if (tid < C::CH) reinterpret_cast<float4 *>(a.k_dst)[((size_t)g * a.cap + new_row) * C::CH + tid] = kn[tid];
         if (tid >= 128 && tid < 128 + C::VCH)
             reinterpret_cast<float4 *>(a.v_dst)[((size_t)g * a.cap + new_row) * C::VCH + tid - 128] = vn[tid - 128];
@@ -336,7 +336,7 @@ __attribute__((amdgpu_waves_per_eu(ExactShape<D, DV, HPK>::WAVES_PER_SIMD))) voi
     }
     // exact-only decode with one work-group per group: it alone read the count
     // (at its start), so it advances it; split ranges leave that to the merge
-    if (a.held && final_out && tid == 0) a.held[g] = n_keys;
+    if (a.held && a.shared && final_out && tid == 0) a.held[g] = n_keys;
 }
 
 // One block of dv threads per call index: merge the key-range partials of
@@ -361,9 +361,9 @@ __global__ void exact_combine_kernel(ExactIO a, int splits)
             den += a.ws_sum[part] * w;
             num += a.ws_num[part * a.dv + c] * w;
         }
-        a.out[((size_t)ci * H + h) * a.dv + c] = (float)(num / den);
+        a.out[((size_t)ci * a.hg + a.h0 + h) * a.dv + c] = (float)(num / den);
     }
-    if (a.held) {
+    if (a.held && a.shared) {
         __syncthreads();  // every thread has read the count
         if (c == 0) a.held[g] = held + 1;
     }
@@ -444,13 +444,26 @@ int exact_splits(int G, int n_visible)
     return s < 1 ? 1 : s;
 }
 
-hipError_t launch_exact(const ExactIO &a, int splits, hipStream_t stream)
+hipError_t launch_exact(const ExactIO &in, int splits, hipStream_t stream)
 {
-    if (a.d == 64 && a.dv == 64) return launch_exact_hpk<64, 64>(a, splits, stream);
-    if (a.d == 96 && a.dv == 96) return launch_exact_hpk<96, 96>(a, splits, stream);
-    if (a.d == 128 && a.dv == 128) return launch_exact_hpk<128, 128>(a, splits, stream);
-    if (a.d == 256 && a.dv == 256) return launch_exact_hpk<256, 256>(a, splits, stream);
-    return hipErrorInvalidValue;
+    // groups of more than kMaxBlockHeads heads: one launch (and merge) per
+    // block of heads, in order; the last stores the appended key and advances
+    // the count, so every earlier block still reads the count it started from
+    for (int h0 = 0; h0 < in.hpk; h0 += kMaxBlockHeads) {
+        ExactIO a = in;
+        a.hg = in.hpk;
+        a.h0 = h0;
+        a.hpk = min(kMaxBlockHeads, in.hpk - h0);
+        a.shared = h0 + kMaxBlockHeads >= in.hpk;
+        hipError_t err;
+        if (a.d == 64 && a.dv == 64) err = launch_exact_hpk<64, 64>(a, splits, stream);
+        else if (a.d == 96 && a.dv == 96) err = launch_exact_hpk<96, 96>(a, splits, stream);
+        else if (a.d == 128 && a.dv == 128) err = launch_exact_hpk<128, 128>(a, splits, stream);
+        else if (a.d == 256 && a.dv == 256) err = launch_exact_hpk<256, 256>(a, splits, stream);
+        else err = hipErrorInvalidValue;
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace o1

@@ -109,10 +109,21 @@ struct PromptView {
     }
 };
 
+// Heads per decode launch: a group of more heads is stepped in blocks of this
+// many (the kernels are compiled for 1, 2, 4 and 8 heads).
+constexpr int kMaxBlockHeads = 8;
+
 struct DecodeIO {
     const float *q, *k, *v;  // q [count][hpk][d], k [count][d], v [count][dv]
     float *out;              // [count][hpk][dv]
     GroupMap map;
+    // Heads h0 .. h0 + hb - 1 of every group (a group of more than 8 heads is
+    // stepped in blocks of at most 8, one launch each, in order).  `shared`:
+    // this launch also makes the group's shared writes (the new row into the
+    // ring, the evicted value row into the held set, the ring position), which
+    // the last block's launch does after every other block has read the ring.
+    int h0 = 0, hb = 0;
+    int shared = 1;
 };
 
 struct PrefillIO {
@@ -132,6 +143,12 @@ struct ExactIO {
     float *out;              // [count][hpk][dv]
     GroupMap map;
     int hpk, d, dv, cap, first, n_keys, per_split;
+    // Set by launch_exact, which runs a group of more than kMaxBlockHeads heads
+    // in blocks: the kernels then see hpk = the block's heads, hg = the
+    // group's (the stride of q and out), h0 = the block's first head, and
+    // shared = 1 for the last block only, which alone stores the appended
+    // key and advances the key count.
+    int hg, h0, shared;
     float scale;
     double *ws_max, *ws_sum, *ws_num;  // split partials [count][splits][hpk](x dv)
     // Append mode (exact-only decode), else all null: key n_keys-1 is the new

@@ -92,10 +92,11 @@ def _create(P, L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(m=3), 1), (dict(w=0), 1), (dict(hpk=0), 1), (dict(sink=-1), 1), (dict(d=0), 1),
     (dict(dv=0), 1), (dict(n_seq=0), 1), (dict(n_layer=0), 1), (dict(n_kv=0), 1), (dict(rect=7), 1),
-    (dict(d=80, dv=80), 6), (dict(d=512, dv=512), 6), (dict(d=256, dv=256, m=33), 6), (dict(hpk=9), 6),
+    (dict(d=80, dv=80), 6), (dict(d=512, dv=512), 6), (dict(d=256, dv=256, m=33), 6), (dict(hpk=17), 6),
     (dict(m=65), 6),
     (dict(d=64, dv=128), 6), (dict(d=96, dv=64), 6),
     (dict(hpk=5, w=596, sink=4), 6),  # run as 8 heads: 8 * 600 near logits pass 32 KB
+    (dict(hpk=12, w=596, sink=4), 6),  # blocks of 8 and 4 heads: the 8-head block's logits pass 32 KB
     (dict(w=2000), 6), (dict(exact_cap=-1), 1), (dict(n_seq=1 << 20, exact_cap=1 << 22), 1),
     (dict(ridge_rel=-1e-6), 1), (dict(ridge_rel=float("inf")), 1), (dict(ridge_rel=float("nan")), 1),
 ])
@@ -137,7 +138,7 @@ def test_exact_comparator_validation_without_device():
     n = ctypes.c_size_t()
     good = dict(n_groups=4, hpk=2, d=128, dv=128, cap=100, first=0, n_keys=100, scale=0.0)
     for kw, code in [(dict(first=100), 1), (dict(n_keys=101), 1), (dict(first=-1), 1),
-                     (dict(n_groups=0), 1), (dict(hpk=9), 6), (dict(d=80, dv=80), 6),
+                     (dict(n_groups=0), 1), (dict(hpk=17), 6), (dict(d=80, dv=80), 6),
                      (dict(dv=64), 6)]:
         args = {**good, **kw}
         desc = P.o1_exact_desc(*[args[f] for f, _ in P.o1_exact_desc._fields_])

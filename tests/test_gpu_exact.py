@@ -37,6 +37,9 @@ def gpu_ready():
     (3, 2, 256, 700, 700, 0, 1.0),        # d = 256: a value row per wave, split key range
     (2048, 2, 256, 100, 100, 0, 1.0),     # d = 256, many groups
     (4, 8, 256, 300, 257, 3, 1.0),        # d = 256, 8 heads
+    (3, 12, 128, 1000, 1000, 0, 2.0),     # 12 heads: blocks of 8 and 4, split key range
+    (1500, 16, 64, 150, 150, 10, 1.0),    # 16 heads, many groups
+    (2, 9, 96, 300, 257, 3, 1.0),         # 9 heads: blocks of 8 and 1
 ])
 def test_exact_attend_matches_oracle(G, H, d, cap, n, first, std):
     say(f"[exact] G={G} hpk={H} d={d} cap={cap} n_keys={n} first={first}")

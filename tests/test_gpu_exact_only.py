@@ -48,6 +48,8 @@ CASES = [
     (_wl("x_d96_h8_split", 1, 1, 1, 8, 96, 32, 500, 4, T=510, steps=12, seed=49), 530),
     (_wl("x_d256_h2_T60", 2, 1, 2, 2, 256, 16, 64, 4, T=60, steps=20, seed=50), 80),
     (_wl("x_d256_h4_split", 1, 1, 1, 4, 256, 32, 500, 4, T=510, steps=12, seed=51), 530),
+    (_wl("x_d128_h12_T140", 2, 1, 2, 12, 128, 32, 128, 4, T=140, steps=24, seed=52), 200),
+    (_wl("x_d64_h16_split", 1, 1, 1, 16, 64, 8, 500, 2, T=505, steps=16, seed=53), 530),
 ]
 
 

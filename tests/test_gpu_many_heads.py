@@ -1,0 +1,53 @@
+"""GPU parity at more than 8 query heads per KV head (9, 12, 16: e.g. 96 or 128
+query heads over 8 KV heads).  The library steps such a group in blocks of at
+most 8 heads, one launch each on the caller's stream; every block reads the
+ring's old row for the evicted key, and the last block alone writes the new row,
+the held value row and the ring position.  Each case checks the prefill freeze
+and every decode step against the oracle as the fixed-shape tests do, on both
+launch paths (512-thread work-groups for small grids, 256-thread ones from 1024
+groups up, where 8-head blocks run two heads per wave)."""
+import pytest
+import torch
+
+import streaming_nystr_attention_amd as P
+from streaming_nystr_attention_amd import workloads as W
+
+from parity_util import decode_parity, prefill_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    P.lib()
+    yield
+
+
+def _wl(name, n_seq, n_kv, hpk, d, m, w, sink, T, steps, std, seed):
+    return W.Workload(name, n_seq, 1, n_kv, hpk, d, d, m, w, sink, T=T, steps=steps, q_std=std,
+                      k_std=std, seed=seed)
+
+
+CASES = [
+    _wl("h12_d128", 2, 2, 12, 128, 32, 64, 4, 300, 40, 2.0, 81),    # blocks of 8 and 4 heads
+    _wl("h16_d64", 2, 2, 16, 64, 16, 32, 2, 200, 30, 1.0, 82),      # two blocks of 8
+    _wl("h9_d128_w7", 2, 2, 9, 128, 32, 7, 2, 200, 30, 2.0, 83),    # 8 + 1 heads; no per-slot logits
+    _wl("h13_d96_m64", 2, 2, 13, 96, 64, 256, 4, 600, 24, 1.0, 84), # 8 + 5 (placeholders), m = 64
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
+def test_many_heads_prefill_and_decode(wl):
+    prefill_parity(wl)
+    decode_parity(wl)
+
+
+def test_many_heads_large_grid_sampled():
+    """1024 groups of 16 heads at d = 128: 256-thread work-groups for both
+    blocks; a declared sample of sequences is compared."""
+    wl = _wl("h16_grid1024", 64, 16, 16, 128, 32, 64, 4, 300, 20, 2.0, 85)
+    sample = W.groups_of_sequences(wl, W.sample_sequences(wl))
+    prefill_parity(wl, sample=sample)
+    decode_parity(wl, sample=sample)
