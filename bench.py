@@ -459,7 +459,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=512,
                     help="groups (whole jobs) in the oracle's timed sample")
-    ap.add_argument("--other-workloads", default="stress_m32_s4,stress_m8_s0,wide_gqa",
+    ap.add_argument("--other-workloads", default="stress_m32_s4,stress_m8_s0,wide_gqa,gqa_h8_b16",
                     help="comma-separated workloads whose decode launches are also timed ('' skips)")
     ap.add_argument("--other-steps", type=int, default=256,
                     help="decode launches timed per other workload")

@@ -78,6 +78,11 @@ WORKLOADS = {
     # wide GQA: 64 query heads over 8 KV heads, long prompt
     "wide_gqa": Workload("wide_gqa", 32, 1, 8, 8, 128, 128, 64, 256, 4, T=4096, steps=2048,
                          seed=4),
+    # eight query heads per KV head (64 query heads over 8 KV heads, the layer
+    # shape of many large GQA models) at the stack's window and prompt: 16
+    # sequences x 32 layers x 8 KV groups
+    "gqa_h8_b16": Workload("gqa_h8_b16", 16, 32, 8, 8, 128, 128, 32, 128, 4, T=256, steps=256,
+                           q_std=2.0, k_std=2.0, seed=5),
 }
 
 _TAG_PROMPT_Q, _TAG_PROMPT_K, _TAG_PROMPT_V, _TAG_STEP = 1, 2, 3, 4
