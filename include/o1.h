@@ -69,8 +69,7 @@ enum o1_rect { O1_RECT_AGGREGATE = 0, O1_RECT_FM = 1 };
 /* Geometry of a batch of groups (NystromState::new_group on the nystrom.rs
  * source page: m >= 4, w >= 1, q_heads >= 1).  Defaults on that page:
  * m = 32, w = 128, sink = 4, rect = AGGREGATE.
- * Compiled shapes: d == dv in {64, 96, 128, 256}, hpk <= 16, m <= 64 (32 at d = 256),
- * sink + w <= 1024
+ * Compiled shapes: d == dv in {64, 96, 128, 256}, hpk <= 16, m <= 64, sink + w <= 1024
  * with hpk' * (sink + w) <= 4096, hpk' being min(hpk, 8) rounded up to a power
  * of two (the kernels for hpk' heads run the groups of hpk' / 2 < hpk <= hpk'
  * heads; a group of more than 8 heads is stepped in blocks of at most 8 heads,

@@ -363,9 +363,9 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     const int m_cap = c.m < o1::kMaxLandmarks ? c.m : o1::kMaxLandmarks;
     if (!o1::decode_supported(c.d, c.dv, c.hpk, m_cap, R) || c.m > o1::kMaxLandmarks)
         return fail(O1_EUNSUPPORTED,
-                    "shape not compiled: needs d == dv in {64,96,128,256}, hpk <= 16, m <= %d (32 at d = "
-                    "256), sink + w <= 1024 with hpk'*(sink+w) <= 4096, hpk' = min(hpk, 8) rounded up to a "
-                    "power of two (got d=%d dv=%d hpk=%d m=%d sink+w=%d)",
+                    "shape not compiled: needs d == dv in {64,96,128,256}, hpk <= 16, m <= %d, sink + w "
+                    "<= 1024 with hpk'*(sink+w) <= 4096, hpk' = min(hpk, 8) rounded up to a power of two "
+                    "(got d=%d dv=%d hpk=%d m=%d sink+w=%d)",
                     o1::kMaxLandmarks, c.d, c.dv, c.hpk, c.m, R);
 
     o1_groups *g = new o1_groups();

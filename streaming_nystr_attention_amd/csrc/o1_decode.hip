@@ -1030,12 +1030,8 @@ hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 template <int D, int DV, int HPK, bool PART = false>
 hipError_t launch_m(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
-    if constexpr (D > 128) {
-        return launch_nt<D, DV, HPK, 32, PART>(s, io, stream);  // m <= 32 at these widths
-    } else {
-        if (s.m <= 32) return launch_nt<D, DV, HPK, 32, PART>(s, io, stream);
-        return launch_nt<D, DV, HPK, kMaxLandmarks, PART>(s, io, stream);
-    }
+    if (s.m <= 32) return launch_nt<D, DV, HPK, 32, PART>(s, io, stream);
+    return launch_nt<D, DV, HPK, kMaxLandmarks, PART>(s, io, stream);
 }
 
 template <int D, int DV>
@@ -1111,8 +1107,6 @@ hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t st
 bool decode_supported(int d, int dv, int hpk, int m, int R)
 {
     if (!(d == dv && (d == 64 || d == 96 || d == 128 || d == 256))) return false;
-    // the prefill's landmark pass keeps K~ and one head's Q~ in f64 LDS
-    if (d > 128 && m > 32) return false;
     if (hpk < 1 || hpk > 2 * kMaxBlockHeads) return false;
     if (m < 4 || m > kMaxLandmarks) return false;
     if (R < 1 || R > 1024) return false;

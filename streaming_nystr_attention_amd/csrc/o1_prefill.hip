@@ -48,6 +48,7 @@ constexpr int kThreads = 256;
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLmThreads = 512;
+constexpr size_t kLmLdsMax = 132 * 1024;  // dynamic LDS of the landmark pass
 
 // Near-state row of prompt key j, or -1: sinks j < sink keep row j, the last w
 // keys go to ring slot (j - sink) mod w (row sink + slot).
@@ -58,17 +59,19 @@ __device__ __forceinline__ int near_row(int j, int S, int w, int T)
     return -1;
 }
 
-// Segment means of the rows of x (row stride pos floats) into dst32 (state, f32)
-// and l64 (LDS, f64, row stride ld): one thread per (segment, 4 components),
-// the segment's rows summed in row order, eight rows' loads in flight at a
-// time.  With `near`, rows that are sinks or ring keys are also copied there.
-__device__ __forceinline__ void seg_means_pass(const float *x, int64_t pos, int T, int m, int d,
-                                               float *dst32, double *l64, int ld, float4 *near,
+// Segment means of columns c0 .. c0 + dc - 1 of the rows of x (row stride pos
+// floats) into dst32 (state, f32, row length d) and l64 (LDS, f64, row stride
+// ld, column c0 at 0): one thread per (segment, 4 components), the segment's
+// rows summed in row order, eight rows' loads in flight at a time.  With
+// `near`, the chunk's columns of rows that are sinks or ring keys are also
+// copied there.
+__device__ __forceinline__ void seg_means_pass(const float *x, int64_t pos, int T, int m, int d, int c0,
+                                               int dc, float *dst32, double *l64, int ld, float4 *near,
                                                int S, int w)
 {
-    const int d4 = d / 4;
-    for (int t = threadIdx.x; t < m * d4; t += kLmThreads) {
-        const int a = t / d4, c4 = t - a * d4, c = c4 * 4;
+    const int d4 = d / 4, dc4 = dc / 4;
+    for (int t = threadIdx.x; t < m * dc4; t += kLmThreads) {
+        const int a = t / dc4, cl = (t - a * dc4) * 4, c = c0 + cl, c4 = c / 4;
         const int lo = (int)((long)a * T / m), hi = (int)((long)(a + 1) * T / m);
         double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
         const float *col = x + c;
@@ -109,80 +112,93 @@ __device__ __forceinline__ void seg_means_pass(const float *x, int64_t pos, int 
         const double mean[4] = {s0 * inv, s1 * inv, s2 * inv, s3 * inv};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            l64[a * ld + c + e] = mean[e];
+            l64[a * ld + cl + e] = mean[e];
             dst32[a * d + c + e] = (float)mean[e];
         }
     }
 }
 
-// Frozen landmarks given by the caller: the state takes them, LDS their f64 values.
-__device__ __forceinline__ void frozen_pass(const float *fz, int m, int d, float *dst32, double *l64, int ld)
+// Frozen landmarks given by the caller, columns c0 .. c0 + dc - 1: the state
+// takes them, LDS their f64 values.
+__device__ __forceinline__ void frozen_pass(const float *fz, int m, int d, int c0, int dc, float *dst32,
+                                            double *l64, int ld)
 {
-    for (int t = threadIdx.x; t < m * d; t += kLmThreads) {
-        const int a = t / d, c = t - a * d;
-        const float v = fz[t];
-        dst32[t] = v;
-        l64[a * ld + c] = (double)v;
+    for (int t = threadIdx.x; t < m * dc; t += kLmThreads) {
+        const int a = t / dc, cl = t - a * dc;
+        const float v = fz[a * d + c0 + cl];
+        dst32[a * d + c0 + cl] = v;
+        l64[a * ld + cl] = (double)v;
     }
 }
 
 // One work-group per group, 512 threads (two per CU, as LDS allows at m <= 32,
-// d = 128: four waves per SIMD); dynamic LDS: K~ and one head's Q~ in
-// f64, [mp][d + 1] each (mp = m rounded up to 16, rows past m zero).  The
-// exp-Gram of head h, A[i][j] = exp(q~_i . k~_j * scale), runs on
-// v_mfma_f64_16x16x4f64 from LDS, one 16 x 16 block per wave, and goes to
-// io.a64[call][h][mp][mp], zero past m, for gram_pinv_kernel (`gram` = 0: M is given frozen and
-// no A is needed).
-__global__ __launch_bounds__(kLmThreads, 4) void landmarks_kernel(DevState s, PrefillIO io, int gram)
+// d = 128: four waves per SIMD); dynamic LDS: K~ and one head's Q~ in f64,
+// [mp][dc + 1] each (mp = m rounded up to 16, rows past m zero) for a chunk of
+// dc of the d components.  The exp-Gram of head h, A[i][j] = exp(q~_i . k~_j
+// * scale), runs on v_mfma_f64_16x16x4f64 from LDS, one 16 x 16 block per wave,
+// and goes to io.a64[call][h][mp][mp], zero past m, for gram_pinv_kernel
+// (`gram` = 0: M is given frozen and no A is needed).  When both [mp][d + 1]
+// arrays do not fit (d = 256, m > 32) the components come in chunks (dc = d /
+// 2): each chunk's key pass, then each head's query pass and the dots over
+// the chunk, the partial dots kept in io.a64 until the last chunk takes the
+// exp.  Every prompt row is still read once.
+__global__ __launch_bounds__(kLmThreads, 4) void landmarks_kernel(DevState s, PrefillIO io, int gram, int dc)
 {
     const int ci = blockIdx.x, g = io.map.state(ci);
     const int d = s.d, m = s.m, T = io.T, H = s.hpk, tid = threadIdx.x;
-    const int nb = (m + 15) / 16, mp = nb * 16, ld = d + 1;
+    const int nb = (m + 15) / 16, mp = nb * 16, ld = dc + 1, nch = d / dc;
     extern __shared__ double lm_lds[];
     double *kt64 = lm_lds, *qt64 = lm_lds + (size_t)mp * ld;
-    // rows past m stay zero for every head
+    // rows past m stay zero for every head and chunk
     for (int t = tid; t < (mp - m) * ld; t += kLmThreads) {
         kt64[m * ld + t] = 0.0;
         qt64[m * ld + t] = 0.0;
     }
 
     float *kt32 = s.k_tilde + (size_t)g * m * d;
-    if (io.fz_kt) {
-        frozen_pass(io.fz_kt + (size_t)ci * m * d, m, d, kt32, kt64, ld);
-    } else {
-        float4 *near = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * s.R * (d / 4);
-        seg_means_pass(io.p.k_row(io.map, ci, 0), io.p.k_pos, T, m, d, kt32, kt64, ld, near, s.sink, s.w);
-    }
-
     const int lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
     const double sc = (double)s.scale;
-    for (int h = 0; h < H; ++h) {
-        float *qt32 = s.q_tilde + ((size_t)g * H + h) * m * d;
-        __syncthreads();  // the previous head's exp-Gram is done with qt64
-        if (io.fz_qt)
-            frozen_pass(io.fz_qt + ((size_t)ci * H + h) * m * d, m, d, qt32, qt64, ld);
-        else
-            seg_means_pass(io.p.q_row(io.map, H, ci, h, 0), io.p.q_pos, T, m, d, qt32, qt64, ld, nullptr,
-                           0, 0);
-        if (!gram) continue;
-        __syncthreads();
-        double *a = io.a64 + ((size_t)ci * H + h) * mp * mp;
-        for (int blk = wave; blk < nb * nb; blk += kLmThreads / 64) {
-            const int bi = blk / nb, bj = blk - bi * nb;
-            const double *qrow = qt64 + (bi * 16 + li) * ld + lk;
-            const double *krow = kt64 + (bj * 16 + li) * ld + lk;
-            f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
-            // k-step ks covers components 4 ks .. 4 ks + 3 (k-lane lk: 4 ks + lk)
-            for (int ks = 0; ks < d / 4; ks += 2) {
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qrow[4 * ks], krow[4 * ks], acc, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(qrow[4 * ks + 4], krow[4 * ks + 4], acc2, 0, 0, 0);
-            }
-            acc += acc2;
-            // lane holds A[bi*16 + lk + 4 r][bj*16 + li]
+    for (int ch = 0; ch < nch; ++ch) {
+        const int c0 = ch * dc;
+        const bool first = ch == 0, last = ch == nch - 1;
+        __syncthreads();  // the previous chunk's dots are done with kt64
+        if (io.fz_kt) {
+            frozen_pass(io.fz_kt + (size_t)ci * m * d, m, d, c0, dc, kt32, kt64, ld);
+        } else {
+            float4 *near = reinterpret_cast<float4 *>(s.near_k) + (size_t)g * s.R * (d / 4);
+            seg_means_pass(io.p.k_row(io.map, ci, 0), io.p.k_pos, T, m, d, c0, dc, kt32, kt64, ld, near,
+                           s.sink, s.w);
+        }
+        for (int h = 0; h < H; ++h) {
+            float *qt32 = s.q_tilde + ((size_t)g * H + h) * m * d;
+            __syncthreads();  // the previous head's exp-Gram is done with qt64
+            if (io.fz_qt)
+                frozen_pass(io.fz_qt + ((size_t)ci * H + h) * m * d, m, d, c0, dc, qt32, qt64, ld);
+            else
+                seg_means_pass(io.p.q_row(io.map, H, ci, h, 0), io.p.q_pos, T, m, d, c0, dc, qt32, qt64, ld,
+                               nullptr, 0, 0);
+            if (!gram) continue;
+            __syncthreads();
+            double *a = io.a64 + ((size_t)ci * H + h) * mp * mp;
+            for (int blk = wave; blk < nb * nb; blk += kLmThreads / 64) {
+                const int bi = blk / nb, bj = blk - bi * nb;
+                const double *qrow = qt64 + (bi * 16 + li) * ld + lk;
+                const double *krow = kt64 + (bj * 16 + li) * ld + lk;
+                f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
+                // k-step ks covers components 4 ks .. 4 ks + 3 (k-lane lk: 4 ks + lk)
+                for (int ks = 0; ks < dc / 4; ks += 2) {
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qrow[4 * ks], krow[4 * ks], acc, 0, 0, 0);
+                    acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(qrow[4 * ks + 4], krow[4 * ks + 4], acc2, 0, 0, 0);
+                }
+                acc += acc2;
+                // lane holds A[bi*16 + lk + 4 r][bj*16 + li]; this thread wrote
+                // the same entries for the earlier chunks
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = bi * 16 + lk + 4 * r, j = bj * 16 + li;
-                a[i * mp + j] = (i < m && j < m) ? exp(acc[r] * sc) : 0.0;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = bi * 16 + lk + 4 * r, j = bj * 16 + li;
+                    const double dot = first ? acc[r] : acc[r] + a[i * mp + j];
+                    a[i * mp + j] = (i < m && j < m) ? (last ? exp(dot * sc) : dot) : 0.0;
+                }
             }
         }
     }
@@ -717,14 +733,17 @@ __global__ void copy_mu_kernel(DevState s, GroupMap map, const float *src)
 
 hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t stream)
 {
-    if (s.d > 256 || s.dv > 256 || s.m > kMaxLandmarks || (s.d > 128 && s.m > 32)) return hipErrorInvalidValue;
+    if (s.d > 256 || s.dv > 256 || s.m > kMaxLandmarks) return hipErrorInvalidValue;
     const int n = io.map.count;
     const int mp = (s.m + 15) / 16 * 16;
-    const size_t lm_lds = sizeof(double) * 2 * mp * (s.d + 1);
+    // K~ and Q~ of the landmark pass as f64 [mp][dc + 1], dc = d unless that
+    // passes 132 KB of LDS (d = 256, m > 32), then half the components at a time
+    const int dc = sizeof(double) * 2 * mp * (s.d + 1) <= kLmLdsMax ? s.d : s.d / 2;
+    const size_t lm_lds = sizeof(double) * 2 * mp * (dc + 1);
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&landmarks_kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lm_lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(landmarks_kernel, dim3(n), dim3(kLmThreads), lm_lds, stream, s, io, io.fz_mu ? 0 : 1);
+    hipLaunchKernelGGL(landmarks_kernel, dim3(n), dim3(kLmThreads), lm_lds, stream, s, io, io.fz_mu ? 0 : 1, dc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(scatter_kernel, dim3(n), dim3(kThreads), 0, stream, s, io);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -745,7 +764,7 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
     if ((err = launch_ring_logits(s, io.map, stream)) != hipSuccess) return err;
     if (s.d == 128 && s.dv == 128) return launch_far_m<128, 128>(s, io, stream);
     if (s.d == 96 && s.dv == 96) return launch_far_m<96, 96>(s, io, stream);
-    if (s.d == 256 && s.dv == 256) return launch_far<256, 256, 32>(s, io, stream);
+    if (s.d == 256 && s.dv == 256) return launch_far_m<256, 256>(s, io, stream);
     if (s.d == 64 && s.dv == 64) return launch_far_m<64, 64>(s, io, stream);
     return hipErrorInvalidValue;
 }
@@ -763,6 +782,13 @@ hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_
     if (s.hpk % hb) hb = 1;
     const dim3 grid(map.count, s.hpk / hb);
     const size_t lds = sizeof(float4) * (size_t)hb * s.m * (s.d / 4 + 1);
+    if (lds > 64 * 1024) {  // 64 landmark rows of 256 floats: above the default dynamic limit
+        hipError_t err = hipSuccess;
+        if (s.d == 256)
+            err = hipFuncSetAttribute(reinterpret_cast<const void *>(&ring_logits_kernel<256>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess) return err;
+    }
     if (s.d == 64)
         hipLaunchKernelGGL(ring_logits_kernel<64>, grid, dim3(256), lds, stream, s, map, hb);
     else if (s.d == 96)

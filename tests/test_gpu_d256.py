@@ -3,10 +3,11 @@ and the decode steps, as the tests at d in {64, 96, 128} check them.  A row of
 256 floats is 64 float4: the decode's row passes split a key row over 8, 16 or
 32 lanes (8, 4 or 2 float4 each), its column passes give each value row a whole
 wave (so it always runs 512-thread work-groups, eight row lanes for the held
-rows), and the landmark pass's f64 K~ and Q~ in LDS bound m at 32.  The shapes
-cover every compiled head count (1, 2, 4, 8 and the partial group of 3), m up
-to 32, windows below, at and above the fold period, a 1024-group grid and the
-Fm rectifier."""
+rows), and above m = 32 the landmark pass takes the components in two chunks
+(its f64 K~ and Q~ at full width would not fit in LDS), keeping the partial
+exp-Gram dots in global memory between them.  The shapes cover every compiled
+head count (1, 2, 4, 8 and the partial group of 3), m up to 64, windows below,
+at and above the fold period, a 1024-group grid and the Fm rectifier."""
 import pytest
 import torch
 
@@ -43,6 +44,12 @@ SHAPES = [
     _wl("d256_h1_m8_w9", 2, 1, 2, 1, 8, 9, 0, T=90, steps=3 * P.FOLD_PERIOD + 5, seed=84, std=2.0),
     # three heads (run as four), m not a multiple of 16
     _wl("d256_h3_m24_w100", 1, 2, 2, 3, 24, 100, 3, T=200, steps=16, seed=85),
+    # m = 64: the landmark pass in two component chunks, the 64-landmark kernels
+    _wl("d256_h2_m64_w128", 2, 1, 4, 2, 64, 128, 4, T=600, steps=3 * P.FOLD_PERIOD, seed=87, std=2.0),
+    # m = 40 (three 16-row tiles), eight heads
+    _wl("d256_h8_m40_w64", 2, 1, 2, 8, 40, 64, 2, T=400, steps=20, seed=88),
+    # m = 48, a window below the fold period, five heads (run as eight)
+    _wl("d256_h5_m48_w5", 2, 1, 2, 5, 48, 5, 3, T=420, steps=20, seed=89),
 ]
 
 
@@ -69,8 +76,8 @@ def test_d256_large_grid():
     decode_parity(wl, sample=W.sample_groups(wl))
 
 
-def test_d256_rejects_more_than_32_landmarks():
-    cfg = P.Config(n_seq=1, n_layer=1, n_kv=1, hpk=2, d=256, dv=256, m=33, w=16, sink=2)
+def test_d256_rejects_more_than_64_landmarks():
+    cfg = P.Config(n_seq=1, n_layer=1, n_kv=1, hpk=2, d=256, dv=256, m=65, w=16, sink=2)
     with pytest.raises(P.O1Error) as e:
         P.O1Groups(cfg)
     assert e.value.status == P.O1_EUNSUPPORTED
