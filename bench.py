@@ -283,7 +283,7 @@ def exact_comparator(wl, ctx, nystrom_us, dev):
         vc = torch.randn(G, ctx, wl.dv, device=dev, generator=g)
         q = torch.randn(G, H, wl.d, device=dev, generator=g)
         out = torch.empty(G, H, wl.dv, device=dev)
-        desc = P._exact_desc(q, kc, ctx, 0, None)
+        desc = P._exact_desc(q, kc, vc, ctx, 0, None)
         need = P.o1_exact_workspace_bytes(desc)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         for _ in range(2):

@@ -301,10 +301,10 @@ def o1_write_field(handle, field: int, src, stream=None):
                                 _stream_handle(stream)))
 
 
-def _exact_desc(q, k, n_keys, first, scale):
+def _exact_desc(q, k, v, n_keys, first, scale):
     G, H, d = q.shape
-    cap = k.shape[1]
-    return o1_exact_desc(G, H, d, d, cap, first, n_keys, 0.0 if scale is None else scale)
+    cap, dv = k.shape[1], v.shape[2]
+    return o1_exact_desc(G, H, d, dv, cap, first, n_keys, 0.0 if scale is None else scale)
 
 
 def o1_exact_workspace_bytes(desc) -> int:
@@ -320,7 +320,7 @@ def o1_exact_attend(q, k, v, out, n_keys: int, first: int = 0, scale=None, works
     tensor of at least o1_exact_workspace_bytes bytes (allocated here if None)."""
     import torch
 
-    desc = _exact_desc(q, k, n_keys, first, scale)
+    desc = _exact_desc(q, k, v, n_keys, first, scale)
     G, H, d = q.shape
     cap, dv = k.shape[1], v.shape[2]
     need = o1_exact_workspace_bytes(desc)
@@ -336,7 +336,7 @@ def o1_exact_attend(q, k, v, out, n_keys: int, first: int = 0, scale=None, works
 def o1_exact_attend_noalloc(q, k, v, out, n_keys: int, first: int = 0, scale=None, stream=None):
     """o1_exact_attend without a work space (the library's static per-device
     buffer holds the split partials); nothing is allocated."""
-    desc = _exact_desc(q, k, n_keys, first, scale)
+    desc = _exact_desc(q, k, v, n_keys, first, scale)
     G, H, d = q.shape
     cap, dv = k.shape[1], v.shape[2]
     _check(lib().o1_exact_attend_noalloc(ctypes.byref(desc), _dev_ptr(q, "q", G * H * d),

@@ -115,8 +115,8 @@ struct DecodeShape {
     static_assert(RED_H >= 1 && HPK % RED_H == 0, "heads must split into reduction rounds");
     static_assert(RL >= kPend, "each held value row needs a row lane of its own");
     static_assert((kPend - 1) * VCH <= NT, "one held value float4 per thread");
-    static_assert(HPK * CH <= NT && (kPend - 1) * CH <= NT && HPK * MM <= NT && 128 + VCH <= NT,
-                  "the prologue loads at most one element of each kind per thread");
+    static_assert(HPK * CH <= NT && HPK * MM <= NT && 128 + VCH <= NT,
+                  "the prologue loads at most one element of each kind per thread (but the fold's keys)");
 };
 
 template <int D, int DV, int HPK, int MM, int NT, bool STREAM, bool PART>
@@ -210,15 +210,23 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
         const bool q_mine = tid < H * C::CH, q_slot = tid < HPK * C::CH, k_mine = tid < C::CH;
         const bool v_mine = tid >= 128 && tid < 128 + C::VCH, st_mine = tid < H * m;
-        const bool kb_mine = ring && fold && tid < (kPend - 1) * C::CH;
-        const int kbj = 1 + tid / C::CH, kbc = tid - (kbj - 1) * C::CH;
-        float4 qv = z4, kin = z4, kev = z4, vin = z4, vev = z4, kbv = z4;
+        // on a fold with ring logits, the keys that arrived since the last
+        // fold (ring slots e-1 .. e-kPend+1): KBP float4 per thread
+        constexpr int KBP = ((kPend - 1) * C::CH + NT - 1) / NT;
+        const bool kb_fold = ring && fold;
+        float4 kbv[KBP];
+        float4 qv = z4, kin = z4, kev = z4, vin = z4, vev = z4;
         if (q_mine) qv = qg[tid];
         if (k_mine) {
             kin = reinterpret_cast<const float4 *>(io.k)[(size_t)ci * C::CH + tid];
             if (!ring) kev = nk[(size_t)slot_row * C::CH + tid];
         }
-        if (kb_mine) kbv = nk[(size_t)(S + (e - kbj + w) % w) * C::CH + kbc];
+#pragma unroll
+        for (int u = 0; u < KBP; ++u) {
+            const int i = tid + u * NT, j = 1 + i / C::CH, c = i - (j - 1) * C::CH;
+            kbv[u] = z4;
+            if (kb_fold && i < (kPend - 1) * C::CH) kbv[u] = nk[(size_t)(S + (e - j + w) % w) * C::CH + c];
+        }
         if (v_mine) {
             vin = reinterpret_cast<const float4 *>(io.v)[(size_t)ci * C::VCH + tid - 128];
             vev = nv[(size_t)slot_row * C::VCH + tid - 128];
@@ -259,7 +267,11 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
             if (!ring) ke_s[tid] = kev;
             else if (fold) kb_s[0][tid] = kin;
         }
-        if (kb_mine) kb_s[kbj][kbc] = kbv;
+#pragma unroll
+        for (int u = 0; u < KBP; ++u) {
+            const int i = tid + u * NT, j = 1 + i / C::CH, c = i - (j - 1) * C::CH;
+            if (kb_fold && i < (kPend - 1) * C::CH) kb_s[j][c] = kbv[u];
+        }
         if (v_mine) {
             vn_s[tid - 128] = vin;
             ve_s[tid - 128] = vev;
@@ -1019,8 +1031,9 @@ template <int D, int DV, int HPK, int MM, bool PART>
 hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     const bool big = s.stream_state != 0;
-    // (rows wider than 128 floats: 512 threads keep a row lane per held slot)
-    if constexpr (HPK * MM < 512 && DV <= 128) {
+    // (value rows wider than 128 floats: 512 threads keep a row lane per held
+    // slot; and one query float4 per thread in the prologue)
+    if constexpr (HPK * MM < 512 && DV <= 128 && HPK * (D / 4) <= 256) {
         if (io.map.count >= kSmallGrid) return launch_shape<D, DV, HPK, MM, 256, true, PART>(s, io, stream);
     }
     if (big) return launch_shape<D, DV, HPK, MM, 512, true, PART>(s, io, stream);
@@ -1106,7 +1119,7 @@ hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t st
 
 bool decode_supported(int d, int dv, int hpk, int m, int R)
 {
-    if (!(d == dv && (d == 64 || d == 96 || d == 128 || d == 256))) return false;
+    if (!widths_compiled(d, dv)) return false;
     if (hpk < 1 || hpk > 2 * kMaxBlockHeads) return false;
     if (m < 4 || m > kMaxLandmarks) return false;
     if (R < 1 || R > 1024) return false;
@@ -1131,6 +1144,7 @@ hipError_t launch_decode(const DevState &s, const DecodeIO &io_in, hipStream_t s
         if (s.d == 64) err = launch_hpk<64, 64>(s, io, stream);
         else if (s.d == 96) err = launch_hpk<96, 96>(s, io, stream);
         else if (s.d == 256) err = launch_hpk<256, 256>(s, io, stream);
+        else if (s.d == 192) err = launch_hpk<192, 128>(s, io, stream);
         else err = launch_hpk<128, 128>(s, io, stream);
         if (err != hipSuccess) return err;
     }

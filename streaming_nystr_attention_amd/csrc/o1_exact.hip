@@ -34,7 +34,6 @@ struct ExactShape {
     // SIMDs; more heads need the registers of a 256-thread work-group
     static constexpr int NT = HPK <= 2 ? 512 : 256;
     static constexpr int NW = NT / 64;
-    static constexpr int WAVES_PER_SIMD = HPK <= 2 ? 4 : (HPK == 8 && D % 16 == 0 && D <= 128 ? 2 : 1);
     static constexpr int CH = D / 4;
     static constexpr int LPR_WANT = HPK <= 2 ? 8 : (HPK <= 4 ? 16 : 32);
     static constexpr int LPR = pow2_divisor(LPR_WANT, CH);
@@ -42,6 +41,10 @@ struct ExactShape {
     static constexpr int RPW = 64 / LPR;
     static constexpr int RPB = RPW * NW;
     static constexpr int UNR = CPL >= 8 ? 1 : (CPL >= 4 ? 2 : (CPL == 3 ? 3 : (CPL == 2 ? 4 : 8)));
+    // (more than 9 key float4 in flight per lane, as 192-float keys take,
+    // do not fit the registers of four waves per SIMD)
+    static constexpr int WAVES_PER_SIMD =
+        HPK <= 2 ? (UNR * CPL > 9 ? 2 : 4) : (HPK == 8 && D % 16 == 0 && D <= 128 ? 2 : 1);
     static constexpr int VCH = DV / 4;
     static constexpr int VCP = pow2_ceil(VCH);  // lanes per value row (VCH used)
     static constexpr int RL = NT / VCP;
@@ -460,6 +463,7 @@ hipError_t launch_exact(const ExactIO &in, int splits, hipStream_t stream)
         else if (a.d == 96 && a.dv == 96) err = launch_exact_hpk<96, 96>(a, splits, stream);
         else if (a.d == 128 && a.dv == 128) err = launch_exact_hpk<128, 128>(a, splits, stream);
         else if (a.d == 256 && a.dv == 256) err = launch_exact_hpk<256, 256>(a, splits, stream);
+        else if (a.d == 192 && a.dv == 128) err = launch_exact_hpk<192, 128>(a, splits, stream);
         else err = hipErrorInvalidValue;
         if (err != hipSuccess) return err;
     }

@@ -113,6 +113,14 @@ struct PromptView {
 // many (the kernels are compiled for 1, 2, 4 and 8 heads).
 constexpr int kMaxBlockHeads = 8;
 
+// Key and value widths the kernels are compiled for: d == dv in {64, 96, 128,
+// 256}, and keys of 192 floats with values of 128 (a head whose queries and
+// keys carry 64 more components than its values).
+constexpr bool widths_compiled(int d, int dv)
+{
+    return (d == dv && (d == 64 || d == 96 || d == 128 || d == 256)) || (d == 192 && dv == 128);
+}
+
 struct DecodeIO {
     const float *q, *k, *v;  // q [count][hpk][d], k [count][d], v [count][dv]
     float *out;              // [count][hpk][dv]

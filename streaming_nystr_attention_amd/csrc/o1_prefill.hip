@@ -766,6 +766,7 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
     if (s.d == 96 && s.dv == 96) return launch_far_m<96, 96>(s, io, stream);
     if (s.d == 256 && s.dv == 256) return launch_far_m<256, 256>(s, io, stream);
     if (s.d == 64 && s.dv == 64) return launch_far_m<64, 64>(s, io, stream);
+    if (s.d == 192 && s.dv == 128) return launch_far_m<192, 128>(s, io, stream);
     return hipErrorInvalidValue;
 }
 
@@ -795,6 +796,8 @@ hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_
         hipLaunchKernelGGL(ring_logits_kernel<96>, grid, dim3(256), lds, stream, s, map, hb);
     else if (s.d == 128)
         hipLaunchKernelGGL(ring_logits_kernel<128>, grid, dim3(256), lds, stream, s, map, hb);
+    else if (s.d == 192)
+        hipLaunchKernelGGL(ring_logits_kernel<192>, grid, dim3(256), lds, stream, s, map, hb);
     else if (s.d == 256)
         hipLaunchKernelGGL(ring_logits_kernel<256>, grid, dim3(256), lds, stream, s, map, hb);
     else

@@ -95,6 +95,7 @@ def _create(P, L, **kw):
     (dict(d=80, dv=80), 6), (dict(d=512, dv=512), 6), (dict(hpk=17), 6),
     (dict(m=65), 6),
     (dict(d=64, dv=128), 6), (dict(d=96, dv=64), 6),
+    (dict(d=192, dv=192), 6), (dict(d=128, dv=192), 6), (dict(d=192, dv=64), 6),
     (dict(hpk=5, w=596, sink=4), 6),  # run as 8 heads: 8 * 600 near logits pass 32 KB
     (dict(hpk=12, w=596, sink=4), 6),  # blocks of 8 and 4 heads: the 8-head block's logits pass 32 KB
     (dict(w=2000), 6), (dict(exact_cap=-1), 1), (dict(n_seq=1 << 20, exact_cap=1 << 22), 1),
@@ -139,7 +140,7 @@ def test_exact_comparator_validation_without_device():
     good = dict(n_groups=4, hpk=2, d=128, dv=128, cap=100, first=0, n_keys=100, scale=0.0)
     for kw, code in [(dict(first=100), 1), (dict(n_keys=101), 1), (dict(first=-1), 1),
                      (dict(n_groups=0), 1), (dict(hpk=17), 6), (dict(d=80, dv=80), 6),
-                     (dict(dv=64), 6)]:
+                     (dict(dv=64), 6), (dict(d=192, dv=192), 6), (dict(d=128, dv=192), 6)]:
         args = {**good, **kw}
         desc = P.o1_exact_desc(*[args[f] for f, _ in P.o1_exact_desc._fields_])
         assert L.o1_exact_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == code, kw
@@ -150,6 +151,10 @@ def test_exact_comparator_validation_without_device():
     # each writing (max, sum, numerator[dv]) per head
     args = {**good, "cap": 1000, "n_keys": 1000}
     desc = P.o1_exact_desc(*[args[f] for f, _ in P.o1_exact_desc._fields_])
+    assert L.o1_exact_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == 0
+    assert n.value == 8 * (4 * 8 * 2 * (128 + 2))
+    # keys of 192 floats with values of 128: the partials are dv wide
+    desc = P.o1_exact_desc(*[{**args, "d": 192}[f] for f, _ in P.o1_exact_desc._fields_])
     assert L.o1_exact_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == 0
     assert n.value == 8 * (4 * 8 * 2 * (128 + 2))
     assert L.o1_exact_attend(ctypes.byref(desc), None, None, None, None, None, 0, None) == 1

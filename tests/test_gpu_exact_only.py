@@ -28,9 +28,9 @@ def gpu_ready():
     yield
 
 
-def _wl(name, n_seq, n_layer, n_kv, hpk, d, m, w, sink, T, steps, seed):
-    return W.Workload(name, n_seq, n_layer, n_kv, hpk, d, d, m, w, sink, T=T, steps=steps,
-                      q_std=2.0, k_std=2.0, seed=seed)
+def _wl(name, n_seq, n_layer, n_kv, hpk, d, m, w, sink, T, steps, seed, dv=None):
+    return W.Workload(name, n_seq, n_layer, n_kv, hpk, d, d if dv is None else dv, m, w, sink, T=T,
+                      steps=steps, q_std=2.0, k_std=2.0, seed=seed)
 
 
 # (workload, exact_cap).  T runs from one key to the mode's upper bound
@@ -50,6 +50,9 @@ CASES = [
     (_wl("x_d256_h4_split", 1, 1, 1, 4, 256, 32, 500, 4, T=510, steps=12, seed=51), 530),
     (_wl("x_d128_h12_T140", 2, 1, 2, 12, 128, 32, 128, 4, T=140, steps=24, seed=52), 200),
     (_wl("x_d64_h16_split", 1, 1, 1, 16, 64, 8, 500, 2, T=505, steps=16, seed=53), 530),
+    # keys of 192 floats with values of 128
+    (_wl("x_d192_h2_T60", 2, 1, 2, 2, 192, 16, 64, 4, T=60, steps=20, seed=54, dv=128), 80),
+    (_wl("x_d192_h8_split", 1, 1, 1, 8, 192, 32, 500, 4, T=510, steps=12, seed=55, dv=128), 530),
 ]
 
 

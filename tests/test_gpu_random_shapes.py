@@ -1,6 +1,7 @@
 """GPU parity at seeded random shapes: each case draws the query heads per group,
 the head width, the landmark budget, window, sinks, prompt length, rectifier,
 input scale and group counts within the compiled limits (d = dv in {64, 96, 128, 256},
+or d = 192 with dv = 128,
 hpk <= 16, m <= 64, sink + w <= 1024 with hpk' * (sink + w) * 8 <= 32 KB for hpk'
 min(hpk, 8) rounded up to a power of two),
 then checks the prefill freeze and the decode steps against the oracle exactly
@@ -45,7 +46,8 @@ def draw(case: int, widths=(64, 128), base=7000, max_m=64, min_hpk=1, max_hpk=8)
         steps = int(r.integers(5, 40))
         name = f"rand{case}" if base == 7000 else (f"rand{case}_h" if base == 7300 else
                                                    f"rand{case}_d{d}" + ("m" if base == 7400 else ""))
-        wl = W.Workload(name, n_seq, n_layer, n_kv, hpk, d, d, m, w, sink, T=T, steps=steps,
+        dv = 128 if d == 192 else d  # keys of 192 floats come with values of 128
+        wl = W.Workload(name, n_seq, n_layer, n_kv, hpk, d, dv, m, w, sink, T=T, steps=steps,
                         q_std=std, k_std=std, seed=900 + case)
         return wl, (O.RECT_AGGREGATE, O.RECT_FM)[rect]
 
@@ -60,6 +62,8 @@ CASES += [draw(i, widths=(256,), base=7200, max_m=32) for i in range(4)]
 CASES += [draw(i, widths=(256,), base=7400) for i in range(3)]
 # 9 to 16 heads per group (stepped in blocks of at most 8), d 64 to 128
 CASES += [draw(10 + i, widths=(64, 96, 128), base=7300, min_hpk=9, max_hpk=16) for i in range(4)]
+# keys of 192 floats with values of 128, 1 to 16 heads
+CASES += [draw(10 + i, widths=(192,), base=7500, max_hpk=16) for i in range(4)]
 
 
 @pytest.mark.parametrize("wl,rect", CASES,
