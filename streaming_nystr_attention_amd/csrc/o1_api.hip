@@ -363,11 +363,11 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     const int m_cap = c.m < o1::kMaxLandmarks ? c.m : o1::kMaxLandmarks;
     if (!o1::decode_supported(c.d, c.dv, c.hpk, m_cap, R) || c.m > o1::kMaxLandmarks)
         return fail(O1_EUNSUPPORTED,
-                    "shape not compiled: needs d == dv in {64,96,128,256} or d = 192 with dv = 128, hpk <= 16, "
+                    "shape not compiled: needs d == dv in {64,96,128,256} or d = 192 with dv = 128, hpk <= %d, "
                     "m <= %d, sink + w "
                     "<= 1024 with hpk'*(sink+w) <= 4096, hpk' = min(hpk, 8) rounded up to a power of two "
                     "(got d=%d dv=%d hpk=%d m=%d sink+w=%d)",
-                    o1::kMaxLandmarks, c.d, c.dv, c.hpk, c.m, R);
+                    o1::kMaxHeads, o1::kMaxLandmarks, c.d, c.dv, c.hpk, c.m, R);
 
     o1_groups *g = new o1_groups();
     memset(&g->st, 0, sizeof g->st);
@@ -748,10 +748,10 @@ static int exact_check(const o1_exact_desc *x, int *splits, size_t *bytes)
     if (x->n_keys < 1 || x->n_keys > x->cap || x->first < 0 || x->first >= x->n_keys)
         return fail(O1_EINVAL, "o1_exact: need 0 <= first < n_keys <= cap (first=%d n_keys=%d cap=%d)",
                     x->first, x->n_keys, x->cap);
-    if (!o1::widths_compiled(x->d, x->dv) || x->hpk > 2 * o1::kMaxBlockHeads)
+    if (!o1::widths_compiled(x->d, x->dv) || x->hpk > o1::kMaxHeads)
         return fail(O1_EUNSUPPORTED,
                     "o1_exact: compiled for d == dv in {64,96,128,256} or d = 192 with dv = 128, hpk <= %d",
-                    2 * o1::kMaxBlockHeads);
+                    o1::kMaxHeads);
     *splits = o1::exact_splits(x->n_groups, x->n_keys - x->first);
     *bytes = *splits == 1 ? 0
                           : sizeof(double) * (size_t)x->n_groups * *splits * x->hpk * (x->dv + 2);

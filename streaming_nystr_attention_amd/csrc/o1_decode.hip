@@ -1120,7 +1120,7 @@ hipError_t launch_fold(const DevState &s, float *dst, bool reset, hipStream_t st
 bool decode_supported(int d, int dv, int hpk, int m, int R)
 {
     if (!widths_compiled(d, dv)) return false;
-    if (hpk < 1 || hpk > 2 * kMaxBlockHeads) return false;
+    if (hpk < 1 || hpk > kMaxHeads) return false;
     if (m < 4 || m > kMaxLandmarks) return false;
     if (R < 1 || R > 1024) return false;
     // dynamic LDS for the near logits of the compiled head count (hpk rounded

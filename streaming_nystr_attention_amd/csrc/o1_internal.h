@@ -110,8 +110,10 @@ struct PromptView {
 };
 
 // Heads per decode launch: a group of more heads is stepped in blocks of this
-// many (the kernels are compiled for 1, 2, 4 and 8 heads).
+// many (the kernels are compiled for 1, 2, 4 and 8 heads), up to kMaxHeads
+// query heads per group (a 64-head attention over one KV head).
 constexpr int kMaxBlockHeads = 8;
+constexpr int kMaxHeads = 64;
 
 // Key and value widths the kernels are compiled for: d == dv in {64, 96, 128,
 // 256}, and keys of 192 floats with values of 128 (a head whose queries and

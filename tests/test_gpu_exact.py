@@ -40,6 +40,8 @@ def gpu_ready():
     (3, 12, 128, 1000, 1000, 0, 2.0),     # 12 heads: blocks of 8 and 4, split key range
     (1500, 16, 64, 150, 150, 10, 1.0),    # 16 heads, many groups
     (2, 9, 96, 300, 257, 3, 1.0),         # 9 heads: blocks of 8 and 1
+    (3, 32, 128, 700, 700, 0, 2.0),       # 32 heads: four blocks, split key range
+    (1200, 64, 64, 150, 150, 10, 1.0),    # 64 heads: eight blocks, many groups
 ])
 def test_exact_attend_matches_oracle(G, H, d, cap, n, first, std):
     say(f"[exact] G={G} hpk={H} d={d} cap={cap} n_keys={n} first={first}")

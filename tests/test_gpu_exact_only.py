@@ -53,6 +53,8 @@ CASES = [
     # keys of 192 floats with values of 128
     (_wl("x_d192_h2_T60", 2, 1, 2, 2, 192, 16, 64, 4, T=60, steps=20, seed=54, dv=128), 80),
     (_wl("x_d192_h8_split", 1, 1, 1, 8, 192, 32, 500, 4, T=510, steps=12, seed=55, dv=128), 530),
+    # 32 heads over one KV head: four blocks
+    (_wl("x_d128_h32_split", 1, 1, 1, 32, 128, 16, 500, 4, T=510, steps=12, seed=56), 530),
 ]
 
 

@@ -30,6 +30,10 @@ def gpu_ready():
 
 WL = W.Workload("layers", n_seq=3, n_layer=4, n_kv=2, hpk=2, d=128, dv=128, m=16, w=32, sink=4,
                 T=180, steps=12, q_std=2.0, k_std=2.0, seed=61)
+# keys wider than values and a partial head group: a stride taken from the
+# wrong width, or a head count taken from the compiled one, shows here
+WL192 = W.Workload("layers_d192", n_seq=2, n_layer=3, n_kv=2, hpk=3, d=192, dv=128, m=16, w=32, sink=4,
+                   T=150, steps=12, q_std=2.0, k_std=2.0, seed=63)
 
 
 def _layer_groups(wl, layer):
@@ -108,9 +112,9 @@ FIELDS = [P.FIELD_NEAR_K, P.FIELD_NEAR_V, P.FIELD_K_TILDE, P.FIELD_Q_TILDE, P.FI
           P.FIELD_LAMBDA, P.FIELD_TRIES]
 
 
+@pytest.mark.parametrize("wl", [WL, WL192], ids=["d128_h2", "d192_dv128_h3"])
 @pytest.mark.parametrize("with_frozen", [False, True])
-def test_layer_path_equals_whole_handle_bitwise(with_frozen):
-    wl = WL
+def test_layer_path_equals_whole_handle_bitwise(wl, with_frozen):
     q, k, v = W.prompt(wl, DEV)
     qs, ks, vs = _step_inputs(wl)
     whole = P.O1Groups(wl.config)

@@ -1,5 +1,5 @@
-"""GPU parity at more than 8 query heads per KV head (9, 12, 16: e.g. 96 or 128
-query heads over 8 KV heads).  The library steps such a group in blocks of at
+"""GPU parity at more than 8 query heads per KV head (9 to 16: e.g. 96 or 128
+query heads over 8 KV heads; 24 to 64: attention with one or two KV heads).  The library steps such a group in blocks of at
 most 8 heads, one launch each on the caller's stream; every block reads the
 ring's old row for the evicted key, and the last block alone writes the new row,
 the held value row and the ring position.  Each case checks the prefill freeze
@@ -25,9 +25,9 @@ def gpu_ready():
     yield
 
 
-def _wl(name, n_seq, n_kv, hpk, d, m, w, sink, T, steps, std, seed):
-    return W.Workload(name, n_seq, 1, n_kv, hpk, d, d, m, w, sink, T=T, steps=steps, q_std=std,
-                      k_std=std, seed=seed)
+def _wl(name, n_seq, n_kv, hpk, d, m, w, sink, T, steps, std, seed, dv=None):
+    return W.Workload(name, n_seq, 1, n_kv, hpk, d, d if dv is None else dv, m, w, sink, T=T,
+                      steps=steps, q_std=std, k_std=std, seed=seed)
 
 
 CASES = [
@@ -35,6 +35,10 @@ CASES = [
     _wl("h16_d64", 2, 2, 16, 64, 16, 32, 2, 200, 30, 1.0, 82),      # two blocks of 8
     _wl("h9_d128_w7", 2, 2, 9, 128, 32, 7, 2, 200, 30, 2.0, 83),    # 8 + 1 heads; no per-slot logits
     _wl("h13_d96_m64", 2, 2, 13, 96, 64, 256, 4, 600, 24, 1.0, 84), # 8 + 5 (placeholders), m = 64
+    _wl("h32_d128_kv1", 2, 1, 32, 128, 32, 64, 4, 300, 24, 2.0, 86),  # four blocks, one KV head
+    _wl("h64_d64_kv1", 2, 1, 64, 64, 16, 32, 2, 200, 20, 1.0, 87),    # eight blocks
+    _wl("h40_d128_w7", 2, 2, 40, 128, 32, 7, 2, 200, 20, 2.0, 88),    # five blocks; no per-slot logits
+    _wl("h24_d192", 2, 1, 24, 192, 32, 64, 4, 300, 20, 1.0, 89, dv=128),  # three blocks, keys wider than values
 ]
 
 

@@ -2,7 +2,7 @@
 the head width, the landmark budget, window, sinks, prompt length, rectifier,
 input scale and group counts within the compiled limits (d = dv in {64, 96, 128, 256},
 or d = 192 with dv = 128,
-hpk <= 16, m <= 64, sink + w <= 1024 with hpk' * (sink + w) * 8 <= 32 KB for hpk'
+hpk <= 64, m <= 64, sink + w <= 1024 with hpk' * (sink + w) * 8 <= 32 KB for hpk'
 min(hpk, 8) rounded up to a power of two),
 then checks the prefill freeze and the decode steps against the oracle exactly
 as the fixed-shape tests do."""
@@ -64,6 +64,8 @@ CASES += [draw(i, widths=(256,), base=7400) for i in range(3)]
 CASES += [draw(10 + i, widths=(64, 96, 128), base=7300, min_hpk=9, max_hpk=16) for i in range(4)]
 # keys of 192 floats with values of 128, 1 to 16 heads
 CASES += [draw(10 + i, widths=(192,), base=7500, max_hpk=16) for i in range(4)]
+# 17 to 64 heads per group (three to eight blocks)
+CASES += [draw(10 + i, widths=(64, 128), base=7600, min_hpk=17, max_hpk=64) for i in range(2)]
 
 
 @pytest.mark.parametrize("wl,rect", CASES,
