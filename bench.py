@@ -219,7 +219,11 @@ def decode_roofline(wl, us_per_launch, traffic=None) -> dict:
            "traffic_unit": "bytes per launch", "bytes_per_launch": alg,
            "bytes_per_group_step": alg / G,
            "kernel_bytes_per_group_step": kern / G,
-           "kernel_GBps": kern / t / 1e9, "kernel_frac": kern / t / 1e9 / HBM_PEAK_GBS}
+           "kernel_GBps": kern / t / 1e9, "kernel_frac": kern / t / 1e9 / HBM_PEAK_GBS,
+           "basis": "achieved/frac: the per-eviction step's algorithmic bytes (every state value read once, "
+                    "its modified part written once, each step); this kernel moves fewer (T^ written and "
+                    "q~ read once per fold period), so frac can pass 1 where those dominate; kernel_*: this "
+                    "kernel's own algorithmic bytes; dram_*: HBM bytes from the rocprofv3 counters"}
     if traffic:
         res["dram_GBps"] = traffic / t / 1e9
         res["dram_frac"] = traffic / t / 1e9 / HBM_PEAK_GBS
