@@ -115,8 +115,8 @@ struct DecodeShape {
     static_assert(RED_H >= 1 && HPK % RED_H == 0, "heads must split into reduction rounds");
     static_assert(RL >= kPend, "each held value row needs a row lane of its own");
     static_assert((kPend - 1) * VCH <= NT, "one held value float4 per thread");
-    static_assert(HPK * CH <= NT && HPK * MM <= NT && 128 + VCH <= NT,
-                  "the prologue loads at most one element of each kind per thread (but the fold's keys)");
+    static_assert(HPK * MM <= NT && 128 + VCH <= NT,
+                  "the prologue loads at most one element of each kind per thread (but queries and the fold's keys)");
 };
 
 template <int D, int DV, int HPK, int MM, int NT, bool STREAM, bool PART>
@@ -208,15 +208,22 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         // one round trip (each thread has at most one element of each kind,
         // a few of M)
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        const bool q_mine = tid < H * C::CH, q_slot = tid < HPK * C::CH, k_mine = tid < C::CH;
+        // the block's queries, QP float4 per thread (placeholder heads: zero)
+        constexpr int QP = (HPK * C::CH + NT - 1) / NT;
+        const bool k_mine = tid < C::CH;
         const bool v_mine = tid >= 128 && tid < 128 + C::VCH, st_mine = tid < H * m;
         // on a fold with ring logits, the keys that arrived since the last
         // fold (ring slots e-1 .. e-kPend+1): KBP float4 per thread
         constexpr int KBP = ((kPend - 1) * C::CH + NT - 1) / NT;
         const bool kb_fold = ring && fold;
         float4 kbv[KBP];
-        float4 qv = z4, kin = z4, kev = z4, vin = z4, vev = z4;
-        if (q_mine) qv = qg[tid];
+        float4 qv[QP], kin = z4, kev = z4, vin = z4, vev = z4;
+#pragma unroll
+        for (int u = 0; u < QP; ++u) {
+            const int i = tid + u * NT;
+            qv[u] = z4;
+            if (i < H * C::CH) qv[u] = qg[i];
+        }
         if (k_mine) {
             kin = reinterpret_cast<const float4 *>(io.k)[(size_t)ci * C::CH + tid];
             if (!ring) kev = nk[(size_t)slot_row * C::CH + tid];
@@ -261,7 +268,9 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
                 for (int k = 0; k < C::CPL; ++k) xh[u][k] = ld4<C::NTL>(row + sub + C::LPR * k);
             }
         }
-        if (q_slot) (&q_s[0][0])[tid] = qv;  // placeholder heads: zero
+#pragma unroll
+        for (int u = 0; u < QP; ++u)
+            if (tid + u * NT < HPK * C::CH) (&q_s[0][0])[tid + u * NT] = qv[u];
         if (k_mine) {
             kn_s[tid] = kin;
             if (!ring) ke_s[tid] = kev;
@@ -1031,9 +1040,8 @@ template <int D, int DV, int HPK, int MM, bool PART>
 hipError_t launch_nt(const DevState &s, const DecodeIO &io, hipStream_t stream)
 {
     const bool big = s.stream_state != 0;
-    // (value rows wider than 128 floats: 512 threads keep a row lane per held
-    // slot; and one query float4 per thread in the prologue)
-    if constexpr (HPK * MM < 512 && DV <= 128 && HPK * (D / 4) <= 256) {
+    // (value rows wider than 128 floats: 512 threads keep a row lane per held slot)
+    if constexpr (HPK * MM < 512 && DV <= 128) {
         if (io.map.count >= kSmallGrid) return launch_shape<D, DV, HPK, MM, 256, true, PART>(s, io, stream);
     }
     if (big) return launch_shape<D, DV, HPK, MM, 512, true, PART>(s, io, stream);
