@@ -69,13 +69,13 @@ enum o1_rect { O1_RECT_AGGREGATE = 0, O1_RECT_FM = 1 };
 /* Geometry of a batch of groups (NystromState::new_group on the nystrom.rs
  * source page: m >= 4, w >= 1, q_heads >= 1).  Defaults on that page:
  * m = 32, w = 128, sink = 4, rect = AGGREGATE.
- * Compiled shapes: d == dv in {64, 96, 128, 256} or d = 192 with dv = 128 (keys
- * wider than values), hpk <= 64, m <= 64, sink + w <= 1024 with
- * hpk' * (sink + w) <= 4096, hpk' being min(hpk, 8) rounded up to a power of
- * two (the kernels for hpk' heads run the groups of hpk' / 2 < hpk <= hpk'
- * heads; a group of more than 8 heads is stepped in blocks of at most 8 heads,
- * one launch each, on the caller's stream); other valid shapes return
- * O1_EUNSUPPORTED.
+ * Compiled shapes: d == dv in {64, 80, 96, 128, 256} or d = 192 with dv = 128
+ * (keys wider than values), hpk <= 64, m <= 64, sink + w <= 1024 with
+ * hpk' * (sink + w) <= 4096, hpk' being min(hpk, B) rounded up to a power of
+ * two, B = 8 heads per block (4 at d = 80) (the kernels for hpk' heads run the
+ * groups of hpk' / 2 < hpk <= hpk' heads; a group of more than B heads is
+ * stepped in blocks of at most B heads, one launch each, on the caller's
+ * stream); other valid shapes return O1_EUNSUPPORTED.
  *
  * exact_cap sizes the exact-only mode (NystromGroup::prefill_shared on the
  * nystrom.rs source page): a prompt of T <= w + sink + 8 tokens builds no
@@ -327,7 +327,7 @@ int o1_write_field(o1_groups *g, int32_t field, const void *src, size_t bytes, v
 typedef struct o1_exact_desc {
     int32_t n_groups; /* G                                        (>= 1)      */
     int32_t hpk;      /* query heads per group                   1 .. 64     */
-    int32_t d, dv;    /* widths: d == dv in {64, 96, 128, 256}, or 192/128 */
+    int32_t d, dv;    /* widths: d == dv in {64, 80, 96, 128, 256}, or 192/128 */
     int32_t cap;      /* rows allocated per group (row stride of k and v)   */
     int32_t first;    /* earliest visible key, 0 <= first < n_keys          */
     int32_t n_keys;   /* keys 0 .. n_keys-1 are stored, n_keys <= cap       */

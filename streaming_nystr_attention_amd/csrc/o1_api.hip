@@ -363,9 +363,9 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
     const int m_cap = c.m < o1::kMaxLandmarks ? c.m : o1::kMaxLandmarks;
     if (!o1::decode_supported(c.d, c.dv, c.hpk, m_cap, R) || c.m > o1::kMaxLandmarks)
         return fail(O1_EUNSUPPORTED,
-                    "shape not compiled: needs d == dv in {64,96,128,256} or d = 192 with dv = 128, hpk <= %d, "
+                    "shape not compiled: needs d == dv in {64,80,96,128,256} or d = 192 with dv = 128, hpk <= %d, "
                     "m <= %d, sink + w "
-                    "<= 1024 with hpk'*(sink+w) <= 4096, hpk' = min(hpk, 8) rounded up to a power of two "
+                    "<= 1024 with hpk'*(sink+w) <= 4096, hpk' = min(hpk, 8 (4 at d = 80)) rounded up to a power of two "
                     "(got d=%d dv=%d hpk=%d m=%d sink+w=%d)",
                     o1::kMaxHeads, o1::kMaxLandmarks, c.d, c.dv, c.hpk, c.m, R);
 
@@ -750,7 +750,7 @@ static int exact_check(const o1_exact_desc *x, int *splits, size_t *bytes)
                     x->first, x->n_keys, x->cap);
     if (!o1::widths_compiled(x->d, x->dv) || x->hpk > o1::kMaxHeads)
         return fail(O1_EUNSUPPORTED,
-                    "o1_exact: compiled for d == dv in {64,96,128,256} or d = 192 with dv = 128, hpk <= %d",
+                    "o1_exact: compiled for d == dv in {64,80,96,128,256} or d = 192 with dv = 128, hpk <= %d",
                     o1::kMaxHeads);
     *splits = o1::exact_splits(x->n_groups, x->n_keys - x->first);
     *bytes = *splits == 1 ? 0

@@ -1067,8 +1067,12 @@ hipError_t launch_hpk(const DevState &s, const DecodeIO &io, hipStream_t stream)
     case 4: return launch_m<D, DV, 4>(s, io, stream);
     case 5:
     case 6:
-    case 7: return launch_m<D, DV, 8, true>(s, io, stream);
-    case 8: return launch_m<D, DV, 8>(s, io, stream);
+    case 7:
+        if constexpr (block_heads(D) >= 8) return launch_m<D, DV, 8, true>(s, io, stream);
+        return hipErrorInvalidValue;
+    case 8:
+        if constexpr (block_heads(D) >= 8) return launch_m<D, DV, 8>(s, io, stream);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -1133,7 +1137,8 @@ bool decode_supported(int d, int dv, int hpk, int m, int R)
     if (R < 1 || R > 1024) return false;
     // dynamic LDS for the near logits of the compiled head count (hpk rounded
     // up to a power of two) stays within 32 KB
-    const int hb = hpk < kMaxBlockHeads ? hpk : kMaxBlockHeads;  // heads of the largest block
+    const int bh = block_heads(d);
+    const int hb = hpk < bh ? hpk : bh;  // heads of the largest block
     const int hc = hb <= 1 ? 1 : hb <= 2 ? 2 : hb <= 4 ? 4 : 8;
     return (size_t)hc * R * sizeof(double) <= (size_t)kMaxDynLds;
 }
@@ -1141,18 +1146,20 @@ bool decode_supported(int d, int dv, int hpk, int m, int R)
 hipError_t launch_decode(const DevState &s, const DecodeIO &io_in, hipStream_t stream)
 {
     if (!decode_supported(s.d, s.dv, s.hpk, s.m, s.R)) return hipErrorInvalidValue;
-    // groups of more than kMaxBlockHeads heads: one launch per block of heads,
+    // groups of more heads than a block holds (block_heads): one launch per block,
     // in order on the stream; the last makes the group's shared writes
-    for (int h0 = 0; h0 < s.hpk; h0 += kMaxBlockHeads) {
+    const int bh = block_heads(s.d);
+    for (int h0 = 0; h0 < s.hpk; h0 += bh) {
         DecodeIO io = io_in;
         io.h0 = h0;
-        io.hb = min(kMaxBlockHeads, s.hpk - h0);
-        io.shared = h0 + kMaxBlockHeads >= s.hpk;
+        io.hb = min(bh, s.hpk - h0);
+        io.shared = h0 + bh >= s.hpk;
         hipError_t err;
         if (s.d == 64) err = launch_hpk<64, 64>(s, io, stream);
         else if (s.d == 96) err = launch_hpk<96, 96>(s, io, stream);
         else if (s.d == 256) err = launch_hpk<256, 256>(s, io, stream);
         else if (s.d == 192) err = launch_hpk<192, 128>(s, io, stream);
+        else if (s.d == 80) err = launch_hpk<80, 80>(s, io, stream);
         else err = launch_hpk<128, 128>(s, io, stream);
         if (err != hipSuccess) return err;
     }

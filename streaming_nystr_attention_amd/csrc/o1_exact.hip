@@ -395,7 +395,9 @@ hipError_t launch_exact_hpk(const ExactIO &a, int splits, hipStream_t stream)
     case 5:
     case 6:
     case 7:
-    case 8: return launch_exact_shape<D, DV, 8>(a, splits, stream);
+    case 8:
+        if constexpr (block_heads(D) >= 8) return launch_exact_shape<D, DV, 8>(a, splits, stream);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -449,21 +451,23 @@ int exact_splits(int G, int n_visible)
 
 hipError_t launch_exact(const ExactIO &in, int splits, hipStream_t stream)
 {
-    // groups of more than kMaxBlockHeads heads: one launch (and merge) per
+    // groups of more heads than a block holds (block_heads): one launch (and merge) per
     // block of heads, in order; the last stores the appended key and advances
     // the count, so every earlier block still reads the count it started from
-    for (int h0 = 0; h0 < in.hpk; h0 += kMaxBlockHeads) {
+    const int bh = block_heads(in.d);
+    for (int h0 = 0; h0 < in.hpk; h0 += bh) {
         ExactIO a = in;
         a.hg = in.hpk;
         a.h0 = h0;
-        a.hpk = min(kMaxBlockHeads, in.hpk - h0);
-        a.shared = h0 + kMaxBlockHeads >= in.hpk;
+        a.hpk = min(bh, in.hpk - h0);
+        a.shared = h0 + bh >= in.hpk;
         hipError_t err;
         if (a.d == 64 && a.dv == 64) err = launch_exact_hpk<64, 64>(a, splits, stream);
         else if (a.d == 96 && a.dv == 96) err = launch_exact_hpk<96, 96>(a, splits, stream);
         else if (a.d == 128 && a.dv == 128) err = launch_exact_hpk<128, 128>(a, splits, stream);
         else if (a.d == 256 && a.dv == 256) err = launch_exact_hpk<256, 256>(a, splits, stream);
         else if (a.d == 192 && a.dv == 128) err = launch_exact_hpk<192, 128>(a, splits, stream);
+        else if (a.d == 80 && a.dv == 80) err = launch_exact_hpk<80, 80>(a, splits, stream);
         else err = hipErrorInvalidValue;
         if (err != hipSuccess) return err;
     }

@@ -115,12 +115,21 @@ struct PromptView {
 constexpr int kMaxBlockHeads = 8;
 constexpr int kMaxHeads = 64;
 
-// Key and value widths the kernels are compiled for: d == dv in {64, 96, 128,
-// 256}, and keys of 192 floats with values of 128 (a head whose queries and
-// keys carry 64 more components than its values).
+// Heads per block at key width d: the row dots split a key row of d/4 float4
+// over a power-of-two number of lanes (at most 32 for 8 heads) that must be at
+// least the block's head count, so widths whose d/4 has a smaller power-of-two
+// factor (d = 80: 20 float4, four lanes of 5) take blocks of fewer heads.
+__host__ __device__ constexpr int block_heads(int d)
+{
+    return pow2_divisor(32, d / 4) < kMaxBlockHeads ? pow2_divisor(32, d / 4) : kMaxBlockHeads;
+}
+
+// Key and value widths the kernels are compiled for: d == dv in {64, 80, 96,
+// 128, 256}, and keys of 192 floats with values of 128 (a head whose queries
+// and keys carry 64 more components than its values).
 constexpr bool widths_compiled(int d, int dv)
 {
-    return (d == dv && (d == 64 || d == 96 || d == 128 || d == 256)) || (d == 192 && dv == 128);
+    return (d == dv && (d == 64 || d == 80 || d == 96 || d == 128 || d == 256)) || (d == 192 && dv == 128);
 }
 
 struct DecodeIO {
@@ -153,7 +162,7 @@ struct ExactIO {
     float *out;              // [count][hpk][dv]
     GroupMap map;
     int hpk, d, dv, cap, first, n_keys, per_split;
-    // Set by launch_exact, which runs a group of more than kMaxBlockHeads heads
+    // Set by launch_exact, which runs a group of more heads than block_heads(d)
     // in blocks: the kernels then see hpk = the block's heads, hg = the
     // group's (the stride of q and out), h0 = the block's first head, and
     // shared = 1 for the last block only, which alone stores the appended

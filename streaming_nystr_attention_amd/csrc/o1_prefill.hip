@@ -767,6 +767,7 @@ hipError_t launch_prefill(const DevState &s, const PrefillIO &io, hipStream_t st
     if (s.d == 256 && s.dv == 256) return launch_far_m<256, 256>(s, io, stream);
     if (s.d == 64 && s.dv == 64) return launch_far_m<64, 64>(s, io, stream);
     if (s.d == 192 && s.dv == 128) return launch_far_m<192, 128>(s, io, stream);
+    if (s.d == 80 && s.dv == 80) return launch_far_m<80, 80>(s, io, stream);
     return hipErrorInvalidValue;
 }
 
@@ -792,6 +793,8 @@ hipError_t launch_ring_logits(const DevState &s, const GroupMap &map, hipStream_
     }
     if (s.d == 64)
         hipLaunchKernelGGL(ring_logits_kernel<64>, grid, dim3(256), lds, stream, s, map, hb);
+    else if (s.d == 80)
+        hipLaunchKernelGGL(ring_logits_kernel<80>, grid, dim3(256), lds, stream, s, map, hb);
     else if (s.d == 96)
         hipLaunchKernelGGL(ring_logits_kernel<96>, grid, dim3(256), lds, stream, s, map, hb);
     else if (s.d == 128)

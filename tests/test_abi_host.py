@@ -92,7 +92,7 @@ def _create(P, L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(m=3), 1), (dict(w=0), 1), (dict(hpk=0), 1), (dict(sink=-1), 1), (dict(d=0), 1),
     (dict(dv=0), 1), (dict(n_seq=0), 1), (dict(n_layer=0), 1), (dict(n_kv=0), 1), (dict(rect=7), 1),
-    (dict(d=80, dv=80), 6), (dict(d=512, dv=512), 6), (dict(hpk=65), 6),
+    (dict(d=72, dv=72), 6), (dict(d=512, dv=512), 6), (dict(hpk=65), 6),
     (dict(m=65), 6),
     (dict(d=64, dv=128), 6), (dict(d=96, dv=64), 6),
     (dict(d=192, dv=192), 6), (dict(d=128, dv=192), 6), (dict(d=192, dv=64), 6),
@@ -139,7 +139,7 @@ def test_exact_comparator_validation_without_device():
     n = ctypes.c_size_t()
     good = dict(n_groups=4, hpk=2, d=128, dv=128, cap=100, first=0, n_keys=100, scale=0.0)
     for kw, code in [(dict(first=100), 1), (dict(n_keys=101), 1), (dict(first=-1), 1),
-                     (dict(n_groups=0), 1), (dict(hpk=65), 6), (dict(d=80, dv=80), 6),
+                     (dict(n_groups=0), 1), (dict(hpk=65), 6), (dict(d=72, dv=72), 6),
                      (dict(dv=64), 6), (dict(d=192, dv=192), 6), (dict(d=128, dv=192), 6)]:
         args = {**good, **kw}
         desc = P.o1_exact_desc(*[args[f] for f, _ in P.o1_exact_desc._fields_])

@@ -1,6 +1,6 @@
 """GPU parity at seeded random shapes: each case draws the query heads per group,
 the head width, the landmark budget, window, sinks, prompt length, rectifier,
-input scale and group counts within the compiled limits (d = dv in {64, 96, 128, 256},
+input scale and group counts within the compiled limits (d = dv in {64, 80, 96, 128, 256},
 or d = 192 with dv = 128,
 hpk <= 64, m <= 64, sink + w <= 1024 with hpk' * (sink + w) * 8 <= 32 KB for hpk'
 min(hpk, 8) rounded up to a power of two),
@@ -66,6 +66,8 @@ CASES += [draw(10 + i, widths=(64, 96, 128), base=7300, min_hpk=9, max_hpk=16) f
 CASES += [draw(10 + i, widths=(192,), base=7500, max_hpk=16) for i in range(4)]
 # 17 to 64 heads per group (three to eight blocks)
 CASES += [draw(10 + i, widths=(64, 128), base=7600, min_hpk=17, max_hpk=64) for i in range(2)]
+# d = 80 (blocks of at most 4 heads), 1 to 12 heads
+CASES += [draw(10 + i, widths=(80,), base=7700, max_hpk=12) for i in range(3)]
 
 
 @pytest.mark.parametrize("wl,rect", CASES,
