@@ -205,8 +205,8 @@ __global__ __launch_bounds__(NT, (DecodeShape<D, DV, HPK, MM, NT, STREAM>::MIN_W
         }
         const float4 *qg = reinterpret_cast<const float4 *>(io.q) + ((size_t)ci * HG + h0) * C::CH;
         // every load is issued before any is stored, so the prologue costs
-        // one round trip (each thread has at most one element of each kind,
-        // a few of M)
+        // one round trip (each thread has at most one element of most kinds;
+        // a few of M, and of the queries and the fold's keys at wide rows)
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
         // the block's queries, QP float4 per thread (placeholder heads: zero)
         constexpr int QP = (HPK * C::CH + NT - 1) / NT;
