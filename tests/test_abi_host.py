@@ -109,6 +109,22 @@ def test_create_rejects_before_touching_the_device(kw, code):
     assert P.o1_last_error()
 
 
+@pytest.mark.parametrize("kw", [
+    dict(d=80, dv=80, hpk=5, w=1020, sink=4),     # blocks of 4 heads: 4 * 1024 near logits fit 32 KB
+    dict(d=192, dv=128, hpk=64, m=32, w=128, sink=4),
+    dict(d=256, dv=256, hpk=2, m=64, w=128, sink=4),
+    dict(d=96, dv=96, hpk=13, m=64, w=256, sink=4),
+])
+def test_create_passes_the_shape_checks_of_compiled_shapes(kw):
+    # Without a GPU the creation fails later, at the device (O1_EHIP / O1_ENOMEM);
+    # with one it succeeds.  Either way the shape checks let it through.
+    P, L = _lib()
+    rc, h = _create(P, L, **kw)
+    if rc == 0:
+        L.o1_destroy_groups(h)
+    assert rc not in (P.O1_EINVAL, P.O1_EUNSUPPORTED), (kw, rc, P.o1_last_error())
+
+
 def test_null_arguments_are_rejected():
     P, L = _lib()
     assert L.o1_create_groups(None, None) == P.O1_EINVAL
