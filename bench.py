@@ -453,6 +453,71 @@ def per_layer_mode(wl, n_tokens, dev):
         return {"error": str(exc)[:200]}
 
 
+# Decode at common model shapes (--model-shapes): (name, n_seq, n_layer, n_kv, hpk, d, dv, m); the
+# stack's window, sinks and 256-token prompts, batches that put 2 816 - 16 384 groups in one launch.
+MODEL_SHAPES = [
+    ("hpk2_d128", 64, 28, 8, 2, 128, 128, 32),
+    ("hpk4_d128", 32, 32, 8, 4, 128, 128, 32),
+    ("hpk5_d128", 32, 28, 8, 5, 128, 128, 32),
+    ("hpk7_d128", 64, 28, 4, 7, 128, 128, 32),
+    ("hpk8_d128", 16, 32, 8, 8, 128, 128, 32),
+    ("hpk3_d128", 64, 28, 8, 3, 128, 128, 32),
+    ("hpk12_d128", 16, 24, 8, 12, 128, 128, 32),
+    ("hpk16_d128", 16, 16, 8, 16, 128, 128, 32),
+    ("hpk2_d64", 64, 16, 16, 2, 64, 64, 32),
+    ("hpk4_d64", 64, 16, 8, 4, 64, 64, 32),
+    ("hpk7_d64", 64, 24, 2, 7, 64, 64, 32),
+    ("hpk8_d64", 32, 22, 4, 8, 64, 64, 32),
+    ("hpk1_d80", 16, 32, 32, 1, 80, 80, 32),
+    ("hpk4_d80", 32, 32, 8, 4, 80, 80, 32),
+    ("hpk1_d96", 16, 32, 32, 1, 96, 96, 32),
+    ("hpk1_d192_v128", 16, 27, 16, 1, 192, 128, 32),
+    ("hpk2_d192_v128", 64, 28, 8, 2, 192, 128, 32),
+    ("hpk8_d192_v128", 16, 32, 8, 8, 192, 128, 32),
+    ("hpk2_d256", 32, 42, 8, 2, 256, 256, 32),
+]
+
+
+def model_shapes(dev, n_steps, only=None):
+    """One JSON line per model shape: prefill, then n_steps decode launches twice
+    (the first pass warms up), the second timed with HIP events."""
+    import torch
+
+    import streaming_nystr_attention_amd as P
+    from streaming_nystr_attention_amd import workloads as W
+
+    base = W.WORKLOADS["qwen3_stack_b64"]
+    for name, ns, nl, nkv, hpk, d, dv, m in MODEL_SHAPES:
+        if only and not any(o in name for o in only):
+            continue
+        wl = base.with_(name=name, n_seq=ns, n_layer=nl, n_kv=nkv, hpk=hpk, d=d, dv=dv, m=m,
+                        layer_scale=None, T=256)
+        G = wl.groups
+        q, k, v = W.prompt(wl, dev)
+        Q = torch.empty(n_steps, G, hpk, d, device=dev)
+        K = torch.empty(n_steps, G, d, device=dev)
+        V = torch.empty(n_steps, G, dv, device=dev)
+        for t in range(n_steps):
+            W.decode_inputs(wl, t, dev, out=(Q[t], K[t], V[t]))
+        out = torch.empty(G, hpk, dv, device=dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        with P.O1Groups(wl.config) as grp:
+            for timed in (False, True):
+                grp.prefill(q, k, v)
+                e[0].record()
+                for t in range(n_steps):
+                    grp.step(Q[t], K[t], V[t], out)
+                e[1].record()
+            torch.cuda.synchronize()
+        us = e[0].elapsed_time(e[1]) * 1e3 / n_steps
+        r = decode_roofline(wl, us)
+        print(json.dumps({"shape": name, "groups": G, "hpk": hpk, "d": d, "dv": dv, "m": m,
+                          "us_per_launch": us, "frac": r["frac"], "kernel_frac": r["kernel_frac"]}),
+              flush=True)
+        del q, k, v, Q, K, V, out
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -477,6 +542,9 @@ def main():
                     help="also time this many tokens stepped one layer at a time (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (for HBM counter scaling)")
+    ap.add_argument("--model-shapes", default=None, metavar="SUBSTRINGS",
+                    help="instead of the bench line: decode timing at common model shapes "
+                         "('all', or comma-separated name substrings)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -496,6 +564,10 @@ def main():
         sys.exit(1)
     P.lib()  # fails loudly when the HIP library is missing
     dev = "cuda"
+    if args.model_shapes:
+        only = None if args.model_shapes == "all" else args.model_shapes.split(",")
+        model_shapes(dev, args.decode_steps or 32, only)
+        return
     wl = W.WORKLOADS[args.workload]
     n_dec = args.decode_steps or wl.steps
     G, H = wl.groups, wl.hpk
