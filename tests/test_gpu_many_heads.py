@@ -6,6 +6,8 @@ the held value row and the ring position.  Each case checks the prefill freeze
 and every decode step against the oracle as the fixed-shape tests do, on both
 launch paths (512-thread work-groups for small grids, 256-thread ones from 1024
 groups up, where 8-head blocks run two heads per wave)."""
+import gc
+
 import pytest
 import torch
 
@@ -55,3 +57,46 @@ def test_many_heads_large_grid_sampled():
     sample = W.groups_of_sequences(wl, W.sample_sequences(wl))
     prefill_parity(wl, sample=sample)
     decode_parity(wl, sample=sample)
+
+
+@pytest.mark.parametrize("hpk,d", [(12, 128), (6, 80)], ids=["h12_d128", "h6_d80"])
+def test_graph_replay_of_head_block_steps_matches_eager(hpk, d):
+    """A whole-handle step of a group stepped in head blocks (8 + 4 heads at
+    d = 128, 4 + 2 at d = 80) captured in a HIP graph and replayed, with eager
+    input copies and synchronisation between the replays; every replay must
+    equal the eager steps of a twin handle, and so must the state after."""
+    wl = _wl(f"graph_h{hpk}_d{d}", 2, 2, hpk, d, 16, 32, 4, 120, 2 * 8 + 3, 2.0, 90 + hpk)
+    G = wl.groups
+    q, k, v = W.prompt(wl, "cuda")
+    qs = torch.empty(wl.steps, G, hpk, d, device="cuda")
+    ks = torch.empty(wl.steps, G, d, device="cuda")
+    vs = torch.empty(wl.steps, G, d, device="cuda")
+    for t in range(wl.steps):
+        W.decode_inputs(wl, t, "cuda", out=(qs[t], ks[t], vs[t]))
+    eager, graphed = P.O1Groups(wl.config), P.O1Groups(wl.config)
+    eager.prefill(q, k, v)
+    graphed.prefill(q, k, v)
+    sq, sk, sv = torch.empty_like(qs[0]), torch.empty_like(ks[0]), torch.empty_like(vs[0])
+    out_g = torch.empty(G, hpk, d, device="cuda")
+    out_e = torch.empty_like(out_g)
+    with P.O1Groups(wl.config) as warm:  # first launches of these kernels outside the capture
+        warm.prefill(q, k, v)
+        warm.step(qs[0], ks[0], vs[0], out_e)
+        torch.cuda.synchronize()
+    gc.collect()  # finalise leftover objects now: destroying a graph during a capture aborts
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graphed.step(sq, sk, sv, out_g)
+    for t in range(wl.steps):  # more than two fold periods
+        eager.step(qs[t], ks[t], vs[t], out_e)
+        sq.copy_(qs[t])
+        sk.copy_(ks[t])
+        sv.copy_(vs[t])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), t
+    for f in (P.FIELD_NEAR_K, P.FIELD_NEAR_V, P.FIELD_T_HAT, P.FIELD_Z_HAT, P.FIELD_M_MAX,
+              P.FIELD_WIN_HEAD, P.FIELD_FAR_LEN):
+        assert torch.equal(graphed.read(f, "cuda"), eager.read(f, "cuda")), f
+    eager.close()
+    graphed.close()
