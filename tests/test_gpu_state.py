@@ -26,8 +26,14 @@ WL = W.Workload("state", 2, 1, 3, 2, 128, 128, 16, 32, 4, T=180, steps=40, q_std
                 seed=31)
 
 
-def test_field_roundtrip_bit_exact():
-    wl = WL
+# keys wider than values: every field's size follows its own width
+WL192 = W.Workload("state_d192", 2, 1, 3, 3, 192, 128, 16, 32, 4, T=180, steps=40, q_std=2.0, k_std=2.0,
+                   seed=32)
+
+
+@pytest.mark.parametrize("wl", [WL, WL192], ids=["d128", "d192_dv128"])
+def test_field_roundtrip_bit_exact(wl):
+    G, H, m, R = wl.groups, wl.hpk, wl.m_eff, wl.sink + wl.w
     q, k, v = W.prompt(wl, DEV)
     grp = P.O1Groups(wl.config)
     grp.prefill(q, k, v)
@@ -43,6 +49,12 @@ def test_field_roundtrip_bit_exact():
     with pytest.raises(P.O1Error) as e:
         grp.write(P.FIELD_T_HAT, torch.zeros(3, device=DEV))
     assert e.value.status == P.O1_EINVAL
+    # element counts: key-width fields d wide, value-width fields dv wide
+    sizes = {P.FIELD_NEAR_K: G * R * wl.d, P.FIELD_NEAR_V: G * R * wl.dv, P.FIELD_K_TILDE: G * m * wl.d,
+             P.FIELD_Q_TILDE: G * H * m * wl.d, P.FIELD_T_HAT: G * H * m * wl.dv, P.FIELD_MU: G * H * m * m}
+    for field, n in sizes.items():
+        assert grp.read(field, device=DEV).numel() == n, field
+    grp.close()
 
 
 def test_decode_from_uploaded_oracle_far_field():
