@@ -57,11 +57,11 @@ def test_field_roundtrip_bit_exact(wl):
     grp.close()
 
 
-def test_decode_from_uploaded_oracle_far_field():
+@pytest.mark.parametrize("wl", [WL, WL192], ids=["d128", "d192_dv128"])
+def test_decode_from_uploaded_oracle_far_field(wl):
     """Decode parity with the whole far field (T^, Z^, running max) taken from
     the oracle's sequential replay, so the decode kernel is checked apart from
     the prefill's far-field kernel."""
-    wl = WL
     G, H, m = wl.groups, wl.hpk, wl.m_eff
     q, k, v = W.prompt(wl, DEV)
     orc = oracle_prefill(wl, cpu(q), cpu(k), cpu(v))
