@@ -70,7 +70,7 @@ enum o1_rect { O1_RECT_AGGREGATE = 0, O1_RECT_FM = 1 };
  * source page: m >= 4, w >= 1, q_heads >= 1).  Defaults on that page:
  * m = 32, w = 128, sink = 4, rect = AGGREGATE.
  * Compiled shapes: d == dv in {64, 80, 96, 128, 256} or d = 192 with dv = 128
- * (keys wider than values), hpk <= 64, m <= 64, sink + w <= 1024 with
+ * (keys wider than values), hpk <= 64, m <= 64, sink + w <= 4096 with
  * hpk' * (sink + w) <= 4096, hpk' being min(hpk, B) rounded up to a power of
  * two, B = 8 heads per block (4 at d = 80) (the kernels for hpk' heads run the
  * groups of hpk' / 2 < hpk <= hpk' heads; a group of more than B heads is

@@ -365,7 +365,7 @@ int o1_create_groups(const o1_config *cfg, o1_groups **out)
         return fail(O1_EUNSUPPORTED,
                     "shape not compiled: needs d == dv in {64,80,96,128,256} or d = 192 with dv = 128, hpk <= %d, "
                     "m <= %d, sink + w "
-                    "<= 1024 with hpk'*(sink+w) <= 4096, hpk' = min(hpk, 8 (4 at d = 80)) rounded up to a power of two "
+                    "<= 4096 with hpk'*(sink+w) <= 4096, hpk' = min(hpk, 8 (4 at d = 80)) rounded up to a power of two "
                     "(got d=%d dv=%d hpk=%d m=%d sink+w=%d)",
                     o1::kMaxHeads, o1::kMaxLandmarks, c.d, c.dv, c.hpk, c.m, R);
 

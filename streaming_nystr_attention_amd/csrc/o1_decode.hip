@@ -1134,9 +1134,10 @@ bool decode_supported(int d, int dv, int hpk, int m, int R)
     if (!widths_compiled(d, dv)) return false;
     if (hpk < 1 || hpk > kMaxHeads) return false;
     if (m < 4 || m > kMaxLandmarks) return false;
-    if (R < 1 || R > 1024) return false;
+    if (R < 1 || R > 4096) return false;
     // dynamic LDS for the near logits of the compiled head count (hpk rounded
-    // up to a power of two) stays within 32 KB
+    // up to a power of two) stays within 32 KB: sink + w up to 4096 at one
+    // head per block, 2048 at two, 1024 at four, 512 at eight
     const int bh = block_heads(d);
     const int hb = hpk < bh ? hpk : bh;  // heads of the largest block
     const int hc = hb <= 1 ? 1 : hb <= 2 ? 2 : hb <= 4 ? 4 : 8;

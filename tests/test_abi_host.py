@@ -98,7 +98,7 @@ def _create(P, L, **kw):
     (dict(d=192, dv=192), 6), (dict(d=128, dv=192), 6), (dict(d=192, dv=64), 6),
     (dict(hpk=5, w=596, sink=4), 6),  # run as 8 heads: 8 * 600 near logits pass 32 KB
     (dict(hpk=12, w=596, sink=4), 6),  # blocks of 8 and 4 heads: the 8-head block's logits pass 32 KB
-    (dict(w=2000), 6), (dict(exact_cap=-1), 1), (dict(n_seq=1 << 20, exact_cap=1 << 22), 1),
+    (dict(w=4095), 6), (dict(hpk=2, w=2040, sink=9), 6), (dict(exact_cap=-1), 1), (dict(n_seq=1 << 20, exact_cap=1 << 22), 1),
     (dict(ridge_rel=-1e-6), 1), (dict(ridge_rel=float("inf")), 1), (dict(ridge_rel=float("nan")), 1),
 ])
 def test_create_rejects_before_touching_the_device(kw, code):
@@ -114,6 +114,8 @@ def test_create_rejects_before_touching_the_device(kw, code):
     dict(d=192, dv=128, hpk=64, m=32, w=128, sink=4),
     dict(d=256, dv=256, hpk=2, m=64, w=128, sink=4),
     dict(d=96, dv=96, hpk=13, m=64, w=256, sink=4),
+    dict(d=128, dv=128, hpk=1, m=32, w=4092, sink=4),   # one head: 4096 near logits fit 32 KB
+    dict(d=64, dv=64, hpk=2, m=32, w=2040, sink=8),
 ])
 def test_create_passes_the_shape_checks_of_compiled_shapes(kw):
     # Without a GPU the creation fails later, at the device (O1_EHIP / O1_ENOMEM);
